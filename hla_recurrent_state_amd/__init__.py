@@ -1,0 +1,211 @@
+"""Python binding of the ready.h C ABI (libready.so, gfx950).
+
+Argument marshalling only: every step of the state reader runs in the HIP
+kernels of libready.so.  If the library is missing, loading raises
+ReadyError -- there is no fallback path.
+
+Low-level names mirror the C functions (readyPlanCreate, readyWorkspaceSize,
+readyStateReader, readyPlanDestroy, readyStatusString, readyVersion) and the C
+structs (readyShape, readyStates, readyWeights, readyOutputs).  StateReader
+wraps them for torch tensors: it forwards data_ptr() values and the current
+HIP stream.
+"""
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libready.so")
+SRC_DIR = os.path.join(_HERE, "csrc")
+INCLUDE_DIR = os.path.join(os.path.dirname(_HERE), "include")
+
+READY_OK = 0
+READY_ERR_NULL_POINTER = 1
+READY_ERR_BAD_SHAPE = 2
+READY_ERR_UNSUPPORTED_DTYPE = 3
+READY_ERR_MISALIGNED = 4
+READY_ERR_WORKSPACE_TOO_SMALL = 5
+READY_ERR_ALIASING = 6
+READY_ERR_LAYER_ID_RANGE = 7
+READY_ERR_HIP = 8
+READY_ERR_ACCEPT_IDX = 9
+READY_ERR_OUT_OF_HOST_MEMORY = 10
+
+READY_F32 = 0
+READY_BF16 = 1
+READY_ACT_SILU = 0
+READY_ACT_GELU_TANH = 1
+READY_ACT_RELU = 2
+
+DTYPES = {"f32": READY_F32, "bf16": READY_BF16}
+ACTS = {"silu": READY_ACT_SILU, "gelu_tanh": READY_ACT_GELU_TANH, "relu": READY_ACT_RELU}
+
+# Every symbol include/ready.h declares.
+EXPORTS = ("readyPlanCreate", "readyPlanDestroy", "readyWorkspaceSize", "readyStateReader",
+           "readyStatusString", "readyVersion")
+
+
+class ReadyError(RuntimeError):
+    def __init__(self, code, what=""):
+        self.code = code
+        name = readyStatusString(code) if _lib is not None else str(code)
+        super().__init__("%s%s" % (name, (": " + what) if what else ""))
+
+
+class readyShape(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in
+                ("B", "P", "n", "L_tot", "L_sel", "H", "d_k", "d_v", "r", "d", "Hm",
+                 "state_dtype", "act_dtype", "weight_dtype", "act", "shared_params")] + \
+               [("state_eps", ctypes.c_float), ("h_eps", ctypes.c_float)]
+
+
+class readyStates(ctypes.Structure):
+    _fields_ = [("base", ctypes.c_void_p), ("stride_b", ctypes.c_int64), ("stride_p", ctypes.c_int64),
+                ("stride_l", ctypes.c_int64), ("stride_h", ctypes.c_int64)]
+
+
+class readyWeights(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in ("wq", "u", "v", "h_gamma", "w1", "b1", "w2", "b2")]
+
+
+class readyOutputs(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in ("gathered", "out", "logrms", "delta", "feat", "dev_status")]
+
+
+_lib = None
+
+
+def load():
+    """Load libready.so (raises ReadyError if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ReadyError(-1, "libready.so not built; run __graft_entry__.build()")
+    lib = ctypes.CDLL(LIB_PATH)
+    P = ctypes.POINTER
+    lib.readyPlanCreate.argtypes = [P(readyShape), P(ctypes.c_int32), P(ctypes.c_void_p)]
+    lib.readyPlanCreate.restype = ctypes.c_int
+    lib.readyPlanDestroy.argtypes = [ctypes.c_void_p]
+    lib.readyPlanDestroy.restype = ctypes.c_int
+    lib.readyWorkspaceSize.argtypes = [ctypes.c_void_p, P(ctypes.c_size_t)]
+    lib.readyWorkspaceSize.restype = ctypes.c_int
+    lib.readyStateReader.argtypes = [ctypes.c_void_p, P(readyStates), ctypes.c_void_p, ctypes.c_void_p,
+                                     P(readyWeights), P(readyOutputs), ctypes.c_void_p, ctypes.c_size_t,
+                                     ctypes.c_void_p]
+    lib.readyStateReader.restype = ctypes.c_int
+    lib.readyStatusString.argtypes = [ctypes.c_int]
+    lib.readyStatusString.restype = ctypes.c_char_p
+    lib.readyVersion.argtypes = []
+    lib.readyVersion.restype = ctypes.c_int32
+    _lib = lib
+    return lib
+
+
+# ------------------------------------------------------------ C-named calls
+
+def readyStatusString(code):
+    return load().readyStatusString(int(code)).decode()
+
+
+def readyVersion():
+    return load().readyVersion()
+
+
+def readyPlanCreate(shape, layer_ids):
+    """shape: readyShape; layer_ids: sequence of ints.  Returns (status, plan)."""
+    ids = (ctypes.c_int32 * max(1, len(layer_ids)))(*layer_ids)
+    plan = ctypes.c_void_p()
+    st = load().readyPlanCreate(ctypes.byref(shape), ids, ctypes.byref(plan))
+    return st, plan
+
+
+def readyPlanDestroy(plan):
+    return load().readyPlanDestroy(plan)
+
+
+def readyWorkspaceSize(plan):
+    """Returns (status, bytes)."""
+    n = ctypes.c_size_t()
+    st = load().readyWorkspaceSize(plan, ctypes.byref(n))
+    return st, n.value
+
+
+def readyStateReader(plan, states, accept_idx, h, weights, outputs, workspace, workspace_bytes, stream):
+    """Raw call: pointers are ints, structs are the ctypes mirrors.  Returns status."""
+    return load().readyStateReader(plan, ctypes.byref(states), accept_idx, h, ctypes.byref(weights),
+                                   ctypes.byref(outputs), workspace, workspace_bytes, stream)
+
+
+# ------------------------------------------------------------ torch wrapper
+
+def make_shape(B, P, n, L_tot, L_sel, H, r, d, Hm, state_dtype="bf16", act_dtype="bf16",
+               weight_dtype="bf16", act="silu", shared=False, state_eps=1e-6, h_eps=1e-6,
+               d_k=128, d_v=128):
+    return readyShape(B=B, P=P, n=n, L_tot=L_tot, L_sel=L_sel, H=H, d_k=d_k, d_v=d_v, r=r, d=d, Hm=Hm,
+                      state_dtype=DTYPES[state_dtype], act_dtype=DTYPES[act_dtype],
+                      weight_dtype=DTYPES[weight_dtype], act=ACTS[act], shared_params=int(bool(shared)),
+                      state_eps=state_eps, h_eps=h_eps)
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+class StateReader:
+    """A plan plus a call that takes torch tensors on the current device.
+
+    reader = StateReader(shape, layer_ids)
+    reader(states, accept_idx, h, weights, gathered, out, logrms=None,
+           delta=None, feat=None, dev_status=None, workspace=None)
+    `states` is a tensor [B][P][L_tot][H][128][128] (any outer strides with a
+    contiguous tile) and `weights` a dict with keys wq, u, v, w1, w2 and
+    optionally h_gamma, b1, b2.  Raises ReadyError on a non-zero status.
+    """
+
+    def __init__(self, shape, layer_ids):
+        self.shape = shape
+        self.layer_ids = list(layer_ids)
+        st, self.plan = readyPlanCreate(shape, self.layer_ids)
+        if st != READY_OK:
+            raise ReadyError(st, "readyPlanCreate")
+        st, self.workspace_bytes = readyWorkspaceSize(self.plan)
+        if st != READY_OK:
+            raise ReadyError(st, "readyWorkspaceSize")
+        self._ws = None
+
+    def close(self):
+        if getattr(self, "plan", None):
+            readyPlanDestroy(self.plan)
+            self.plan = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def workspace(self, device):
+        import torch
+        if self._ws is None or self._ws.device != torch.device(device):
+            self._ws = torch.empty(max(self.workspace_bytes, 256), dtype=torch.uint8, device=device)
+        return self._ws
+
+    def __call__(self, states, accept_idx, h, weights, gathered, out, logrms=None, delta=None,
+                 feat=None, dev_status=None, workspace=None, stream=None):
+        import torch
+        if states.dim() != 6:
+            raise ReadyError(READY_ERR_BAD_SHAPE, "states must be [B][P][L_tot][H][128][128]")
+        st = states.stride()
+        sd = readyStates(base=states.data_ptr(), stride_b=st[0], stride_p=st[1], stride_l=st[2],
+                         stride_h=st[3])
+        wd = readyWeights(**{k: _ptr(weights.get(k)) for k in ("wq", "u", "v", "h_gamma", "w1", "b1", "w2", "b2")})
+        od = readyOutputs(gathered=_ptr(gathered), out=_ptr(out), logrms=_ptr(logrms), delta=_ptr(delta),
+                          feat=_ptr(feat), dev_status=_ptr(dev_status))
+        if workspace is None:
+            workspace = self.workspace(h.device)
+        if stream is None:
+            stream = torch.cuda.current_stream(h.device).cuda_stream
+        code = readyStateReader(self.plan, sd, accept_idx.data_ptr(), h.data_ptr(), wd, od,
+                                workspace.data_ptr(), workspace.numel() * workspace.element_size(), stream)
+        if code != READY_OK:
+            raise ReadyError(code, "readyStateReader")

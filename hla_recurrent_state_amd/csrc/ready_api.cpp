@@ -1,0 +1,269 @@
+// Host side of the ready.h C ABI: argument validation, the plan (kernel
+// choices and workspace layout) and the launch sequence.
+//
+// The launch sequence for one call, on the caller's stream:
+//   1. k_gemm<EPI_PARTIAL>   z partial sums W_q (gamma*h) per K split, and the
+//                            partial sums of squares of h (RMSNorm of h).
+//   2. k_state               per (sequence, pair): gather, RMS, log-RMS,
+//                            T = V^T S_bar, q = U^T z, u = T q / sqrt(d_k),
+//                            packing into f.
+//   3. k_gemm<EPI_BIAS_ACT>  a = act(W1 f + b1).
+//   4. k_gemm<EPI_RESID>     out = h + W2 a + b2 (and Delta h).
+// Validation never touches the HIP runtime, so every argument error can be
+// exercised on a machine without a GPU.
+#include <stdlib.h>
+#include <string.h>
+
+#include <algorithm>
+#include <new>
+#include <vector>
+
+#include "ready_internal.h"
+
+struct readyPlan {
+  readyShape s;
+  int32_t slot[READY_MAX_LSEL];
+  int M, F, R, Mz, Nz;
+  int z_ksplit, z_kchunk;
+  size_t off_zpart, off_hss, off_f, off_a, off_flags, ws_bytes;
+};
+
+namespace {
+
+size_t dsize(int dt) { return dt == READY_BF16 ? 2 : 4; }
+bool dtype_ok(int dt) { return dt == READY_F32 || dt == READY_BF16; }
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+struct Range {
+  uintptr_t lo, hi;  // [lo, hi)
+  bool empty() const { return hi <= lo; }
+};
+Range range_of(const void* p, size_t bytes) { return Range{(uintptr_t)p, (uintptr_t)p + bytes}; }
+bool overlap(const Range& a, const Range& b) {
+  return !a.empty() && !b.empty() && a.lo < b.hi && b.lo < a.hi;
+}
+
+readyStatus validate_shape(const readyShape& s, const int32_t* layer_ids) {
+  if (!dtype_ok(s.state_dtype) || !dtype_ok(s.act_dtype) || !dtype_ok(s.weight_dtype))
+    return READY_ERR_UNSUPPORTED_DTYPE;
+  if (s.act != READY_ACT_SILU && s.act != READY_ACT_GELU_TANH && s.act != READY_ACT_RELU)
+    return READY_ERR_UNSUPPORTED_DTYPE;
+  if (s.B < 0 || s.P < 1 || s.P > 64 || s.n < 1 || s.n > 16) return READY_ERR_BAD_SHAPE;
+  if ((int64_t)s.B * s.n > (1 << 20)) return READY_ERR_BAD_SHAPE;
+  if (s.L_sel < 1 || s.L_sel > READY_MAX_LSEL || s.L_tot < 1 || s.H < 1) return READY_ERR_BAD_SHAPE;
+  if ((int64_t)s.L_sel * s.H > 4096) return READY_ERR_BAD_SHAPE;
+  if (s.d_k != READY_TILE || s.d_v != READY_TILE) return READY_ERR_BAD_SHAPE;
+  if (s.r < 8 || s.r > 128 || s.r % 8 != 0) return READY_ERR_BAD_SHAPE;
+  if (s.d < 8 || s.d % 8 != 0 || s.Hm < 1 || s.Hm > 4096) return READY_ERR_BAD_SHAPE;
+  if (s.shared_params != 0 && s.shared_params != 1) return READY_ERR_BAD_SHAPE;
+  if (!(s.state_eps >= 0.0f) || !(s.h_eps >= 0.0f)) return READY_ERR_BAD_SHAPE;
+  for (int l = 0; l < s.L_sel; ++l)
+    if (layer_ids[l] < 0 || layer_ids[l] >= s.L_tot) return READY_ERR_LAYER_ID_RANGE;
+  return READY_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t readyVersion(void) { return READY_VERSION; }
+
+const char* readyStatusString(readyStatus st) {
+  switch (st) {
+    case READY_OK: return "READY_OK";
+    case READY_ERR_NULL_POINTER: return "READY_ERR_NULL_POINTER";
+    case READY_ERR_BAD_SHAPE: return "READY_ERR_BAD_SHAPE";
+    case READY_ERR_UNSUPPORTED_DTYPE: return "READY_ERR_UNSUPPORTED_DTYPE";
+    case READY_ERR_MISALIGNED: return "READY_ERR_MISALIGNED";
+    case READY_ERR_WORKSPACE_TOO_SMALL: return "READY_ERR_WORKSPACE_TOO_SMALL";
+    case READY_ERR_ALIASING: return "READY_ERR_ALIASING";
+    case READY_ERR_LAYER_ID_RANGE: return "READY_ERR_LAYER_ID_RANGE";
+    case READY_ERR_HIP: return "READY_ERR_HIP";
+    case READY_ERR_ACCEPT_IDX: return "READY_ERR_ACCEPT_IDX";
+    case READY_ERR_OUT_OF_HOST_MEMORY: return "READY_ERR_OUT_OF_HOST_MEMORY";
+  }
+  return "READY_ERR_UNKNOWN";
+}
+
+readyStatus readyPlanCreate(const readyShape* shape, const int32_t* layer_ids, readyPlan** plan) {
+  if (!shape || !layer_ids || !plan) return READY_ERR_NULL_POINTER;
+  *plan = nullptr;
+  const readyShape& s = *shape;
+  if (s.L_sel < 1 || s.L_sel > READY_MAX_LSEL) return READY_ERR_BAD_SHAPE;
+  readyStatus st = validate_shape(s, layer_ids);
+  if (st != READY_OK) return st;
+  readyPlan* p = new (std::nothrow) readyPlan;
+  if (!p) return READY_ERR_OUT_OF_HOST_MEMORY;
+  memset(p, 0, sizeof(*p));
+  p->s = s;
+  for (int l = 0; l < s.L_sel; ++l) p->slot[l] = layer_ids[l];
+  p->M = s.L_sel * s.H;
+  p->F = p->M * (s.r + 1);
+  p->R = s.B * s.n;
+  p->Mz = s.shared_params ? 1 : p->M;
+  p->Nz = p->Mz * s.r;
+
+  // K split of the query GEMM: aim for about 512 workgroups in total, with
+  // every split a multiple of 128 columns of h.
+  const int64_t base_wgs = cdiv(p->Nz, READY_GEMM_COLS) * cdiv(std::max(p->R, 1), READY_GEMM_RB);
+  int64_t ks = std::max<int64_t>(1, cdiv(512, base_wgs));
+  ks = std::min<int64_t>(ks, cdiv(s.d, 128));
+  int64_t kchunk = align_up((size_t)cdiv(s.d, ks), 128);
+  ks = cdiv(s.d, kchunk);
+  p->z_ksplit = (int)ks;
+  p->z_kchunk = (int)kchunk;
+
+  const size_t R = (size_t)p->R;
+  size_t off = 0;
+  p->off_zpart = off; off = align_up(off + 4 * (size_t)ks * R * p->Nz, 256);
+  p->off_hss = off;   off = align_up(off + 4 * (size_t)ks * R, 256);
+  p->off_f = off;     off = align_up(off + 4 * R * p->F, 256);
+  p->off_a = off;     off = align_up(off + 4 * R * s.Hm, 256);
+  p->off_flags = off; off = align_up(off + 4 * (size_t)std::max(s.B, 1), 256);
+  p->ws_bytes = off;
+  *plan = p;
+  return READY_OK;
+}
+
+readyStatus readyPlanDestroy(readyPlan* plan) {
+  delete plan;
+  return READY_OK;
+}
+
+readyStatus readyWorkspaceSize(const readyPlan* plan, size_t* bytes) {
+  if (!plan || !bytes) return READY_ERR_NULL_POINTER;
+  *bytes = plan->ws_bytes;
+  return READY_OK;
+}
+
+readyStatus readyStateReader(const readyPlan* plan, const readyStates* states,
+                             const int32_t* accept_idx, const void* h,
+                             const readyWeights* w, const readyOutputs* o,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+  if (!plan || !states || !w || !o) return READY_ERR_NULL_POINTER;
+  const readyShape& s = plan->s;
+  if (!states->base || !accept_idx || !h || !w->wq || !w->u || !w->v || !w->w1 || !w->w2 ||
+      !o->gathered || !o->out || !workspace)
+    return READY_ERR_NULL_POINTER;
+  if (workspace_bytes < plan->ws_bytes) return READY_ERR_WORKSPACE_TOO_SMALL;
+
+  const size_t ss = dsize(s.state_dtype), as = dsize(s.act_dtype), ws = dsize(s.weight_dtype);
+  // alignment: 16 bytes for everything read or written with vector accesses
+  const void* vec_ptrs[] = {states->base, h, w->wq, w->u, w->v, w->w1, w->w2, o->gathered, o->out};
+  for (const void* ptr : vec_ptrs)
+    if (ptr && !aligned16(ptr)) return READY_ERR_MISALIGNED;
+  if (((uintptr_t)workspace & 255u) != 0) return READY_ERR_MISALIGNED;
+  const int64_t strides[4] = {states->stride_b, states->stride_p, states->stride_l, states->stride_h};
+  for (int64_t st : strides) {
+    if (st < 0) return READY_ERR_BAD_SHAPE;
+    if ((st * (int64_t)ss) % 16 != 0) return READY_ERR_MISALIGNED;
+  }
+
+  // address ranges for the aliasing rules
+  const size_t M = plan->M, R = plan->R, F = plan->F, Hm = s.Hm, d = s.d;
+  const int64_t span = s.B == 0 ? 0 :
+                       (int64_t)(s.B - 1) * states->stride_b + (int64_t)(s.P - 1) * states->stride_p +
+                       (int64_t)(s.L_tot - 1) * states->stride_l + (int64_t)(s.H - 1) * states->stride_h +
+                       READY_TILE_ELEMS;
+  const Range r_states = range_of(states->base, (size_t)span * ss);
+  const Range r_gath = range_of(o->gathered, (size_t)s.B * M * READY_TILE_ELEMS * ss);
+  const Range r_h = range_of(h, R * d * as);
+  const Range r_out = range_of(o->out, R * d * as);
+  const Range r_ws = range_of(workspace, plan->ws_bytes);
+  const Range r_acc = range_of(accept_idx, (size_t)s.B * 4);
+  const size_t mz = s.shared_params ? 1 : M;
+  const Range inputs[] = {
+      r_states, r_acc,
+      range_of(w->wq, mz * s.r * d * ws), range_of(w->u, mz * s.r * READY_TILE * ws),
+      range_of(w->v, mz * READY_TILE * s.r * ws), range_of(w->h_gamma, w->h_gamma ? d * ws : 0),
+      range_of(w->w1, Hm * F * ws), range_of(w->b1, w->b1 ? Hm * ws : 0),
+      range_of(w->w2, d * Hm * ws), range_of(w->b2, w->b2 ? d * ws : 0)};
+  const Range outputs[] = {r_gath, r_out, range_of(o->logrms, o->logrms ? (size_t)s.B * M * 4 : 0),
+                           range_of(o->delta, o->delta ? R * d * 4 : 0),
+                           range_of(o->feat, o->feat ? R * F * 4 : 0),
+                           range_of(o->dev_status, o->dev_status ? 4 : 0), r_ws};
+  const int n_out = (int)(sizeof(outputs) / sizeof(outputs[0]));
+  for (int i = 0; i < n_out; ++i) {
+    for (const Range& in : inputs)
+      if (overlap(outputs[i], in)) return READY_ERR_ALIASING;
+    for (int j = i + 1; j < n_out; ++j)
+      if (overlap(outputs[i], outputs[j])) return READY_ERR_ALIASING;
+  }
+  // out may be h itself (in place); any other overlap with h is an error
+  if (o->out != h && overlap(r_out, r_h)) return READY_ERR_ALIASING;
+  for (int i = 0; i < n_out; ++i)
+    if (i != 1 && overlap(outputs[i], r_h)) return READY_ERR_ALIASING;
+
+  if (s.B == 0) return READY_OK;
+
+  hipStream_t strm = (hipStream_t)stream;
+  char* wsb = (char*)workspace;
+  float* zpart = (float*)(wsb + plan->off_zpart);
+  float* hss = (float*)(wsb + plan->off_hss);
+  float* fbuf = (float*)(wsb + plan->off_f);
+  float* abuf = (float*)(wsb + plan->off_a);
+  int32_t* flags = (int32_t*)(wsb + plan->off_flags);
+  const int wvw = (int)(16 / ws);
+
+  // 1. z partials and sums of squares of h
+  {
+    GemmArgs g;
+    memset(&g, 0, sizeof(g));
+    g.X = h; g.ldx = d; g.W = w->wq; g.ldw = d;
+    g.R = (int)R; g.N = plan->Nz; g.K = (int)d; g.kchunk = plan->z_kchunk;
+    g.vec_ok = (d % wvw == 0) && (plan->z_kchunk % wvw == 0);
+    g.gamma = w->h_gamma; g.hss = hss; g.ypart = zpart;
+    const dim3 grid((unsigned)cdiv(plan->Nz, READY_GEMM_COLS), (unsigned)plan->z_ksplit,
+                    (unsigned)cdiv(R, READY_GEMM_RB));
+    const size_t lds = 4 * READY_GEMM_RB * (size_t)std::min(plan->z_kchunk, READY_GEMM_KSTAGE);
+    if (ready_launch_gemm(g, s.act_dtype, s.weight_dtype, s.act_dtype, EPI_PARTIAL, grid, lds, strm) != hipSuccess)
+      return READY_ERR_HIP;
+  }
+  // 2. per-state work
+  {
+    StateArgs a;
+    memset(&a, 0, sizeof(a));
+    a.states = states->base;
+    a.sb = states->stride_b; a.sp = states->stride_p; a.sl = states->stride_l; a.sh = states->stride_h;
+    a.accept_idx = accept_idx;
+    for (int l = 0; l < s.L_sel; ++l) a.slot[l] = plan->slot[l];
+    a.B = s.B; a.P = s.P; a.n = s.n; a.M = (int)M; a.H = s.H; a.r = s.r; a.d = (int)d; a.F = (int)F;
+    a.shared = s.shared_params; a.state_eps = s.state_eps; a.h_eps = s.h_eps;
+    a.u = w->u; a.v = w->v;
+    a.zpart = zpart; a.hss = hss; a.ksz = plan->z_ksplit; a.nz = plan->Nz;
+    a.gathered = o->gathered; a.logrms = o->logrms; a.f = fbuf; a.feat = o->feat;
+    a.dev_status = o->dev_status; a.seq_invalid = flags;
+    if (ready_launch_state(a, s.state_dtype, s.weight_dtype, strm) != hipSuccess) return READY_ERR_HIP;
+  }
+  // 3. a = act(W1 f + b1)
+  {
+    GemmArgs g;
+    memset(&g, 0, sizeof(g));
+    g.X = fbuf; g.ldx = F; g.W = w->w1; g.ldw = F;
+    g.R = (int)R; g.N = (int)Hm; g.K = (int)F; g.kchunk = (int)F;
+    g.vec_ok = (F % wvw == 0);
+    g.bias = w->b1; g.act = s.act; g.yout = abuf;
+    const dim3 grid((unsigned)cdiv(Hm, READY_GEMM_COLS), 1u, (unsigned)cdiv(R, READY_GEMM_RB));
+    const size_t lds = 4 * READY_GEMM_RB * (size_t)std::min((int)F, READY_GEMM_KSTAGE);
+    if (ready_launch_gemm(g, READY_F32, s.weight_dtype, s.act_dtype, EPI_BIAS_ACT, grid, lds, strm) != hipSuccess)
+      return READY_ERR_HIP;
+  }
+  // 4. out = h + W2 a + b2
+  {
+    GemmArgs g;
+    memset(&g, 0, sizeof(g));
+    g.X = abuf; g.ldx = Hm; g.W = w->w2; g.ldw = Hm;
+    g.R = (int)R; g.N = (int)d; g.K = (int)Hm; g.kchunk = (int)Hm;
+    g.vec_ok = (Hm % wvw == 0);
+    g.bias = w->b2; g.h = h; g.out = o->out; g.delta = o->delta; g.seq_invalid = flags; g.n = s.n;
+    const dim3 grid((unsigned)cdiv(d, READY_GEMM_COLS), 1u, (unsigned)cdiv(R, READY_GEMM_RB));
+    const size_t lds = 4 * READY_GEMM_RB * (size_t)std::min((int)Hm, READY_GEMM_KSTAGE);
+    if (ready_launch_gemm(g, READY_F32, s.weight_dtype, s.act_dtype, EPI_RESID, grid, lds, strm) != hipSuccess)
+      return READY_ERR_HIP;
+  }
+  return READY_OK;
+}
+
+}  // extern "C"

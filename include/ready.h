@@ -1,0 +1,190 @@
+/*
+ * ready.h -- C ABI of the ReaDy state-reader library for AMD Instinct MI355X
+ * (gfx950).
+ *
+ * The state reader conditions a block of n draft representations h_j on the
+ * committed Gated DeltaNet states of a hybrid-linear-attention target
+ * (ReaDy arXiv text, section 3.1 "State-Conditioned Block Drafting"; rainbus
+ * summary, 方法步骤详情; onedev summary, 어떻게 동작하나).  One call runs, for
+ * B independent sequences:
+ *
+ *   1. gather     G[b][m] = states[b][accept_idx[b]][layer_ids[l]][a],
+ *                 m = l*H + a, written to a caller-preallocated buffer
+ *                 (arXiv text, section 3.2 "Avoiding redundant data movement";
+ *                 section 3.1 "Drafting, verification, and commitment").
+ *   2. prepare    rms = sqrt(mean(G^2) + state_eps), S_bar = G / rms,
+ *                 ell = ln(rms)  (section 3.1 "Position-conditioned reading",
+ *                 "Fusion and residual injection").
+ *   3. project    T = V^T S_bar, r x d_k, once per state (section 3.1;
+ *                 section 3.2 "State-access footprint").
+ *   4. query      h_hat = gamma * h_j / sqrt(mean(h_j^2) + h_eps),
+ *                 z = W_q h_hat, q = U^T z, u = T q / sqrt(d_k)
+ *                 (section 3.1, Eq. (3), written out in the rainbus summary,
+ *                 方法步骤详情 step (2)).
+ *   5. fuse       f_j = [u^0, ell_0, u^1, ell_1, ...] (M (r+1) values),
+ *                 Delta h = W2 act(W1 f + b1) + b2, out = h + Delta h
+ *                 (section 3.1 "Fusion and residual injection", Eq. (4)).
+ *
+ * Conventions for every function:
+ *   - All functions are extern "C", never throw, and return a readyStatus.
+ *   - Argument errors are detected on the host before anything is launched;
+ *     on error nothing is launched and no output is touched.
+ *   - Device pointers are caller-owned memory on the current HIP device.  The
+ *     library never allocates, frees or copies device memory and never
+ *     synchronises the stream on the call path.
+ *   - "elements" counts values of the array's own dtype.
+ */
+#ifndef READY_H
+#define READY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define READY_VERSION 100 /* 1.0.0 */
+
+typedef enum readyStatus {
+  READY_OK = 0,
+  READY_ERR_NULL_POINTER = 1,       /* a required pointer is NULL */
+  READY_ERR_BAD_SHAPE = 2,          /* a size is out of the supported range */
+  READY_ERR_UNSUPPORTED_DTYPE = 3,  /* a dtype / activation code is unknown */
+  READY_ERR_MISALIGNED = 4,         /* a pointer or outer stride is not 16-byte aligned */
+  READY_ERR_WORKSPACE_TOO_SMALL = 5,
+  READY_ERR_ALIASING = 6,           /* outputs overlap inputs in a forbidden way */
+  READY_ERR_LAYER_ID_RANGE = 7,     /* a layer id is outside [0, L_tot) */
+  READY_ERR_HIP = 8,                /* the HIP runtime reported an error at launch */
+  READY_ERR_ACCEPT_IDX = 9,         /* device-side only: accept_idx[b] outside [0, P) */
+  READY_ERR_OUT_OF_HOST_MEMORY = 10
+} readyStatus;
+
+typedef enum readyDtype { READY_F32 = 0, READY_BF16 = 1 } readyDtype;
+
+/* Activation of the bottleneck MLP (the pages do not name it; SiLU default). */
+typedef enum readyAct { READY_ACT_SILU = 0, READY_ACT_GELU_TANH = 1, READY_ACT_RELU = 2 } readyAct;
+
+/*
+ * Problem shape.  Supported ranges (READY_ERR_BAD_SHAPE otherwise):
+ *   B >= 0 (B = 0 is a valid no-op), B * n <= 1 << 20
+ *   1 <= P <= 64 positions per verify buffer (root + drafts; the pages use 8)
+ *   1 <= n <= 16 draft positions per block (the pages use 7)
+ *   1 <= L_sel <= 64 selected layers, 1 <= L_tot, 1 <= H, M = L_sel * H <= 4096
+ *   d_k = d_v = 128 (the pages' per-head state size)
+ *   r in {8, 16, 24, ..., 128} (multiple of 8; the pages use 8 and 128)
+ *   d >= 8 and a multiple of 8; 1 <= Hm <= 4096
+ * Dtypes: state_dtype (states, gathered), act_dtype (h, out), weight_dtype
+ * (W_q, U, V, gamma, W1, b1, W2, b2), each READY_F32 or READY_BF16.
+ * Arithmetic is fp32 throughout; bf16 values are widened exactly.
+ */
+typedef struct readyShape {
+  int32_t B, P, n;
+  int32_t L_tot, L_sel, H;
+  int32_t d_k, d_v, r, d, Hm;
+  int32_t state_dtype, act_dtype, weight_dtype;
+  int32_t act;             /* readyAct */
+  int32_t shared_params;   /* 0: W_q, U, V stacked per pair; 1: one set for all pairs */
+  float state_eps;         /* added to mean(S^2); the pages are silent, 1e-6 suggested */
+  float h_eps;             /* added to mean(h^2) in RMSNorm(h); 1e-6 suggested */
+} readyShape;
+
+/*
+ * Verify-step per-position state buffer (read only).  Element
+ * [b][p][slot][a][v][k] is at base + b*stride_b + p*stride_p + slot*stride_l
+ * + a*stride_h + v*128 + k: each 128 x 128 tile is contiguous, value-by-key
+ * (row v = value index, column k = key index; arXiv text, section 3.1
+ * "State interface").  Strides are in elements and must keep every tile
+ * 16-byte aligned.
+ */
+typedef struct readyStates {
+  const void* base;
+  int64_t stride_b, stride_p, stride_l, stride_h;
+} readyStates;
+
+/*
+ * Reader weights, all in weight_dtype, row-major, device memory:
+ *   wq [M][r][d] (or [r][d] when shared_params)  -- z = W_q h_hat
+ *   u  [M][r][d_k] (or [r][d_k])                  -- q = U^T z
+ *   v  [M][d_v][r] (or [d_v][r])                  -- T = V^T S_bar
+ *   h_gamma [d] or NULL (gain of RMSNorm(h), ones when NULL)
+ *   w1 [Hm][F], F = M (r + 1); b1 [Hm] or NULL
+ *   w2 [d][Hm]; b2 [d] or NULL
+ */
+typedef struct readyWeights {
+  const void* wq;
+  const void* u;
+  const void* v;
+  const void* h_gamma;
+  const void* w1;
+  const void* b1;
+  const void* w2;
+  const void* b2;
+} readyWeights;
+
+/*
+ * Outputs (device memory, caller-owned):
+ *   gathered  [B][M][d_v][d_k] in state_dtype (required).  Must not overlap
+ *             the states' address range.
+ *   out       [B][n][d] in act_dtype (required): h + Delta h, rounded to
+ *             nearest even for bf16.  May be exactly h (in place); any other
+ *             overlap with an input is READY_ERR_ALIASING.
+ *   logrms    [B][M] fp32 ell = ln rms (optional, NULL to skip)
+ *   delta     [B][n][d] fp32 Delta h before the residual (optional)
+ *   feat      [B][n][F] fp32 packed features f_j (optional)
+ *   dev_status  one int32 (optional).  When accept_idx[b] is outside [0, P)
+ *             the kernels store READY_ERR_ACCEPT_IDX there and leave that
+ *             sequence's gathered, logrms, out and delta unwritten (its feat
+ *             row is zero).  The library never clears it; the caller does.
+ */
+typedef struct readyOutputs {
+  void* gathered;
+  void* out;
+  float* logrms;
+  float* delta;
+  float* feat;
+  int32_t* dev_status;
+} readyOutputs;
+
+typedef struct readyPlan readyPlan;
+
+/*
+ * Validate a shape and the selected layer slots, and build a plan.
+ * layer_ids: host array of L_sel slots on the buffer's layer axis (each in
+ * [0, L_tot); repeats allowed).  The plan copies what it needs; it is
+ * immutable afterwards and may be used from several host threads.  This is the
+ * only function that allocates (host memory, for the plan).
+ */
+readyStatus readyPlanCreate(const readyShape* shape, const int32_t* layer_ids, readyPlan** plan);
+
+/* Release a plan (NULL is accepted). */
+readyStatus readyPlanDestroy(readyPlan* plan);
+
+/* Bytes of device workspace readyStateReader needs for this plan. */
+readyStatus readyWorkspaceSize(const readyPlan* plan, size_t* bytes);
+
+/*
+ * Run steps 1-5 for every sequence, asynchronously on `stream` (a
+ * hipStream_t; NULL = the default stream).  accept_idx: device int32 [B].
+ * h: device [B][n][d] in act_dtype.  workspace: device memory of at least
+ * readyWorkspaceSize() bytes, 256-byte aligned, used as scratch by this call
+ * only (concurrent calls need separate workspaces).  The enqueued work
+ * allocates nothing and synchronises nothing, so it may be captured into a
+ * HIP graph.  Returns READY_ERR_HIP if a launch fails.
+ */
+readyStatus readyStateReader(const readyPlan* plan, const readyStates* states,
+                             const int32_t* accept_idx, const void* h,
+                             const readyWeights* weights, const readyOutputs* outputs,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+/* Static, human-readable name of a status code. */
+const char* readyStatusString(readyStatus status);
+
+/* READY_VERSION of the built library. */
+int32_t readyVersion(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* READY_H */

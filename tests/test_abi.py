@@ -1,0 +1,235 @@
+"""Host-side tests of the C ABI (CPU only, no GPU needed).
+
+The library must load, export every symbol include/ready.h declares, and
+reject every malformed argument before touching the HIP runtime.  No test
+here lets a call reach a kernel launch: each either fails validation or has
+B = 0 (a valid no-op).
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import hla_recurrent_state_amd as R
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _lib():
+    try:
+        return R.load()
+    except R.ReadyError:
+        import __graft_entry__
+        __graft_entry__.build_library()
+        return R.load()
+
+
+def test_exports_every_declared_symbol():
+    lib = _lib()
+    header = open(os.path.join(ROOT, "include", "ready.h")).read()
+    declared = set(re.findall(r"^\s*(?:readyStatus|const char\*|int32_t)\s+(ready\w+)\s*\(", header, re.M))
+    assert declared == set(R.EXPORTS)
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert R.readyVersion() == 100
+
+
+def test_status_strings():
+    _lib()
+    for code, name in [(0, "READY_OK"), (6, "READY_ERR_ALIASING"), (9, "READY_ERR_ACCEPT_IDX")]:
+        assert R.readyStatusString(code) == name
+    assert R.readyStatusString(999) == "READY_ERR_UNKNOWN"
+
+
+def _shape(**kw):
+    base = dict(B=2, P=8, n=7, L_tot=3, L_sel=2, H=4, r=8, d=512, Hm=64)
+    base.update(kw)
+    return R.make_shape(**base)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(B=-1), R.READY_ERR_BAD_SHAPE),
+    (dict(P=0), R.READY_ERR_BAD_SHAPE),
+    (dict(P=65), R.READY_ERR_BAD_SHAPE),
+    (dict(n=0), R.READY_ERR_BAD_SHAPE),
+    (dict(n=17), R.READY_ERR_BAD_SHAPE),
+    (dict(H=0), R.READY_ERR_BAD_SHAPE),
+    (dict(r=12), R.READY_ERR_BAD_SHAPE),
+    (dict(r=136), R.READY_ERR_BAD_SHAPE),
+    (dict(d=100), R.READY_ERR_BAD_SHAPE),
+    (dict(Hm=0), R.READY_ERR_BAD_SHAPE),
+    (dict(d_k=64), R.READY_ERR_BAD_SHAPE),
+    (dict(state_eps=-1.0), R.READY_ERR_BAD_SHAPE),
+    (dict(B=1 << 19, n=4), R.READY_ERR_BAD_SHAPE),
+])
+def test_plan_rejects_bad_shapes(kw, code):
+    _lib()
+    st, plan = R.readyPlanCreate(_shape(**kw), [0, 1])
+    assert st == code
+    assert not plan.value
+
+
+def test_plan_rejects_bad_dtype_and_activation():
+    _lib()
+    s = _shape()
+    s.state_dtype = 7
+    assert R.readyPlanCreate(s, [0, 1])[0] == R.READY_ERR_UNSUPPORTED_DTYPE
+    s = _shape()
+    s.act = 9
+    assert R.readyPlanCreate(s, [0, 1])[0] == R.READY_ERR_UNSUPPORTED_DTYPE
+
+
+def test_plan_rejects_layer_ids_out_of_range():
+    _lib()
+    assert R.readyPlanCreate(_shape(), [0, 3])[0] == R.READY_ERR_LAYER_ID_RANGE
+    assert R.readyPlanCreate(_shape(), [-1, 0])[0] == R.READY_ERR_LAYER_ID_RANGE
+    st, plan = R.readyPlanCreate(_shape(), [2, 2])      # repeats are allowed
+    assert st == R.READY_OK
+    R.readyPlanDestroy(plan)
+
+
+def test_null_arguments():
+    lib = _lib()
+    assert lib.readyPlanCreate(None, None, None) == R.READY_ERR_NULL_POINTER
+    assert lib.readyWorkspaceSize(None, None) == R.READY_ERR_NULL_POINTER
+    assert lib.readyPlanDestroy(None) == R.READY_OK
+
+
+def test_workspace_size_grows_with_batch():
+    _lib()
+    sizes = []
+    for B in (0, 1, 64):
+        st, plan = R.readyPlanCreate(_shape(B=B), [0, 1])
+        assert st == R.READY_OK
+        st, n = R.readyWorkspaceSize(plan)
+        assert st == R.READY_OK and n % 256 == 0
+        sizes.append(n)
+        R.readyPlanDestroy(plan)
+    assert sizes[0] <= sizes[1] < sizes[2]
+
+
+class _Fake:
+    """Host-side fake device addresses (never dereferenced: every call below
+    fails validation or is a B = 0 no-op)."""
+
+    def __init__(self, shape):
+        self.s = shape
+        self.next = 1 << 40
+
+    def alloc(self, nbytes):
+        p = self.next
+        self.next += (nbytes + 4095) // 4096 * 4096 + 4096
+        return p
+
+
+def _call(shape, layer_ids=(0, 1), mutate=None):
+    _lib()
+    st, plan = R.readyPlanCreate(shape, list(layer_ids))
+    assert st == R.READY_OK
+    _, ws_bytes = R.readyWorkspaceSize(plan)
+    f = _Fake(shape)
+    B, P, L, H, n, d, r, Hm = shape.B, shape.P, shape.L_tot, shape.H, shape.n, shape.d, shape.r, shape.Hm
+    M = shape.L_sel * H
+    F = M * (r + 1)
+    es = 2
+    tile = 128 * 128
+    states = R.readyStates(base=f.alloc(B * P * L * H * tile * es), stride_b=P * L * H * tile,
+                           stride_p=L * H * tile, stride_l=H * tile, stride_h=tile)
+    w = R.readyWeights(wq=f.alloc(M * r * d * es), u=f.alloc(M * r * 128 * es), v=f.alloc(M * r * 128 * es),
+                       h_gamma=None, w1=f.alloc(Hm * F * es), b1=None, w2=f.alloc(d * Hm * es), b2=None)
+    o = R.readyOutputs(gathered=f.alloc(B * M * tile * es), out=f.alloc(B * n * d * es), logrms=None,
+                       delta=None, feat=None, dev_status=None)
+    args = dict(plan=plan, states=states, accept_idx=f.alloc(4 * max(B, 1)), h=f.alloc(B * n * d * es),
+                weights=w, outputs=o, workspace=f.alloc(ws_bytes), workspace_bytes=ws_bytes, stream=None)
+    if mutate:
+        mutate(args)
+    code = R.readyStateReader(**args)
+    R.readyPlanDestroy(plan)
+    return code
+
+
+def test_zero_batch_valid_call_is_ok():
+    assert _call(_shape(B=0)) == R.READY_OK
+
+
+def test_reader_null_pointers():
+    def m(field):
+        def f(a):
+            if field == "states":
+                a["states"].base = None
+            elif field.startswith("w."):
+                setattr(a["weights"], field[2:], None)
+            elif field.startswith("o."):
+                setattr(a["outputs"], field[2:], None)
+            else:
+                a[field] = None
+        return f
+    for field in ("states", "accept_idx", "h", "workspace", "w.wq", "w.u", "w.v", "w.w1", "w.w2",
+                  "o.gathered", "o.out"):
+        assert _call(_shape(), mutate=m(field)) == R.READY_ERR_NULL_POINTER, field
+
+
+def test_reader_workspace_too_small():
+    def m(a):
+        a["workspace_bytes"] -= 256
+    assert _call(_shape(), mutate=m) == R.READY_ERR_WORKSPACE_TOO_SMALL
+
+
+def test_reader_misaligned_pointers_and_strides():
+    for what in ("h", "wq", "gathered", "states", "workspace"):
+        def m(a, what=what):
+            if what == "h":
+                a["h"] += 2
+            elif what == "wq":
+                a["weights"].wq += 8
+            elif what == "gathered":
+                a["outputs"].gathered += 4
+            elif what == "states":
+                a["states"].base += 2
+            else:
+                a["workspace"] += 16
+        assert _call(_shape(), mutate=m) == R.READY_ERR_MISALIGNED, what
+
+    def stride(a):
+        a["states"].stride_h += 3          # 6 bytes: tiles no longer 16-byte aligned
+    assert _call(_shape(), mutate=stride) == R.READY_ERR_MISALIGNED
+
+    def negative(a):
+        a["states"].stride_p = -a["states"].stride_p
+    assert _call(_shape(), mutate=negative) == R.READY_ERR_BAD_SHAPE
+
+
+def test_reader_aliasing_rules():
+    def gathered_in_states(a):
+        a["outputs"].gathered = a["states"].base + 128 * 128 * 2
+    assert _call(_shape(), mutate=gathered_in_states) == R.READY_ERR_ALIASING
+
+    def out_overlaps_h(a):
+        a["outputs"].out = a["h"] + 64            # partial overlap
+    assert _call(_shape(), mutate=out_overlaps_h) == R.READY_ERR_ALIASING
+
+    def out_on_weights(a):
+        a["outputs"].out = a["weights"].w2
+    assert _call(_shape(), mutate=out_on_weights) == R.READY_ERR_ALIASING
+
+    def ws_on_gathered(a):
+        a["workspace"] = a["outputs"].gathered
+    assert _call(_shape(), mutate=ws_on_gathered) == R.READY_ERR_ALIASING
+
+    def delta_on_feat(a):
+        p = a["workspace"] + (1 << 30)
+        a["outputs"].delta = p
+        a["outputs"].feat = p + 16
+    assert _call(_shape(), mutate=delta_on_feat) == R.READY_ERR_ALIASING
+
+    def in_place_b0(a):
+        a["outputs"].out = a["h"]                 # exactly in place is allowed
+    assert _call(_shape(B=0), mutate=in_place_b0) == R.READY_OK
+
+
+def test_python_binding_raises_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(R, "_lib", None)
+    monkeypatch.setattr(R, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(R.ReadyError):
+        R.load()

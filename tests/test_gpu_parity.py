@@ -1,0 +1,206 @@
+"""GPU parity of the HIP state reader against the float64 CPU oracle.
+
+Every case calls libready.so through its C ABI (ctypes) on seeded synthetic
+inputs and compares element by element with the oracle run on the same
+stored values: bit-exact gather, Delta h within the normwise tolerance, out
+within one ulp of the rounded oracle sum, log-RMS within 1e-5.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import synth
+from synth.gen import make_shape
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+def _dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch.device("cuda:0")
+
+
+def _say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def _check(inp, seqs=None, inplace=False, expect_ok=True):
+    from tests.gpu_util import compare, oracle_reference, run_reader
+    dev = _dev()
+    _say("case", inp.cfg.name, "B", inp.cfg.B, "M", inp.cfg.M, "r", inp.cfg.r, inp.cfg.state_dtype)
+    res = run_reader(inp, dev, inplace=inplace)
+    ref = oracle_reference(inp, seqs)
+    rep = compare(inp, res, ref)
+    _say("  report", rep)
+    if expect_ok:
+        assert rep["ok"], rep
+    return res, ref, rep
+
+
+# ------------------------------------------------------------ the five configurations
+
+def test_tiny():
+    _check(synth.make("tiny", seed=1))
+
+
+def test_paper_shape():
+    _check(synth.make("paper", seed=1))
+
+
+def test_wide_heads():
+    _check(synth.make("wide", seed=1))
+
+
+def test_batched():
+    _check(synth.make("batched", seed=1))
+
+
+def test_rank_ablation_sampled():
+    """B = 256, 48 pairs, r = 128: the oracle checks a sample of sequences,
+    and the gather is checked bit-exact for all of them."""
+    inp = synth.make("rank", seed=1)
+    res, ref, rep = _check(inp, seqs=[0, 1, 97, 128, 200, 255])
+    want = inp.buf[np.arange(inp.cfg.B), inp.accept_idx][:, list(inp.cfg.slots)]
+    want = want.reshape(inp.cfg.B, inp.cfg.M, 128, 128)
+    assert np.array_equal(res["gathered"], want)
+
+
+# ------------------------------------------------------------ multi-tile cases with ragged tails
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("act", ["silu", "gelu_tanh", "relu"])
+def test_ragged_shapes(dt, act):
+    """Rows B*n = 15 (two row blocks, ragged), d = 1048 (ragged K splits),
+    Hm = 100 (unaligned rows: scalar weight path), scattered layer slots,
+    r = 16, with gain and biases."""
+    cfg = make_shape("tiny", B=3, n=5, H=3, L_tot=4, slots=(3, 1), t=12, r=16, d=1048, Hm=100,
+                     state_dtype=dt, act_dtype=dt, weight_dtype=dt, act=act)
+    inp = synth.make(cfg, seed=7)
+    rng = np.random.default_rng(3)
+    store = synth.gen._store
+    inp.gamma = store(1.0 + 0.1 * rng.standard_normal(cfg.d), dt)
+    inp.b1 = store(0.2 * rng.standard_normal(cfg.Hm), dt)
+    inp.b2 = store(0.2 * rng.standard_normal(cfg.d), dt)
+    _check(inp)
+
+
+@pytest.mark.parametrize("r", [8, 24, 128])
+def test_ranks_and_mixed_dtypes(r):
+    cfg = make_shape("tiny", B=2, H=2, t=8, r=r, d=640, Hm=64, state_dtype="bf16", act_dtype="f32",
+                     weight_dtype="bf16")
+    _check(synth.make(cfg, seed=11))
+
+
+def test_shared_reader_parameters():
+    cfg = make_shape("tiny", B=2, H=4, t=8, d=512, Hm=32, shared=True, state_dtype="bf16",
+                     act_dtype="bf16", weight_dtype="bf16")
+    _check(synth.make(cfg, seed=12))
+
+
+def test_long_block_and_many_rows():
+    """n = 16 positions and B*n = 48 rows with fp32 states and bf16 weights."""
+    cfg = make_shape("tiny", B=3, n=16, P=16, H=2, t=20, d=256, Hm=48, state_dtype="f32",
+                     act_dtype="bf16", weight_dtype="bf16")
+    _check(synth.make(cfg, seed=13))
+
+
+# ------------------------------------------------------------ accept index edge cases
+
+@pytest.mark.parametrize("pattern", ["zeros", "last", "mixed"])
+def test_accept_index_edges(pattern):
+    cfg = make_shape("paper", B=5, t=16)
+    inp = synth.make(cfg, seed=21)
+    inp.accept_idx = {"zeros": np.zeros(5), "last": np.full(5, cfg.P - 1),
+                      "mixed": np.array([0, 7, 3, 7, 0])}[pattern].astype(np.int32)
+    _check(inp)
+
+
+def test_out_of_range_accept_index_sets_status_and_skips_sequence():
+    from tests.gpu_util import run_reader
+    dev = _dev()
+    cfg = make_shape("paper", B=3, t=16)
+    inp = synth.make(cfg, seed=22)
+    inp.accept_idx = np.array([2, 8, -1], dtype=np.int32)
+    import tests.gpu_util as gu
+    d = synth.device.to_device(inp, dev)
+    from hla_recurrent_state_amd import StateReader
+    reader = StateReader(gu.reader_shape(cfg), cfg.slots)
+    o = gu.alloc_outputs(cfg, dev)
+    sentinel_bits = 0x7FC1
+    o["gathered"].view(torch.int16).fill_(sentinel_bits)
+    o["out"].view(torch.int16).fill_(sentinel_bits)
+    reader(d["states"], d["accept_idx"], d["h"], d["weights"], o["gathered"], o["out"],
+           logrms=o["logrms"], delta=o["delta"], feat=o["feat"], dev_status=o["dev_status"])
+    torch.cuda.synchronize()
+    from hla_recurrent_state_amd import READY_ERR_ACCEPT_IDX
+    assert int(o["dev_status"].item()) == READY_ERR_ACCEPT_IDX
+    g = o["gathered"].view(torch.int16).cpu().numpy()
+    out = o["out"].view(torch.int16).cpu().numpy()
+    assert np.all(g[1:] == sentinel_bits) and np.all(out[1:] == sentinel_bits)
+    # the valid sequence is still computed correctly
+    from tests.gpu_util import compare, oracle_reference
+    res = {"gathered": g.view(np.uint16), "out": out.view(np.uint16),
+           "logrms": o["logrms"].cpu().numpy(), "delta": o["delta"].cpu().numpy(),
+           "feat": o["feat"].cpu().numpy(), "dev_status": 0}
+    ok = synth.make(cfg, seed=22)
+    ok.accept_idx = inp.accept_idx.copy()
+    ok.accept_idx[1:] = 0
+    rep = compare(ok, res, oracle_reference(ok, [0]))
+    assert rep["ok"], rep
+
+
+# ------------------------------------------------------------ properties
+
+def test_in_place_output():
+    _check(synth.make(make_shape("paper", B=2, t=16), seed=31), inplace=True)
+
+
+def test_zero_w2_gives_out_equal_h_bitwise():
+    from tests.gpu_util import run_reader
+    inp = synth.make(make_shape("paper", B=2, t=16), seed=32)
+    inp.w2 = np.zeros_like(inp.w2)
+    res = run_reader(inp, _dev())
+    assert np.array_equal(res["out"], inp.h)
+    assert np.all(res["delta"] == 0.0)
+
+
+def test_run_to_run_bitwise_determinism():
+    from tests.gpu_util import run_reader
+    inp = synth.make(make_shape("batched", B=8, t=16), seed=33)
+    a = run_reader(inp, _dev())
+    b = run_reader(inp, _dev())
+    for k in ("gathered", "out", "logrms", "delta", "feat"):
+        assert np.array_equal(a[k], b[k]), k
+
+
+def test_batch_permutation_equivariance():
+    from tests.gpu_util import run_reader
+    inp = synth.make(make_shape("batched", B=6, t=16), seed=34)
+    a = run_reader(inp, _dev())
+    perm = np.array([3, 0, 5, 1, 4, 2])
+    inp.buf = np.ascontiguousarray(inp.buf[perm])
+    inp.accept_idx = inp.accept_idx[perm]
+    inp.h = np.ascontiguousarray(inp.h[perm])
+    b = run_reader(inp, _dev())
+    for k in ("gathered", "out", "logrms", "delta", "feat"):
+        assert np.array_equal(a[k][perm], b[k]), k
+
+
+def test_zero_batch_is_a_no_op():
+    from hla_recurrent_state_amd import StateReader
+    import tests.gpu_util as gu
+    dev = _dev()
+    cfg = make_shape("paper", B=1, t=4)
+    inp = synth.make(cfg, seed=35)
+    d = synth.device.to_device(inp, dev)
+    reader = StateReader(gu.reader_shape(cfg, B=0), cfg.slots)
+    o = gu.alloc_outputs(cfg, dev, B=1)
+    o["out"].fill_(3.0)
+    reader(d["states"], d["accept_idx"], d["h"], d["weights"], o["gathered"], o["out"])
+    torch.cuda.synchronize()
+    assert torch.all(o["out"] == 3.0)
