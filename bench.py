@@ -1,0 +1,539 @@
+#!/usr/bin/env python
+"""Benchmark of the ReaDy state-reader path on one AMD Instinct MI355X.
+
+One step = one readyStateReader call over one batch of seeded synthetic
+input already resident in HBM (all five steps: gather, state preparation,
+projection, query/readout, packing + MLP + residual).
+
+value      committed-state GB/s on the batched workload (B = 64 sequences,
+           32 layer-head pairs, bf16 128 x 128 states): (state bytes read +
+           gathered bytes written) per step / time per step.  Steps rotate
+           over several copies of the inputs so the 256 MB last-level cache
+           cannot hold them.
+roofline   the dominant kernel (k_state): its algorithmic bytes per launch /
+           its average duration, timed with HIP events recorded around it on
+           the launch stream inside the timed loop, against 8 TB/s.
+b1_latency single-block latency at the paper shape (B = 1), eager and
+           graph-replayed, cache-cold and warm, next to an unfused PyTorch
+           eager composition of the same five steps.
+cpu_baseline  the float64 oracle on a bounded sample of the batched
+           workload, on the host (1 thread), with a parity check of the GPU
+           outputs on that sample.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+import argparse
+import ctypes
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "state-reader µs per 7-token draft block (B=1); committed-state GB/s at B=64"
+HBM_PEAK_GBS = 8000.0
+KERNEL_SRC = os.path.join(ROOT, "hla_recurrent_state_amd", "csrc", "ready_kernels.hip")
+PMC_SUMMARY = os.path.join(ROOT, "profiles", "k_state_batched_pmc.md")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ---------------------------------------------------------------- HIP events
+
+class Hip:
+    def __init__(self):
+        self.lib = ctypes.CDLL("libamdhip64.so")
+        self.lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def event(self):
+        ev = ctypes.c_void_p()
+        if self.lib.hipEventCreate(ctypes.byref(ev)) != 0:
+            raise RuntimeError("hipEventCreate failed")
+        return ev.value
+
+    def record(self, ev, stream):
+        if self.lib.hipEventRecord(ev, stream) != 0:
+            raise RuntimeError("hipEventRecord failed")
+
+    def ms(self, a, b):
+        f = ctypes.c_float()
+        if self.lib.hipEventElapsedTime(ctypes.byref(f), a, b) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return f.value
+
+    def destroy(self, ev):
+        self.lib.hipEventDestroy(ev)
+
+
+# ---------------------------------------------------------------- helpers
+
+def pct(xs, p):
+    xs = sorted(xs)
+    k = (len(xs) - 1) * p / 100.0
+    lo, hi = math.floor(k), math.ceil(k)
+    return xs[lo] + (xs[hi] - xs[lo]) * (k - lo)
+
+
+def esize(dt):
+    return 2 if dt == "bf16" else 4
+
+
+def algorithmic_bytes(cfg):
+    """Bytes the method must move per call (states read at the accepted
+    positions only, gathered written, h read, out written, every weight read
+    once, accept indices)."""
+    s, a, w = esize(cfg.state_dtype), esize(cfg.act_dtype), esize(cfg.weight_dtype)
+    M, r, d, F, Hm, B, n = cfg.M, cfg.r, cfg.d, cfg.F, cfg.Hm, cfg.B, cfg.n
+    mz = 1 if cfg.shared else M
+    committed = 2 * B * M * 128 * 128 * s
+    weights = (mz * r * d + 2 * mz * r * 128 + Hm * F + d * Hm) * w
+    acts = 2 * B * n * d * a
+    return {"committed_state": committed, "weights": weights, "activations": acts,
+            "accept_idx": 4 * B, "total": committed + weights + acts + 4 * B}
+
+
+def state_kernel_bytes(cfg):
+    """Algorithmic bytes of one k_state launch: committed states read and
+    written, U and V read once, q-side inputs (z of every pair) and the packed
+    features written."""
+    s, w = esize(cfg.state_dtype), esize(cfg.weight_dtype)
+    mz = 1 if cfg.shared else cfg.M
+    rows = cfg.B * cfg.n
+    return (2 * cfg.B * cfg.M * 128 * 128 * s + 2 * mz * cfg.r * 128 * w
+            + rows * mz * cfg.r * 4 + rows * cfg.F * 4 + cfg.B * cfg.M * 4)
+
+
+def kernel_src_hash():
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def read_traffic():
+    """HBM bytes per k_state launch from the committed PMC summary, if it was
+    taken on the current kernel source."""
+    if not os.path.exists(PMC_SUMMARY):
+        return None
+    vals = {}
+    for line in open(PMC_SUMMARY, encoding="utf-8"):
+        if ":" in line and line.startswith("- "):
+            k, v = line[2:].split(":", 1)
+            vals[k.strip()] = v.strip().strip("`")
+    if vals.get("kernel_source_sha256_16") != kernel_src_hash():
+        return None
+    try:
+        return int(float(vals["traffic_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
+
+
+# ---------------------------------------------------------------- device setup
+
+class Prepared:
+    """ctypes argument tuples built once, so the timed loop does no Python
+    work beyond the call itself."""
+
+    def __init__(self, R, reader, dev_in, outs, ws, stream):
+        st = dev_in["states"].stride()
+        self.keep = (dev_in, outs, ws)
+        self.sd = R.readyStates(base=dev_in["states"].data_ptr(), stride_b=st[0], stride_p=st[1],
+                                stride_l=st[2], stride_h=st[3])
+        w = dev_in["weights"]
+        self.wd = R.readyWeights(**{k: (w[k].data_ptr() if k in w else None)
+                                    for k in ("wq", "u", "v", "h_gamma", "w1", "b1", "w2", "b2")})
+        self.od = R.readyOutputs(gathered=outs["gathered"].data_ptr(), out=outs["out"].data_ptr(),
+                                 logrms=None, delta=None, feat=None, dev_status=outs["dev_status"].data_ptr())
+        self.args = (reader.plan, ctypes.byref(self.sd), dev_in["accept_idx"].data_ptr(),
+                     dev_in["h"].data_ptr(), ctypes.byref(self.wd), ctypes.byref(self.od),
+                     ws.data_ptr(), ws.numel(), stream)
+
+
+def device_sets(inp, nsets, device, reader, stream):
+    import torch
+    from synth.device import to_device, torch_dtype
+    import hla_recurrent_state_amd as R
+    cfg = inp.cfg
+    base = to_device(inp, device)
+    sets = []
+    for i in range(nsets):
+        d = dict(base) if i == 0 else {
+            "states": base["states"].clone(), "accept_idx": base["accept_idx"].clone(),
+            "h": base["h"].clone(), "weights": base["weights"]}
+        outs = {
+            "gathered": torch.empty((cfg.B, cfg.M, 128, 128), dtype=torch_dtype(cfg.state_dtype), device=device),
+            "out": torch.empty((cfg.B, cfg.n, cfg.d), dtype=torch_dtype(cfg.act_dtype), device=device),
+            "dev_status": torch.zeros(1, dtype=torch.int32, device=device),
+        }
+        ws = torch.empty(max(reader.workspace_bytes, 256), dtype=torch.uint8, device=device)
+        sets.append(Prepared(R, reader, d, outs, ws, stream))
+    return sets
+
+
+# ---------------------------------------------------------------- batched throughput
+
+def run_batched(args, hip, torch, R, synth, seed=0):
+    device = torch.device("cuda:0")
+    cfg = synth.make_shape("batched")
+    t0 = time.time()
+    inp = synth.make(cfg, seed=seed)
+    log("batched inputs generated in %.1f s" % (time.time() - t0))
+    reader = R.StateReader(shape_of(R, cfg), cfg.slots)
+    stream = torch.cuda.current_stream(device).cuda_stream
+    foot = algorithmic_bytes(cfg)["total"]
+    nsets = max(2, int(math.ceil(1.0e9 / foot)))
+    sets = device_sets(inp, nsets, device, reader, stream)
+    lib = R.load()
+    K, W = args.steps, args.warmup
+    ev_s = [hip.event() for _ in range(K)]
+    ev_e = [hip.event() for _ in range(K)]
+    ev_arrays = [(ctypes.c_void_p * (R.READY_STAGES + 1))(None, ev_s[i], ev_e[i], None, None) for i in range(K)]
+    for i in range(W):
+        code = lib.readyStateReader(*sets[i % nsets].args)
+        if code != 0:
+            raise R.ReadyError(code, "warmup")
+    torch.cuda.synchronize(device)
+    start, stop = hip.event(), hip.event()
+    hip.record(start, stream)
+    t_host = time.perf_counter()
+    for i in range(K):
+        code = lib.readyStateReaderProfiled(*sets[i % nsets].args, ev_arrays[i])
+        if code != 0:
+            raise R.ReadyError(code, "timed")
+    hip.record(stop, stream)
+    torch.cuda.synchronize(device)
+    host_s = time.perf_counter() - t_host
+    total_ms = hip.ms(start, stop)
+    kern_us = [1000.0 * hip.ms(ev_s[i], ev_e[i]) for i in range(K)]
+    # stage breakdown (separate, untimed-for-value pass)
+    stage_us = stage_breakdown(hip, lib, sets, R, stream, torch, device, reps=min(K, 50))
+    for s in sets:
+        if int(s.keep[1]["dev_status"].item()) != 0:
+            raise RuntimeError("device status set during the batched run")
+    result = {"cfg": cfg, "inp": inp, "reader": reader, "set0": sets[0], "nsets": nsets,
+              "ms_per_step": total_ms / K, "host_s": host_s, "kern_us": kern_us, "stage_us": stage_us}
+    return result
+
+
+def stage_breakdown(hip, lib, sets, R, stream, torch, device, reps):
+    n = R.READY_STAGES + 1
+    evs = [[hip.event() for _ in range(n)] for _ in range(reps)]
+    for i in range(reps):
+        arr = (ctypes.c_void_p * n)(*evs[i])
+        code = lib.readyStateReaderProfiled(*sets[i % len(sets)].args, arr)
+        if code != 0:
+            raise R.ReadyError(code, "stages")
+    torch.cuda.synchronize(device)
+    names = ["query_gemm", "state_kernel", "mlp1", "mlp2_residual"]
+    out = {}
+    for s, name in enumerate(names):
+        vals = [1000.0 * hip.ms(evs[i][s], evs[i][s + 1]) for i in range(reps)]
+        out[name] = round(pct(vals, 50), 2)
+    return out
+
+
+def shape_of(R, cfg, B=None):
+    return R.make_shape(B=cfg.B if B is None else B, P=cfg.P, n=cfg.n, L_tot=cfg.L_tot, L_sel=cfg.L_sel,
+                        H=cfg.H, r=cfg.r, d=cfg.d, Hm=cfg.Hm, state_dtype=cfg.state_dtype,
+                        act_dtype=cfg.act_dtype, weight_dtype=cfg.weight_dtype, act=cfg.act,
+                        shared=cfg.shared, state_eps=cfg.state_eps, h_eps=cfg.h_eps)
+
+
+# ---------------------------------------------------------------- B = 1 latency
+
+def unfused_torch(dev_in, cfg, gathered, torch):
+    """PyTorch eager composition of the five steps (index then copy into the
+    execution buffer, casts, pow-mean-rsqrt, matmuls, cat, silu, add): the
+    unfused comparator."""
+    import torch.nn.functional as Fn
+    B, n, M, r, d = cfg.B, cfg.n, cfg.M, cfg.r, cfg.d
+    w = dev_in["weights"]
+    slots = dev_in["_slots"]
+    sel = dev_in["states"][torch.arange(B, device=gathered.device), dev_in["accept_idx"].long()]
+    gathered.copy_(sel[:, slots].reshape(B, M, 128, 128))
+    Sf = gathered.float()
+    rms = (Sf.pow(2).mean(dim=(2, 3), keepdim=True) + cfg.state_eps).sqrt()
+    T = torch.matmul(dev_in["_Vt"], Sf / rms)                          # [B][M][r][128]
+    hf = dev_in["h"].float()
+    hh = hf * torch.rsqrt(hf.pow(2).mean(-1, keepdim=True) + cfg.h_eps)
+    z = Fn.linear(hh, dev_in["_Wq2"])                                  # [B][n][M r]
+    q = torch.matmul(z.view(B, n, M, 1, r), dev_in["_U"]).squeeze(3)  # [B][n][M][128]
+    qt = q.permute(0, 2, 3, 1).contiguous()                           # [B][M][128][n]
+    u = torch.matmul(T, qt).permute(0, 3, 1, 2) / math.sqrt(128.0)    # [B][n][M][r]
+    ell = torch.log(rms.view(B, 1, M, 1)).expand(B, n, M, 1)
+    f = torch.cat([u, ell], dim=-1).reshape(B, n, M * (r + 1))
+    a = Fn.silu(Fn.linear(f, dev_in["_W1"]))
+    dh = Fn.linear(a, dev_in["_W2"])
+    return (hf + dh).to(dev_in["h"].dtype)
+
+
+def run_b1(args, hip, torch, R, synth, seed=0):
+    device = torch.device("cuda:0")
+    cfg = synth.make_shape("paper")
+    inp = synth.make(cfg, seed=seed)
+    reader = R.StateReader(shape_of(R, cfg), cfg.slots)
+    stream = torch.cuda.current_stream(device).cuda_stream
+    sets = device_sets(inp, 1, device, reader, stream)
+    s0 = sets[0]
+    lib = R.load()
+    K = args.b1_steps
+    flush = torch.empty(128 * 1024 * 1024, dtype=torch.float32, device=device)  # 512 MB
+
+    def call():
+        code = lib.readyStateReader(*s0.args)
+        if code != 0:
+            raise R.ReadyError(code, "b1")
+
+    def timed(fn, cold, reps):
+        starts = [hip.event() for _ in range(reps)]
+        ends = [hip.event() for _ in range(reps)]
+        for i in range(reps):
+            if cold:
+                flush.add_(1.0)
+            hip.record(starts[i], stream)
+            fn()
+            hip.record(ends[i], stream)
+        torch.cuda.synchronize(device)
+        vals = [1000.0 * hip.ms(starts[i], ends[i]) for i in range(reps)]
+        for e in starts + ends:
+            hip.destroy(e)
+        return vals
+
+    def back_to_back(fn, reps):
+        a, b = hip.event(), hip.event()
+        for _ in range(5):
+            fn()
+        torch.cuda.synchronize(device)
+        hip.record(a, stream)
+        for _ in range(reps):
+            fn()
+        hip.record(b, stream)
+        torch.cuda.synchronize(device)
+        return 1000.0 * hip.ms(a, b) / reps
+
+    for _ in range(10):
+        call()
+    torch.cuda.synchronize(device)
+    res = {}
+    res["fused_eager_cold_us"] = timed(call, True, K)
+    res["fused_eager_warm_us"] = back_to_back(call, K)
+
+    # the same call captured into a HIP graph
+    g = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream(device)
+    cap.wait_stream(torch.cuda.current_stream(device))
+    with torch.cuda.stream(cap):
+        gargs = list(s0.args)
+        gargs[-1] = cap.cuda_stream
+        lib.readyStateReader(*gargs)  # warm the capture stream
+        torch.cuda.synchronize(device)
+        with torch.cuda.graph(g, stream=cap):
+            code = lib.readyStateReader(*gargs)
+    if code != 0:
+        raise R.ReadyError(code, "capture")
+    torch.cuda.current_stream(device).wait_stream(cap)
+    torch.cuda.synchronize(device)
+    res["fused_graph_cold_us"] = timed(g.replay, True, K)
+    res["fused_graph_warm_us"] = back_to_back(g.replay, K)
+
+    # unfused comparator
+    dev_in = dict(s0.keep[0])
+    w = dev_in["weights"]
+    dev_in["_slots"] = torch.tensor(list(cfg.slots), device=device)
+    dev_in["_Vt"] = w["v"].float().transpose(1, 2).contiguous()
+    dev_in["_Wq2"] = w["wq"].float().reshape(cfg.M * cfg.r, cfg.d).contiguous()
+    dev_in["_U"] = w["u"].float().contiguous()
+    dev_in["_W1"] = w["w1"].float().contiguous()
+    dev_in["_W2"] = w["w2"].float().contiguous()
+    gath2 = torch.empty_like(s0.keep[1]["gathered"])
+    ref_out = unfused_torch(dev_in, cfg, gath2, torch)
+    torch.cuda.synchronize(device)
+    res["unfused_torch_cold_us"] = timed(lambda: unfused_torch(dev_in, cfg, gath2, torch), True, K)
+    res["unfused_torch_warm_us"] = back_to_back(lambda: unfused_torch(dev_in, cfg, gath2, torch), K)
+    # sanity: the two paths agree
+    call()
+    torch.cuda.synchronize(device)
+    ours = s0.keep[1]["out"].float()
+    diff = (ours - ref_out.float()).abs().max().item()
+    res["unfused_vs_fused_max_abs_diff"] = diff
+    res["gathered_equal"] = bool(torch.equal(gath2.view(torch.int16), s0.keep[1]["gathered"].view(torch.int16)))
+    res["cfg"] = cfg
+    return res
+
+
+# ---------------------------------------------------------------- CPU oracle baseline
+
+def cpu_baseline(bat, budget_s):
+    """Time the float64 oracle on a bounded sample of the batched workload and
+    check the GPU outputs of the same sequences against it."""
+    try:
+        from threadpoolctl import threadpool_limits
+    except ImportError:
+        threadpool_limits = None
+    from tests.gpu_util import compare, oracle_reference
+    from synth.device import to_numpy_bits
+    import contextlib
+    inp, cfg = bat["inp"], bat["cfg"]
+    ctx = threadpool_limits(limits=1) if threadpool_limits else contextlib.nullcontext()
+    with ctx:
+        t0 = time.perf_counter()
+        oracle_reference(inp, [0])
+        one = time.perf_counter() - t0
+        nseq = int(max(1, min(cfg.B, budget_s / max(one, 1e-3))))
+        seqs = list(range(nseq))
+        t0 = time.perf_counter()
+        ref = oracle_reference(inp, seqs)
+        el = time.perf_counter() - t0
+    committed = 2 * nseq * cfg.M * 128 * 128 * esize(cfg.state_dtype)
+    # parity of the GPU outputs (set 0) on the sampled sequences
+    s0 = bat["set0"]
+    outs = s0.keep[1]
+    import torch
+    import hla_recurrent_state_amd as R
+    dev = outs["out"].device
+    extra = {"logrms": torch.empty((cfg.B, cfg.M), dtype=torch.float32, device=dev),
+             "delta": torch.empty((cfg.B, cfg.n, cfg.d), dtype=torch.float32, device=dev),
+             "feat": torch.empty((cfg.B, cfg.n, cfg.F), dtype=torch.float32, device=dev)}
+    d = s0.keep[0]
+    bat["reader"](d["states"], d["accept_idx"], d["h"], d["weights"], outs["gathered"], outs["out"],
+                  logrms=extra["logrms"], delta=extra["delta"], feat=extra["feat"],
+                  dev_status=outs["dev_status"], workspace=s0.keep[2])
+    torch.cuda.synchronize(dev)
+    res = {"gathered": to_numpy_bits(outs["gathered"], cfg.state_dtype),
+           "out": to_numpy_bits(outs["out"], cfg.act_dtype),
+           "logrms": extra["logrms"].cpu().numpy(), "delta": extra["delta"].cpu().numpy(),
+           "feat": extra["feat"].cpu().numpy(), "dev_status": int(outs["dev_status"].item())}
+    rep = compare(inp, res, ref)
+    base = {"value": round(committed / el / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": "float64 numpy oracle, steps 1-5, on %d of the %d sequences of the batched "
+                      "workload (%.1f s; committed-state bytes of the sample / time)" % (nseq, cfg.B, el)}
+    return base, rep
+
+
+# ---------------------------------------------------------------- main
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--b1-steps", type=int, default=200)
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-b1", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the state reader shards by sequence with no "
+              "communication, so a multi-GPU figure is not part of this benchmark "
+              "(got --gpus %d)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    if not os.path.exists(os.path.join(ROOT, "hla_recurrent_state_amd", "libready.so")):
+        import __graft_entry__
+        __graft_entry__.build()
+    import hla_recurrent_state_amd as R
+    import synth
+    R.load()
+    hip = Hip()
+
+    bat = run_batched(args, hip, torch, R, synth)
+    cfg = bat["cfg"]
+    alg = algorithmic_bytes(cfg)
+    ms = bat["ms_per_step"]
+    value = alg["committed_state"] / (ms * 1e-3) / 1e9
+    kern_avg_us = sum(bat["kern_us"]) / len(bat["kern_us"])
+    kb = state_kernel_bytes(cfg)
+    achieved = kb / (kern_avg_us * 1e-6) / 1e9
+    traffic = read_traffic()
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": "batched: B=64 sequences, M=32 layer-head pairs (layers 30, 62 x 16 heads), "
+                        "bf16 128x128 states from the fp32 gated delta rule at t=4096, verify buffer of 8 "
+                        "positions, block n=7, d=5120, r=8, MLP 288->256->5120 SiLU, bf16 storage with fp32 "
+                        "arithmetic",
+            "B": cfg.B, "M": cfg.M, "n": cfg.n, "r": cfg.r, "d": cfg.d, "Hm": cfg.Hm,
+            "storage": "bf16", "input_sets_rotated": bat["nsets"],
+            "algorithmic_bytes_per_step": alg["total"],
+            "committed_state_bytes_per_step": alg["committed_state"],
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "k_state",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": kb,
+            "avg_launch_us": round(kern_avg_us, 3),
+        },
+        "whole_step": {
+            "algorithmic_GBps": round(alg["total"] / (ms * 1e-3) / 1e9, 1),
+            "frac_of_hbm_peak": round(alg["total"] / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "stage_median_us": bat["stage_us"],
+            "host_enqueue_us_per_step": round(1e6 * bat["host_s"] / args.steps, 2),
+        },
+    }
+    if not args.no_b1:
+        b1 = run_b1(args, hip, torch, R, synth)
+        pcfg = b1["cfg"]
+        pbytes = algorithmic_bytes(pcfg)["total"]
+        roof_us = pbytes / (HBM_PEAK_GBS * 1e9) * 1e6
+
+        def summ(v):
+            return {"p10": round(pct(v, 10), 2), "p50": round(pct(v, 50), 2), "p90": round(pct(v, 90), 2)}
+        best = pct(b1["fused_graph_cold_us"], 50)
+        out["b1_latency"] = {
+            "workload": "paper shape: B=1, M=32 (layers 30, 62 x 16 heads), bf16 states at t=4096, n=7, "
+                        "d=5120, r=8, MLP 288->256->5120",
+            "unit": "us per 7-token draft block",
+            "fused_graph_cold": summ(b1["fused_graph_cold_us"]),
+            "fused_eager_cold": summ(b1["fused_eager_cold_us"]),
+            "fused_graph_warm_mean": round(b1["fused_graph_warm_us"], 2),
+            "fused_eager_warm_mean": round(b1["fused_eager_warm_us"], 2),
+            "unfused_torch_cold": summ(b1["unfused_torch_cold_us"]),
+            "unfused_torch_warm_mean": round(b1["unfused_torch_warm_us"], 2),
+            "algorithmic_bytes": pbytes,
+            "hbm_roofline_us": round(roof_us, 3),
+            "frac_of_hbm_roofline": round(roof_us / best, 4),
+            "unfused_vs_fused_max_abs_diff": b1["unfused_vs_fused_max_abs_diff"],
+            "unfused_gathered_equal": b1["gathered_equal"],
+        }
+    ok = True
+    if not args.no_cpu:
+        base, rep = cpu_baseline(bat, args.cpu_budget)
+        out["cpu_baseline"] = base
+        out["parity"] = {k: rep[k] for k in ("gather_bitexact", "dh_rel", "logrms_err", "feat_rel", "ok")}
+        ok = rep["ok"]
+    print(json.dumps(out))
+    sys.stdout.flush()
+    if not ok:
+        print("PARITY FAILED", file=sys.stderr)
+        sys.exit(1)
+
+
+if __name__ == "__main__":
+    main()

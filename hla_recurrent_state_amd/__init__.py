@@ -41,7 +41,8 @@ ACTS = {"silu": READY_ACT_SILU, "gelu_tanh": READY_ACT_GELU_TANH, "relu": READY_
 
 # Every symbol include/ready.h declares.
 EXPORTS = ("readyPlanCreate", "readyPlanDestroy", "readyWorkspaceSize", "readyStateReader",
-           "readyStatusString", "readyVersion")
+           "readyStateReaderProfiled", "readyStatusString", "readyVersion")
+READY_STAGES = 4
 
 
 class ReadyError(RuntimeError):
@@ -93,6 +94,8 @@ def load():
                                      P(readyWeights), P(readyOutputs), ctypes.c_void_p, ctypes.c_size_t,
                                      ctypes.c_void_p]
     lib.readyStateReader.restype = ctypes.c_int
+    lib.readyStateReaderProfiled.argtypes = lib.readyStateReader.argtypes + [P(ctypes.c_void_p)]
+    lib.readyStateReaderProfiled.restype = ctypes.c_int
     lib.readyStatusString.argtypes = [ctypes.c_int]
     lib.readyStatusString.restype = ctypes.c_char_p
     lib.readyVersion.argtypes = []
@@ -134,6 +137,15 @@ def readyStateReader(plan, states, accept_idx, h, weights, outputs, workspace, w
     """Raw call: pointers are ints, structs are the ctypes mirrors.  Returns status."""
     return load().readyStateReader(plan, ctypes.byref(states), accept_idx, h, ctypes.byref(weights),
                                    ctypes.byref(outputs), workspace, workspace_bytes, stream)
+
+
+def readyStateReaderProfiled(plan, states, accept_idx, h, weights, outputs, workspace, workspace_bytes,
+                             stream, events):
+    """As readyStateReader; `events` is a sequence of READY_STAGES + 1
+    hipEvent_t handles (ints) or None entries."""
+    ev = (ctypes.c_void_p * (READY_STAGES + 1))(*[e for e in events])
+    return load().readyStateReaderProfiled(plan, ctypes.byref(states), accept_idx, h, ctypes.byref(weights),
+                                           ctypes.byref(outputs), workspace, workspace_bytes, stream, ev)
 
 
 # ------------------------------------------------------------ torch wrapper
@@ -191,7 +203,7 @@ class StateReader:
         return self._ws
 
     def __call__(self, states, accept_idx, h, weights, gathered, out, logrms=None, delta=None,
-                 feat=None, dev_status=None, workspace=None, stream=None):
+                 feat=None, dev_status=None, workspace=None, stream=None, events=None):
         import torch
         if states.dim() != 6:
             raise ReadyError(READY_ERR_BAD_SHAPE, "states must be [B][P][L_tot][H][128][128]")
@@ -205,7 +217,11 @@ class StateReader:
             workspace = self.workspace(h.device)
         if stream is None:
             stream = torch.cuda.current_stream(h.device).cuda_stream
-        code = readyStateReader(self.plan, sd, accept_idx.data_ptr(), h.data_ptr(), wd, od,
-                                workspace.data_ptr(), workspace.numel() * workspace.element_size(), stream)
+        args = (self.plan, sd, accept_idx.data_ptr(), h.data_ptr(), wd, od, workspace.data_ptr(),
+                workspace.numel() * workspace.element_size(), stream)
+        if events is None:
+            code = readyStateReader(*args)
+        else:
+            code = readyStateReaderProfiled(*args, events)
         if code != READY_OK:
             raise ReadyError(code, "readyStateReader")

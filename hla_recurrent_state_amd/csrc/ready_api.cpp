@@ -138,10 +138,16 @@ readyStatus readyWorkspaceSize(const readyPlan* plan, size_t* bytes) {
   return READY_OK;
 }
 
-readyStatus readyStateReader(const readyPlan* plan, const readyStates* states,
-                             const int32_t* accept_idx, const void* h,
-                             const readyWeights* w, const readyOutputs* o,
-                             void* workspace, size_t workspace_bytes, void* stream) {
+namespace {
+
+readyStatus mark(void* const* events, int i, hipStream_t s) {
+  if (events && events[i] && hipEventRecord((hipEvent_t)events[i], s) != hipSuccess) return READY_ERR_HIP;
+  return READY_OK;
+}
+
+readyStatus run_reader(const readyPlan* plan, const readyStates* states, const int32_t* accept_idx,
+                       const void* h, const readyWeights* w, const readyOutputs* o, void* workspace,
+                       size_t workspace_bytes, void* stream, void* const* events) {
   if (!plan || !states || !w || !o) return READY_ERR_NULL_POINTER;
   const readyShape& s = plan->s;
   if (!states->base || !accept_idx || !h || !w->wq || !w->u || !w->v || !w->w1 || !w->w2 ||
@@ -208,6 +214,7 @@ readyStatus readyStateReader(const readyPlan* plan, const readyStates* states,
   const int wvw = (int)(16 / ws);
 
   // 1. z partials and sums of squares of h
+  if (mark(events, 0, strm) != READY_OK) return READY_ERR_HIP;
   {
     GemmArgs g;
     memset(&g, 0, sizeof(g));
@@ -222,6 +229,7 @@ readyStatus readyStateReader(const readyPlan* plan, const readyStates* states,
       return READY_ERR_HIP;
   }
   // 2. per-state work
+  if (mark(events, 1, strm) != READY_OK) return READY_ERR_HIP;
   {
     StateArgs a;
     memset(&a, 0, sizeof(a));
@@ -238,6 +246,7 @@ readyStatus readyStateReader(const readyPlan* plan, const readyStates* states,
     if (ready_launch_state(a, s.state_dtype, s.weight_dtype, strm) != hipSuccess) return READY_ERR_HIP;
   }
   // 3. a = act(W1 f + b1)
+  if (mark(events, 2, strm) != READY_OK) return READY_ERR_HIP;
   {
     GemmArgs g;
     memset(&g, 0, sizeof(g));
@@ -251,6 +260,7 @@ readyStatus readyStateReader(const readyPlan* plan, const readyStates* states,
       return READY_ERR_HIP;
   }
   // 4. out = h + W2 a + b2
+  if (mark(events, 3, strm) != READY_OK) return READY_ERR_HIP;
   {
     GemmArgs g;
     memset(&g, 0, sizeof(g));
@@ -263,7 +273,24 @@ readyStatus readyStateReader(const readyPlan* plan, const readyStates* states,
     if (ready_launch_gemm(g, READY_F32, s.weight_dtype, s.act_dtype, EPI_RESID, grid, lds, strm) != hipSuccess)
       return READY_ERR_HIP;
   }
-  return READY_OK;
+  return mark(events, READY_STAGES, strm);
+}
+
+}  // namespace
+
+readyStatus readyStateReader(const readyPlan* plan, const readyStates* states,
+                             const int32_t* accept_idx, const void* h,
+                             const readyWeights* w, const readyOutputs* o,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+  return run_reader(plan, states, accept_idx, h, w, o, workspace, workspace_bytes, stream, nullptr);
+}
+
+readyStatus readyStateReaderProfiled(const readyPlan* plan, const readyStates* states,
+                                     const int32_t* accept_idx, const void* h,
+                                     const readyWeights* w, const readyOutputs* o,
+                                     void* workspace, size_t workspace_bytes, void* stream,
+                                     void* const* events) {
+  return run_reader(plan, states, accept_idx, h, w, o, workspace, workspace_bytes, stream, events);
 }
 
 }  // extern "C"

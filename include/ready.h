@@ -177,6 +177,22 @@ readyStatus readyStateReader(const readyPlan* plan, const readyStates* states,
                              const readyWeights* weights, const readyOutputs* outputs,
                              void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Same computation as readyStateReader, with timing marks: events[i] (a
+ * hipEvent_t, or NULL to skip) is recorded on `stream` right before launch
+ * stage i and events[READY_STAGES] right after the last stage.  Stages:
+ * 0 query GEMM (z and the sums of squares of h), 1 per-state kernel (gather,
+ * RMS, T, readout, packing), 2 first MLP layer, 3 second MLP layer and
+ * residual.  The events must have been created by the caller on the device
+ * of `stream`; the library only records them.
+ */
+#define READY_STAGES 4
+readyStatus readyStateReaderProfiled(const readyPlan* plan, const readyStates* states,
+                                     const int32_t* accept_idx, const void* h,
+                                     const readyWeights* weights, const readyOutputs* outputs,
+                                     void* workspace, size_t workspace_bytes, void* stream,
+                                     void* const* events);
+
 /* Static, human-readable name of a status code. */
 const char* readyStatusString(readyStatus status);
 
