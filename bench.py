@@ -36,7 +36,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "state-reader µs per 7-token draft block (B=1); committed-state GB/s at B=64"
 HBM_PEAK_GBS = 8000.0
-KERNEL_SRC = os.path.join(ROOT, "hla_recurrent_state_amd", "csrc", "ready_kernels.hip")
+KERNEL_SRC = os.path.join(ROOT, "hla_recurrent_state_amd", "csrc", "ready_state.hip")
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "k_state_batched_pmc.md")
 
 
@@ -321,7 +321,7 @@ def run_b1(args, hip, torch, R, synth, seed=0):
     for _ in range(10):
         call()
     torch.cuda.synchronize(device)
-    res = {}
+    res = {"stage_us": stage_breakdown(hip, lib, sets, R, stream, torch, device, reps=50)}
     res["fused_eager_cold_us"] = timed(call, True, K)
     res["fused_eager_warm_us"] = back_to_back(call, K)
 
@@ -519,6 +519,7 @@ def main():
             "algorithmic_bytes": pbytes,
             "hbm_roofline_us": round(roof_us, 3),
             "frac_of_hbm_roofline": round(roof_us / best, 4),
+            "stage_median_us": b1["stage_us"],
             "unfused_vs_fused_max_abs_diff": b1["unfused_vs_fused_max_abs_diff"],
             "unfused_gathered_equal": b1["gathered_equal"],
         }

@@ -1,14 +1,24 @@
 // Host side of the ready.h C ABI: argument validation, the plan (kernel
 // choices and workspace layout) and the launch sequence.
 //
-// The launch sequence for one call, on the caller's stream:
-//   1. k_gemm<EPI_PARTIAL>   z partial sums W_q (gamma*h) per K split, and the
-//                            partial sums of squares of h (RMSNorm of h).
-//   2. k_state               per (sequence, pair): gather, RMS, log-RMS,
-//                            T = V^T S_bar, q = U^T z, u = T q / sqrt(d_k),
-//                            packing into f.
-//   3. k_gemm<EPI_BIAS_ACT>  a = act(W1 f + b1).
-//   4. k_gemm<EPI_RESID>     out = h + W2 a + b2 (and Delta h).
+// Two launch sequences, both on the caller's stream:
+//
+// decoupled (bf16 states and weights, r <= 32):
+//   0. query GEMM   z partial sums W_q (gamma h) and sums of squares of h
+//   1. k_state_p    per (sequence, pair): gather, RMS, log-RMS and
+//                   P = V^T S_bar U^T / sqrt(d_k) (r x r)
+//   2. k_feat       f_j = [P z_j / rms(h_j), ell] per pair;
+//      MLP layer 1  a = act(W1 f + b1)
+//   3. MLP layer 2  out = h + W2 a + b2
+// coupled (any other dtype mix or rank):
+//   0. query GEMM
+//   1. k_state      gather, RMS, log-RMS, T = V^T S_bar, q = U^T z,
+//                   u = T q / sqrt(d_k), packing into f
+//   2. MLP layer 1
+//   3. MLP layer 2
+// Each GEMM runs on the matrix cores when the weights are bf16 and the rows
+// are 16-byte aligned, on the VALU otherwise.
+//
 // Validation never touches the HIP runtime, so every argument error can be
 // exercised on a machine without a GPU.
 #include <stdlib.h>
@@ -20,12 +30,20 @@
 
 #include "ready_internal.h"
 
+struct GemmPlan {
+  int mfma;      // matrix-core kernel
+  int bm;        // rows per tile (matrix-core kernel)
+  int ksplit;    // K splits (query GEMM only)
+  int kchunk;
+};
+
 struct readyPlan {
   readyShape s;
   int32_t slot[READY_MAX_LSEL];
   int M, F, R, Mz, Nz;
-  int z_ksplit, z_kchunk;
-  size_t off_zpart, off_hss, off_f, off_a, off_flags, ws_bytes;
+  int decoupled;
+  GemmPlan gz, g1, g2;
+  size_t off_zpart, off_hss, off_f, off_a, off_flags, off_pmat, off_ell, ws_bytes;
 };
 
 namespace {
@@ -105,23 +123,49 @@ readyStatus readyPlanCreate(const readyShape* shape, const int32_t* layer_ids, r
   p->Mz = s.shared_params ? 1 : p->M;
   p->Nz = p->Mz * s.r;
 
-  // K split of the query GEMM: aim for about 512 workgroups in total, with
-  // every split a multiple of 128 columns of h.
-  const int64_t base_wgs = cdiv(p->Nz, READY_GEMM_COLS) * cdiv(std::max(p->R, 1), READY_GEMM_RB);
-  int64_t ks = std::max<int64_t>(1, cdiv(512, base_wgs));
-  ks = std::min<int64_t>(ks, cdiv(s.d, 128));
-  int64_t kchunk = align_up((size_t)cdiv(s.d, ks), 128);
-  ks = cdiv(s.d, kchunk);
-  p->z_ksplit = (int)ks;
-  p->z_kchunk = (int)kchunk;
+  const bool wbf = s.weight_dtype == READY_BF16;
+  p->decoupled = (s.state_dtype == READY_BF16 && wbf && s.r <= 32) ? 1 : 0;
+
+  // query GEMM: matrix cores for bf16 h and weights; K split so that about
+  // 256 (matrix cores) or 512 (VALU) workgroups run
+  p->gz.mfma = (wbf && s.act_dtype == READY_BF16) ? 1 : 0;
+  if (p->gz.mfma) {
+    p->gz.bm = p->R <= 16 ? 16 : 64;
+    const int64_t tiles = cdiv(p->Nz, READY_MFMA_BN) * cdiv(std::max(p->R, 1), p->gz.bm);
+    int64_t ks = std::max<int64_t>(1, cdiv(256, tiles));
+    ks = std::min<int64_t>(ks, cdiv(s.d, READY_MFMA_BK));
+    const int64_t kchunk = align_up((size_t)cdiv(s.d, ks), READY_MFMA_BK);
+    p->gz.kchunk = (int)kchunk;
+    p->gz.ksplit = (int)cdiv(s.d, kchunk);
+  } else {
+    const int64_t tiles = cdiv(p->Nz, READY_GEMM_COLS) * cdiv(std::max(p->R, 1), READY_GEMM_RB);
+    int64_t ks = std::max<int64_t>(1, cdiv(512, tiles));
+    ks = std::min<int64_t>(ks, cdiv(s.d, 128));
+    const int64_t kchunk = align_up((size_t)cdiv(s.d, ks), 128);
+    p->gz.kchunk = (int)kchunk;
+    p->gz.ksplit = (int)cdiv(s.d, kchunk);
+  }
+  // MLP layers: f and a are fp32 rows of F and Hm values
+  p->g1.mfma = (wbf && p->F % 8 == 0) ? 1 : 0;
+  p->g1.bm = p->R <= 16 ? 16 : 64;
+  p->g1.ksplit = 1;
+  p->g1.kchunk = p->F;
+  p->g2.mfma = (wbf && s.Hm % 8 == 0) ? 1 : 0;
+  p->g2.bm = p->R <= 16 ? 16 : 64;
+  p->g2.ksplit = 1;
+  p->g2.kchunk = s.Hm;
 
   const size_t R = (size_t)p->R;
+  const size_t BM = (size_t)s.B * p->M;
+  const size_t ks = (size_t)p->gz.ksplit;
   size_t off = 0;
-  p->off_zpart = off; off = align_up(off + 4 * (size_t)ks * R * p->Nz, 256);
-  p->off_hss = off;   off = align_up(off + 4 * (size_t)ks * R, 256);
+  p->off_zpart = off; off = align_up(off + 4 * ks * R * p->Nz, 256);
+  p->off_hss = off;   off = align_up(off + 4 * ks * R, 256);
   p->off_f = off;     off = align_up(off + 4 * R * p->F, 256);
   p->off_a = off;     off = align_up(off + 4 * R * s.Hm, 256);
   p->off_flags = off; off = align_up(off + 4 * (size_t)std::max(s.B, 1), 256);
+  p->off_pmat = off;  off = align_up(off + (p->decoupled ? 4 * BM * s.r * s.r : 0), 256);
+  p->off_ell = off;   off = align_up(off + (p->decoupled ? 4 * BM : 0), 256);
   p->ws_bytes = off;
   *plan = p;
   return READY_OK;
@@ -211,24 +255,33 @@ readyStatus run_reader(const readyPlan* plan, const readyStates* states, const i
   float* fbuf = (float*)(wsb + plan->off_f);
   float* abuf = (float*)(wsb + plan->off_a);
   int32_t* flags = (int32_t*)(wsb + plan->off_flags);
+  float* pmat = (float*)(wsb + plan->off_pmat);
+  float* ellw = (float*)(wsb + plan->off_ell);
   const int wvw = (int)(16 / ws);
 
-  // 1. z partials and sums of squares of h
+  // 0. z partials and sums of squares of h
   if (mark(events, 0, strm) != READY_OK) return READY_ERR_HIP;
   {
     GemmArgs g;
     memset(&g, 0, sizeof(g));
     g.X = h; g.ldx = d; g.W = w->wq; g.ldw = d;
-    g.R = (int)R; g.N = plan->Nz; g.K = (int)d; g.kchunk = plan->z_kchunk;
-    g.vec_ok = (d % wvw == 0) && (plan->z_kchunk % wvw == 0);
+    g.R = (int)R; g.N = plan->Nz; g.K = (int)d; g.kchunk = plan->gz.kchunk;
+    g.vec_ok = (d % wvw == 0) && (plan->gz.kchunk % wvw == 0);
     g.gamma = w->h_gamma; g.hss = hss; g.ypart = zpart;
-    const dim3 grid((unsigned)cdiv(plan->Nz, READY_GEMM_COLS), (unsigned)plan->z_ksplit,
-                    (unsigned)cdiv(R, READY_GEMM_RB));
-    const size_t lds = 4 * READY_GEMM_RB * (size_t)std::min(plan->z_kchunk, READY_GEMM_KSTAGE);
-    if (ready_launch_gemm(g, s.act_dtype, s.weight_dtype, s.act_dtype, EPI_PARTIAL, grid, lds, strm) != hipSuccess)
-      return READY_ERR_HIP;
+    hipError_t e;
+    if (plan->gz.mfma) {
+      const dim3 grid((unsigned)cdiv(plan->Nz, READY_MFMA_BN), (unsigned)plan->gz.ksplit,
+                      (unsigned)cdiv(R, plan->gz.bm));
+      e = ready_launch_gemm_mfma(g, s.act_dtype, s.act_dtype, EPI_PARTIAL, plan->gz.bm, grid, strm);
+    } else {
+      const dim3 grid((unsigned)cdiv(plan->Nz, READY_GEMM_COLS), (unsigned)plan->gz.ksplit,
+                      (unsigned)cdiv(R, READY_GEMM_RB));
+      const size_t lds = 4 * READY_GEMM_RB * (size_t)std::min(plan->gz.kchunk, READY_GEMM_KSTAGE);
+      e = ready_launch_gemm(g, s.act_dtype, s.weight_dtype, s.act_dtype, EPI_PARTIAL, grid, lds, strm);
+    }
+    if (e != hipSuccess) return READY_ERR_HIP;
   }
-  // 2. per-state work
+  // 1. per-state work
   if (mark(events, 1, strm) != READY_OK) return READY_ERR_HIP;
   {
     StateArgs a;
@@ -240,13 +293,26 @@ readyStatus run_reader(const readyPlan* plan, const readyStates* states, const i
     a.B = s.B; a.P = s.P; a.n = s.n; a.M = (int)M; a.H = s.H; a.r = s.r; a.d = (int)d; a.F = (int)F;
     a.shared = s.shared_params; a.state_eps = s.state_eps; a.h_eps = s.h_eps;
     a.u = w->u; a.v = w->v;
-    a.zpart = zpart; a.hss = hss; a.ksz = plan->z_ksplit; a.nz = plan->Nz;
-    a.gathered = o->gathered; a.logrms = o->logrms; a.f = fbuf; a.feat = o->feat;
+    a.gathered = o->gathered; a.logrms = o->logrms;
     a.dev_status = o->dev_status; a.seq_invalid = flags;
-    if (ready_launch_state(a, s.state_dtype, s.weight_dtype, strm) != hipSuccess) return READY_ERR_HIP;
+    a.zpart = zpart; a.hss = hss; a.ksz = plan->gz.ksplit; a.nz = plan->Nz;
+    a.f = fbuf; a.feat = o->feat;
+    a.pmat = pmat; a.ell = ellw;
+    const hipError_t e = plan->decoupled ? ready_launch_state_p(a, strm)
+                                         : ready_launch_state(a, s.state_dtype, s.weight_dtype, strm);
+    if (e != hipSuccess) return READY_ERR_HIP;
   }
-  // 3. a = act(W1 f + b1)
+  // 2. (decoupled: f = [P z, ell]) then a = act(W1 f + b1)
   if (mark(events, 2, strm) != READY_OK) return READY_ERR_HIP;
+  if (plan->decoupled) {
+    FeatArgs fa;
+    memset(&fa, 0, sizeof(fa));
+    fa.pmat = pmat; fa.ell = ellw; fa.zpart = zpart; fa.hss = hss;
+    fa.ksz = plan->gz.ksplit; fa.nz = plan->Nz; fa.R = (int)R; fa.n = s.n; fa.M = (int)M; fa.r = s.r;
+    fa.F = (int)F; fa.d = (int)d; fa.shared = s.shared_params; fa.h_eps = s.h_eps;
+    fa.f = fbuf; fa.feat = o->feat;
+    if (ready_launch_feat(fa, strm) != hipSuccess) return READY_ERR_HIP;
+  }
   {
     GemmArgs g;
     memset(&g, 0, sizeof(g));
@@ -254,12 +320,18 @@ readyStatus run_reader(const readyPlan* plan, const readyStates* states, const i
     g.R = (int)R; g.N = (int)Hm; g.K = (int)F; g.kchunk = (int)F;
     g.vec_ok = (F % wvw == 0);
     g.bias = w->b1; g.act = s.act; g.yout = abuf;
-    const dim3 grid((unsigned)cdiv(Hm, READY_GEMM_COLS), 1u, (unsigned)cdiv(R, READY_GEMM_RB));
-    const size_t lds = 4 * READY_GEMM_RB * (size_t)std::min((int)F, READY_GEMM_KSTAGE);
-    if (ready_launch_gemm(g, READY_F32, s.weight_dtype, s.act_dtype, EPI_BIAS_ACT, grid, lds, strm) != hipSuccess)
-      return READY_ERR_HIP;
+    hipError_t e;
+    if (plan->g1.mfma) {
+      const dim3 grid((unsigned)cdiv(Hm, READY_MFMA_BN), 1u, (unsigned)cdiv(R, plan->g1.bm));
+      e = ready_launch_gemm_mfma(g, READY_F32, s.act_dtype, EPI_BIAS_ACT, plan->g1.bm, grid, strm);
+    } else {
+      const dim3 grid((unsigned)cdiv(Hm, READY_GEMM_COLS), 1u, (unsigned)cdiv(R, READY_GEMM_RB));
+      const size_t lds = 4 * READY_GEMM_RB * (size_t)std::min((int)F, READY_GEMM_KSTAGE);
+      e = ready_launch_gemm(g, READY_F32, s.weight_dtype, s.act_dtype, EPI_BIAS_ACT, grid, lds, strm);
+    }
+    if (e != hipSuccess) return READY_ERR_HIP;
   }
-  // 4. out = h + W2 a + b2
+  // 3. out = h + W2 a + b2
   if (mark(events, 3, strm) != READY_OK) return READY_ERR_HIP;
   {
     GemmArgs g;
@@ -268,10 +340,16 @@ readyStatus run_reader(const readyPlan* plan, const readyStates* states, const i
     g.R = (int)R; g.N = (int)d; g.K = (int)Hm; g.kchunk = (int)Hm;
     g.vec_ok = (Hm % wvw == 0);
     g.bias = w->b2; g.h = h; g.out = o->out; g.delta = o->delta; g.seq_invalid = flags; g.n = s.n;
-    const dim3 grid((unsigned)cdiv(d, READY_GEMM_COLS), 1u, (unsigned)cdiv(R, READY_GEMM_RB));
-    const size_t lds = 4 * READY_GEMM_RB * (size_t)std::min((int)Hm, READY_GEMM_KSTAGE);
-    if (ready_launch_gemm(g, READY_F32, s.weight_dtype, s.act_dtype, EPI_RESID, grid, lds, strm) != hipSuccess)
-      return READY_ERR_HIP;
+    hipError_t e;
+    if (plan->g2.mfma) {
+      const dim3 grid((unsigned)cdiv(d, READY_MFMA_BN), 1u, (unsigned)cdiv(R, plan->g2.bm));
+      e = ready_launch_gemm_mfma(g, READY_F32, s.act_dtype, EPI_RESID, plan->g2.bm, grid, strm);
+    } else {
+      const dim3 grid((unsigned)cdiv(d, READY_GEMM_COLS), 1u, (unsigned)cdiv(R, READY_GEMM_RB));
+      const size_t lds = 4 * READY_GEMM_RB * (size_t)std::min((int)Hm, READY_GEMM_KSTAGE);
+      e = ready_launch_gemm(g, READY_F32, s.weight_dtype, s.act_dtype, EPI_RESID, grid, lds, strm);
+    }
+    if (e != hipSuccess) return READY_ERR_HIP;
   }
   return mark(events, READY_STAGES, strm);
 }

@@ -1,0 +1,310 @@
+// GEMM kernels of the ReaDy state reader for gfx950: Y = X W^T over rows of
+// X (draft positions) and rows of W (output features), used for
+//   z   = W_q (gamma * h)        (query bottleneck; split-K partial sums, with
+//                                 the sums of squares of h for RMSNorm),
+//   a   = act(W1 f + b1)         (first layer of the bottleneck MLP),
+//   out = h + W2 a + b2          (second layer and the residual).
+// ReaDy arXiv text, section 3.1 "Position-conditioned reading" and "Fusion and
+// residual injection" (Eqs. (3)-(4); rainbus summary, 方法步骤详情 (2)-(3)).
+//
+//   k_gemm       VALU: each workgroup owns 16 columns and 8 rows, stages X in
+//                LDS in fp32 and streams W with 16-byte loads (any dtypes).
+//   k_gemm_mfma  matrix cores: bf16 operands (X narrowed to bf16 when it is
+//                fp32), fp32 accumulation, 64-column tiles of 16 or 64 rows.
+#include "ready_common.h"
+
+// ---------------------------------------------------------------- k_gemm
+
+// Each workgroup owns 16 output columns (4 waves x 4 groups of LPC = 16
+// lanes), READY_GEMM_RB rows and one K split.  X rows are staged in LDS in fp32
+// by passes of READY_GEMM_KSTAGE; each lane group streams its column of W
+// with 16-byte loads and keeps RB accumulators.
+template <typename TX, typename TW, typename TO, int EPI>
+__global__ __launch_bounds__(256) void k_gemm(GemmArgs g) {
+  constexpr int RB = READY_GEMM_RB;
+  constexpr int LPC = 16;
+  constexpr int VW = Elem<TW>::VW;
+  extern __shared__ float xs[];  // [RB][klen]
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int grp = lane / LPC, lic = lane - grp * LPC;
+  const int c = blockIdx.x * READY_GEMM_COLS + wave * 4 + grp;
+  const int ks = blockIdx.y;
+  const int row0 = blockIdx.z * RB;
+  const int nrows = min(RB, g.R - row0);
+  const int kbeg = ks * g.kchunk;
+  const int kend = min(g.K, kbeg + g.kchunk);
+  const bool want_hss = (EPI == EPI_PARTIAL) && g.hss != nullptr && blockIdx.x == 0;
+
+  float acc[RB];
+#pragma unroll
+  for (int i = 0; i < RB; ++i) acc[i] = 0.0f;
+  float hsq0 = 0.0f, hsq1 = 0.0f;  // rows `wave` and `wave + 4`
+
+  for (int k0 = kbeg; k0 < kend; k0 += READY_GEMM_KSTAGE) {
+    const int klen = min(READY_GEMM_KSTAGE, kend - k0);
+    __syncthreads();
+    for (int e = tid; e < RB * klen; e += 256) {
+      const int rr = e / klen, kk = e - rr * klen;
+      float x = 0.0f;
+      if (rr < nrows) x = Elem<TX>::ld(g.X, (int64_t)(row0 + rr) * g.ldx + k0 + kk);
+      xs[e] = x;
+    }
+    __syncthreads();
+    if (want_hss) {
+      for (int kk = lane; kk < klen; kk += 64) {
+        const float x0 = xs[wave * klen + kk], x1 = xs[(wave + 4) * klen + kk];
+        hsq0 += x0 * x0;
+        hsq1 += x1 * x1;
+      }
+    }
+    if (EPI == EPI_PARTIAL && g.gamma != nullptr) {
+      __syncthreads();
+      for (int e = tid; e < RB * klen; e += 256) {
+        const int kk = e % klen;
+        xs[e] *= Elem<TW>::ld(g.gamma, k0 + kk);
+      }
+      __syncthreads();
+    }
+    if (c < g.N) {
+      const TW* wrow = (const TW*)g.W + (int64_t)c * g.ldw + k0;
+      if (g.vec_ok) {
+        for (int kk = lic * VW; kk < klen; kk += LPC * VW) {
+          float w[VW];
+          Elem<TW>::unpack(*(const u32x4*)(wrow + kk), w);
+#pragma unroll
+          for (int rr = 0; rr < RB; ++rr)
+#pragma unroll
+            for (int e = 0; e < VW; ++e) acc[rr] += w[e] * xs[rr * klen + kk + e];
+        }
+      } else {
+        for (int kk = lic; kk < klen; kk += LPC) {
+          const float w = Elem<TW>::ld(wrow, kk);
+#pragma unroll
+          for (int rr = 0; rr < RB; ++rr) acc[rr] += w * xs[rr * klen + kk];
+        }
+      }
+    }
+  }
+
+#pragma unroll
+  for (int rr = 0; rr < RB; ++rr)
+#pragma unroll
+    for (int off = LPC / 2; off > 0; off >>= 1) acc[rr] += __shfl_xor(acc[rr], off, 64);
+
+  if (want_hss) {
+    hsq0 = wave_sum(hsq0);
+    hsq1 = wave_sum(hsq1);
+    if (lane == 0) {
+      if (wave < nrows) g.hss[(int64_t)ks * g.R + row0 + wave] = hsq0;
+      if (wave + 4 < nrows) g.hss[(int64_t)ks * g.R + row0 + wave + 4] = hsq1;
+    }
+  }
+
+  if (lic != 0 || c >= g.N) return;
+  for (int rr = 0; rr < nrows; ++rr) {
+    const int64_t rho = row0 + rr;
+    if (EPI == EPI_PARTIAL) {
+      g.ypart[((int64_t)ks * g.R + rho) * g.N + c] = acc[rr];
+    } else if (EPI == EPI_BIAS_ACT) {
+      const float pre = acc[rr] + (g.bias ? Elem<TW>::ld(g.bias, c) : 0.0f);
+      g.yout[rho * g.N + c] = activation(pre, g.act);
+    } else {
+      if (g.seq_invalid[rho / g.n]) continue;
+      const float dh = acc[rr] + (g.bias ? Elem<TW>::ld(g.bias, c) : 0.0f);
+      const float hv = Elem<TO>::ld(g.h, rho * g.N + c);
+      Elem<TO>::st(g.out, rho * g.N + c, hv + dh);
+      if (g.delta) g.delta[rho * g.N + c] = dh;
+    }
+  }
+}
+
+
+// ---------------------------------------------------------------- k_gemm_mfma
+
+// Tile BM x 64 outputs, K in steps of 64 staged in LDS as bf16 (rows padded to
+// 72 elements).  Wave w owns output columns [16 w, 16 w + 16) and every 16-row
+// block of the tile; per K step it issues 2 x (BM / 16) 16 x 16 x 32 matrix
+// instructions.  Requires K, ldx and ldw to keep 16-byte row chunks aligned.
+template <typename TX, typename TO, int EPI, int BM>
+__global__ __launch_bounds__(256) void k_gemm_mfma(GemmArgs g) {
+  constexpr int BN = READY_MFMA_BN, BK = READY_MFMA_BK, LDK = BK + 8;
+  constexpr int WM = BM / 16;
+  constexpr bool XBF = sizeof(TX) == 2;
+  constexpr int XCH = XBF ? BM * 8 : BM * 16;          // 16-byte X chunks per K step
+  constexpr int NIT = (XCH + 255) / 256;
+  __shared__ __attribute__((aligned(16))) uint16_t sX[BM * LDK];
+  __shared__ __attribute__((aligned(16))) uint16_t sW[BN * LDK];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int col0 = blockIdx.x * BN, ks = blockIdx.y, row0 = blockIdx.z * BM;
+  const int kbeg = ks * g.kchunk;
+  const int kend = min(g.K, kbeg + g.kchunk);
+  const bool want_hss = (EPI == EPI_PARTIAL) && XBF && g.hss != nullptr && blockIdx.x == 0;
+  const uint16_t* W = (const uint16_t*)g.W;
+
+  f32x4 acc[WM];
+#pragma unroll
+  for (int rb = 0; rb < WM; ++rb) acc[rb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  float hsq[NIT];
+#pragma unroll
+  for (int it = 0; it < NIT; ++it) hsq[it] = 0.0f;
+
+  for (int k0 = kbeg; k0 < kend; k0 += BK) {
+    // W tile: 64 rows x 64 k = 512 chunks of 8 bf16
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+      const int c = tid + 256 * it;
+      const int nn = c >> 3, kc = (c & 7) * 8;
+      const int gn = col0 + nn, gk = k0 + kc;
+      u32x4 v = u32x4{0u, 0u, 0u, 0u};
+      if (gn < g.N && gk < kend) v = *(const u32x4*)(W + (int64_t)gn * g.ldw + gk);
+      *(u32x4*)&sW[nn * LDK + kc] = v;
+    }
+    // X tile: BM rows x 64 k, narrowed to bf16
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
+      const int c = tid + 256 * it;
+      if (c < XCH) {
+        if (XBF) {
+          const int rr = c >> 3, kc = (c & 7) * 8;
+          const int gr = row0 + rr, gk = k0 + kc;
+          u32x4 v = u32x4{0u, 0u, 0u, 0u};
+          if (gr < g.R && gk < kend) v = *(const u32x4*)((const uint16_t*)g.X + (int64_t)gr * g.ldx + gk);
+          if (want_hss || g.gamma != nullptr) {
+            float x[8];
+            Elem<uint16_t>::unpack(v, x);
+            if (want_hss) {
+              float sq = 0.0f;
+#pragma unroll
+              for (int e = 0; e < 8; ++e) sq += x[e] * x[e];
+              // the 8 chunks of one row sit in 8 consecutive lanes
+              sq += __shfl_xor(sq, 1, 64);
+              sq += __shfl_xor(sq, 2, 64);
+              sq += __shfl_xor(sq, 4, 64);
+              hsq[it] += sq;
+            }
+            if (g.gamma != nullptr && gk < kend) {
+              uint32_t w4[4];
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                const float a0 = x[2 * e] * Elem<uint16_t>::ld(g.gamma, gk + 2 * e);
+                const float a1 = x[2 * e + 1] * Elem<uint16_t>::ld(g.gamma, gk + 2 * e + 1);
+                w4[e] = (uint32_t)f32_to_bf16_rne(a0) | ((uint32_t)f32_to_bf16_rne(a1) << 16);
+              }
+              v = u32x4{w4[0], w4[1], w4[2], w4[3]};
+            }
+          }
+          *(u32x4*)&sX[rr * LDK + kc] = v;
+        } else {
+          const int rr = c >> 4, kc = (c & 15) * 4;
+          const int gr = row0 + rr, gk = k0 + kc;
+          u32x4 v = u32x4{0u, 0u, 0u, 0u};
+          if (gr < g.R && gk < kend) v = *(const u32x4*)((const float*)g.X + (int64_t)gr * g.ldx + gk);
+          const uint32_t lo = (uint32_t)f32_to_bf16_rne(__uint_as_float(v.x)) |
+                              ((uint32_t)f32_to_bf16_rne(__uint_as_float(v.y)) << 16);
+          const uint32_t hi = (uint32_t)f32_to_bf16_rne(__uint_as_float(v.z)) |
+                              ((uint32_t)f32_to_bf16_rne(__uint_as_float(v.w)) << 16);
+          *(uint2*)&sX[rr * LDK + kc] = make_uint2(lo, hi);
+        }
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const u32x4 bop = *(const u32x4*)&sW[(16 * wave + (lane & 15)) * LDK + 32 * kk + 8 * (lane >> 4)];
+#pragma unroll
+      for (int rb = 0; rb < WM; ++rb) {
+        const u32x4 aop = *(const u32x4*)&sX[(16 * rb + (lane & 15)) * LDK + 32 * kk + 8 * (lane >> 4)];
+        acc[rb] = mfma16x16x32(aop, bop, acc[rb]);
+      }
+    }
+    __syncthreads();
+  }
+
+  if (want_hss) {
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
+      const int c = tid + 256 * it;
+      const int gr = row0 + (c >> 3);
+      if (c < XCH && (c & 7) == 0 && gr < g.R) g.hss[(int64_t)ks * g.R + gr] = hsq[it];
+    }
+  }
+
+  const int col = col0 + 16 * wave + (lane & 15);
+  if (col >= g.N) return;
+  float bias = 0.0f;
+  if (EPI != EPI_PARTIAL && g.bias != nullptr) bias = Elem<uint16_t>::ld(g.bias, col);
+#pragma unroll
+  for (int rb = 0; rb < WM; ++rb)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int64_t rho = row0 + 16 * rb + 4 * (lane >> 4) + e;
+      if (rho >= g.R) continue;
+      const float y = acc[rb][e];
+      if (EPI == EPI_PARTIAL) {
+        g.ypart[((int64_t)ks * g.R + rho) * g.N + col] = y;
+      } else if (EPI == EPI_BIAS_ACT) {
+        g.yout[rho * g.N + col] = activation(y + bias, g.act);
+      } else {
+        if (g.seq_invalid[rho / g.n]) continue;
+        const float dh = y + bias;
+        const float hv = Elem<TO>::ld(g.h, rho * g.N + col);
+        Elem<TO>::st(g.out, rho * g.N + col, hv + dh);
+        if (g.delta) g.delta[rho * g.N + col] = dh;
+      }
+    }
+}
+
+// ---------------------------------------------------------------- launchers
+template <int EPI>
+static void launch_gemm_epi(const GemmArgs& g, int x_dt, int w_dt, int out_dt, dim3 grid,
+                            size_t lds, hipStream_t s) {
+  const dim3 block(256);
+#define READY_GEMM_CASE(TX, TW, TO) hipLaunchKernelGGL((k_gemm<TX, TW, TO, EPI>), grid, block, lds, s, g)
+  if (EPI == EPI_PARTIAL) {
+    if (x_dt == READY_BF16 && w_dt == READY_BF16) READY_GEMM_CASE(uint16_t, uint16_t, float);
+    else if (x_dt == READY_BF16) READY_GEMM_CASE(uint16_t, float, float);
+    else if (w_dt == READY_BF16) READY_GEMM_CASE(float, uint16_t, float);
+    else READY_GEMM_CASE(float, float, float);
+  } else if (EPI == EPI_BIAS_ACT) {
+    if (w_dt == READY_BF16) READY_GEMM_CASE(float, uint16_t, float);
+    else READY_GEMM_CASE(float, float, float);
+  } else {
+    if (w_dt == READY_BF16 && out_dt == READY_BF16) READY_GEMM_CASE(float, uint16_t, uint16_t);
+    else if (w_dt == READY_BF16) READY_GEMM_CASE(float, uint16_t, float);
+    else if (out_dt == READY_BF16) READY_GEMM_CASE(float, float, uint16_t);
+    else READY_GEMM_CASE(float, float, float);
+  }
+#undef READY_GEMM_CASE
+  (void)x_dt;
+}
+
+hipError_t ready_launch_gemm(const GemmArgs& g, int x_dt, int w_dt, int out_dt, int epi,
+                             dim3 grid, size_t lds_bytes, hipStream_t s) {
+  if (epi == EPI_PARTIAL) launch_gemm_epi<EPI_PARTIAL>(g, x_dt, w_dt, out_dt, grid, lds_bytes, s);
+  else if (epi == EPI_BIAS_ACT) launch_gemm_epi<EPI_BIAS_ACT>(g, x_dt, w_dt, out_dt, grid, lds_bytes, s);
+  else launch_gemm_epi<EPI_RESID>(g, x_dt, w_dt, out_dt, grid, lds_bytes, s);
+  return hipGetLastError();
+}
+
+template <int BM>
+static void launch_mfma_bm(const GemmArgs& g, int x_dt, int out_dt, int epi, dim3 grid, hipStream_t s) {
+  const dim3 block(256);
+  if (epi == EPI_PARTIAL) {
+    if (x_dt == READY_BF16) hipLaunchKernelGGL((k_gemm_mfma<uint16_t, float, EPI_PARTIAL, BM>), grid, block, 0, s, g);
+    else hipLaunchKernelGGL((k_gemm_mfma<float, float, EPI_PARTIAL, BM>), grid, block, 0, s, g);
+  } else if (epi == EPI_BIAS_ACT) {
+    hipLaunchKernelGGL((k_gemm_mfma<float, float, EPI_BIAS_ACT, BM>), grid, block, 0, s, g);
+  } else {
+    if (out_dt == READY_BF16) hipLaunchKernelGGL((k_gemm_mfma<float, uint16_t, EPI_RESID, BM>), grid, block, 0, s, g);
+    else hipLaunchKernelGGL((k_gemm_mfma<float, float, EPI_RESID, BM>), grid, block, 0, s, g);
+  }
+}
+
+hipError_t ready_launch_gemm_mfma(const GemmArgs& g, int x_dt, int out_dt, int epi, int bm, dim3 grid,
+                                  hipStream_t s) {
+  if (bm == 16) launch_mfma_bm<16>(g, x_dt, out_dt, epi, grid, s);
+  else launch_mfma_bm<64>(g, x_dt, out_dt, epi, grid, s);
+  return hipGetLastError();
+}

@@ -10,9 +10,10 @@
 #define READY_MAX_LSEL 64
 #define READY_TILE 128            // d_k = d_v
 #define READY_TILE_ELEMS (READY_TILE * READY_TILE)
+#define READY_HIDDEN __attribute__((visibility("hidden")))
 
-// Arguments of the per-state kernel (steps 1-4 and packing for one
-// (sequence, pair) tile per workgroup).
+// Arguments of the per-state kernels (one (sequence, pair) tile per
+// workgroup).
 struct StateArgs {
   const void* states;
   int64_t sb, sp, sl, sh;          // element strides of the verify buffer
@@ -23,15 +24,31 @@ struct StateArgs {
   float state_eps, h_eps;
   const void* u;                   // [M][r][128] weight dtype
   const void* v;                   // [M][128][r] weight dtype
+  void* gathered;                  // [B][M][128][128] state dtype
+  float* logrms;                   // [B][M] or null
+  int32_t* dev_status;             // or null
+  int32_t* seq_invalid;            // [B] workspace
+  // coupled form (k_state): readout from q = U^T z, packing into f
   const float* zpart;              // [ksz][B*n][nz] raw partial sums of W_q (gamma*h)
   const float* hss;                // [ksz][B*n] partial sums of h^2
   int ksz, nz;
-  void* gathered;                  // [B][M][128][128] state dtype
-  float* logrms;                   // [B][M] or null
   float* f;                        // [B*n][F] workspace
   float* feat;                     // [B*n][F] or null
-  int32_t* dev_status;             // or null
-  int32_t* seq_invalid;            // [B] workspace
+  // decoupled form (k_state_p): P = V^T S_bar U^T / sqrt(d_k) and ell per tile
+  float* pmat;                     // [B*M][r][r]
+  float* ell;                      // [B*M]
+};
+
+// Packing of f_j from P, the raw query sums and ell (decoupled form).
+struct FeatArgs {
+  const float* pmat;               // [B*M][r][r]
+  const float* ell;                // [B*M]
+  const float* zpart;              // [ksz][R][nz]
+  const float* hss;                // [ksz][R]
+  int ksz, nz, R, n, M, r, F, d, shared;
+  float h_eps;
+  float* f;                        // [R][F]
+  float* feat;                     // [R][F] or null
 };
 
 enum { EPI_PARTIAL = 0, EPI_BIAS_ACT = 1, EPI_RESID = 2 };
@@ -63,13 +80,19 @@ struct GemmArgs {
   int n;
 };
 
-#define READY_HIDDEN __attribute__((visibility("hidden")))
+// VALU skinny GEMM tiling
+#define READY_GEMM_RB 8           // rows of X per workgroup
+#define READY_GEMM_KSTAGE 1024    // K elements staged in LDS per pass
+#define READY_GEMM_COLS 16        // output columns per workgroup
+// MFMA GEMM tiling
+#define READY_MFMA_BN 64
+#define READY_MFMA_BK 64
 
 READY_HIDDEN hipError_t ready_launch_state(const StateArgs& a, int state_dt, int weight_dt, hipStream_t s);
+READY_HIDDEN hipError_t ready_launch_state_p(const StateArgs& a, hipStream_t s);
+READY_HIDDEN hipError_t ready_launch_feat(const FeatArgs& a, hipStream_t s);
 READY_HIDDEN hipError_t ready_launch_gemm(const GemmArgs& g, int x_dt, int w_dt, int out_dt, int epi,
-                             dim3 grid, size_t lds_bytes, hipStream_t s);
-
-// Rows of X staged in LDS per workgroup, and K elements staged per pass.
-#define READY_GEMM_RB 8
-#define READY_GEMM_KSTAGE 1024
-#define READY_GEMM_COLS 16
+                                          dim3 grid, size_t lds_bytes, hipStream_t s);
+// bm: rows per workgroup tile (16 or 64); weights must be bf16
+READY_HIDDEN hipError_t ready_launch_gemm_mfma(const GemmArgs& g, int x_dt, int out_dt, int epi, int bm,
+                                               dim3 grid, hipStream_t s);

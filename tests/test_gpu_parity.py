@@ -204,3 +204,41 @@ def test_zero_batch_is_a_no_op():
     reader(d["states"], d["accept_idx"], d["h"], d["weights"], o["gathered"], o["out"])
     torch.cuda.synchronize()
     assert torch.all(o["out"] == 3.0)
+
+
+def test_graph_capture_replays_match_eager():
+    """The call captured into a HIP graph, replayed several times with eager
+    work and synchronisations in between; every replay equals the eager run."""
+    from hla_recurrent_state_amd import StateReader
+    import tests.gpu_util as gu
+    dev = _dev()
+    cfg = make_shape("batched", B=4, t=16)
+    inp = synth.make(cfg, seed=40)
+    d = synth.device.to_device(inp, dev)
+    reader = StateReader(gu.reader_shape(cfg), cfg.slots)
+    ws = reader.workspace(dev)
+    o = gu.alloc_outputs(cfg, dev)
+    reader(d["states"], d["accept_idx"], d["h"], d["weights"], o["gathered"], o["out"], delta=o["delta"],
+           workspace=ws)
+    torch.cuda.synchronize()
+    eager = {k: o[k].clone() for k in ("gathered", "out", "delta")}
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream(dev)
+    s.wait_stream(torch.cuda.current_stream(dev))
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            reader(d["states"], d["accept_idx"], d["h"], d["weights"], o["gathered"], o["out"],
+                   delta=o["delta"], workspace=ws, stream=s.cuda_stream)
+    torch.cuda.current_stream(dev).wait_stream(s)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        for k in ("gathered", "out", "delta"):
+            o[k].zero_()
+        junk = torch.randn(1 << 20, device=dev).sum()     # unrelated eager work
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for k in ("gathered", "out", "delta"):
+            assert torch.equal(o[k].view(torch.int8) if o[k].dtype != torch.float32 else o[k], 
+                               eager[k].view(torch.int8) if eager[k].dtype != torch.float32 else eager[k]), (rep, k)
+        del junk
