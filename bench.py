@@ -10,9 +10,10 @@ value      committed-state GB/s on the batched workload (B = 64 sequences,
            gathered bytes written) per step / time per step.  Steps rotate
            over several copies of the inputs so the 256 MB last-level cache
            cannot hold them.
-roofline   the dominant kernel (k_state): its algorithmic bytes per launch /
-           its average duration, timed with HIP events recorded around it on
-           the launch stream inside the timed loop, against 8 TB/s.
+roofline   the dominant kernel (k_fused): its algorithmic bytes per launch /
+           its average duration, timed inside the timed loop with HIP events
+           that its own launch records (hipExtLaunchKernelGGL) on the launch
+           stream, against 8 TB/s.
 b1_latency single-block latency at the paper shape (B = 1), eager and
            graph-replayed, cache-cold and warm, next to an unfused PyTorch
            eager composition of the same five steps.
@@ -36,8 +37,8 @@ sys.path.insert(0, ROOT)
 
 METRIC = "state-reader µs per 7-token draft block (B=1); committed-state GB/s at B=64"
 HBM_PEAK_GBS = 8000.0
-KERNEL_SRC = os.path.join(ROOT, "hla_recurrent_state_amd", "csrc", "ready_state.hip")
-PMC_SUMMARY = os.path.join(ROOT, "profiles", "k_state_batched_pmc.md")
+KERNEL_SRC = os.path.join(ROOT, "hla_recurrent_state_amd", "csrc", "ready_fast.hip")
+PMC_SUMMARY = os.path.join(ROOT, "profiles", "k_fused_batched_pmc.md")
 
 
 def log(*a):
@@ -101,15 +102,20 @@ def algorithmic_bytes(cfg):
             "accept_idx": 4 * B, "total": committed + weights + acts + 4 * B}
 
 
-def state_kernel_bytes(cfg):
-    """Algorithmic bytes of one k_state launch: committed states read and
-    written, U and V read once, q-side inputs (z of every pair) and the packed
-    features written."""
-    s, w = esize(cfg.state_dtype), esize(cfg.weight_dtype)
+def fused_kernel_bytes(cfg):
+    """Algorithmic bytes of one launch of the fused kernel (k_fused: every
+    step but the query GEMM), per unit: each (sequence, pair) tile reads its
+    committed 128 x 128 state and writes the copy (2 x 32768 B at bf16); each
+    draft position reads h_j for the residual and writes out_j (2 x d x 2 B);
+    the weights it applies (U, V, W1, W2) are read once; 4 B per accept index.
+    Intermediates passed between its work items (P, ell, a) and the query
+    GEMM's partial sums are implementation traffic, not counted."""
+    s, a, w = esize(cfg.state_dtype), esize(cfg.act_dtype), esize(cfg.weight_dtype)
     mz = 1 if cfg.shared else cfg.M
+    tiles = cfg.B * cfg.M
     rows = cfg.B * cfg.n
-    return (2 * cfg.B * cfg.M * 128 * 128 * s + 2 * mz * cfg.r * 128 * w
-            + rows * mz * cfg.r * 4 + rows * cfg.F * 4 + cfg.B * cfg.M * 4)
+    weights = (2 * mz * cfg.r * 128 + cfg.Hm * cfg.F + cfg.d * cfg.Hm) * w
+    return tiles * 2 * 128 * 128 * s + rows * 2 * cfg.d * a + weights + 4 * cfg.B
 
 
 def kernel_src_hash():
@@ -118,7 +124,7 @@ def kernel_src_hash():
 
 
 def read_traffic():
-    """HBM bytes per k_state launch from the committed PMC summary, if it was
+    """HBM bytes per k_fused launch from the committed PMC summary, if it was
     taken on the current kernel source."""
     if not os.path.exists(PMC_SUMMARY):
         return None
@@ -194,7 +200,9 @@ def run_batched(args, hip, torch, R, synth, seed=0):
     K, W = args.steps, args.warmup
     ev_s = [hip.event() for _ in range(K)]
     ev_e = [hip.event() for _ in range(K)]
-    ev_arrays = [(ctypes.c_void_p * (R.READY_STAGES + 1))(None, ev_s[i], ev_e[i], None, None) for i in range(K)]
+    # stage 1 (the fused kernel): its start and end, recorded by its own launch
+    ev_arrays = [(ctypes.c_void_p * (2 * R.READY_STAGES))(None, None, ev_s[i], ev_e[i], None, None, None, None)
+                 for i in range(K)]
     for i in range(W):
         code = lib.readyStateReader(*sets[i % nsets].args)
         if code != 0:
@@ -223,7 +231,10 @@ def run_batched(args, hip, torch, R, synth, seed=0):
 
 
 def stage_breakdown(hip, lib, sets, R, stream, torch, device, reps):
-    n = R.READY_STAGES + 1
+    """Median kernel duration of each launch (start and end recorded by the
+    launch itself), and of the whole call (first start to last end).  The
+    bf16 path has two launches: the query GEMM and the fused kernel."""
+    n = 2 * R.READY_STAGES
     evs = [[hip.event() for _ in range(n)] for _ in range(reps)]
     for i in range(reps):
         arr = (ctypes.c_void_p * n)(*evs[i])
@@ -231,11 +242,15 @@ def stage_breakdown(hip, lib, sets, R, stream, torch, device, reps):
         if code != 0:
             raise R.ReadyError(code, "stages")
     torch.cuda.synchronize(device)
-    names = ["query_gemm", "state_kernel", "mlp1", "mlp2_residual"]
+    names = ["k_zgemm", "k_fused"]
     out = {}
     for s, name in enumerate(names):
-        vals = [1000.0 * hip.ms(evs[i][s], evs[i][s + 1]) for i in range(reps)]
+        vals = [1000.0 * hip.ms(evs[i][2 * s], evs[i][2 * s + 1]) for i in range(reps)]
         out[name] = round(pct(vals, 50), 2)
+    out["first_start_to_last_end"] = round(pct([1000.0 * hip.ms(evs[i][0], evs[i][3]) for i in range(reps)], 50), 2)
+    for row in evs:
+        for e in row:
+            hip.destroy(e)
     return out
 
 
@@ -453,7 +468,7 @@ def main():
     ms = bat["ms_per_step"]
     value = alg["committed_state"] / (ms * 1e-3) / 1e9
     kern_avg_us = sum(bat["kern_us"]) / len(bat["kern_us"])
-    kb = state_kernel_bytes(cfg)
+    kb = fused_kernel_bytes(cfg)
     achieved = kb / (kern_avg_us * 1e-6) / 1e9
     traffic = read_traffic()
     out = {
@@ -467,7 +482,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "bf16",
         "data": "synthetic",
         "config": {
             "workload": "batched: B=64 sequences, M=32 layer-head pairs (layers 30, 62 x 16 heads), "
@@ -475,13 +490,13 @@ def main():
                         "positions, block n=7, d=5120, r=8, MLP 288->256->5120 SiLU, bf16 storage with fp32 "
                         "arithmetic",
             "B": cfg.B, "M": cfg.M, "n": cfg.n, "r": cfg.r, "d": cfg.d, "Hm": cfg.Hm,
-            "storage": "bf16", "input_sets_rotated": bat["nsets"],
+            "storage": "bf16", "accumulation": "fp32", "input_sets_rotated": bat["nsets"],
             "algorithmic_bytes_per_step": alg["total"],
             "committed_state_bytes_per_step": alg["committed_state"],
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": "k_state",
+            "kernel": "k_fused",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",

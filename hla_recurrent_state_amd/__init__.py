@@ -29,6 +29,7 @@ READY_ERR_LAYER_ID_RANGE = 7
 READY_ERR_HIP = 8
 READY_ERR_ACCEPT_IDX = 9
 READY_ERR_OUT_OF_HOST_MEMORY = 10
+READY_ERR_SYNC_TIMEOUT = 11
 
 READY_F32 = 0
 READY_BF16 = 1
@@ -141,9 +142,10 @@ def readyStateReader(plan, states, accept_idx, h, weights, outputs, workspace, w
 
 def readyStateReaderProfiled(plan, states, accept_idx, h, weights, outputs, workspace, workspace_bytes,
                              stream, events):
-    """As readyStateReader; `events` is a sequence of READY_STAGES + 1
-    hipEvent_t handles (ints) or None entries."""
-    ev = (ctypes.c_void_p * (READY_STAGES + 1))(*[e for e in events])
+    """As readyStateReader; `events` is a sequence of 2 * READY_STAGES
+    hipEvent_t handles (ints) or None entries: start and end of each stage's
+    kernel."""
+    ev = (ctypes.c_void_p * (2 * READY_STAGES))(*[e for e in events])
     return load().readyStateReaderProfiled(plan, ctypes.byref(states), accept_idx, h, ctypes.byref(weights),
                                            ctypes.byref(outputs), workspace, workspace_bytes, stream, ev)
 

@@ -3,21 +3,21 @@
 //
 // Two launch sequences, both on the caller's stream:
 //
-// decoupled (bf16 states and weights, r <= 32):
-//   0. query GEMM   z partial sums W_q (gamma h) and sums of squares of h
-//   1. k_state_p    per (sequence, pair): gather, RMS, log-RMS and
-//                   P = V^T S_bar U^T / sqrt(d_k) (r x r)
-//   2. k_feat       f_j = [P z_j / rms(h_j), ell] per pair;
-//      MLP layer 1  a = act(W1 f + b1)
-//   3. MLP layer 2  out = h + W2 a + b2
-// coupled (any other dtype mix or rank):
-//   0. query GEMM
-//   1. k_state      gather, RMS, log-RMS, T = V^T S_bar, q = U^T z,
-//                   u = T q / sqrt(d_k), packing into f
+// fast (bf16 states, activations and weights, r <= 32, F and Hm multiples of 8):
+//   0. k_zgemm    z partial sums W_q (gamma h) over K chunks, sums of squares
+//                 of h; clears the counters of k_fused
+//   1. k_fused    ticketed work items: per (sequence, pair) tile the gather,
+//                 RMS, log-RMS and P = V^T S_bar U^T / sqrt(d_k); per 16 rows
+//                 f_j = [P z_j / rms(h_j), ell] and a = act(W1 f + b1); per
+//                 output tile out = h + W2 a + b2
+// general (any other dtype mix or rank):
+//   0. query GEMM (split-K partial sums of z and of the squares of h)
+//   1. k_state    gather, RMS, log-RMS, T = V^T S_bar, q = U^T z,
+//                 u = T q / sqrt(d_k), packing into f
 //   2. MLP layer 1
-//   3. MLP layer 2
-// Each GEMM runs on the matrix cores when the weights are bf16 and the rows
-// are 16-byte aligned, on the VALU otherwise.
+//   3. MLP layer 2 and residual
+//   Each GEMM runs on the matrix cores when the weights are bf16 and the rows
+//   are 16-byte aligned, on the VALU otherwise.
 //
 // Validation never touches the HIP runtime, so every argument error can be
 // exercised on a machine without a GPU.
@@ -41,9 +41,11 @@ struct readyPlan {
   readyShape s;
   int32_t slot[READY_MAX_LSEL];
   int M, F, R, Mz, Nz;
-  int decoupled;
+  int fast;
+  int zbm, obm;  // fast path: row tile of the query GEMM and of MLP layer 2
+  int n_s, n_a, n_o, n_counters;
   GemmPlan gz, g1, g2;
-  size_t off_zpart, off_hss, off_f, off_a, off_flags, off_pmat, off_ell, ws_bytes;
+  size_t off_zpart, off_hss, off_f, off_a, off_flags, off_pmat, off_ell, off_ctr, ws_bytes;
 };
 
 namespace {
@@ -101,6 +103,7 @@ const char* readyStatusString(readyStatus st) {
     case READY_ERR_HIP: return "READY_ERR_HIP";
     case READY_ERR_ACCEPT_IDX: return "READY_ERR_ACCEPT_IDX";
     case READY_ERR_OUT_OF_HOST_MEMORY: return "READY_ERR_OUT_OF_HOST_MEMORY";
+    case READY_ERR_SYNC_TIMEOUT: return "READY_ERR_SYNC_TIMEOUT";
   }
   return "READY_ERR_UNKNOWN";
 }
@@ -124,36 +127,59 @@ readyStatus readyPlanCreate(const readyShape* shape, const int32_t* layer_ids, r
   p->Nz = p->Mz * s.r;
 
   const bool wbf = s.weight_dtype == READY_BF16;
-  p->decoupled = (s.state_dtype == READY_BF16 && wbf && s.r <= 32) ? 1 : 0;
+  const bool allbf = wbf && s.state_dtype == READY_BF16 && s.act_dtype == READY_BF16;
+  // (the fast path addresses P and a with 32-bit byte offsets)
+  const bool small_ws = (int64_t)s.B * p->M * s.r * s.r * 4 < (1LL << 31) &&
+                        (int64_t)p->R * s.Hm * 2 < (1LL << 31);
+  p->fast = (allbf && s.r <= 32 && p->F % 8 == 0 && p->F <= READY_FAST_MAX_F && s.Hm % 8 == 0 && small_ws) ? 1 : 0;
 
-  // query GEMM: matrix cores for bf16 h and weights; K split so that about
-  // 256 (matrix cores) or 512 (VALU) workgroups run
-  p->gz.mfma = (wbf && s.act_dtype == READY_BF16) ? 1 : 0;
-  if (p->gz.mfma) {
-    p->gz.bm = p->R <= 16 ? 16 : 64;
-    const int64_t tiles = cdiv(p->Nz, READY_MFMA_BN) * cdiv(std::max(p->R, 1), p->gz.bm);
-    int64_t ks = std::max<int64_t>(1, cdiv(256, tiles));
-    ks = std::min<int64_t>(ks, cdiv(s.d, READY_MFMA_BK));
-    const int64_t kchunk = align_up((size_t)cdiv(s.d, ks), READY_MFMA_BK);
-    p->gz.kchunk = (int)kchunk;
-    p->gz.ksplit = (int)cdiv(s.d, kchunk);
-  } else {
-    const int64_t tiles = cdiv(p->Nz, READY_GEMM_COLS) * cdiv(std::max(p->R, 1), READY_GEMM_RB);
-    int64_t ks = std::max<int64_t>(1, cdiv(512, tiles));
+  if (p->fast) {
+    // query GEMM: BM x 64 tiles of z over K chunks of at most 640 values (each
+    // wave loads its quarter of the chunk at once); 8 chunks for large row
+    // counts (the items of one chunk then share an XCD), 16 for at most 16
+    // rows, where the K split is the only source of parallelism
+    p->zbm = p->R <= 16 ? 16 : 64;
+    p->obm = p->R <= 16 ? 16 : 64;
+    int64_t ks = std::max<int64_t>(p->R <= 16 ? 16 : 8, cdiv(s.d, 640));
     ks = std::min<int64_t>(ks, cdiv(s.d, 128));
     const int64_t kchunk = align_up((size_t)cdiv(s.d, ks), 128);
     p->gz.kchunk = (int)kchunk;
     p->gz.ksplit = (int)cdiv(s.d, kchunk);
+    const int64_t nrb16 = cdiv(std::max(p->R, 1), 16);
+    p->n_s = s.B * p->M;
+    p->n_a = (int)(nrb16 * cdiv(s.Hm, 64));
+    p->n_o = (int)(cdiv(std::max(p->R, 1), p->obm) * cdiv(s.d, 64));
+    p->n_counters = (int)(READY_CTR_STRIDE * (2 + s.B + nrb16));
+  } else {
+    // query GEMM: matrix cores for bf16 h and weights; K split so that about
+    // 256 (matrix cores) or 512 (VALU) workgroups run
+    p->gz.mfma = (wbf && s.act_dtype == READY_BF16) ? 1 : 0;
+    if (p->gz.mfma) {
+      p->gz.bm = p->R <= 16 ? 16 : 64;
+      const int64_t tiles = cdiv(p->Nz, READY_MFMA_BN) * cdiv(std::max(p->R, 1), p->gz.bm);
+      int64_t ks = std::max<int64_t>(1, cdiv(256, tiles));
+      ks = std::min<int64_t>(ks, cdiv(s.d, READY_MFMA_BK));
+      const int64_t kchunk = align_up((size_t)cdiv(s.d, ks), READY_MFMA_BK);
+      p->gz.kchunk = (int)kchunk;
+      p->gz.ksplit = (int)cdiv(s.d, kchunk);
+    } else {
+      const int64_t tiles = cdiv(p->Nz, READY_GEMM_COLS) * cdiv(std::max(p->R, 1), READY_GEMM_RB);
+      int64_t ks = std::max<int64_t>(1, cdiv(512, tiles));
+      ks = std::min<int64_t>(ks, cdiv(s.d, 128));
+      const int64_t kchunk = align_up((size_t)cdiv(s.d, ks), 128);
+      p->gz.kchunk = (int)kchunk;
+      p->gz.ksplit = (int)cdiv(s.d, kchunk);
+    }
+    // MLP layers: f and a are fp32 rows of F and Hm values
+    p->g1.mfma = (wbf && p->F % 8 == 0) ? 1 : 0;
+    p->g1.bm = p->R <= 16 ? 16 : 64;
+    p->g1.ksplit = 1;
+    p->g1.kchunk = p->F;
+    p->g2.mfma = (wbf && s.Hm % 8 == 0) ? 1 : 0;
+    p->g2.bm = p->R <= 16 ? 16 : 64;
+    p->g2.ksplit = 1;
+    p->g2.kchunk = s.Hm;
   }
-  // MLP layers: f and a are fp32 rows of F and Hm values
-  p->g1.mfma = (wbf && p->F % 8 == 0) ? 1 : 0;
-  p->g1.bm = p->R <= 16 ? 16 : 64;
-  p->g1.ksplit = 1;
-  p->g1.kchunk = p->F;
-  p->g2.mfma = (wbf && s.Hm % 8 == 0) ? 1 : 0;
-  p->g2.bm = p->R <= 16 ? 16 : 64;
-  p->g2.ksplit = 1;
-  p->g2.kchunk = s.Hm;
 
   const size_t R = (size_t)p->R;
   const size_t BM = (size_t)s.B * p->M;
@@ -161,11 +187,13 @@ readyStatus readyPlanCreate(const readyShape* shape, const int32_t* layer_ids, r
   size_t off = 0;
   p->off_zpart = off; off = align_up(off + 4 * ks * R * p->Nz, 256);
   p->off_hss = off;   off = align_up(off + 4 * ks * R, 256);
-  p->off_f = off;     off = align_up(off + 4 * R * p->F, 256);
-  p->off_a = off;     off = align_up(off + 4 * R * s.Hm, 256);
+  p->off_f = off;     off = align_up(off + (p->fast ? 0 : 4 * R * p->F), 256);
+  // a: bf16 on the fast path, fp32 otherwise
+  p->off_a = off;     off = align_up(off + (p->fast ? 2 : 4) * R * s.Hm, 256);
   p->off_flags = off; off = align_up(off + 4 * (size_t)std::max(s.B, 1), 256);
-  p->off_pmat = off;  off = align_up(off + (p->decoupled ? 4 * BM * s.r * s.r : 0), 256);
-  p->off_ell = off;   off = align_up(off + (p->decoupled ? 4 * BM : 0), 256);
+  p->off_pmat = off;  off = align_up(off + (p->fast ? 4 * BM * s.r * s.r : 0), 256);
+  p->off_ell = off;   off = align_up(off + (p->fast ? 4 * BM : 0), 256);
+  p->off_ctr = off;   off = align_up(off + 4 * (size_t)p->n_counters, 256);
   p->ws_bytes = off;
   *plan = p;
   return READY_OK;
@@ -184,9 +212,13 @@ readyStatus readyWorkspaceSize(const readyPlan* plan, size_t* bytes) {
 
 namespace {
 
-readyStatus mark(void* const* events, int i, hipStream_t s) {
-  if (events && events[i] && hipEventRecord((hipEvent_t)events[i], s) != hipSuccess) return READY_ERR_HIP;
-  return READY_OK;
+StageEvents stage_events(void* const* events, int i) {
+  StageEvents ev{nullptr, nullptr};
+  if (events) {
+    ev.start = (hipEvent_t)events[2 * i];
+    ev.stop = (hipEvent_t)events[2 * i + 1];
+  }
+  return ev;
 }
 
 readyStatus run_reader(const readyPlan* plan, const readyStates* states, const int32_t* accept_idx,
@@ -201,7 +233,8 @@ readyStatus run_reader(const readyPlan* plan, const readyStates* states, const i
 
   const size_t ss = dsize(s.state_dtype), as = dsize(s.act_dtype), ws = dsize(s.weight_dtype);
   // alignment: 16 bytes for everything read or written with vector accesses
-  const void* vec_ptrs[] = {states->base, h, w->wq, w->u, w->v, w->w1, w->w2, o->gathered, o->out};
+  const void* vec_ptrs[] = {states->base, h, w->wq, w->u, w->v, w->h_gamma, w->w1, w->w2, w->b2,
+                            o->gathered, o->out, o->delta, o->feat};
   for (const void* ptr : vec_ptrs)
     if (ptr && !aligned16(ptr)) return READY_ERR_MISALIGNED;
   if (((uintptr_t)workspace & 255u) != 0) return READY_ERR_MISALIGNED;
@@ -257,10 +290,43 @@ readyStatus run_reader(const readyPlan* plan, const readyStates* states, const i
   int32_t* flags = (int32_t*)(wsb + plan->off_flags);
   float* pmat = (float*)(wsb + plan->off_pmat);
   float* ellw = (float*)(wsb + plan->off_ell);
-  const int wvw = (int)(16 / ws);
 
+  if (plan->fast) {
+    FastArgs a;
+    memset(&a, 0, sizeof(a));
+    a.states = (const uint16_t*)states->base;
+    a.sb = states->stride_b; a.sp = states->stride_p; a.sl = states->stride_l; a.sh = states->stride_h;
+    a.accept_idx = accept_idx;
+    for (int l = 0; l < s.L_sel; ++l) a.slot[l] = plan->slot[l];
+    a.h = (const uint16_t*)h;
+    a.wq = (const uint16_t*)w->wq; a.u = (const uint16_t*)w->u; a.v = (const uint16_t*)w->v;
+    a.gamma = (const uint16_t*)w->h_gamma;
+    a.w1 = (const uint16_t*)w->w1; a.b1 = (const uint16_t*)w->b1;
+    a.w2 = (const uint16_t*)w->w2; a.b2 = (const uint16_t*)w->b2;
+    a.gathered = (uint16_t*)o->gathered; a.out = (uint16_t*)o->out;
+    a.logrms = o->logrms; a.delta = o->delta; a.feat = o->feat; a.dev_status = o->dev_status;
+    a.zpart = zpart; a.hss = hss; a.pmat = pmat; a.ell = ellw; a.abuf = (uint16_t*)abuf;
+    a.seq_invalid = (uint32_t*)flags;
+    uint32_t* ctr = (uint32_t*)(wsb + plan->off_ctr);
+    a.counters = ctr; a.n_counters = plan->n_counters;
+    a.ticket = ctr; a.abort_flag = ctr + READY_CTR_STRIDE; a.seqdone = ctr + 2 * READY_CTR_STRIDE;
+    a.adone = ctr + READY_CTR_STRIDE * (2 + s.B);
+    a.n_s = plan->n_s; a.n_a = plan->n_a; a.n_o = plan->n_o;
+    a.B = s.B; a.P = s.P; a.n = s.n; a.M = (int)M; a.H = s.H; a.r = s.r; a.d = (int)d; a.F = (int)F;
+    a.Hm = (int)Hm; a.R = (int)R; a.Nz = plan->Nz; a.shared = s.shared_params;
+    a.ksplit = plan->gz.ksplit; a.kchunk = plan->gz.kchunk; a.act = s.act;
+    a.state_eps = s.state_eps; a.h_eps = s.h_eps;
+    if (ready_launch_zgemm(a, plan->zbm, strm, stage_events(events, 0)) != hipSuccess) return READY_ERR_HIP;
+    if (ready_launch_fused(a, plan->obm, strm, stage_events(events, 1)) != hipSuccess) return READY_ERR_HIP;
+    // stages 2 and 3 run inside the fused kernel: their marks (if any) are
+    // recorded together after it
+    for (int i = 4; events && i < 2 * READY_STAGES; ++i)
+      if (events[i] && hipEventRecord((hipEvent_t)events[i], strm) != hipSuccess) return READY_ERR_HIP;
+    return READY_OK;
+  }
+
+  const int wvw = (int)(16 / ws);
   // 0. z partials and sums of squares of h
-  if (mark(events, 0, strm) != READY_OK) return READY_ERR_HIP;
   {
     GemmArgs g;
     memset(&g, 0, sizeof(g));
@@ -269,20 +335,20 @@ readyStatus run_reader(const readyPlan* plan, const readyStates* states, const i
     g.vec_ok = (d % wvw == 0) && (plan->gz.kchunk % wvw == 0);
     g.gamma = w->h_gamma; g.hss = hss; g.ypart = zpart;
     hipError_t e;
+    const StageEvents ev = stage_events(events, 0);
     if (plan->gz.mfma) {
       const dim3 grid((unsigned)cdiv(plan->Nz, READY_MFMA_BN), (unsigned)plan->gz.ksplit,
                       (unsigned)cdiv(R, plan->gz.bm));
-      e = ready_launch_gemm_mfma(g, s.act_dtype, s.act_dtype, EPI_PARTIAL, plan->gz.bm, grid, strm);
+      e = ready_launch_gemm_mfma(g, s.act_dtype, s.act_dtype, EPI_PARTIAL, plan->gz.bm, grid, strm, ev);
     } else {
       const dim3 grid((unsigned)cdiv(plan->Nz, READY_GEMM_COLS), (unsigned)plan->gz.ksplit,
                       (unsigned)cdiv(R, READY_GEMM_RB));
       const size_t lds = 4 * READY_GEMM_RB * (size_t)std::min(plan->gz.kchunk, READY_GEMM_KSTAGE);
-      e = ready_launch_gemm(g, s.act_dtype, s.weight_dtype, s.act_dtype, EPI_PARTIAL, grid, lds, strm);
+      e = ready_launch_gemm(g, s.act_dtype, s.weight_dtype, s.act_dtype, EPI_PARTIAL, grid, lds, strm, ev);
     }
     if (e != hipSuccess) return READY_ERR_HIP;
   }
   // 1. per-state work
-  if (mark(events, 1, strm) != READY_OK) return READY_ERR_HIP;
   {
     StateArgs a;
     memset(&a, 0, sizeof(a));
@@ -297,22 +363,10 @@ readyStatus run_reader(const readyPlan* plan, const readyStates* states, const i
     a.dev_status = o->dev_status; a.seq_invalid = flags;
     a.zpart = zpart; a.hss = hss; a.ksz = plan->gz.ksplit; a.nz = plan->Nz;
     a.f = fbuf; a.feat = o->feat;
-    a.pmat = pmat; a.ell = ellw;
-    const hipError_t e = plan->decoupled ? ready_launch_state_p(a, strm)
-                                         : ready_launch_state(a, s.state_dtype, s.weight_dtype, strm);
-    if (e != hipSuccess) return READY_ERR_HIP;
+    if (ready_launch_state(a, s.state_dtype, s.weight_dtype, strm, stage_events(events, 1)) != hipSuccess)
+      return READY_ERR_HIP;
   }
-  // 2. (decoupled: f = [P z, ell]) then a = act(W1 f + b1)
-  if (mark(events, 2, strm) != READY_OK) return READY_ERR_HIP;
-  if (plan->decoupled) {
-    FeatArgs fa;
-    memset(&fa, 0, sizeof(fa));
-    fa.pmat = pmat; fa.ell = ellw; fa.zpart = zpart; fa.hss = hss;
-    fa.ksz = plan->gz.ksplit; fa.nz = plan->Nz; fa.R = (int)R; fa.n = s.n; fa.M = (int)M; fa.r = s.r;
-    fa.F = (int)F; fa.d = (int)d; fa.shared = s.shared_params; fa.h_eps = s.h_eps;
-    fa.f = fbuf; fa.feat = o->feat;
-    if (ready_launch_feat(fa, strm) != hipSuccess) return READY_ERR_HIP;
-  }
+  // 2. a = act(W1 f + b1)
   {
     GemmArgs g;
     memset(&g, 0, sizeof(g));
@@ -321,18 +375,18 @@ readyStatus run_reader(const readyPlan* plan, const readyStates* states, const i
     g.vec_ok = (F % wvw == 0);
     g.bias = w->b1; g.act = s.act; g.yout = abuf;
     hipError_t e;
+    const StageEvents ev = stage_events(events, 2);
     if (plan->g1.mfma) {
       const dim3 grid((unsigned)cdiv(Hm, READY_MFMA_BN), 1u, (unsigned)cdiv(R, plan->g1.bm));
-      e = ready_launch_gemm_mfma(g, READY_F32, s.act_dtype, EPI_BIAS_ACT, plan->g1.bm, grid, strm);
+      e = ready_launch_gemm_mfma(g, READY_F32, s.act_dtype, EPI_BIAS_ACT, plan->g1.bm, grid, strm, ev);
     } else {
       const dim3 grid((unsigned)cdiv(Hm, READY_GEMM_COLS), 1u, (unsigned)cdiv(R, READY_GEMM_RB));
       const size_t lds = 4 * READY_GEMM_RB * (size_t)std::min((int)F, READY_GEMM_KSTAGE);
-      e = ready_launch_gemm(g, READY_F32, s.weight_dtype, s.act_dtype, EPI_BIAS_ACT, grid, lds, strm);
+      e = ready_launch_gemm(g, READY_F32, s.weight_dtype, s.act_dtype, EPI_BIAS_ACT, grid, lds, strm, ev);
     }
     if (e != hipSuccess) return READY_ERR_HIP;
   }
   // 3. out = h + W2 a + b2
-  if (mark(events, 3, strm) != READY_OK) return READY_ERR_HIP;
   {
     GemmArgs g;
     memset(&g, 0, sizeof(g));
@@ -341,17 +395,18 @@ readyStatus run_reader(const readyPlan* plan, const readyStates* states, const i
     g.vec_ok = (Hm % wvw == 0);
     g.bias = w->b2; g.h = h; g.out = o->out; g.delta = o->delta; g.seq_invalid = flags; g.n = s.n;
     hipError_t e;
+    const StageEvents ev = stage_events(events, 3);
     if (plan->g2.mfma) {
       const dim3 grid((unsigned)cdiv(d, READY_MFMA_BN), 1u, (unsigned)cdiv(R, plan->g2.bm));
-      e = ready_launch_gemm_mfma(g, READY_F32, s.act_dtype, EPI_RESID, plan->g2.bm, grid, strm);
+      e = ready_launch_gemm_mfma(g, READY_F32, s.act_dtype, EPI_RESID, plan->g2.bm, grid, strm, ev);
     } else {
       const dim3 grid((unsigned)cdiv(d, READY_GEMM_COLS), 1u, (unsigned)cdiv(R, READY_GEMM_RB));
       const size_t lds = 4 * READY_GEMM_RB * (size_t)std::min((int)Hm, READY_GEMM_KSTAGE);
-      e = ready_launch_gemm(g, READY_F32, s.weight_dtype, s.act_dtype, EPI_RESID, grid, lds, strm);
+      e = ready_launch_gemm(g, READY_F32, s.weight_dtype, s.act_dtype, EPI_RESID, grid, lds, strm, ev);
     }
     if (e != hipSuccess) return READY_ERR_HIP;
   }
-  return mark(events, READY_STAGES, strm);
+  return READY_OK;
 }
 
 }  // namespace

@@ -3,6 +3,7 @@
 // wave reductions, the MLP activations and the MFMA operand types.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -72,3 +73,45 @@ __device__ __forceinline__ float activation(float x, int act) {
   return fmaxf(x, 0.0f);
 }
 
+
+// Pack 8 fp32 values into 8 bf16 (round to nearest even), element 0 in the
+// low half of the first word.
+__device__ __forceinline__ u32x4 pack_bf16x8(const float* x) {
+  u32x4 v;
+  v.x = (uint32_t)f32_to_bf16_rne(x[0]) | ((uint32_t)f32_to_bf16_rne(x[1]) << 16);
+  v.y = (uint32_t)f32_to_bf16_rne(x[2]) | ((uint32_t)f32_to_bf16_rne(x[3]) << 16);
+  v.z = (uint32_t)f32_to_bf16_rne(x[4]) | ((uint32_t)f32_to_bf16_rne(x[5]) << 16);
+  v.w = (uint32_t)f32_to_bf16_rne(x[6]) | ((uint32_t)f32_to_bf16_rne(x[7]) << 16);
+  return v;
+}
+
+// Sum of squares of the 8 bf16 values of a 16-byte chunk.
+__device__ __forceinline__ float sumsq_bf16x8(const u32x4& v) {
+  float x[8];
+  Elem<uint16_t>::unpack(v, x);
+  float s = 0.0f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) s += x[e] * x[e];
+  return s;
+}
+
+// The hardware hands workgroup i to XCD i % 8, and each XCD has its own L2.
+// With a grid of 8 * per blocks, this gives each XCD the contiguous work
+// items [xcd * per, xcd * per + per), so items that share operands (numbered
+// next to each other by the caller) meet in one L2.  Returns -1 for the
+// padding blocks past `total`.
+__device__ __forceinline__ int xcd_remap(int bid, int nblocks, int total) {
+  const int per = nblocks >> 3;
+  const int q = (bid & 7) * per + (bid >> 3);
+  return q < total ? q : -1;
+}
+
+// Launch on `s`; with stage events the start and stop of the kernel itself
+// are recorded by the dispatch.
+#define READY_LAUNCH(kern, grid, block, lds, s, ev, ...)                                         \
+  do {                                                                                           \
+    if ((ev).start || (ev).stop)                                                                 \
+      hipExtLaunchKernelGGL(kern, grid, block, lds, s, (ev).start, (ev).stop, 0u, __VA_ARGS__); \
+    else                                                                                         \
+      hipLaunchKernelGGL(kern, grid, block, lds, s, __VA_ARGS__);                                \
+  } while (0)

@@ -259,9 +259,9 @@ __global__ __launch_bounds__(256) void k_gemm_mfma(GemmArgs g) {
 // ---------------------------------------------------------------- launchers
 template <int EPI>
 static void launch_gemm_epi(const GemmArgs& g, int x_dt, int w_dt, int out_dt, dim3 grid,
-                            size_t lds, hipStream_t s) {
+                            size_t lds, hipStream_t s, StageEvents ev) {
   const dim3 block(256);
-#define READY_GEMM_CASE(TX, TW, TO) hipLaunchKernelGGL((k_gemm<TX, TW, TO, EPI>), grid, block, lds, s, g)
+#define READY_GEMM_CASE(TX, TW, TO) READY_LAUNCH((k_gemm<TX, TW, TO, EPI>), grid, block, lds, s, ev, g)
   if (EPI == EPI_PARTIAL) {
     if (x_dt == READY_BF16 && w_dt == READY_BF16) READY_GEMM_CASE(uint16_t, uint16_t, float);
     else if (x_dt == READY_BF16) READY_GEMM_CASE(uint16_t, float, float);
@@ -281,30 +281,31 @@ static void launch_gemm_epi(const GemmArgs& g, int x_dt, int w_dt, int out_dt, d
 }
 
 hipError_t ready_launch_gemm(const GemmArgs& g, int x_dt, int w_dt, int out_dt, int epi,
-                             dim3 grid, size_t lds_bytes, hipStream_t s) {
-  if (epi == EPI_PARTIAL) launch_gemm_epi<EPI_PARTIAL>(g, x_dt, w_dt, out_dt, grid, lds_bytes, s);
-  else if (epi == EPI_BIAS_ACT) launch_gemm_epi<EPI_BIAS_ACT>(g, x_dt, w_dt, out_dt, grid, lds_bytes, s);
-  else launch_gemm_epi<EPI_RESID>(g, x_dt, w_dt, out_dt, grid, lds_bytes, s);
+                             dim3 grid, size_t lds_bytes, hipStream_t s, StageEvents ev) {
+  if (epi == EPI_PARTIAL) launch_gemm_epi<EPI_PARTIAL>(g, x_dt, w_dt, out_dt, grid, lds_bytes, s, ev);
+  else if (epi == EPI_BIAS_ACT) launch_gemm_epi<EPI_BIAS_ACT>(g, x_dt, w_dt, out_dt, grid, lds_bytes, s, ev);
+  else launch_gemm_epi<EPI_RESID>(g, x_dt, w_dt, out_dt, grid, lds_bytes, s, ev);
   return hipGetLastError();
 }
 
 template <int BM>
-static void launch_mfma_bm(const GemmArgs& g, int x_dt, int out_dt, int epi, dim3 grid, hipStream_t s) {
+static void launch_mfma_bm(const GemmArgs& g, int x_dt, int out_dt, int epi, dim3 grid, hipStream_t s,
+                           StageEvents ev) {
   const dim3 block(256);
   if (epi == EPI_PARTIAL) {
-    if (x_dt == READY_BF16) hipLaunchKernelGGL((k_gemm_mfma<uint16_t, float, EPI_PARTIAL, BM>), grid, block, 0, s, g);
-    else hipLaunchKernelGGL((k_gemm_mfma<float, float, EPI_PARTIAL, BM>), grid, block, 0, s, g);
+    if (x_dt == READY_BF16) READY_LAUNCH((k_gemm_mfma<uint16_t, float, EPI_PARTIAL, BM>), grid, block, 0, s, ev, g);
+    else READY_LAUNCH((k_gemm_mfma<float, float, EPI_PARTIAL, BM>), grid, block, 0, s, ev, g);
   } else if (epi == EPI_BIAS_ACT) {
-    hipLaunchKernelGGL((k_gemm_mfma<float, float, EPI_BIAS_ACT, BM>), grid, block, 0, s, g);
+    READY_LAUNCH((k_gemm_mfma<float, float, EPI_BIAS_ACT, BM>), grid, block, 0, s, ev, g);
   } else {
-    if (out_dt == READY_BF16) hipLaunchKernelGGL((k_gemm_mfma<float, uint16_t, EPI_RESID, BM>), grid, block, 0, s, g);
-    else hipLaunchKernelGGL((k_gemm_mfma<float, float, EPI_RESID, BM>), grid, block, 0, s, g);
+    if (out_dt == READY_BF16) READY_LAUNCH((k_gemm_mfma<float, uint16_t, EPI_RESID, BM>), grid, block, 0, s, ev, g);
+    else READY_LAUNCH((k_gemm_mfma<float, float, EPI_RESID, BM>), grid, block, 0, s, ev, g);
   }
 }
 
 hipError_t ready_launch_gemm_mfma(const GemmArgs& g, int x_dt, int out_dt, int epi, int bm, dim3 grid,
-                                  hipStream_t s) {
-  if (bm == 16) launch_mfma_bm<16>(g, x_dt, out_dt, epi, grid, s);
-  else launch_mfma_bm<64>(g, x_dt, out_dt, epi, grid, s);
+                                  hipStream_t s, StageEvents ev) {
+  if (bm == 16) launch_mfma_bm<16>(g, x_dt, out_dt, epi, grid, s, ev);
+  else launch_mfma_bm<64>(g, x_dt, out_dt, epi, grid, s, ev);
   return hipGetLastError();
 }

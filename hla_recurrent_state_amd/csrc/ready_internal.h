@@ -28,28 +28,61 @@ struct StateArgs {
   float* logrms;                   // [B][M] or null
   int32_t* dev_status;             // or null
   int32_t* seq_invalid;            // [B] workspace
-  // coupled form (k_state): readout from q = U^T z, packing into f
+  // readout from q = U^T z, packing into f
   const float* zpart;              // [ksz][B*n][nz] raw partial sums of W_q (gamma*h)
   const float* hss;                // [ksz][B*n] partial sums of h^2
   int ksz, nz;
   float* f;                        // [B*n][F] workspace
   float* feat;                     // [B*n][F] or null
-  // decoupled form (k_state_p): P = V^T S_bar U^T / sqrt(d_k) and ell per tile
-  float* pmat;                     // [B*M][r][r]
-  float* ell;                      // [B*M]
 };
 
-// Packing of f_j from P, the raw query sums and ell (decoupled form).
-struct FeatArgs {
-  const float* pmat;               // [B*M][r][r]
-  const float* ell;                // [B*M]
-  const float* zpart;              // [ksz][R][nz]
-  const float* hss;                // [ksz][R]
-  int ksz, nz, R, n, M, r, F, d, shared;
-  float h_eps;
-  float* f;                        // [R][F]
+// Fast path (bf16 states, activations and weights; r <= 32): two launches
+//   k_zgemm   z partial sums W_q (gamma h) over K chunks and the sums of
+//             squares of h (matrix cores); clears the counters of k_fused
+//   k_fused   ticketed work items: S (gather, RMS, log-RMS,
+//             P = V^T S_bar U^T / sqrt(d_k) per tile), A (f and
+//             a = act(W1 f + b1) per 16 rows) and O (out = h + W2 a + b2)
+struct FastArgs {
+  const uint16_t* states;
+  int64_t sb, sp, sl, sh;          // element strides of the verify buffer
+  const int32_t* accept_idx;       // [B]
+  int32_t slot[READY_MAX_LSEL];
+  const uint16_t* h;               // [R][d]
+  const uint16_t* wq;              // [Nz][d]  (Nz = Mz r)
+  const uint16_t* u;               // [Mz][r][128]
+  const uint16_t* v;               // [Mz][128][r]
+  const uint16_t* gamma;           // [d] or null
+  const uint16_t* w1;              // [Hm][F]
+  const uint16_t* b1;              // [Hm] or null
+  const uint16_t* w2;              // [d][Hm]
+  const uint16_t* b2;              // [d] or null
+  uint16_t* gathered;              // [B][M][128][128]
+  uint16_t* out;                   // [R][d]
+  float* logrms;                   // [B][M] or null
+  float* delta;                    // [R][d] or null
   float* feat;                     // [R][F] or null
+  int32_t* dev_status;             // or null
+  float* zpart;                    // [ksplit][R][Nz]
+  float* hss;                      // [ksplit][R]
+  float* pmat;                     // [B M][r][r]
+  float* ell;                      // [B M]
+  uint16_t* abuf;                  // [R][Hm] bf16
+  uint32_t* seq_invalid;           // [B]
+  // counters of k_fused (cleared by k_zgemm): ticket, abort flag, per
+  // sequence the S items done, per 16 rows the A items done
+  uint32_t* counters;
+  int n_counters;
+  uint32_t* ticket;
+  uint32_t* abort_flag;
+  uint32_t* seqdone;               // [B] (stride READY_CTR_STRIDE)
+  uint32_t* adone;                 // [cdiv(R, 16)] (stride READY_CTR_STRIDE)
+  int n_s, n_a, n_o;               // work items of k_fused per kind
+  int B, P, n, M, H, r, d, F, Hm, R, Nz, shared, ksplit, kchunk, act;
+  float state_eps, h_eps;
 };
+
+#define READY_FAST_MAX_F 1536      // f rows of 16 positions staged in LDS
+#define READY_CTR_STRIDE 32        // counters of k_fused sit 128 bytes apart
 
 enum { EPI_PARTIAL = 0, EPI_BIAS_ACT = 1, EPI_RESID = 2 };
 
@@ -88,11 +121,21 @@ struct GemmArgs {
 #define READY_MFMA_BN 64
 #define READY_MFMA_BK 64
 
-READY_HIDDEN hipError_t ready_launch_state(const StateArgs& a, int state_dt, int weight_dt, hipStream_t s);
-READY_HIDDEN hipError_t ready_launch_state_p(const StateArgs& a, hipStream_t s);
-READY_HIDDEN hipError_t ready_launch_feat(const FeatArgs& a, hipStream_t s);
+// Every launcher takes a pair of caller events (or nulls): when either is
+// set, the kernel is launched with hipExtLaunchKernelGGL, which records the
+// start and stop of that kernel itself, with no marker packet in between.
+struct StageEvents {
+  hipEvent_t start, stop;
+};
+
+READY_HIDDEN hipError_t ready_launch_state(const StateArgs& a, int state_dt, int weight_dt, hipStream_t s,
+                                           StageEvents ev);
 READY_HIDDEN hipError_t ready_launch_gemm(const GemmArgs& g, int x_dt, int w_dt, int out_dt, int epi,
-                                          dim3 grid, size_t lds_bytes, hipStream_t s);
+                                          dim3 grid, size_t lds_bytes, hipStream_t s, StageEvents ev);
 // bm: rows per workgroup tile (16 or 64); weights must be bf16
 READY_HIDDEN hipError_t ready_launch_gemm_mfma(const GemmArgs& g, int x_dt, int out_dt, int epi, int bm,
-                                               dim3 grid, hipStream_t s);
+                                               dim3 grid, hipStream_t s, StageEvents ev);
+// fast path; bm: rows per tile (16 or 64)
+READY_HIDDEN hipError_t ready_launch_zgemm(const FastArgs& a, int bm, hipStream_t s, StageEvents ev);
+READY_HIDDEN hipError_t ready_launch_fused(const FastArgs& a, int obm, hipStream_t s, StageEvents ev);
+READY_HIDDEN size_t ready_fused_lds(int r, int F, int obm);

@@ -1,20 +1,13 @@
-// Per-state kernels of the ReaDy state reader for gfx950.
+// Per-state kernel of the ReaDy state reader for gfx950, general form (any
+// dtype mix and any rank up to 128; the bf16 fast path of rank <= 32 is in
+// ready_fast.hip).
 //
-//   k_state    coupled form, any dtype mix and rank: one workgroup per
-//              (sequence, layer-head pair) tile does the fused gather at the
-//              accept index (step 1), the mean square and log-RMS (step 2),
-//              T = V^T S_bar by chunks of 8 ranks on the VALU (step 3), the
-//              readout u_j = T q_j / sqrt(d_k) with q_j = U^T z_j (step 4) and
-//              the packing of [u, ell] (step 5, first half).  Needs the query
-//              sums z first.
-//   k_state_p  decoupled form for bf16 states and weights, r <= 32: the same
-//              gather and RMS, then P = V^T (S U^T) / (rms sqrt(d_k)), an r x r
-//              matrix per tile, with S U^T on the matrix cores straight from
-//              the loaded 16-byte row chunks (the contraction runs along the
-//              contiguous key axis).  u_j = P z_j is the same readout
-//              (T q_j = V^T S_bar U^T z_j), so this kernel does not wait for the
-//              query GEMM.
-//   k_feat     decoupled form: f_j = [P z_j / rms(h_j), ell] per pair.
+//   k_state    one workgroup per (sequence, layer-head pair) tile does the
+//              fused gather at the accept index (step 1), the mean square and
+//              log-RMS (step 2), T = V^T S_bar by chunks of 8 ranks on the
+//              VALU (step 3), the readout u_j = T q_j / sqrt(d_k) with
+//              q_j = U^T z_j (step 4) and the packing of [u, ell] (step 5,
+//              first half).  Needs the query sums z first.
 // Formulas: ReaDy arXiv text, section 3.1 "Position-conditioned reading" and
 // "Fusion and residual injection" (Eq. (3), written out in the rainbus summary,
 // 方法步骤详情 steps (1)-(3)); section 3.2 "Avoiding redundant data movement"
@@ -186,220 +179,19 @@ __global__ __launch_bounds__(256) void k_state(StateArgs a) {
 }
 
 
-// ---------------------------------------------------------------- k_state_p
-
-// Wave w owns tile rows [32 w, 32 w + 32) as two 16-row blocks.  Lane l holds,
-// for block mb and key step ks, the 16-byte chunk S[32 w + 16 mb + l % 16]
-// [32 ks + 8 (l / 16) .. + 7]: exactly the A operand of a 16 x 16 x 32 matrix
-// instruction, so the loaded tile feeds S U^T without any reshuffle.  The B
-// operand is U^T: lane l needs U[i = 16 nb + l % 16][32 ks + 8 (l / 16) .. + 7],
-// again a contiguous 16-byte chunk.
-template <int RR>
-__global__ __launch_bounds__(256) void k_state_p(StateArgs a) {
-  constexpr int NB = (RR + 15) / 16;  // 16-column blocks of U^T
-  constexpr int RMAX = RR;            // the rank, known at compile time
-  __shared__ float s_red[4][NB * RMAX * 16];
-  __shared__ float s_wsum[4];
-
-  const int tile = blockIdx.x;
-  const int b = tile / a.M;
-  const int m = tile - b * a.M;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  constexpr int r = RR;
-  const int mz = a.shared ? 0 : m;
-  float* P = a.pmat + (int64_t)tile * r * r;
-
-  const int p_acc = a.accept_idx[b];
-  if (p_acc < 0 || p_acc >= a.P) {
-    if (tid == 0) {
-      if (a.dev_status) a.dev_status[0] = READY_ERR_ACCEPT_IDX;
-      if (m == 0) a.seq_invalid[b] = 1;
-      a.ell[tile] = 0.0f;
-    }
-    for (int e = tid; e < r * r; e += 256) P[e] = 0.0f;
-    return;
-  }
-  if (m == 0 && tid == 0) a.seq_invalid[b] = 0;
-
-  // ---- step 1: gather ----
-  const int l = m / a.H, hh = m - (m / a.H) * a.H;
-  const uint16_t* src = (const uint16_t*)a.states + (int64_t)b * a.sb + (int64_t)p_acc * a.sp +
-                        (int64_t)a.slot[l] * a.sl + (int64_t)hh * a.sh;
-  uint16_t* dst = (uint16_t*)a.gathered + (int64_t)tile * READY_TILE_ELEMS;
-  const int lrow = lane & 15, lk = (lane >> 4) * 8;
-  u32x4 data[2][4];
-#pragma unroll
-  for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-      data[mb][ks] = __builtin_nontemporal_load(
-          (const u32x4*)(src + (32 * wave + 16 * mb + lrow) * READY_TILE + 32 * ks + lk));
-#pragma unroll
-  for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-      __builtin_nontemporal_store(data[mb][ks],
-                                  (u32x4*)(dst + (32 * wave + 16 * mb + lrow) * READY_TILE + 32 * ks + lk));
-
-  // ---- step 2: mean square ----
-  float ss = 0.0f;
-#pragma unroll
-  for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      float x[8];
-      Elem<uint16_t>::unpack(data[mb][ks], x);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) ss += x[e] * x[e];
-    }
-  ss = wave_sum(ss);
-  if (lane == 0) s_wsum[wave] = ss;
-
-  // ---- S U^T on the matrix cores ----
-  const uint16_t* U = (const uint16_t*)a.u + (int64_t)mz * r * READY_TILE;
-  f32x4 acc[2][NB];
-#pragma unroll
-  for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-    const int i = 16 * nb + lrow;
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      u32x4 ub = u32x4{0u, 0u, 0u, 0u};
-      if (i < r) ub = *(const u32x4*)(U + (int64_t)i * READY_TILE + 32 * ks + lk);
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb) acc[mb][nb] = mfma16x16x32(data[mb][ks], ub, acc[mb][nb]);
-    }
-  }
-
-  // ---- P = V^T (S U^T): lane partial sums over its 8 rows ----
-  // acc[mb][nb][e] = (S U^T)[v = 32 w + 16 mb + 4 (l / 16) + e][i' = 16 nb + l % 16]
-  const uint16_t* V = (const uint16_t*)a.v + (int64_t)mz * READY_TILE * r;
-  float part[NB][RMAX];
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-    for (int i = 0; i < RMAX; ++i) part[nb][i] = 0.0f;
-#pragma unroll
-  for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int v = 32 * wave + 16 * mb + 4 * (lane >> 4) + e;
-      float vrow[RMAX];
-#pragma unroll
-      for (int c = 0; c < RMAX / 8; ++c) {
-        const u32x4 q = *(const u32x4*)(V + (int64_t)v * r + 8 * c);
-        Elem<uint16_t>::unpack(q, vrow + 8 * c);
-      }
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-        for (int i = 0; i < RMAX; ++i) part[nb][i] += vrow[i] * acc[mb][nb][e];
-    }
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-    for (int i = 0; i < RMAX; ++i) {
-      part[nb][i] += __shfl_xor(part[nb][i], 16, 64);
-      part[nb][i] += __shfl_xor(part[nb][i], 32, 64);
-    }
-  if (lane < 16) {
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-      for (int i = 0; i < RMAX; ++i) s_red[wave][(nb * RMAX + i) * 16 + lane] = part[nb][i];
-  }
-  __syncthreads();
-
-  const float ms = ((s_wsum[0] + s_wsum[1]) + (s_wsum[2] + s_wsum[3])) * (1.0f / READY_TILE_ELEMS);
-  const float rms = sqrtf(ms + a.state_eps);
-  const float scale = 0.08838834764831845f / rms;  // 1 / (rms sqrt(d_k)), d_k = 128
-  for (int e = tid; e < r * r; e += 256) {
-    const int i = e / r, ip = e - (e / r) * r;
-    const int idx = ((ip >> 4) * RMAX + i) * 16 + (ip & 15);
-    P[e] = ((s_red[0][idx] + s_red[1][idx]) + (s_red[2][idx] + s_red[3][idx])) * scale;
-  }
-  if (tid == 0) {
-    const float ell = logf(rms);
-    a.ell[tile] = ell;
-    if (a.logrms) a.logrms[tile] = ell;
-  }
-}
-
-// ---------------------------------------------------------------- k_feat
-
-// One thread per (row rho = b n + j, pair m): z_j of the pair from the split-K
-// partial sums, scaled by 1 / rms(h_j), then u = P z and the log-RMS scale.
-__global__ __launch_bounds__(256) void k_feat(FeatArgs a) {
-  const int t = blockIdx.x * 256 + threadIdx.x;
-  if (t >= a.R * a.M) return;
-  const int rho = t / a.M;
-  const int m = t - rho * a.M;
-  const int b = rho / a.n;
-  const int r = a.r;
-  const int mz = a.shared ? 0 : m;
-  float hs = 0.0f;
-  for (int ks = 0; ks < a.ksz; ++ks) hs += a.hss[(int64_t)ks * a.R + rho];
-  const float rs = 1.0f / sqrtf(hs / (float)a.d + a.h_eps);
-  float z[32];
-#pragma unroll
-  for (int i = 0; i < 32; ++i) {
-    float s = 0.0f;
-    if (i < r)
-      for (int ks = 0; ks < a.ksz; ++ks) s += a.zpart[((int64_t)ks * a.R + rho) * a.nz + mz * r + i];
-    z[i] = s * rs;
-  }
-  const float* P = a.pmat + ((int64_t)b * a.M + m) * r * r;
-  float* frow = a.f + (int64_t)rho * a.F + m * (r + 1);
-  float* xrow = a.feat ? a.feat + (int64_t)rho * a.F + m * (r + 1) : nullptr;
-#pragma unroll
-  for (int i = 0; i < 32; ++i) {
-    if (i < r) {
-      float u = 0.0f;
-#pragma unroll
-      for (int ip = 0; ip < 32; ++ip)
-        if (ip < r) u += P[i * r + ip] * z[ip];
-      frow[i] = u;
-      if (xrow) xrow[i] = u;
-    }
-  }
-  const float ell = a.ell[(int64_t)b * a.M + m];
-  frow[r] = ell;
-  if (xrow) xrow[r] = ell;
-}
-
 // ---------------------------------------------------------------- launchers
 
-hipError_t ready_launch_state(const StateArgs& a, int state_dt, int weight_dt, hipStream_t s) {
+hipError_t ready_launch_state(const StateArgs& a, int state_dt, int weight_dt, hipStream_t s,
+                              StageEvents ev) {
   const dim3 grid((unsigned)(a.B * a.M)), block(256);
   if (state_dt == READY_BF16 && weight_dt == READY_BF16)
-    hipLaunchKernelGGL((k_state<uint16_t, uint16_t>), grid, block, 0, s, a);
+    READY_LAUNCH((k_state<uint16_t, uint16_t>), grid, block, 0, s, ev, a);
   else if (state_dt == READY_BF16)
-    hipLaunchKernelGGL((k_state<uint16_t, float>), grid, block, 0, s, a);
+    READY_LAUNCH((k_state<uint16_t, float>), grid, block, 0, s, ev, a);
   else if (weight_dt == READY_BF16)
-    hipLaunchKernelGGL((k_state<float, uint16_t>), grid, block, 0, s, a);
+    READY_LAUNCH((k_state<float, uint16_t>), grid, block, 0, s, ev, a);
   else
-    hipLaunchKernelGGL((k_state<float, float>), grid, block, 0, s, a);
+    READY_LAUNCH((k_state<float, float>), grid, block, 0, s, ev, a);
   return hipGetLastError();
 }
 
-
-hipError_t ready_launch_state_p(const StateArgs& a, hipStream_t s) {
-  const dim3 grid((unsigned)(a.B * a.M)), block(256);
-  switch (a.r) {
-    case 8: hipLaunchKernelGGL((k_state_p<8>), grid, block, 0, s, a); break;
-    case 16: hipLaunchKernelGGL((k_state_p<16>), grid, block, 0, s, a); break;
-    case 24: hipLaunchKernelGGL((k_state_p<24>), grid, block, 0, s, a); break;
-    default: hipLaunchKernelGGL((k_state_p<32>), grid, block, 0, s, a); break;
-  }
-  return hipGetLastError();
-}
-
-hipError_t ready_launch_feat(const FeatArgs& a, hipStream_t s) {
-  const int threads = a.R * a.M;
-  const dim3 grid((unsigned)((threads + 255) / 256)), block(256);
-  hipLaunchKernelGGL(k_feat, grid, block, 0, s, a);
-  return hipGetLastError();
-}

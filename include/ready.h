@@ -57,7 +57,9 @@ typedef enum readyStatus {
   READY_ERR_LAYER_ID_RANGE = 7,     /* a layer id is outside [0, L_tot) */
   READY_ERR_HIP = 8,                /* the HIP runtime reported an error at launch */
   READY_ERR_ACCEPT_IDX = 9,         /* device-side only: accept_idx[b] outside [0, P) */
-  READY_ERR_OUT_OF_HOST_MEMORY = 10
+  READY_ERR_OUT_OF_HOST_MEMORY = 10,
+  READY_ERR_SYNC_TIMEOUT = 11       /* device-side only: a wait between work items of one launch
+                                       gave up (should never happen; outputs are then invalid) */
 } readyStatus;
 
 typedef enum readyDtype { READY_F32 = 0, READY_BF16 = 1 } readyDtype;
@@ -103,7 +105,8 @@ typedef struct readyStates {
 } readyStates;
 
 /*
- * Reader weights, all in weight_dtype, row-major, device memory:
+ * Reader weights, all in weight_dtype, row-major, device memory (wq, u, v,
+ * h_gamma, w1, w2 and b2 16-byte aligned):
  *   wq [M][r][d] (or [r][d] when shared_params)  -- z = W_q h_hat
  *   u  [M][r][d_k] (or [r][d_k])                  -- q = U^T z
  *   v  [M][d_v][r] (or [d_v][r])                  -- T = V^T S_bar
@@ -130,8 +133,9 @@ typedef struct readyWeights {
  *             nearest even for bf16.  May be exactly h (in place); any other
  *             overlap with an input is READY_ERR_ALIASING.
  *   logrms    [B][M] fp32 ell = ln rms (optional, NULL to skip)
- *   delta     [B][n][d] fp32 Delta h before the residual (optional)
- *   feat      [B][n][F] fp32 packed features f_j (optional)
+ *   delta     [B][n][d] fp32 Delta h before the residual (optional,
+ *             16-byte aligned)
+ *   feat      [B][n][F] fp32 packed features f_j (optional, 16-byte aligned)
  *   dev_status  one int32 (optional).  When accept_idx[b] is outside [0, P)
  *             the kernels store READY_ERR_ACCEPT_IDX there and leave that
  *             sequence's gathered, logrms, out and delta unwritten (its feat
@@ -178,13 +182,15 @@ readyStatus readyStateReader(const readyPlan* plan, const readyStates* states,
                              void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * Same computation as readyStateReader, with timing marks: events[i] (a
- * hipEvent_t, or NULL to skip) is recorded on `stream` right before launch
- * stage i and events[READY_STAGES] right after the last stage.  Stages:
- * 0 query GEMM (z and the sums of squares of h), 1 per-state kernel (gather,
- * RMS, T, readout, packing), 2 first MLP layer, 3 second MLP layer and
- * residual.  The events must have been created by the caller on the device
- * of `stream`; the library only records them.
+ * Same computation as readyStateReader, with per-stage kernel timestamps:
+ * events[2 i] and events[2 i + 1] (hipEvent_t, or NULL to skip) are recorded
+ * at the start and at the end of the kernel of launch stage i itself (the
+ * launch records them; no marker packet is inserted between stages).
+ * Stages: 0 query GEMM (z and the sums of squares of h), 1 per-state kernel
+ * (gather, RMS, log-RMS, projection), 2 first MLP layer (with the readout and
+ * packing of f on the fast path), 3 second MLP layer and residual.  The
+ * events must have been created by the caller on the device of `stream`
+ * with timing enabled; the library only records them.
  */
 #define READY_STAGES 4
 readyStatus readyStateReaderProfiled(const readyPlan* plan, const readyStates* states,

@@ -89,6 +89,30 @@ def test_ragged_shapes(dt, act):
     _check(inp)
 
 
+@pytest.mark.parametrize("r", [8, 16, 24, 32])
+@pytest.mark.parametrize("rows", ["one_tile", "several_tiles"])
+def test_bf16_fast_path_ragged(r, rows):
+    """All-bf16 path: B*n = 15 (one 16-row tile) or 35 (one ragged 64-row
+    tile, several sequences per tile), d = 1048 (ragged K chunks), Hm = 72
+    (ragged 64-column tiles of the first MLP layer), scattered layer slots,
+    with gain and biases."""
+    B, n = (3, 5) if rows == "one_tile" else (5, 7)
+    cfg = make_shape("paper", B=B, n=n, H=8, L_tot=5, slots=(4, 1), t=12, r=r, d=1048, Hm=72)
+    inp = synth.make(cfg, seed=8 + r)
+    rng = np.random.default_rng(r)
+    store = synth.gen._store
+    inp.gamma = store(1.0 + 0.1 * rng.standard_normal(cfg.d), "bf16")
+    inp.b1 = store(0.2 * rng.standard_normal(cfg.Hm), "bf16")
+    inp.b2 = store(0.2 * rng.standard_normal(cfg.d), "bf16")
+    _check(inp)
+
+
+@pytest.mark.parametrize("act", ["gelu_tanh", "relu"])
+def test_bf16_fast_path_activations(act):
+    cfg = make_shape("paper", B=2, t=12, act=act)
+    _check(synth.make(cfg, seed=14))
+
+
 @pytest.mark.parametrize("r", [8, 24, 128])
 def test_ranks_and_mixed_dtypes(r):
     cfg = make_shape("tiny", B=2, H=2, t=8, r=r, d=640, Hm=64, state_dtype="bf16", act_dtype="f32",
