@@ -10,7 +10,7 @@ value      committed-state GB/s on the batched workload (B = 64 sequences,
            gathered bytes written) per step / time per step.  Steps rotate
            over several copies of the inputs so the 256 MB last-level cache
            cannot hold them.
-roofline   the dominant kernel (k_fused): its algorithmic bytes per launch /
+roofline   the dominant (and only) kernel, k_reader: its algorithmic bytes per launch /
            its average duration, timed inside the timed loop with HIP events
            that its own launch records (hipExtLaunchKernelGGL) on the launch
            stream, against 8 TB/s.
@@ -38,7 +38,7 @@ sys.path.insert(0, ROOT)
 METRIC = "state-reader µs per 7-token draft block (B=1); committed-state GB/s at B=64"
 HBM_PEAK_GBS = 8000.0
 KERNEL_SRC = os.path.join(ROOT, "hla_recurrent_state_amd", "csrc", "ready_fast.hip")
-PMC_SUMMARY = os.path.join(ROOT, "profiles", "k_fused_batched_pmc.md")
+PMC_SUMMARY = os.path.join(ROOT, "profiles", "k_reader_batched_pmc.md")
 
 
 def log(*a):
@@ -102,20 +102,15 @@ def algorithmic_bytes(cfg):
             "accept_idx": 4 * B, "total": committed + weights + acts + 4 * B}
 
 
-def fused_kernel_bytes(cfg):
-    """Algorithmic bytes of one launch of the fused kernel (k_fused: every
-    step but the query GEMM), per unit: each (sequence, pair) tile reads its
+def reader_kernel_bytes(cfg):
+    """Algorithmic bytes of one launch of the bf16 path's single kernel
+    (k_reader: all five steps), per unit: each (sequence, pair) tile reads its
     committed 128 x 128 state and writes the copy (2 x 32768 B at bf16); each
-    draft position reads h_j for the residual and writes out_j (2 x d x 2 B);
-    the weights it applies (U, V, W1, W2) are read once; 4 B per accept index.
-    Intermediates passed between its work items (P, ell, a) and the query
-    GEMM's partial sums are implementation traffic, not counted."""
-    s, a, w = esize(cfg.state_dtype), esize(cfg.act_dtype), esize(cfg.weight_dtype)
-    mz = 1 if cfg.shared else cfg.M
-    tiles = cfg.B * cfg.M
-    rows = cfg.B * cfg.n
-    weights = (2 * mz * cfg.r * 128 + cfg.Hm * cfg.F + cfg.d * cfg.Hm) * w
-    return tiles * 2 * 128 * 128 * s + rows * 2 * cfg.d * a + weights + 4 * cfg.B
+    draft position reads h_j and writes out_j (2 x d x 2 B); every weight
+    (W_q, U, V, W1, W2) is read once; 4 B per accept index.  This equals the
+    whole call's algorithmic bytes.  Intermediates passed between work items
+    (z partial sums, P, ell, a) are implementation traffic, not counted."""
+    return algorithmic_bytes(cfg)["total"]
 
 
 def kernel_src_hash():
@@ -124,7 +119,7 @@ def kernel_src_hash():
 
 
 def read_traffic():
-    """HBM bytes per k_fused launch from the committed PMC summary, if it was
+    """HBM bytes per k_reader launch from the committed PMC summary, if it was
     taken on the current kernel source."""
     if not os.path.exists(PMC_SUMMARY):
         return None
@@ -178,7 +173,7 @@ def device_sets(inp, nsets, device, reader, stream):
             "out": torch.empty((cfg.B, cfg.n, cfg.d), dtype=torch_dtype(cfg.act_dtype), device=device),
             "dev_status": torch.zeros(1, dtype=torch.int32, device=device),
         }
-        ws = torch.empty(max(reader.workspace_bytes, 256), dtype=torch.uint8, device=device)
+        ws = reader.new_workspace(device)
         sets.append(Prepared(R, reader, d, outs, ws, stream))
     return sets
 
@@ -200,7 +195,7 @@ def run_batched(args, hip, torch, R, synth, seed=0):
     K, W = args.steps, args.warmup
     ev_s = [hip.event() for _ in range(K)]
     ev_e = [hip.event() for _ in range(K)]
-    # stage 1 (the fused kernel): its start and end, recorded by its own launch
+    # stage 1 (the single kernel of the bf16 path): its start and end, recorded by its own launch
     ev_arrays = [(ctypes.c_void_p * (2 * R.READY_STAGES))(None, None, ev_s[i], ev_e[i], None, None, None, None)
                  for i in range(K)]
     for i in range(W):
@@ -231,9 +226,8 @@ def run_batched(args, hip, torch, R, synth, seed=0):
 
 
 def stage_breakdown(hip, lib, sets, R, stream, torch, device, reps):
-    """Median kernel duration of each launch (start and end recorded by the
-    launch itself), and of the whole call (first start to last end).  The
-    bf16 path has two launches: the query GEMM and the fused kernel."""
+    """Median kernel duration of the bf16 path's single kernel (start and end
+    recorded by its launch)."""
     n = 2 * R.READY_STAGES
     evs = [[hip.event() for _ in range(n)] for _ in range(reps)]
     for i in range(reps):
@@ -242,12 +236,7 @@ def stage_breakdown(hip, lib, sets, R, stream, torch, device, reps):
         if code != 0:
             raise R.ReadyError(code, "stages")
     torch.cuda.synchronize(device)
-    names = ["k_zgemm", "k_fused"]
-    out = {}
-    for s, name in enumerate(names):
-        vals = [1000.0 * hip.ms(evs[i][2 * s], evs[i][2 * s + 1]) for i in range(reps)]
-        out[name] = round(pct(vals, 50), 2)
-    out["first_start_to_last_end"] = round(pct([1000.0 * hip.ms(evs[i][0], evs[i][3]) for i in range(reps)], 50), 2)
+    out = {"k_reader": round(pct([1000.0 * hip.ms(evs[i][2], evs[i][3]) for i in range(reps)], 50), 2)}
     for row in evs:
         for e in row:
             hip.destroy(e)
@@ -468,7 +457,7 @@ def main():
     ms = bat["ms_per_step"]
     value = alg["committed_state"] / (ms * 1e-3) / 1e9
     kern_avg_us = sum(bat["kern_us"]) / len(bat["kern_us"])
-    kb = fused_kernel_bytes(cfg)
+    kb = reader_kernel_bytes(cfg)
     achieved = kb / (kern_avg_us * 1e-6) / 1e9
     traffic = read_traffic()
     out = {
@@ -496,7 +485,7 @@ def main():
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": "k_fused",
+            "kernel": "k_reader",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",

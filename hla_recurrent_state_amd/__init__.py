@@ -30,6 +30,7 @@ READY_ERR_HIP = 8
 READY_ERR_ACCEPT_IDX = 9
 READY_ERR_OUT_OF_HOST_MEMORY = 10
 READY_ERR_SYNC_TIMEOUT = 11
+READY_ERR_WORKSPACE_UNINIT = 12
 
 READY_F32 = 0
 READY_BF16 = 1
@@ -41,8 +42,8 @@ DTYPES = {"f32": READY_F32, "bf16": READY_BF16}
 ACTS = {"silu": READY_ACT_SILU, "gelu_tanh": READY_ACT_GELU_TANH, "relu": READY_ACT_RELU}
 
 # Every symbol include/ready.h declares.
-EXPORTS = ("readyPlanCreate", "readyPlanDestroy", "readyWorkspaceSize", "readyStateReader",
-           "readyStateReaderProfiled", "readyStatusString", "readyVersion")
+EXPORTS = ("readyPlanCreate", "readyPlanDestroy", "readyWorkspaceSize", "readyWorkspaceInit",
+           "readyStateReader", "readyStateReaderProfiled", "readyStatusString", "readyVersion")
 READY_STAGES = 4
 
 
@@ -91,6 +92,8 @@ def load():
     lib.readyPlanDestroy.restype = ctypes.c_int
     lib.readyWorkspaceSize.argtypes = [ctypes.c_void_p, P(ctypes.c_size_t)]
     lib.readyWorkspaceSize.restype = ctypes.c_int
+    lib.readyWorkspaceInit.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    lib.readyWorkspaceInit.restype = ctypes.c_int
     lib.readyStateReader.argtypes = [ctypes.c_void_p, P(readyStates), ctypes.c_void_p, ctypes.c_void_p,
                                      P(readyWeights), P(readyOutputs), ctypes.c_void_p, ctypes.c_size_t,
                                      ctypes.c_void_p]
@@ -134,6 +137,11 @@ def readyWorkspaceSize(plan):
     return st, n.value
 
 
+def readyWorkspaceInit(plan, workspace, workspace_bytes, stream):
+    """Enqueue the preparation of a workspace for `plan`.  Returns status."""
+    return load().readyWorkspaceInit(plan, workspace, workspace_bytes, stream)
+
+
 def readyStateReader(plan, states, accept_idx, h, weights, outputs, workspace, workspace_bytes, stream):
     """Raw call: pointers are ints, structs are the ctypes mirrors.  Returns status."""
     return load().readyStateReader(plan, ctypes.byref(states), accept_idx, h, ctypes.byref(weights),
@@ -144,7 +152,7 @@ def readyStateReaderProfiled(plan, states, accept_idx, h, weights, outputs, work
                              stream, events):
     """As readyStateReader; `events` is a sequence of 2 * READY_STAGES
     hipEvent_t handles (ints) or None entries: start and end of each stage's
-    kernel."""
+    kernel (on the bf16 path the single kernel is stage 1)."""
     ev = (ctypes.c_void_p * (2 * READY_STAGES))(*[e for e in events])
     return load().readyStateReaderProfiled(plan, ctypes.byref(states), accept_idx, h, ctypes.byref(weights),
                                            ctypes.byref(outputs), workspace, workspace_bytes, stream, ev)
@@ -171,6 +179,8 @@ class StateReader:
     reader = StateReader(shape, layer_ids)
     reader(states, accept_idx, h, weights, gathered, out, logrms=None,
            delta=None, feat=None, dev_status=None, workspace=None)
+    A workspace passed in must come from new_workspace() (or have been
+    prepared with init_workspace()); by default the reader keeps its own.
     `states` is a tensor [B][P][L_tot][H][128][128] (any outer strides with a
     contiguous tile) and `weights` a dict with keys wq, u, v, w1, w2 and
     optionally h_gamma, b1, b2.  Raises ReadyError on a non-zero status.
@@ -198,10 +208,26 @@ class StateReader:
         except Exception:
             pass
 
+    def new_workspace(self, device, stream=None):
+        """A workspace for this plan, prepared by readyWorkspaceInit on the
+        current (or given) stream."""
+        import torch
+        ws = torch.empty(max(self.workspace_bytes, 256), dtype=torch.uint8, device=device)
+        self.init_workspace(ws, stream)
+        return ws
+
+    def init_workspace(self, ws, stream=None):
+        import torch
+        if stream is None:
+            stream = torch.cuda.current_stream(ws.device).cuda_stream
+        code = readyWorkspaceInit(self.plan, ws.data_ptr(), ws.numel() * ws.element_size(), stream)
+        if code != READY_OK:
+            raise ReadyError(code, "readyWorkspaceInit")
+
     def workspace(self, device):
         import torch
         if self._ws is None or self._ws.device != torch.device(device):
-            self._ws = torch.empty(max(self.workspace_bytes, 256), dtype=torch.uint8, device=device)
+            self._ws = self.new_workspace(device)
         return self._ws
 
     def __call__(self, states, accept_idx, h, weights, gathered, out, logrms=None, delta=None,

@@ -3,13 +3,10 @@
 //
 // Two launch sequences, both on the caller's stream:
 //
-// fast (bf16 states, activations and weights, r <= 32, F and Hm multiples of 8):
-//   0. k_zgemm    z partial sums W_q (gamma h) over K chunks, sums of squares
-//                 of h; clears the counters of k_fused
-//   1. k_fused    ticketed work items: per (sequence, pair) tile the gather,
-//                 RMS, log-RMS and P = V^T S_bar U^T / sqrt(d_k); per 16 rows
-//                 f_j = [P z_j / rms(h_j), ell] and a = act(W1 f + b1); per
-//                 output tile out = h + W2 a + b2
+// fast (bf16 states, activations and weights, r <= 32, F and Hm multiples of
+// 8): one persistent launch, k_reader (query sums, state tiles, f and the
+// first MLP layer, the second MLP layer and the residual as work items of one
+// grid that the GPU holds at once)
 // general (any other dtype mix or rank):
 //   0. query GEMM (split-K partial sums of z and of the squares of h)
 //   1. k_state    gather, RMS, log-RMS, T = V^T S_bar, q = U^T z,
@@ -42,8 +39,10 @@ struct readyPlan {
   int32_t slot[READY_MAX_LSEL];
   int M, F, R, Mz, Nz;
   int fast;
-  int zbm, obm;  // fast path: row tile of the query GEMM and of MLP layer 2
-  int n_s, n_a, n_o, n_counters;
+  int small;     // fast path: at most 16 rows (16-row tiles; 64 otherwise)
+  int n_z, n_s, n_a, n_o, n_counters;
+  int c_zdone, c_sdone, c_adone;  // first counter slot of each group
+  size_t lds;
   GemmPlan gz, g1, g2;
   size_t off_zpart, off_hss, off_f, off_a, off_flags, off_pmat, off_ell, off_ctr, ws_bytes;
 };
@@ -104,6 +103,7 @@ const char* readyStatusString(readyStatus st) {
     case READY_ERR_ACCEPT_IDX: return "READY_ERR_ACCEPT_IDX";
     case READY_ERR_OUT_OF_HOST_MEMORY: return "READY_ERR_OUT_OF_HOST_MEMORY";
     case READY_ERR_SYNC_TIMEOUT: return "READY_ERR_SYNC_TIMEOUT";
+    case READY_ERR_WORKSPACE_UNINIT: return "READY_ERR_WORKSPACE_UNINIT";
   }
   return "READY_ERR_UNKNOWN";
 }
@@ -128,28 +128,34 @@ readyStatus readyPlanCreate(const readyShape* shape, const int32_t* layer_ids, r
 
   const bool wbf = s.weight_dtype == READY_BF16;
   const bool allbf = wbf && s.state_dtype == READY_BF16 && s.act_dtype == READY_BF16;
-  // (the fast path addresses P and a with 32-bit byte offsets)
+  // (the fast path addresses z partial sums, P and a with 32-bit byte offsets)
+  const int64_t zchunk = p->R <= 16 ? READY_ZCHUNK_SMALL : READY_ZCHUNK_LARGE;
+  const int64_t fks = cdiv(s.d, zchunk);
   const bool small_ws = (int64_t)s.B * p->M * s.r * s.r * 4 < (1LL << 31) &&
-                        (int64_t)p->R * s.Hm * 2 < (1LL << 31);
-  p->fast = (allbf && s.r <= 32 && p->F % 8 == 0 && p->F <= READY_FAST_MAX_F && s.Hm % 8 == 0 && small_ws) ? 1 : 0;
+                        (int64_t)p->R * s.Hm * 2 < (1LL << 31) &&
+                        fks * p->R * p->Nz * 4 < (1LL << 31);
+  p->small = p->R <= 16 ? 1 : 0;
+  const bool fits = allbf && s.r <= 32 && p->F % 8 == 0 && p->F <= READY_FAST_MAX_F && s.Hm % 8 == 0 &&
+                    p->Nz <= READY_FAST_MAX_NZ && small_ws;
+  p->lds = fits ? ready_reader_lds(s.r, p->F, p->Nz, p->small) : 0;
+  p->fast = (fits && p->lds <= 80 * 1024) ? 1 : 0;  // two workgroups per CU
 
   if (p->fast) {
-    // query GEMM: BM x 64 tiles of z over K chunks of at most 640 values (each
-    // wave loads its quarter of the chunk at once); 8 chunks for large row
-    // counts (the items of one chunk then share an XCD), 16 for at most 16
-    // rows, where the K split is the only source of parallelism
-    p->zbm = p->R <= 16 ? 16 : 64;
-    p->obm = p->R <= 16 ? 16 : 64;
-    int64_t ks = std::max<int64_t>(p->R <= 16 ? 16 : 8, cdiv(s.d, 640));
-    ks = std::min<int64_t>(ks, cdiv(s.d, 128));
-    const int64_t kchunk = align_up((size_t)cdiv(s.d, ks), 128);
-    p->gz.kchunk = (int)kchunk;
-    p->gz.ksplit = (int)cdiv(s.d, kchunk);
-    const int64_t nrb16 = cdiv(std::max(p->R, 1), 16);
+    // work items of k_reader
+    const int bm = p->small ? 16 : 64;
+    const int64_t nrbz = cdiv(std::max(p->R, 1), bm), nrb16 = cdiv(std::max(p->R, 1), 16);
+    p->gz.ksplit = (int)fks;
+    p->gz.kchunk = (int)zchunk;
+    p->n_z = (int)(nrbz * cdiv(p->Nz, 64) * fks);
     p->n_s = s.B * p->M;
     p->n_a = (int)(nrb16 * cdiv(s.Hm, 64));
-    p->n_o = (int)(cdiv(std::max(p->R, 1), p->obm) * cdiv(s.d, 64));
-    p->n_counters = (int)(READY_CTR_STRIDE * (2 + s.B + nrb16));
+    p->n_o = (int)(nrbz * cdiv(s.d, 64));
+    // counter slots: magic, abort, READY_DONE_GROUPS + 1 done counts, then
+    // per row tile of z, per 16 rows, per row tile of out
+    p->c_zdone = 2 + READY_DONE_GROUPS + 1;
+    p->c_sdone = (int)(p->c_zdone + nrbz);
+    p->c_adone = (int)(p->c_sdone + nrb16);
+    p->n_counters = (int)(READY_CTR_STRIDE * (p->c_adone + nrbz));
   } else {
     // query GEMM: matrix cores for bf16 h and weights; K split so that about
     // 256 (matrix cores) or 512 (VALU) workgroups run
@@ -309,19 +315,35 @@ readyStatus run_reader(const readyPlan* plan, const readyStates* states, const i
     a.seq_invalid = (uint32_t*)flags;
     uint32_t* ctr = (uint32_t*)(wsb + plan->off_ctr);
     a.counters = ctr; a.n_counters = plan->n_counters;
-    a.ticket = ctr; a.abort_flag = ctr + READY_CTR_STRIDE; a.seqdone = ctr + 2 * READY_CTR_STRIDE;
-    a.adone = ctr + READY_CTR_STRIDE * (2 + s.B);
-    a.n_s = plan->n_s; a.n_a = plan->n_a; a.n_o = plan->n_o;
+    a.magic = READY_WS_MAGIC ^ (uint32_t)plan->n_counters;
+    a.abort_flag = ctr + READY_CTR_STRIDE;
+    a.done = ctr + 2 * READY_CTR_STRIDE;
+    a.zdone = ctr + READY_CTR_STRIDE * plan->c_zdone;
+    a.sdone = ctr + READY_CTR_STRIDE * plan->c_sdone;
+    a.adone = ctr + READY_CTR_STRIDE * plan->c_adone;
+    a.n_z = plan->n_z; a.n_s = plan->n_s; a.n_a = plan->n_a; a.n_o = plan->n_o;
     a.B = s.B; a.P = s.P; a.n = s.n; a.M = (int)M; a.H = s.H; a.r = s.r; a.d = (int)d; a.F = (int)F;
     a.Hm = (int)Hm; a.R = (int)R; a.Nz = plan->Nz; a.shared = s.shared_params;
     a.ksplit = plan->gz.ksplit; a.kchunk = plan->gz.kchunk; a.act = s.act;
     a.state_eps = s.state_eps; a.h_eps = s.h_eps;
-    if (ready_launch_zgemm(a, plan->zbm, strm, stage_events(events, 0)) != hipSuccess) return READY_ERR_HIP;
-    if (ready_launch_fused(a, plan->obm, strm, stage_events(events, 1)) != hipSuccess) return READY_ERR_HIP;
-    // stages 2 and 3 run inside the fused kernel: their marks (if any) are
+    // the grid is what the GPU holds at once: every wait in the kernel is
+    // for a workgroup that is already running
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return READY_ERR_HIP;
+    const int per_cu = std::min(2, ready_reader_per_cu(s.r, plan->small, plan->lds));
+    if (per_cu < 1 || cus < 1) return READY_ERR_HIP;
+    const int grid = per_cu * cus;
+    a.g_t = std::max(1, std::min(plan->n_a, std::max(4, grid / 8)));
+    a.g_s = grid - a.g_t;
+    if (ready_launch_reader(a, plan->small, grid, strm, stage_events(events, 1)) != hipSuccess)
+      return READY_ERR_HIP;
+    // the other stages run inside the same kernel: their marks (if any) are
     // recorded together after it
-    for (int i = 4; events && i < 2 * READY_STAGES; ++i)
-      if (events[i] && hipEventRecord((hipEvent_t)events[i], strm) != hipSuccess) return READY_ERR_HIP;
+    for (int i = 0; events && i < 2 * READY_STAGES; ++i)
+      if ((i < 2 || i > 3) && events[i] && hipEventRecord((hipEvent_t)events[i], strm) != hipSuccess)
+        return READY_ERR_HIP;
     return READY_OK;
   }
 
@@ -410,6 +432,18 @@ readyStatus run_reader(const readyPlan* plan, const readyStates* states, const i
 }
 
 }  // namespace
+
+readyStatus readyWorkspaceInit(const readyPlan* plan, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!plan || !workspace) return READY_ERR_NULL_POINTER;
+  if (((uintptr_t)workspace & 255u) != 0) return READY_ERR_MISALIGNED;
+  if (workspace_bytes < plan->ws_bytes) return READY_ERR_WORKSPACE_TOO_SMALL;
+  if (!plan->fast || plan->n_counters == 0) return READY_OK;  // the general path keeps no counters
+  uint32_t* ctr = (uint32_t*)((char*)workspace + plan->off_ctr);
+  if (ready_launch_ws_init(ctr, plan->n_counters, READY_WS_MAGIC ^ (uint32_t)plan->n_counters,
+                           (hipStream_t)stream) != hipSuccess)
+    return READY_ERR_HIP;
+  return READY_OK;
+}
 
 readyStatus readyStateReader(const readyPlan* plan, const readyStates* states,
                              const int32_t* accept_idx, const void* h,

@@ -36,12 +36,14 @@ struct StateArgs {
   float* feat;                     // [B*n][F] or null
 };
 
-// Fast path (bf16 states, activations and weights; r <= 32): two launches
-//   k_zgemm   z partial sums W_q (gamma h) over K chunks and the sums of
-//             squares of h (matrix cores); clears the counters of k_fused
-//   k_fused   ticketed work items: S (gather, RMS, log-RMS,
-//             P = V^T S_bar U^T / sqrt(d_k) per tile), A (f and
-//             a = act(W1 f + b1) per 16 rows) and O (out = h + W2 a + b2)
+// Fast path (bf16 states, activations and weights; r <= 32): one persistent
+// launch, k_reader, whose workgroups run four kinds of work items:
+//   Z  query sums z = W_q (gamma h) per 64 x 64 tile and K chunk, and the
+//      sums of squares of h
+//   S  per (sequence, pair) tile: gather, RMS, log-RMS and
+//      P = V^T S_bar U^T / sqrt(d_k)
+//   A  per 16 rows and 64 columns of a: f and a = act(W1 f + b1)
+//   O  per output tile: out = h + W2 a + b2
 struct FastArgs {
   const uint16_t* states;
   int64_t sb, sp, sl, sh;          // element strides of the verify buffer
@@ -68,21 +70,32 @@ struct FastArgs {
   float* ell;                      // [B M]
   uint16_t* abuf;                  // [R][Hm] bf16
   uint32_t* seq_invalid;           // [B]
-  // counters of k_fused (cleared by k_zgemm): ticket, abort flag, per
-  // sequence the S items done, per 16 rows the A items done
+  // Counters, READY_CTR_STRIDE words apart: [0] the workspace magic,
+  // [1] abort flag, [2 .. 2 + READY_DONE_GROUPS] workgroups finished per
+  // group and overall, then the Z items done per row tile of z, the S items
+  // done per 16 rows, the A items done per row tile of out.  The last
+  // workgroup to finish clears all of them except the magic.
   uint32_t* counters;
-  int n_counters;
-  uint32_t* ticket;
+  int n_counters;                  // words
+  uint32_t magic;
   uint32_t* abort_flag;
-  uint32_t* seqdone;               // [B] (stride READY_CTR_STRIDE)
-  uint32_t* adone;                 // [cdiv(R, 16)] (stride READY_CTR_STRIDE)
-  int n_s, n_a, n_o;               // work items of k_fused per kind
+  uint32_t* done;                  // [READY_DONE_GROUPS + 1]
+  uint32_t* zdone;                 // [cdiv(R, BMZ)]
+  uint32_t* sdone;                 // [cdiv(R, 16)]
+  uint32_t* adone;                 // [cdiv(R, OBM)]
+  int n_z, n_s, n_a, n_o;          // work items per kind
+  int g_s, g_t;                    // workgroups that run S items; the rest (g_t) run A items
   int B, P, n, M, H, r, d, F, Hm, R, Nz, shared, ksplit, kchunk, act;
   float state_eps, h_eps;
 };
 
 #define READY_FAST_MAX_F 1536      // f rows of 16 positions staged in LDS
-#define READY_CTR_STRIDE 32        // counters of k_fused sit 128 bytes apart
+#define READY_FAST_MAX_NZ 1024     // query sums of 16 positions staged in LDS
+#define READY_CTR_STRIDE 32        // counters sit 128 bytes apart
+#define READY_DONE_GROUPS 16
+#define READY_WS_MAGIC 0x52454459u // "READY"
+#define READY_ZCHUNK_SMALL 640     // K chunk of a Z item, at most 16 rows (160 per wave)
+#define READY_ZCHUNK_LARGE 384     // K chunk of a Z item, 64-row tiles (96 per wave)
 
 enum { EPI_PARTIAL = 0, EPI_BIAS_ACT = 1, EPI_RESID = 2 };
 
@@ -135,7 +148,8 @@ READY_HIDDEN hipError_t ready_launch_gemm(const GemmArgs& g, int x_dt, int w_dt,
 // bm: rows per workgroup tile (16 or 64); weights must be bf16
 READY_HIDDEN hipError_t ready_launch_gemm_mfma(const GemmArgs& g, int x_dt, int out_dt, int epi, int bm,
                                                dim3 grid, hipStream_t s, StageEvents ev);
-// fast path; bm: rows per tile (16 or 64)
-READY_HIDDEN hipError_t ready_launch_zgemm(const FastArgs& a, int bm, hipStream_t s, StageEvents ev);
-READY_HIDDEN hipError_t ready_launch_fused(const FastArgs& a, int obm, hipStream_t s, StageEvents ev);
-READY_HIDDEN size_t ready_fused_lds(int r, int F, int obm);
+// fast path; small: at most 16 rows (16-row tiles), else 64-row tiles
+READY_HIDDEN hipError_t ready_launch_reader(const FastArgs& a, int small, int grid, hipStream_t s, StageEvents ev);
+READY_HIDDEN hipError_t ready_launch_ws_init(uint32_t* counters, int n_counters, uint32_t magic, hipStream_t s);
+READY_HIDDEN size_t ready_reader_lds(int r, int F, int Nz, int small);
+READY_HIDDEN int ready_reader_per_cu(int r, int small, size_t lds);

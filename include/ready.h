@@ -58,8 +58,10 @@ typedef enum readyStatus {
   READY_ERR_HIP = 8,                /* the HIP runtime reported an error at launch */
   READY_ERR_ACCEPT_IDX = 9,         /* device-side only: accept_idx[b] outside [0, P) */
   READY_ERR_OUT_OF_HOST_MEMORY = 10,
-  READY_ERR_SYNC_TIMEOUT = 11       /* device-side only: a wait between work items of one launch
+  READY_ERR_SYNC_TIMEOUT = 11,      /* device-side only: a wait between work items of one launch
                                        gave up (should never happen; outputs are then invalid) */
+  READY_ERR_WORKSPACE_UNINIT = 12   /* device-side only: the workspace was not prepared by
+                                       readyWorkspaceInit for this plan; nothing was computed */
 } readyStatus;
 
 typedef enum readyDtype { READY_F32 = 0, READY_BF16 = 1 } readyDtype;
@@ -168,11 +170,26 @@ readyStatus readyPlanDestroy(readyPlan* plan);
 readyStatus readyWorkspaceSize(const readyPlan* plan, size_t* bytes);
 
 /*
+ * Prepare a workspace for use with `plan`: enqueue on `stream` a small kernel
+ * that clears the synchronisation counters the state reader keeps in the
+ * workspace and stamps it for this plan.  Call it once after allocating the
+ * workspace (and again before using the workspace with a different plan);
+ * every readyStateReader call leaves the counters cleared for the next call.
+ * A call on an unprepared workspace computes nothing and stores
+ * READY_ERR_WORKSPACE_UNINIT in the caller's device status word.  The
+ * function allocates nothing and does not synchronise.  Returns
+ * READY_ERR_NULL_POINTER, READY_ERR_MISALIGNED (workspace not 256-byte
+ * aligned), READY_ERR_WORKSPACE_TOO_SMALL or READY_ERR_HIP.
+ */
+readyStatus readyWorkspaceInit(const readyPlan* plan, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Run steps 1-5 for every sequence, asynchronously on `stream` (a
  * hipStream_t; NULL = the default stream).  accept_idx: device int32 [B].
  * h: device [B][n][d] in act_dtype.  workspace: device memory of at least
- * readyWorkspaceSize() bytes, 256-byte aligned, used as scratch by this call
- * only (concurrent calls need separate workspaces).  The enqueued work
+ * readyWorkspaceSize() bytes, 256-byte aligned, prepared once by
+ * readyWorkspaceInit, used as scratch by this call only (concurrent calls
+ * need separate workspaces).  The enqueued work
  * allocates nothing and synchronises nothing, so it may be captured into a
  * HIP graph.  Returns READY_ERR_HIP if a launch fails.
  */
@@ -182,14 +199,16 @@ readyStatus readyStateReader(const readyPlan* plan, const readyStates* states,
                              void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * Same computation as readyStateReader, with per-stage kernel timestamps:
- * events[2 i] and events[2 i + 1] (hipEvent_t, or NULL to skip) are recorded
- * at the start and at the end of the kernel of launch stage i itself (the
- * launch records them; no marker packet is inserted between stages).
- * Stages: 0 query GEMM (z and the sums of squares of h), 1 per-state kernel
- * (gather, RMS, log-RMS, projection), 2 first MLP layer (with the readout and
- * packing of f on the fast path), 3 second MLP layer and residual.  The
- * events must have been created by the caller on the device of `stream`
+ * Same computation as readyStateReader, with kernel timestamps: events[2 i]
+ * and events[2 i + 1] (hipEvent_t, or NULL to skip) are recorded at the
+ * start and at the end of the kernel of launch stage i itself (the launch
+ * records them; no marker packet is inserted between stages).  On the bf16
+ * path (bf16 states, activations and weights, r <= 32) the whole call is one
+ * kernel: stage 1 carries its start and end, and the events of stages 0, 2
+ * and 3 are recorded right after it.  On the general path the stages are
+ * 0 query GEMM, 1 per-state kernel (gather, RMS, log-RMS, projection,
+ * readout, packing), 2 first MLP layer, 3 second MLP layer and residual.
+ * The events must have been created by the caller on the device of `stream`
  * with timing enabled; the library only records them.
  */
 #define READY_STAGES 4

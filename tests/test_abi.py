@@ -233,3 +233,21 @@ def test_python_binding_raises_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(R, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(R.ReadyError):
         R.load()
+
+
+def test_workspace_init_validation():
+    """readyWorkspaceInit rejects bad arguments on the host, before any launch."""
+    _lib()
+    st, plan = R.readyPlanCreate(_shape(), [0, 1])
+    assert st == R.READY_OK
+    _, n = R.readyWorkspaceSize(plan)
+    assert R.readyWorkspaceInit(None, 1 << 40, n, None) == R.READY_ERR_NULL_POINTER
+    assert R.readyWorkspaceInit(plan, None, n, None) == R.READY_ERR_NULL_POINTER
+    assert R.readyWorkspaceInit(plan, (1 << 40) + 16, n, None) == R.READY_ERR_MISALIGNED
+    assert R.readyWorkspaceInit(plan, 1 << 40, n - 1, None) == R.READY_ERR_WORKSPACE_TOO_SMALL
+    R.readyPlanDestroy(plan)
+    # the general path keeps no counters: nothing to prepare, nothing launched
+    st, plan = R.readyPlanCreate(_shape(state_dtype="f32", act_dtype="f32", weight_dtype="f32"), [0, 1])
+    _, n = R.readyWorkspaceSize(plan)
+    assert R.readyWorkspaceInit(plan, 1 << 40, n, None) == R.READY_OK
+    R.readyPlanDestroy(plan)

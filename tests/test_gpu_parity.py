@@ -266,3 +266,65 @@ def test_graph_capture_replays_match_eager():
             assert torch.equal(o[k].view(torch.int8) if o[k].dtype != torch.float32 else o[k], 
                                eager[k].view(torch.int8) if eager[k].dtype != torch.float32 else eager[k]), (rep, k)
         del junk
+
+
+# ------------------------------------------------------------ workspace contract
+
+def test_unprepared_workspace_is_reported_and_computes_nothing():
+    """A workspace that readyWorkspaceInit did not prepare: the call stores
+    READY_ERR_WORKSPACE_UNINIT and leaves every output untouched."""
+    from hla_recurrent_state_amd import READY_ERR_WORKSPACE_UNINIT, StateReader
+    import tests.gpu_util as gu
+    dev = _dev()
+    cfg = make_shape("paper", B=2, t=8)
+    inp = synth.make(cfg, seed=41)
+    d = synth.device.to_device(inp, dev)
+    reader = StateReader(gu.reader_shape(cfg), cfg.slots)
+    ws = torch.zeros(max(reader.workspace_bytes, 256), dtype=torch.uint8, device=dev)
+    o = gu.alloc_outputs(cfg, dev)
+    o["out"].view(torch.int16).fill_(0x7FC1)
+    o["gathered"].view(torch.int16).fill_(0x7FC1)
+    reader(d["states"], d["accept_idx"], d["h"], d["weights"], o["gathered"], o["out"],
+           dev_status=o["dev_status"], workspace=ws)
+    torch.cuda.synchronize()
+    assert int(o["dev_status"].item()) == READY_ERR_WORKSPACE_UNINIT
+    assert bool(torch.all(o["out"].view(torch.int16) == 0x7FC1))
+    assert bool(torch.all(o["gathered"].view(torch.int16) == 0x7FC1))
+
+
+def test_repeated_calls_on_one_workspace():
+    """Calls on one prepared workspace: each call leaves its counters cleared
+    for the next, so repeated calls (with changed accept indices in between)
+    reproduce single-call results bit for bit."""
+    from hla_recurrent_state_amd import StateReader
+    import tests.gpu_util as gu
+    from synth.device import to_numpy_bits
+    dev = _dev()
+    cfg = make_shape("batched", B=6, t=16)
+    inp = synth.make(cfg, seed=42)
+    d = synth.device.to_device(inp, dev)
+    reader = StateReader(gu.reader_shape(cfg), cfg.slots)
+    ws = reader.new_workspace(dev)
+    o = gu.alloc_outputs(cfg, dev)
+
+    def call(acc):
+        d["accept_idx"].copy_(torch.from_numpy(acc.astype(np.int32)))
+        reader(d["states"], d["accept_idx"], d["h"], d["weights"], o["gathered"], o["out"],
+               logrms=o["logrms"], delta=o["delta"], dev_status=o["dev_status"], workspace=ws)
+        torch.cuda.synchronize()
+        return {k: (to_numpy_bits(o[k], cfg.act_dtype) if k == "out" else o[k].cpu().numpy().copy())
+                for k in ("out", "logrms", "delta")}
+
+    first = call(inp.accept_idx)
+    other = call((inp.accept_idx + 3) % cfg.P)
+    again = call(inp.accept_idx)
+    for k in first:
+        assert np.array_equal(first[k], again[k]), k
+    assert not np.array_equal(first["logrms"], other["logrms"])
+    assert int(o["dev_status"].item()) == 0
+    rep = __import__("tests.gpu_util", fromlist=["compare"]).compare(
+        inp, {"gathered": to_numpy_bits(o["gathered"], cfg.state_dtype), "out": first["out"],
+              "logrms": first["logrms"], "delta": first["delta"],
+              "feat": np.zeros((cfg.B, cfg.n, cfg.F), np.float32), "dev_status": 0},
+        __import__("tests.gpu_util", fromlist=["oracle_reference"]).oracle_reference(inp))
+    assert rep["gather_bitexact"] and rep["dh_rel"] <= rep["tol"] and rep["logrms_err"] <= 1e-5, rep
