@@ -41,7 +41,7 @@ struct readyPlan {
   int fast;
   int small;     // fast path: at most 16 rows (16-row tiles; 64 otherwise)
   int n_z, n_s, n_a, n_o, n_counters;
-  int c_zdone, c_sdone, c_adone;  // first counter slot of each group
+  int c_zcnt, c_zdone, c_sdone, c_adone, c_tk;  // first counter slot of each group
   size_t lds;
   GemmPlan gz, g1, g2;
   size_t off_zpart, off_hss, off_f, off_a, off_flags, off_pmat, off_ell, off_ctr, ws_bytes;
@@ -142,20 +142,23 @@ readyStatus readyPlanCreate(const readyShape* shape, const int32_t* layer_ids, r
 
   if (p->fast) {
     // work items of k_reader
-    const int bm = p->small ? 16 : 64;
-    const int64_t nrbz = cdiv(std::max(p->R, 1), bm), nrb16 = cdiv(std::max(p->R, 1), 16);
+    const int bmz = p->small ? 16 : 64, bmo = p->small ? 16 : 64;
+    const int64_t rows = std::max(p->R, 1);
+    const int64_t nrbz = cdiv(rows, bmz), ncbz = cdiv(p->Nz, 64), nrb16 = cdiv(rows, 16), nrbo = cdiv(rows, bmo);
     p->gz.ksplit = (int)fks;
     p->gz.kchunk = (int)zchunk;
-    p->n_z = (int)(nrbz * cdiv(p->Nz, 64) * fks);
+    p->n_z = (int)(nrbz * ncbz * fks);
     p->n_s = s.B * p->M;
     p->n_a = (int)(nrb16 * cdiv(s.Hm, 64));
-    p->n_o = (int)(nrbz * cdiv(s.d, 64));
+    p->n_o = (int)(nrbo * cdiv(s.d, READY_OCOLS));
     // counter slots: magic, abort, READY_DONE_GROUPS + 1 done counts, then
-    // per row tile of z, per 16 rows, per row tile of out
-    p->c_zdone = 2 + READY_DONE_GROUPS + 1;
+    // per tile of z, per row block of z, per 16 rows, per row block of out
+    p->c_zcnt = 2 + READY_DONE_GROUPS + 1;
+    p->c_zdone = (int)(p->c_zcnt + nrbz * ncbz);
     p->c_sdone = (int)(p->c_zdone + nrbz);
     p->c_adone = (int)(p->c_sdone + nrb16);
-    p->n_counters = (int)(READY_CTR_STRIDE * (p->c_adone + nrbz));
+    p->c_tk = (int)(p->c_adone + nrbo);
+    p->n_counters = (int)(READY_CTR_STRIDE * (p->c_tk + READY_TICKET_GROUPS));
   } else {
     // query GEMM: matrix cores for bf16 h and weights; K split so that about
     // 256 (matrix cores) or 512 (VALU) workgroups run
@@ -193,7 +196,8 @@ readyStatus readyPlanCreate(const readyShape* shape, const int32_t* layer_ids, r
   size_t off = 0;
   p->off_zpart = off; off = align_up(off + 4 * ks * R * p->Nz, 256);
   p->off_hss = off;   off = align_up(off + 4 * ks * R, 256);
-  p->off_f = off;     off = align_up(off + (p->fast ? 0 : 4 * R * p->F), 256);
+  // f on the general path, z summed over the K chunks on the fast path
+  p->off_f = off;     off = align_up(off + 4 * R * (p->fast ? p->Nz : p->F), 256);
   // a: bf16 on the fast path, fp32 otherwise
   p->off_a = off;     off = align_up(off + (p->fast ? 2 : 4) * R * s.Hm, 256);
   p->off_flags = off; off = align_up(off + 4 * (size_t)std::max(s.B, 1), 256);
@@ -225,6 +229,13 @@ StageEvents stage_events(void* const* events, int i) {
     ev.stop = (hipEvent_t)events[2 * i + 1];
   }
   return ev;
+}
+
+// Items are dealt to the 8 XCDs round robin when the grid allows it; the
+// state tiles are drawn through READY_TICKET_GROUPS ticket counters.
+void reader_roles(FastArgs& a, int grid) {
+  a.nxcd = (grid % 8 == 0) ? 8 : 1;
+  a.ntg = std::min(grid, READY_TICKET_GROUPS);
 }
 
 readyStatus run_reader(const readyPlan* plan, const readyStates* states, const int32_t* accept_idx,
@@ -311,16 +322,18 @@ readyStatus run_reader(const readyPlan* plan, const readyStates* states, const i
     a.w2 = (const uint16_t*)w->w2; a.b2 = (const uint16_t*)w->b2;
     a.gathered = (uint16_t*)o->gathered; a.out = (uint16_t*)o->out;
     a.logrms = o->logrms; a.delta = o->delta; a.feat = o->feat; a.dev_status = o->dev_status;
-    a.zpart = zpart; a.hss = hss; a.pmat = pmat; a.ell = ellw; a.abuf = (uint16_t*)abuf;
+    a.zpart = zpart; a.hss = hss; a.zfin = (float*)(wsb + plan->off_f); a.pmat = pmat; a.ell = ellw; a.abuf = (uint16_t*)abuf;
     a.seq_invalid = (uint32_t*)flags;
     uint32_t* ctr = (uint32_t*)(wsb + plan->off_ctr);
     a.counters = ctr; a.n_counters = plan->n_counters;
     a.magic = READY_WS_MAGIC ^ (uint32_t)plan->n_counters;
     a.abort_flag = ctr + READY_CTR_STRIDE;
     a.done = ctr + 2 * READY_CTR_STRIDE;
+    a.zcnt = ctr + READY_CTR_STRIDE * plan->c_zcnt;
     a.zdone = ctr + READY_CTR_STRIDE * plan->c_zdone;
     a.sdone = ctr + READY_CTR_STRIDE * plan->c_sdone;
     a.adone = ctr + READY_CTR_STRIDE * plan->c_adone;
+    a.tk = ctr + READY_CTR_STRIDE * plan->c_tk;
     a.n_z = plan->n_z; a.n_s = plan->n_s; a.n_a = plan->n_a; a.n_o = plan->n_o;
     a.B = s.B; a.P = s.P; a.n = s.n; a.M = (int)M; a.H = s.H; a.r = s.r; a.d = (int)d; a.F = (int)F;
     a.Hm = (int)Hm; a.R = (int)R; a.Nz = plan->Nz; a.shared = s.shared_params;
@@ -335,8 +348,7 @@ readyStatus run_reader(const readyPlan* plan, const readyStates* states, const i
     const int per_cu = std::min(2, ready_reader_per_cu(s.r, plan->small, plan->lds));
     if (per_cu < 1 || cus < 1) return READY_ERR_HIP;
     const int grid = per_cu * cus;
-    a.g_t = std::max(1, std::min(plan->n_a, std::max(4, grid / 8)));
-    a.g_s = grid - a.g_t;
+    reader_roles(a, grid);
     if (ready_launch_reader(a, plan->small, grid, strm, stage_events(events, 1)) != hipSuccess)
       return READY_ERR_HIP;
     // the other stages run inside the same kernel: their marks (if any) are

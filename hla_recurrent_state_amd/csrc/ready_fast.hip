@@ -3,26 +3,32 @@
 //
 // Its grid is two workgroups per CU, which the register and LDS budget of
 // the kernel lets the GPU hold at the same time.  Work is assigned
-// statically; each workgroup runs, in this order:
-//   Z  at most one (or a few) query item: a BM x 64 tile of the partial sums
-//      z = W_q (gamma h) over one K chunk, plus the sums of squares of h for
-//      RMSNorm(h_j)                                        (step 4, query)
-//   S  (workgroups [0, g_s)) the state tiles t = rank, rank + g_s, ...: fused
-//      gather at the accept index into the caller's buffer, mean square,
-//      log-RMS and P = V^T S_bar U^T / sqrt(d_k), an r x r matrix; the next
-//      tile's loads are issued before the current tile is processed
-//                                                          (steps 1-3)
-//   A  (workgroups [g_s, G)) items of 16 rows and 64 columns of a, in row
-//      order: f_j = [P z_j / rms(h_j), ell] per pair (u_j = T q_j / sqrt(d_k)
-//      with T = V^T S_bar and q_j = U^T z_j, reassociated through P), then
-//      a = act(W1 f + b1)                        (step 4 readout, step 5)
-//   O  items o = g, g + G, ...: a BM x 64 tile of out = h + W2 a + b2 (step 5)
-// An A item waits for the Z items of its rows and the S items of its
-// sequences; an O item waits for the A items of its rows.  Z and S items
-// never wait and A items wait only for Z and S items, so with every
-// workgroup resident at once each wait ends; while the state tiles stream,
-// the A workgroups already run the MLP of the sequences whose states are
-// complete.
+// statically to three groups of workgroups:
+//   workers   (the first g_w): Z items, a BM x 64 tile of the partial sums
+//             z = W_q (gamma h) over one K chunk plus the sums of squares of
+//             h for RMSNorm(h_j) (step 4, query); then the A items of the
+//             early rows, 16 rows x 64 columns of a: f_j = [P z_j / rms(h_j),
+//             ell] per pair (u_j = T q_j / sqrt(d_k) with T = V^T S_bar and
+//             q_j = U^T z_j, reassociated through P), a = act(W1 f + b1)
+//             (step 4 readout, step 5); then the O items of the early row
+//             blocks, a BM x 64 tile of out = h + W2 a + b2 (step 5); then the
+//             A items of the late rows.
+//   streamers (the next g_s): the state tiles t = s, s + g_s, ...: fused
+//             gather at the accept index into the caller's buffer, mean
+//             square, log-RMS and P = V^T S_bar U^T / sqrt(d_k), an r x r
+//             matrix (steps 1-3); two tiles are in flight while one is
+//             processed.  Then O items of the late row blocks.
+//   the rest: O items of the late row blocks only.
+// "Late" rows belong to sequences whose tiles are among the last two turns
+// of the streamers; their MLP runs after the stream, everything else while
+// it runs.  Z and S items never wait; A items wait for Z and S items; O
+// items wait for A items, and a worker finishes its early A items before it
+// takes an O item.  With every workgroup resident at once each wait ends.
+//
+// The K chunks of the Z items, and the column blocks of the O items, are
+// dealt to the XCDs round robin (the hardware hands workgroup g to XCD
+// g % 8), so the h and W_q columns of a chunk, and the W2 rows of a column
+// block, are read from HBM once and then served by that XCD's L2.
 //
 // Cross-workgroup data (z partial sums, P, ell, the invalid-sequence flags,
 // a) is written with device-coherent stores (sc1), made complete with a wait
@@ -91,8 +97,8 @@ __device__ __forceinline__ uint32_t count_up(uint32_t* c) {
 __device__ __forceinline__ uint32_t* ctr(uint32_t* base, int i) { return base + READY_CTR_STRIDE * i; }
 
 // Poll *c until it reaches `want`, backing off from about 100 ns to about
-// 0.9 us between polls so that waiting workgroups do not flood the memory
-// channel that holds the counter while the state tiles stream.  Bounded:
+// 0.4 us between polls so that waiting workgroups do not flood the memory
+// channel that holds the counter.  Bounded:
 // after about a second, or as soon as another workgroup has given up, it
 // raises the abort flag, reports READY_ERR_SYNC_TIMEOUT and returns false.
 constexpr int SPIN_LIMIT = 1 << 20;
@@ -109,11 +115,9 @@ __device__ bool wait_count(const uint32_t* c, uint32_t want, uint32_t* abort_fla
     switch (nap) {  // s_sleep takes an immediate operand
       case 0: __builtin_amdgcn_s_sleep(4); break;
       case 1: __builtin_amdgcn_s_sleep(8); break;
-      case 2: __builtin_amdgcn_s_sleep(16); break;
-      case 3: __builtin_amdgcn_s_sleep(24); break;
-      default: __builtin_amdgcn_s_sleep(32); break;
+      default: __builtin_amdgcn_s_sleep(16); break;
     }
-    if (nap < 4) ++nap;
+    if (nap < 2) ++nap;
   }
 }
 
@@ -130,166 +134,218 @@ __device__ bool wg_wait(const uint32_t* c, uint32_t want, const FastArgs& a, int
 
 // ---------------------------------------------------------------- Z items
 
-// Item q = (ks * ncb + cb) * nrb + rb: a BM x 64 tile of z over K chunk ks
-// of 128 KS values.  The four waves take consecutive quarters of the chunk
-// (KS k-steps of 32 each) and load them straight into registers before the
-// matrix instructions; the quarters are summed through LDS in a fixed order
-// and the tile is stored with 16-byte device-coherent stores.  Column block
-// 0 also sums the squares of the h values it loads (before the gain).
-template <int BM, int KS>
-__device__ void z_item(const FastArgs& a, int q, unsigned char* smem) {
-  constexpr int RB = BM / 16;
-  constexpr int ZCH = 128 * KS;  // K chunk
+// 16-byte slot of chunk c (of 16) in row v of a 256-byte-per-row LDS tile:
+// rotated by v % 16 so that both row-wise writes and matrix-operand reads
+// (16 rows at one chunk) hit distinct banks.
+__device__ __forceinline__ int tile_slot(int v, int c) { return v * 16 + (c ^ (v & 15)); }
+
+// Rows [BMZ rb, BMZ rb + BMZ) and columns [64 cb, 64 cb + 64) of the partial
+// sums of z = W_q (gamma h) over K chunk ks.  The chunk is walked in stages
+// of 128 values of K: the workgroup loads a stage of h and W_q rows with
+// row-contiguous 16-byte loads (a wave instruction moves whole 256-byte row
+// pieces; three stages are in flight at a time), applies the gain and parks
+// one stage at a time in LDS for the matrix instructions; each wave owns a
+// (16 WR) x (16 WC) block of the tile.  Column block 0 also stores the sums
+// of squares of the h values (before the gain), for RMSNorm(h_j).  The item
+// that completes the last chunk of a tile (counted per tile) sums the chunks
+// in chunk order into zfin, so the result does not depend on which item came
+// last.
+template <int BMZ>
+struct ZStage {
+  static constexpr int HC = BMZ / 16;  // h chunks per thread
+  u32x4 h[HC];
+  u32x4 w[4];                          // W_q chunks per thread
+  u32x4 g;                             // gain chunk
+};
+
+template <int BMZ>
+__device__ __forceinline__ void z_stage_load(const FastArgs& a, int rb, int cb, int k0, int kend, ZStage<BMZ>& S) {
+  const int tid = threadIdx.x;
+  const int kk = k0 + 8 * (tid & 15);
+  const bool kv = kk < kend;
+  const u32x4 zero = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int q = 0; q < ZStage<BMZ>::HC; ++q) {
+    const int row = rb * BMZ + (tid >> 4) + 16 * q;
+    S.h[q] = (kv && row < a.R) ? *(const u32x4*)(a.h + (int64_t)row * a.d + kk) : zero;
+  }
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int col = cb * 64 + (tid >> 4) + 16 * q;
+    S.w[q] = (kv && col < a.Nz) ? *(const u32x4*)(a.wq + (int64_t)col * a.d + kk) : zero;
+  }
+  S.g = (kv && a.gamma != nullptr) ? *(const u32x4*)(a.gamma + kk) : zero;
+}
+
+template <int BMZ, int NST>
+__device__ __forceinline__ void z_item(const FastArgs& a, int ks, int cb, int rb, unsigned char* smem) {
+  constexpr int RBT = BMZ / 16;                  // 16-row blocks of the tile
+  constexpr int WR = RBT >= 4 ? 2 : 1;           // row blocks per wave
+  constexpr int WC = (RBT * 4) / (4 * WR);       // column blocks per wave
+  constexpr int HC = ZStage<BMZ>::HC;
   constexpr int LD = 68;
-  float* red = (float*)smem;              // [3][BM][LD]
-  float* hred = red + 3 * BM * LD;        // [4][BM]
+  u32x4* sH = (u32x4*)smem;                      // [BMZ][16 slots]
+  u32x4* sW = sH + BMZ * 16;                     // [64][16 slots]
+  float* red = (float*)smem;                     // [BMZ][LD], after the stages
+  int* s_flag = (int*)(smem + (BMZ + 64) * 256);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int nrb = cdiv_d(a.R, BM), ncb = cdiv_d(a.Nz, 64);
-  const int rb = q % nrb;
-  const int cb = (q / nrb) % ncb;
-  const int ks = q / (nrb * ncb);
   const int lr = lane & 15, lg = lane >> 4;
-  const int kbeg = ks * ZCH;
-  const int kend = min(a.d, kbeg + ZCH);
-  const int wk0 = kbeg + wave * (ZCH / 4);
-  const int wk1 = min(kend, wk0 + ZCH / 4);
+  const int rbw = (wave % (RBT / WR)) * WR, cbw = (wave / (RBT / WR)) * WC;
+  const int kbeg = ks * a.kchunk;
+  const int kend = min(a.d, kbeg + a.kchunk);
   const bool want_hss = (cb == 0);
-  const u32x4 zero = u32x4{0u, 0u, 0u, 0u};
 
-  f32x4 acc[RB][4];
-  float hsq[RB];
+  f32x4 acc[WR][WC];
 #pragma unroll
-  for (int i = 0; i < RB; ++i) {
-    hsq[i] = 0.0f;
+  for (int i = 0; i < WR; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-  }
-  {
-    u32x4 A[KS][RB], Bw[KS][4];
+    for (int j = 0; j < WC; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  float hsq[HC];
 #pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      const int kk = wk0 + 32 * s + 8 * lg;
-      const bool kv = kk < wk1;
+  for (int q = 0; q < HC; ++q) hsq[q] = 0.0f;
+
+  // a ring of ZR stages in registers: the first ZR are requested at once,
+  // and each later one as soon as a slot has been written to LDS
+  constexpr int ZR = NST < 3 ? NST : 3;
+  ZStage<BMZ> S[ZR];
 #pragma unroll
-      for (int i = 0; i < RB; ++i) {
-        const int row = rb * BM + 16 * i + lr;
-        A[s][i] = (kv && row < a.R) ? *(const u32x4*)(a.h + (int64_t)row * a.d + kk) : zero;
-      }
+  for (int st = 0; st < ZR; ++st) z_stage_load<BMZ>(a, rb, cb, kbeg + 128 * st, kend, S[st]);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int col = cb * 64 + 16 * j + lr;
-        Bw[s][j] = (kv && col < a.Nz) ? *(const u32x4*)(a.wq + (int64_t)col * a.d + kk) : zero;
-      }
-    }
-    if (a.gamma != nullptr) {
+  for (int st = 0; st < NST; ++st) {
+    ZStage<BMZ>& Sc = S[st % ZR];
+    // the gain and the sums of squares, on the way into LDS
+    if (a.gamma != nullptr || want_hss) {
+      float g[8];
+      Elem<uint16_t>::unpack(Sc.g, g);
 #pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        const int kk = wk0 + 32 * s + 8 * lg;
-        if (kk < wk1) {
-          float g[8];
-          Elem<uint16_t>::unpack(*(const u32x4*)(a.gamma + kk), g);
+      for (int q = 0; q < HC; ++q) {
+        float x[8];
+        Elem<uint16_t>::unpack(Sc.h[q], x);
+        if (want_hss) {
 #pragma unroll
-          for (int i = 0; i < RB; ++i) {
-            float x[8];
-            Elem<uint16_t>::unpack(A[s][i], x);
-            if (want_hss) {
+          for (int e = 0; e < 8; ++e) hsq[q] += x[e] * x[e];
+        }
+        if (a.gamma != nullptr) {
 #pragma unroll
-              for (int e = 0; e < 8; ++e) hsq[i] += x[e] * x[e];
-            }
-#pragma unroll
-            for (int e = 0; e < 8; ++e) x[e] *= g[e];
-            A[s][i] = pack_bf16x8(x);
-          }
+          for (int e = 0; e < 8; ++e) x[e] *= g[e];
+          Sc.h[q] = pack_bf16x8(x);
         }
       }
-    } else if (want_hss) {
-#pragma unroll
-      for (int s = 0; s < KS; ++s)
-#pragma unroll
-        for (int i = 0; i < RB; ++i) hsq[i] += sumsq_bf16x8(A[s][i]);
     }
+    __syncthreads();  // the previous stage (or item) is done with the LDS area
 #pragma unroll
-    for (int s = 0; s < KS; ++s)
+    for (int q = 0; q < HC; ++q) sH[tile_slot((tid >> 4) + 16 * q, tid & 15)] = Sc.h[q];
 #pragma unroll
-      for (int i = 0; i < RB; ++i)
+    for (int q = 0; q < 4; ++q) sW[tile_slot((tid >> 4) + 16 * q, tid & 15)] = Sc.w[q];
+    if (st + ZR < NST) z_stage_load<BMZ>(a, rb, cb, kbeg + 128 * (st + ZR), kend, Sc);
+    __syncthreads();
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = mfma16x16x32(A[s][i], Bw[s][j], acc[i][j]);
+    for (int s = 0; s < 4; ++s) {
+      u32x4 av[WR], bv[WC];
+#pragma unroll
+      for (int i = 0; i < WR; ++i) av[i] = sH[tile_slot(16 * (rbw + i) + lr, 4 * s + lg)];
+#pragma unroll
+      for (int j = 0; j < WC; ++j) bv[j] = sW[tile_slot(16 * (cbw + j) + lr, 4 * s + lg)];
+#pragma unroll
+      for (int i = 0; i < WR; ++i)
+#pragma unroll
+        for (int j = 0; j < WC; ++j) acc[i][j] = mfma16x16x32(av[i], bv[j], acc[i][j]);
+    }
   }
 
-  __syncthreads();  // the LDS area may still be in use by the previous item
-  if (wave > 0) {
+  __syncthreads();  // the stages are done with the LDS area
 #pragma unroll
-    for (int i = 0; i < RB; ++i)
+  for (int i = 0; i < WR; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < WC; ++j)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) red[(wave - 1) * BM * LD + (16 * i + 4 * lg + e) * LD + 16 * j + lr] = acc[i][j][e];
-  }
-  if (want_hss) {
-#pragma unroll
-    for (int i = 0; i < RB; ++i) {
-      float v = hsq[i];
-      v += __shfl_xor(v, 16, 64);
-      v += __shfl_xor(v, 32, 64);
-      if (lg == 0) hred[wave * BM + 16 * i + lr] = v;
-    }
-  }
+      for (int e = 0; e < 4; ++e) red[(16 * (rbw + i) + 4 * lg + e) * LD + 16 * (cbw + j) + lr] = acc[i][j][e];
   __syncthreads();
-  if (wave == 0) {
-#pragma unroll
-    for (int i = 0; i < RB; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int o = (16 * i + 4 * lg + e) * LD + 16 * j + lr;
-          red[o] = ((acc[i][j][e] + red[o]) + red[BM * LD + o]) + red[2 * BM * LD + o];
-        }
-  }
-  __syncthreads();
-  for (int c = tid; c < BM * 16; c += 256) {
+  for (int c = tid; c < BMZ * 16; c += 256) {
     const int rr = c >> 4, c4 = (c & 15) * 4;
-    const int row = rb * BM + rr, col = cb * 64 + c4;
+    const int row = rb * BMZ + rr, col = cb * 64 + c4;
     if (row < a.R && col < a.Nz)
       st_coh16(a.zpart, (uint32_t)(4 * ((ks * a.R + row) * a.Nz + col)), *(const u32x4*)&red[rr * LD + c4]);
   }
   if (want_hss) {
-    for (int rr = tid; rr < BM; rr += 256) {
-      const int row = rb * BM + rr;
-      if (row < a.R)
-        st_coh_f32(a.hss + ks * a.R + row,
-                   ((hred[rr] + hred[BM + rr]) + hred[2 * BM + rr]) + hred[3 * BM + rr]);
+    // lanes 16 k .. 16 k + 15 hold the pieces of rows (tid >> 4) + 16 q
+#pragma unroll
+    for (int q = 0; q < HC; ++q) {
+      float v = hsq[q];
+      v += __shfl_xor(v, 1, 64);
+      v += __shfl_xor(v, 2, 64);
+      v += __shfl_xor(v, 4, 64);
+      v += __shfl_xor(v, 8, 64);
+      const int row = rb * BMZ + (tid >> 4) + 16 * q;
+      if ((tid & 15) == 0 && row < a.R) st_coh_f32(a.hss + ks * a.R + row, v);
     }
   }
   wait_mem();
   __syncthreads();
-  if (tid == 0) count_up(ctr(a.zdone, rb));
+  const int ncbz = cdiv_d(a.Nz, 64);
+  if (tid == 0) *s_flag = count_up(ctr(a.zcnt, rb * ncbz + cb)) == (uint32_t)(a.ksplit - 1) ? 1 : 0;
+  __syncthreads();
+  if (*s_flag) {
+    // every chunk of the tile is stored (each item waited for its stores
+    // before counting): sum them in chunk order, up to 8 chunks per trip
+    constexpr int KG = 8;
+#pragma unroll
+    for (int q = 0; q < RBT; ++q) {
+      const int c = tid + 256 * q;
+      const int rr = c >> 4, c4 = (c & 15) * 4;
+      const int row = rb * BMZ + rr, col = cb * 64 + c4;
+      if (row < a.R && col < a.Nz) {
+        float4 sum = make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int k0 = 0; k0 < a.ksplit; k0 += KG) {
+          u32x4 v[KG];
+#pragma unroll
+          for (int k = 0; k < KG; ++k)
+            v[k] = k0 + k < a.ksplit ? ld_coh16(a.zpart, (uint32_t)(4 * (((k0 + k) * a.R + row) * a.Nz + col)))
+                                     : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+          for (int k = 0; k < KG; ++k) {
+            sum.x += __uint_as_float(v[k].x); sum.y += __uint_as_float(v[k].y);
+            sum.z += __uint_as_float(v[k].z); sum.w += __uint_as_float(v[k].w);
+          }
+        }
+        st_coh16(a.zfin, (uint32_t)(4 * (row * a.Nz + col)),
+                 u32x4{__float_as_uint(sum.x), __float_as_uint(sum.y), __float_as_uint(sum.z), __float_as_uint(sum.w)});
+      }
+    }
+    wait_mem();
+    __syncthreads();
+    if (tid == 0) count_up(ctr(a.zdone, rb));
+  }
+  __syncthreads();  // s_flag and the LDS area are reused by the next item
 }
 
 // ---------------------------------------------------------------- S items
 
-// Tile t = (sequence b, pair m).  Wave w owns tile rows [32 w, 32 w + 32) as
-// two 16-row blocks; lane l holds, for block mb and key step ks, the 16-byte
-// chunk S[32 w + 16 mb + l % 16][32 ks + 8 (l / 16) .. + 7], which is exactly
-// the A operand of S U^T (the contraction runs along the contiguous key
-// axis).  Each thread also carries NW 16-byte chunks of the pair's U and V,
+// Tile t = (sequence b, pair m).  Thread i loads and stores the 16-byte
+// chunks i + 256 j, j < 8, of the tile (rows 16 j + i / 16, column chunk
+// i % 16): each wave instruction moves four whole rows, 1 KB in a row of
+// addresses, which is what lets the gather run at copy speed.  The S U^T
+// operand is read back from an LDS copy of the tile in which chunk c of row
+// v sits at slot c ^ (v % 16) of the row, so that both the row-wise writes
+// and the matrix-operand reads (16 rows at one column chunk) hit distinct
+// banks.  Each thread also carries RR / 8 chunks of the pair's U and V,
 // parked in LDS when the tile is processed.
 template <int RR>
 struct TileRegs {
   static constexpr int NW = 2 * RR * 16 / 256;  // weight chunks per thread
-  u32x4 data[2][4];
+  u32x4 data[8];
   u32x4 w[NW];
   int p;  // accept index of the tile's sequence
 };
 
 template <int RR>
-__device__ __forceinline__ void tile_issue(const FastArgs& a, int t, TileRegs<RR>& R) {
+__device__ __forceinline__ void tile_issue(const FastArgs& a, int t, TileRegs<RR>& R, const int* s_acc) {
   constexpr int WCH = RR * 16;
   const int b = t / a.M, m = t - (t / a.M) * a.M;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x;
   const int mz = a.shared ? 0 : m;
-  R.p = a.accept_idx[b];
+  R.p = b < READY_ACC_LDS ? s_acc[b] : a.accept_idx[b];
   const u32x4* Ug = (const u32x4*)(a.u + (int64_t)mz * RR * READY_TILE);
   const u32x4* Vg = (const u32x4*)(a.v + (int64_t)mz * READY_TILE * RR);
 #pragma unroll
@@ -299,41 +355,38 @@ __device__ __forceinline__ void tile_issue(const FastArgs& a, int t, TileRegs<RR
   }
   if (R.p < 0 || R.p >= a.P) return;
   const int l = m / a.H, hh = m - (m / a.H) * a.H;
-  const uint16_t* src = a.states + (int64_t)b * a.sb + (int64_t)R.p * a.sp + (int64_t)a.slot[l] * a.sl +
-                        (int64_t)hh * a.sh;
-  const int lrow = lane & 15, lk = (lane >> 4) * 8;
+  const u32x4* src = (const u32x4*)(a.states + (int64_t)b * a.sb + (int64_t)R.p * a.sp + (int64_t)a.slot[l] * a.sl +
+                                    (int64_t)hh * a.sh);
 #pragma unroll
-  for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-      R.data[mb][ks] = __builtin_nontemporal_load(
-          (const u32x4*)(src + (32 * wave + 16 * mb + lrow) * READY_TILE + 32 * ks + lk));
+  for (int j = 0; j < 8; ++j) R.data[j] = __builtin_nontemporal_load(src + tid + 256 * j);
 }
 
-// Process tile t whose loads have arrived: copy to `gathered`, sum of
-// squares, S U^T, P, ell.  Its stores are complete (and the tile can be
-// announced) after the caller's next wait_mem().
-template <int RR>
-__device__ __forceinline__ void tile_process(const FastArgs& a, int t, const TileRegs<RR>& R, unsigned char* smem,
-                                             int announce);
 __device__ __forceinline__ void tile_count(const FastArgs& a, int t) {
   const int b = t / a.M;
   const int r0 = b * a.n, r1 = b * a.n + a.n - 1;
   for (int q = r0 / 16; q <= r1 / 16; ++q) count_up(ctr(a.sdone, q));
 }
 
+// Process tile t whose loads were issued: copy to `gathered`, sum of
+// squares, S U^T, P, ell.  Thread 0 also publishes `pub` (a ticket) in
+// *s_pub, readable by every thread once this returns.  Tile `announce` (if >= 0) is counted as done on
+// the way: its stores were issued before this tile's loads, and with the
+// in-order completion of the memory counter they are complete once every
+// wave has waited for this tile's data (the barrier after the LDS copy).
+// This tile's own stores are complete after the caller's next such wait.
 template <int RR>
 __device__ __forceinline__ void tile_process(const FastArgs& a, int t, const TileRegs<RR>& R, unsigned char* smem,
-                                             int announce) {
+                                             int announce, uint32_t* s_pub, uint32_t pub) {
   constexpr int NB = (RR + 15) / 16;  // 16-column blocks of U^T
   constexpr int VC = RR / 8;          // 16-byte chunks per V row
   constexpr int LU = READY_TILE + 8;  // padded U row in LDS (bf16)
   constexpr int WCH = RR * 16;
   constexpr int WS = NB * RR * 16;    // per-wave partials of P
-  uint16_t* sU = (uint16_t*)smem;                       // [RR][LU]
-  uint16_t* sV = sU + RR * LU;                          // [128][RR]
-  float* s_red = (float*)(sV + READY_TILE * RR);        // [4][WS]
-  float* s_wsum = s_red + 4 * WS;                       // [4]
+  u32x4* sS = (u32x4*)smem;                              // [128 rows][16 slots]
+  uint16_t* sU = (uint16_t*)(sS + READY_TILE * 16);      // [RR][LU]
+  uint16_t* sV = sU + RR * LU;                           // [128][RR]
+  float* s_red = (float*)(sV + READY_TILE * RR);         // [4][WS]
+  float* s_wsum = s_red + 4 * WS;                        // [4]
 
   const int b = t / a.M, m = t - (t / a.M) * a.M;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -342,6 +395,8 @@ __device__ __forceinline__ void tile_process(const FastArgs& a, int t, const Til
   if (R.p < 0 || R.p >= a.P) {
     // out-of-range accept index: flag it and leave this sequence's outputs.
     // No tile loads were issued, so wait explicitly before announcing.
+    __syncthreads();  // every thread has read the last published ticket
+    if (tid == 0) *s_pub = pub;
     for (int e = tid; e < RR * RR; e += 256) st_coh_f32(P + e, 0.0f);
     if (tid == 0) {
       if (a.dev_status) st_coh_u32(a.dev_status, (uint32_t)READY_ERR_ACCEPT_IDX);
@@ -354,51 +409,47 @@ __device__ __forceinline__ void tile_process(const FastArgs& a, int t, const Til
     return;
   }
 
-  const int lrow = lane & 15, lk = (lane >> 4) * 8;
-  uint16_t* dst = a.gathered + (int64_t)t * READY_TILE_ELEMS;
+  u32x4* dst = (u32x4*)(a.gathered + (int64_t)t * READY_TILE_ELEMS);
+  __syncthreads();  // the previous tile is done with the LDS area and the last published ticket
+  if (tid == 0) *s_pub = pub;
+  float ss = 0.0f;
 #pragma unroll
-  for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-      __builtin_nontemporal_store(R.data[mb][ks],
-                                  (u32x4*)(dst + (32 * wave + 16 * mb + lrow) * READY_TILE + 32 * ks + lk));
-
-  // The stores above waited for this tile's loads, issued after the stores
-  // of tile `announce` (two turns back): with in-order completion of the
-  // memory counter those are complete on every thread after this barrier.
-  __syncthreads();  // (also: the previous tile is done with the LDS area)
-  if (tid == 0 && announce >= 0) tile_count(a, announce);
+  for (int j = 0; j < 8; ++j) {
+    const int c = tid + 256 * j;
+    __builtin_nontemporal_store(R.data[j], dst + c);
+    sS[tile_slot(c >> 4, c & 15)] = R.data[j];
+    ss += sumsq_bf16x8(R.data[j]);
+  }
 #pragma unroll
   for (int k = 0; k < TileRegs<RR>::NW; ++k) {
     const int c = tid + 256 * k;
     if (c < WCH) *(u32x4*)&sU[(c >> 4) * LU + 8 * (c & 15)] = R.w[k];
     else *(u32x4*)&sV[8 * (c - WCH)] = R.w[k];
   }
-
   // ---- step 2: mean square ----
-  float ss = 0.0f;
-#pragma unroll
-  for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) ss += sumsq_bf16x8(R.data[mb][ks]);
   ss = wave_sum(ss);
   if (lane == 0) s_wsum[wave] = ss;
   __syncthreads();
+  if (tid == 0 && announce >= 0) tile_count(a, announce);
 
-  // ---- S U^T on the matrix cores ----
+  // ---- S U^T on the matrix cores; wave w takes rows [32 w, 32 w + 32) ----
+  const int lrow = lane & 15, lq = lane >> 4;
   f32x4 acc[2][NB];
 #pragma unroll
   for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-    const int i = 16 * nb + lrow;
+  for (int ks = 0; ks < 4; ++ks) {
+    u32x4 sa[2];
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const u32x4 ub = (i < RR) ? *(const u32x4*)&sU[i * LU + 32 * ks + lk] : u32x4{0u, 0u, 0u, 0u};
+    for (int mb = 0; mb < 2; ++mb) sa[mb] = sS[tile_slot(32 * wave + 16 * mb + lrow, 4 * ks + lq)];
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb) acc[mb][nb] = mfma16x16x32(R.data[mb][ks], ub, acc[mb][nb]);
+    for (int nb = 0; nb < NB; ++nb) {
+      const int i = 16 * nb + lrow;
+      const u32x4 ub = (i < RR) ? *(const u32x4*)&sU[i * LU + 32 * ks + 8 * lq] : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) acc[mb][nb] = mfma16x16x32(sa[mb], ub, acc[mb][nb]);
     }
   }
 
@@ -413,7 +464,7 @@ __device__ __forceinline__ void tile_process(const FastArgs& a, int t, const Til
   for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const int v = 32 * wave + 16 * mb + 4 * (lane >> 4) + e;
+      const int v = 32 * wave + 16 * mb + 4 * lq + e;
       float vrow[RR];
 #pragma unroll
       for (int c = 0; c < VC; ++c) Elem<uint16_t>::unpack(*(const u32x4*)&sV[v * RR + 8 * c], vrow + 8 * c);
@@ -453,41 +504,76 @@ __device__ __forceinline__ void tile_process(const FastArgs& a, int t, const Til
   }
 }
 
-// The S items of one workgroup: tiles t = rank, rank + g_s, ...  Two tiles
-// are in flight while one is processed: the loads of tile t + 2 g_s are
-// issued right after tile t's P is stored.  Tile t is announced while tile
-// t + 2 g_s is processed (see tile_process); the last two at the end.
-template <int RR>
-__device__ void s_phase(const FastArgs& a, int rank, TileRegs<RR>& r0, TileRegs<RR>& r1, unsigned char* smem) {
-  const int gs = a.g_s;
-  int t = rank;
-  for (; t < a.n_s; t += gs) {
-    const int tb = t - 2 * gs;
-    tile_process<RR>(a, t, r0, smem, tb >= rank ? tb : -1);
+// The S items of workgroup g: the tiles t = q + ntg i (q = g % ntg), i a
+// ticket.  In each group the workgroups without Z items take tickets
+// 0 .. 2 k - 1 two by two, in order, without asking (k of them); every other
+// ticket is drawn from counter q (offset by 2 k), so that a workgroup that
+// started late, after Z items, simply draws fewer.  Two tiles are in flight
+// while one is processed, and the ticket of the one after them is in flight
+// too: it is requested before the loads of the tile it follows, so that
+// waiting for it never waits for tile data.  The tile processed two turns
+// back is announced while a tile is processed; the last two at the end.
+// has_z(w) tells whether workgroup w runs Z items.
+template <int RR, typename HasZ>
+__device__ __forceinline__ void s_phase(const FastArgs& a, int g, int G, unsigned char* smem, const int* s_acc,
+                                        uint32_t* s_tk, HasZ has_z) {
+  const int tid = threadIdx.x;
+  const int nq = a.ntg, q = g % nq, j = g / nq, nj = (G - q + nq - 1) / nq;
+  const uint32_t nt = (uint32_t)((a.n_s - q + nq - 1) / nq);
+  uint32_t* tk = ctr(a.tk, q);
+  int nzr = 0, nzall = 0;
+  for (int jj = 0; jj < nj; ++jj)
+    if (!has_z(q + nq * jj)) {
+      nzr += jj < j ? 1 : 0;
+      ++nzall;
+    }
+  const uint32_t base = 2u * (uint32_t)nzall;
+  uint32_t i0 = 2u * (uint32_t)nzr;
+  if (has_z(g)) {
+    if (tid == 0) *s_tk = base + __hip_atomic_fetch_add(tk, 2u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    i0 = *s_tk;
+  }
+  int t0 = i0 < nt ? q + nq * (int)i0 : -1;
+  int t1 = i0 + 1 < nt ? q + nq * (int)(i0 + 1) : -1;
+  uint32_t pend = 0xffffffffu;  // thread 0: the ticket after t1
+  if (tid == 0 && t1 >= 0) pend = base + count_up(tk);
+  TileRegs<RR> r0, r1;
+  if (t0 >= 0) tile_issue<RR>(a, t0, r0, s_acc);
+  if (t1 >= 0) tile_issue<RR>(a, t1, r1, s_acc);
+  int h1 = -1, h2 = -1;  // tiles processed one and two turns back
+  while (t0 >= 0) {
+    tile_process<RR>(a, t0, r0, smem, h2, s_tk, pend);
+    const uint32_t i2 = *s_tk;
+    h2 = h1;
+    h1 = t0;
+    t0 = t1;
     r0 = r1;
-    if (t + 2 * gs < a.n_s) tile_issue<RR>(a, t + 2 * gs, r1);
+    t1 = (t0 >= 0 && i2 < nt) ? q + nq * (int)i2 : -1;
+    pend = 0xffffffffu;
+    if (tid == 0 && t1 >= 0) pend = base + count_up(tk);
+    if (t1 >= 0) tile_issue<RR>(a, t1, r1, s_acc);
   }
   wait_mem();
   __syncthreads();
-  if (threadIdx.x == 0) {
-    for (int k = 1; k <= 2; ++k) {
-      const int tb = t - k * gs;
-      if (tb >= rank) tile_count(a, tb);
-    }
+  if (tid == 0) {
+    if (h1 >= 0) tile_count(a, h1);
+    if (h2 >= 0) tile_count(a, h2);
   }
+  __syncthreads();  // the LDS area is reused by the next item
 }
 
 // ---------------------------------------------------------------- A items
 
 // Rows [16 rb, 16 rb + 16) of f and a, columns [64 cb, 64 cb + 64) of a.
-// After the Z items of the rows' tile are counted, the z partial sums are
-// reduced into LDS; after the S items of the rows' sequences are counted,
-// each thread builds f for one (row, pair) at a time (u = P z / rms(h), then
-// ell) into LDS in bf16 (and into `feat` in fp32).  Wave w computes a's
-// columns 64 cb + 16 w .. + 15 on the matrix cores, W1 rows streaming
-// straight from memory.
-template <int RR, int BMZ, int OBM>
-__device__ void mlp1_item(const FastArgs& a, int item, unsigned char* smem) {
+// After the tiles of zfin of these rows and the S items of their sequences
+// are counted, one trip to memory brings z (into LDS), the sums of squares of
+// h, and the P rows and log-RMS this thread applies: f = [u = P z / rms(h),
+// ell] per (row, pair), into LDS in bf16 and into `feat` in fp32.
+// Wave w computes a's columns 64 cb + 16 w .. + 15 on the matrix cores, W1
+// rows streaming straight from memory.
+template <int RR, int BMZ, int BMO>
+__device__ __forceinline__ void mlp1_item(const FastArgs& a, int item, unsigned char* smem) {
   const int ncb = cdiv_d(a.Hm, 64);
   const int rb = item / ncb, cb = item - (item / ncb) * ncb;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -506,50 +592,53 @@ __device__ void mlp1_item(const FastArgs& a, int item, unsigned char* smem) {
   const int col = cb * 64 + 16 * wave + lr;
   const bool cv = col < a.Hm;
   const uint16_t* wrow = a.w1 + (int64_t)col * F;
-  u32x4 bq[8];
+  constexpr int W1S = 12;  // steps of 32 values of K per pass (F <= 384: one pass)
+  u32x4 bq[W1S];
 #pragma unroll
-  for (int s = 0; s < 8; ++s) {
+  for (int s = 0; s < W1S; ++s) {
     const int kk = 32 * s + 8 * lg;
     bq[s] = (cv && kk < F) ? *(const u32x4*)(wrow + kk) : u32x4{0u, 0u, 0u, 0u};
   }
 
-  bool ok = wg_wait(ctr(a.zdone, row0 / BMZ), (uint32_t)(cdiv_d(Nz, 64) * a.ksplit), a, s_flag);
+  bool ok = wg_wait(ctr(a.zdone, row0 / BMZ), (uint32_t)cdiv_d(Nz, 64), a, s_flag);
+  const int b0 = row0 / a.n, b1 = (row0 + rows - 1) / a.n;
+  if (!wg_wait(ctr(a.sdone, rb), (uint32_t)(a.M * (b1 - b0 + 1)), a, s_flag)) ok = false;
 
-  // z of the 16 rows from the K partial sums (up to 16 loads in flight per
-  // thread), and 1 / rms(h)
-  const int nc4 = Nz / 4;
-  for (int c0 = tid; c0 < 16 * nc4; c0 += 256 * 4) {
-    float4 s4[4];
+  // ---- one trip to memory: z of the 16 rows, the sums of squares of h,
+  // and the P rows and log-RMS of this thread's first f item.  An f item is
+  // (pair m, output i): it holds row i of P[b][m] for the sequences b of this
+  // block (up to PS at a time) and applies it to each of their rows here.
+  constexpr int CR4 = RR / 4;   // 16-byte chunks of a row of P
+  constexpr int PS = RR <= 16 ? 4 : 2;  // sequences per load group
+  const int nseq = b1 - b0 + 1;
+  const int nmi = a.M * RR;
+  u32x4 pv[PS][CR4];
+  float ellv[PS];
+  auto load_p = [&](int e, int s0) {
+    const int m = e / RR, i = e - (e / RR) * RR;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) s4[j] = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int k0 = 0; k0 < a.ksplit; k0 += 4) {
-      u32x4 v[4][4];
+    for (int s = 0; s < PS; ++s) {
+      const int b = b0 + s0 + s;
+      const bool live = e < nmi && s0 + s < nseq && ok;
+      const uint32_t pofs = (uint32_t)((((b * a.M + m) * RR + i) * RR) * 4);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int c = c0 + 256 * j;
-        const int rr = c / nc4, c4 = c - (c / nc4) * nc4;
-        const bool live = c < 16 * nc4 && rr < rows && ok;
+      for (int c = 0; c < CR4; ++c) pv[s][c] = live ? ld_coh16(a.pmat, pofs + 16 * c) : u32x4{0u, 0u, 0u, 0u};
+      ellv[s] = (live && i == 0) ? ld_coh_f32(a.ell + b * a.M + m) : 0.0f;
+    }
+  };
+  load_p(tid, 0);
+  const int nzc = rows * (Nz / 4);
+  for (int c0 = tid; c0 < 16 * (Nz / 4); c0 += 256 * 4) {
+    u32x4 v[4];
 #pragma unroll
-        for (int k = 0; k < 4; ++k)
-          v[j][k] = (live && k0 + k < a.ksplit)
-                        ? ld_coh16(a.zpart, (uint32_t)(4 * (((k0 + k) * a.R + row0 + rr) * Nz + 4 * c4)))
-                        : u32x4{0u, 0u, 0u, 0u};
-      }
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          s4[j].x += __uint_as_float(v[j][k].x); s4[j].y += __uint_as_float(v[j][k].y);
-          s4[j].z += __uint_as_float(v[j][k].z); s4[j].w += __uint_as_float(v[j][k].w);
-        }
+    for (int j = 0; j < 4; ++j) {
+      const int c = c0 + 256 * j;
+      v[j] = (c < nzc && ok) ? ld_coh16(a.zfin, (uint32_t)(4 * (row0 * Nz + 4 * c))) : u32x4{0u, 0u, 0u, 0u};
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int c = c0 + 256 * j;
-      if (c < 16 * nc4) {
-        const int rr = c / nc4, c4 = c - (c / nc4) * nc4;
-        *(float4*)&z_s[rr * Nz + 4 * c4] = s4[j];
-      }
+      if (c < 16 * (Nz / 4)) *(u32x4*)&z_s[4 * c] = v[j];
     }
   }
   if (tid < 16) {
@@ -566,94 +655,53 @@ __device__ void mlp1_item(const FastArgs& a, int item, unsigned char* smem) {
     }
     s_rs[tid] = rs;
   }
-  const int padw = Fs - F;
-  for (int e = tid; e < 16 * padw; e += 256) {
-    const int rr = e / padw;
-    fsh[rr * Fs + F + (e - rr * padw)] = 0;
-  }
+  // f starts at zero (rows past the end, padding columns); Fs is a multiple of 8
+  for (int e = tid; e < 2 * Fs; e += 256) ((u32x4*)fsh)[e] = u32x4{0u, 0u, 0u, 0u};
+  __syncthreads();
 
-  // the state tiles of the sequences these rows belong to
-  const int b0 = row0 / a.n, b1 = (row0 + rows - 1) / a.n;
-  if (!wg_wait(ctr(a.sdone, rb), (uint32_t)(a.M * (b1 - b0 + 1)), a, s_flag)) ok = false;
-
-  // f for one (row, pair) at a time; at r = 8 a thread's two items load
-  // their P matrices in one round
-  constexpr int PCH = RR * RR / 4;             // 16-byte chunks of P
-  constexpr int IPR = PCH <= 16 ? 2 : 1;       // items per round
-  constexpr int PG = PCH < 32 ? PCH : 32;      // chunks per load group
-  for (int e0 = tid; e0 < 16 * a.M; e0 += 256 * IPR) {
-    u32x4 pv[IPR][PG];
-    float ellv[IPR];
-    int rrv[IPR], mv[IPR];
-    bool live[IPR];
+  for (int e0 = tid; e0 < nmi; e0 += 256) {
+    const int m = e0 / RR, i = e0 - (e0 / RR) * RR;
+    const int mz = a.shared ? 0 : m;
+    for (int s0 = 0; s0 < nseq; s0 += PS) {
+      if (e0 != tid || s0 != 0) load_p(e0, s0);
 #pragma unroll
-    for (int it = 0; it < IPR; ++it) {
-      const int e = e0 + 256 * it;
-      rrv[it] = e / a.M;
-      mv[it] = e - (e / a.M) * a.M;
-      live[it] = e < 16 * a.M && rrv[it] < rows && ok;
-      const int b = (row0 + rrv[it]) / a.n;
-      const uint32_t pofs = (uint32_t)(((b * a.M + mv[it]) * RR * RR) * 4);
+      for (int s = 0; s < PS; ++s) {
+        if (s0 + s >= nseq) break;
+        const int b = b0 + s0 + s;
+        const int ra = max(row0, b * a.n) - row0, rz = min(row0 + rows, (b + 1) * a.n) - row0;
+        for (int rr = ra; rr < rz; ++rr) {
+          float u = 0.0f;
 #pragma unroll
-      for (int c = 0; c < PG; ++c) pv[it][c] = live[it] ? ld_coh16(a.pmat, pofs + 16 * c) : u32x4{0u, 0u, 0u, 0u};
-      ellv[it] = live[it] ? ld_coh_f32(a.ell + b * a.M + mv[it]) : 0.0f;
-    }
-#pragma unroll
-    for (int it = 0; it < IPR; ++it) {
-      const int e = e0 + 256 * it;
-      if (e >= 16 * a.M) break;
-      const int rr = rrv[it], m = mv[it];
-      float u[RR + 1];
-#pragma unroll
-      for (int i = 0; i <= RR; ++i) u[i] = 0.0f;
-      if (live[it]) {
-        const int b = (row0 + rr) / a.n;
-        const int mz = a.shared ? 0 : m;
-        const float rs = s_rs[rr];
-        float z[RR];
-#pragma unroll
-        for (int c = 0; c < RR / 4; ++c) {
-          const float4 v = *(const float4*)&z_s[rr * Nz + mz * RR + 4 * c];
-          z[4 * c] = v.x * rs; z[4 * c + 1] = v.y * rs; z[4 * c + 2] = v.z * rs; z[4 * c + 3] = v.w * rs;
-        }
-        const uint32_t pofs = (uint32_t)(((b * a.M + m) * RR * RR) * 4);
-#pragma unroll
-        for (int g0 = 0; g0 < PCH; g0 += PG) {
-          u32x4 pq[PG];
-#pragma unroll
-          for (int c = 0; c < PG; ++c) pq[c] = g0 == 0 ? pv[it][c] : ld_coh16(a.pmat, pofs + 16 * (g0 + c));
-#pragma unroll
-          for (int c = 0; c < PG; ++c) {
-            const int i = (g0 + c) / (RR / 4), c4 = (g0 + c) % (RR / 4);
-            u[i] += __uint_as_float(pq[c].x) * z[4 * c4] + __uint_as_float(pq[c].y) * z[4 * c4 + 1] +
-                    __uint_as_float(pq[c].z) * z[4 * c4 + 2] + __uint_as_float(pq[c].w) * z[4 * c4 + 3];
+          for (int c = 0; c < CR4; ++c) {
+            const float4 zv = *(const float4*)&z_s[rr * Nz + mz * RR + 4 * c];
+            u += __uint_as_float(pv[s][c].x) * zv.x + __uint_as_float(pv[s][c].y) * zv.y +
+                 __uint_as_float(pv[s][c].z) * zv.z + __uint_as_float(pv[s][c].w) * zv.w;
+          }
+          u *= s_rs[rr];
+          fsh[rr * Fs + m * (RR + 1) + i] = f32_to_bf16_rne(u);
+          if (i == 0) fsh[rr * Fs + m * (RR + 1) + RR] = f32_to_bf16_rne(ellv[s]);
+          if (a.feat && cb == 0) {
+            float* fr = a.feat + (int64_t)(row0 + rr) * F + m * (RR + 1);
+            fr[i] = u;
+            if (i == 0) fr[RR] = ellv[s];
           }
         }
-        u[RR] = ellv[it];
-        if (a.feat && cb == 0) {
-          float* fr = a.feat + (int64_t)(row0 + rr) * F + m * (RR + 1);
-#pragma unroll
-          for (int i = 0; i <= RR; ++i) fr[i] = u[i];
-        }
       }
-      uint16_t* fr = fsh + rr * Fs + m * (RR + 1);
-#pragma unroll
-      for (int i = 0; i <= RR; ++i) fr[i] = f32_to_bf16_rne(u[i]);
     }
   }
   __syncthreads();
 
   f32x4 acc = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-  for (int k0 = 0; k0 < Fp; k0 += 256) {
+  for (int k0 = 0; k0 < Fp; k0 += 32 * W1S) {
     if (k0 > 0) {
 #pragma unroll
-      for (int s = 0; s < 8; ++s) {
+      for (int s = 0; s < W1S; ++s) {
         const int kk = k0 + 32 * s + 8 * lg;
         bq[s] = (cv && kk < F) ? *(const u32x4*)(wrow + kk) : u32x4{0u, 0u, 0u, 0u};
       }
     }
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
+    for (int s = 0; s < W1S; ++s) {
       const int kb = k0 + 32 * s;
       if (kb < Fp) {
         const u32x4 aop = *(const u32x4*)&fsh[lr * Fs + kb + 8 * lg];
@@ -673,68 +721,88 @@ __device__ void mlp1_item(const FastArgs& a, int item, unsigned char* smem) {
   }
   wait_mem();
   __syncthreads();
-  if (tid == 0) count_up(ctr(a.adone, row0 / OBM));
+  if (tid == 0) count_up(ctr(a.adone, row0 / BMO));
   __syncthreads();  // the LDS area is reused by the next item
 }
 
 // ---------------------------------------------------------------- O items
 
-// Item q = cb * nrb + rb: a BM x 64 tile of out.  The W2 rows of the lane's
-// column are loaded before waiting; after the A items of the tile's rows are
-// counted, the a rows are staged in LDS by passes of 256 values of K
-// (device-coherent loads) for the matrix instructions.  The epilogue goes
-// through LDS so that h, out and delta move in 16-byte row chunks.
+// Rows [BM rb, BM rb + BM) and columns [128 cb, 128 cb + 128) of out; wave w
+// computes columns 128 cb + 32 w .. + 31.  The W2 rows of the lane's two
+// columns and the tile's h values are loaded before waiting; after the A
+// items of the rows are counted, the a rows are staged in LDS by passes of
+// 256 values of K (device-coherent loads) for the matrix instructions.  The
+// epilogue goes through LDS so that h, out and delta move in 16-byte row
+// chunks.
 template <int BM>
-__device__ void mlp2_item(const FastArgs& a, int item, unsigned char* smem) {
-  constexpr int KT = 256, LA = KT + 8, LO = 68;
+__device__ __forceinline__ void mlp2_item(const FastArgs& a, int rb, int cb, unsigned char* smem) {
+  constexpr int OC = READY_OCOLS, KT = 256, LA = KT + 8, LO = OC + 4;
   constexpr int SA = BM * LA * 2, SO = BM * LO * 4;
   uint16_t* sA = (uint16_t*)smem;   // [BM][LA]
   float* sO = (float*)smem;         // [BM][LO], after the K passes
   int* s_flag = (int*)(smem + (SA > SO ? SA : SO));
 
-  const int nrb = cdiv_d(a.R, BM);
-  const int rb = item % nrb, cb = item / nrb;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lr = lane & 15, lg = lane >> 4;
-  const int row0 = rb * BM, col0 = cb * 64;
+  const int row0 = rb * BM, col0 = cb * OC;
   const int rows = min(BM, a.R - row0);
-  const int col = col0 + 16 * wave + lr;
-  const bool cv = col < a.d;
-  const uint16_t* wrow = a.w2 + (int64_t)col * a.Hm;
-
-  u32x4 bq[KT / 32];
+  int colv[2];
+  bool cv[2];
 #pragma unroll
-  for (int s = 0; s < KT / 32; ++s) {
-    const int kk = 32 * s + 8 * lg;
-    bq[s] = (cv && kk < a.Hm) ? *(const u32x4*)(wrow + kk) : u32x4{0u, 0u, 0u, 0u};
+  for (int h2 = 0; h2 < 2; ++h2) {
+    colv[h2] = col0 + 32 * wave + 16 * h2 + lr;
+    cv[h2] = colv[h2] < a.d;
   }
 
-  // the epilogue's h chunks (BM rows x 8 chunks of 8 values: up to 2 per thread)
-  constexpr int EPT = (BM * 8 + 255) / 256;
+  u32x4 bq[2][KT / 32];
+#pragma unroll
+  for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+    for (int s = 0; s < KT / 32; ++s) {
+      const int kk = 32 * s + 8 * lg;
+      bq[h2][s] = (cv[h2] && kk < a.Hm) ? *(const u32x4*)(a.w2 + (int64_t)colv[h2] * a.Hm + kk) : u32x4{0u, 0u, 0u, 0u};
+    }
+
+  // the epilogue's h chunks (BM rows x 16 chunks of 8 values)
+  constexpr int CPR = OC / 8;
+  constexpr int EPT = (BM * CPR + 255) / 256;
   u32x4 hq[EPT];
 #pragma unroll
   for (int k = 0; k < EPT; ++k) {
     const int c = tid + 256 * k;
-    const int rr = c >> 3, gc = col0 + (c & 7) * 8;
-    hq[k] = (c < BM * 8 && rr < rows && gc < a.d) ? *(const u32x4*)(a.h + (int64_t)(row0 + rr) * a.d + gc)
-                                                 : u32x4{0u, 0u, 0u, 0u};
+    const int rr = c / CPR, gc = col0 + (c % CPR) * 8;
+    hq[k] = (c < BM * CPR && rr < rows && gc < a.d) ? *(const u32x4*)(a.h + (int64_t)(row0 + rr) * a.d + gc)
+                                                   : u32x4{0u, 0u, 0u, 0u};
   }
 
   const uint32_t want = (uint32_t)(cdiv_d(rows, 16) * cdiv_d(a.Hm, 64));
   if (!wg_wait(ctr(a.adone, rb), want, a, s_flag)) return;
-
-  f32x4 acc[BM / 16];
+  // the invalid-sequence flags of the epilogue's rows, with the a loads
+  uint32_t inv[EPT];
 #pragma unroll
-  for (int i = 0; i < BM / 16; ++i) acc[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  for (int k = 0; k < EPT; ++k) {
+    const int c = tid + 256 * k;
+    const int rr = c / CPR;
+    inv[k] = (c < BM * CPR && rr < rows) ? ld_coh_u32(a.seq_invalid + (row0 + rr) / a.n) : 1u;
+  }
+
+  f32x4 acc[BM / 16][2];
+#pragma unroll
+  for (int i = 0; i < BM / 16; ++i)
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) acc[i][h2] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
   for (int kb = 0; kb < a.Hm; kb += KT) {
     const int klen = min(KT, a.Hm - kb);
     if (kb > 0) {
 #pragma unroll
-      for (int s = 0; s < KT / 32; ++s) {
-        const int kk = 32 * s + 8 * lg;
-        bq[s] = (cv && kk < klen) ? *(const u32x4*)(wrow + kb + kk) : u32x4{0u, 0u, 0u, 0u};
-      }
+      for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+        for (int s = 0; s < KT / 32; ++s) {
+          const int kk = 32 * s + 8 * lg;
+          bq[h2][s] = (cv[h2] && kk < klen) ? *(const u32x4*)(a.w2 + (int64_t)colv[h2] * a.Hm + kb + kk)
+                                            : u32x4{0u, 0u, 0u, 0u};
+        }
     }
     __syncthreads();
     for (int c = tid; c < BM * (KT / 8); c += 256) {
@@ -750,7 +818,8 @@ __device__ void mlp2_item(const FastArgs& a, int item, unsigned char* smem) {
 #pragma unroll
         for (int i = 0; i < BM / 16; ++i) {
           const u32x4 aop = *(const u32x4*)&sA[(16 * i + lr) * LA + 32 * s + 8 * lg];
-          acc[i] = mfma16x16x32(aop, bq[s], acc[i]);
+#pragma unroll
+          for (int h2 = 0; h2 < 2; ++h2) acc[i][h2] = mfma16x16x32(aop, bq[h2][s], acc[i][h2]);
         }
       }
     }
@@ -760,15 +829,16 @@ __device__ void mlp2_item(const FastArgs& a, int item, unsigned char* smem) {
 #pragma unroll
   for (int i = 0; i < BM / 16; ++i)
 #pragma unroll
-    for (int e = 0; e < 4; ++e) sO[(16 * i + 4 * lg + e) * LO + 16 * wave + lr] = acc[i][e];
+    for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sO[(16 * i + 4 * lg + e) * LO + 32 * wave + 16 * h2 + lr] = acc[i][h2][e];
   __syncthreads();
 #pragma unroll
   for (int k = 0; k < EPT; ++k) {
     const int c = tid + 256 * k;
-    const int rr = c >> 3, c8 = (c & 7) * 8;
+    const int rr = c / CPR, c8 = (c % CPR) * 8;
     const int row = row0 + rr, gc = col0 + c8;
-    if (c >= BM * 8 || rr >= rows || gc >= a.d) continue;
-    if (ld_coh_u32(a.seq_invalid + row / a.n)) continue;
+    if (c >= BM * CPR || rr >= rows || gc >= a.d || inv[k]) continue;
     float dv[8];
     const float4 d0 = *(const float4*)&sO[rr * LO + c8];
     const float4 d1 = *(const float4*)&sO[rr * LO + c8 + 4];
@@ -797,49 +867,61 @@ __device__ void mlp2_item(const FastArgs& a, int item, unsigned char* smem) {
 // ---------------------------------------------------------------- k_reader
 
 // Two workgroups of four waves per CU: at most 256 registers per lane.
-// Z item of workgroup g's j-th turn, or -1.  The hardware hands workgroup g
-// to XCD g % 8; K chunk ks goes to XCD ks % 8, so the items that share a
-// chunk's h and W_q columns meet in one L2.
-__device__ __forceinline__ int z_of(const FastArgs& a, int g, int G, int j) {
-  const int tiles = cdiv_d(a.R, a.R <= 16 ? 16 : 64) * cdiv_d(a.Nz, 64);
-  if ((G & 7) != 0) {
-    const int q = g + j * G;
-    return q < a.n_z ? q : -1;
-  }
-  const int x = g & 7;
-  const int i = (g >> 3) + j * (G >> 3);  // item within the XCD
-  const int ks = x + 8 * (i / tiles);
-  if (ks >= a.ksplit) return -1;
-  return ks * tiles + i % tiles;
-}
-
-template <int RR, int BM>
+// Every workgroup runs its Z items, then its state tiles, then its A items,
+// then its O items.  Items of one kind are dealt to the workgroups in order
+// (Z items and O items per XCD: the K chunks ks with ks % nxcd == x, and the
+// column blocks cb with cb % nxcd == x, go to the workgroups on XCD x).
+template <int RR, int SMALL>
 __global__ __launch_bounds__(256, 2) void k_reader(FastArgs a) {
+  constexpr int BMZ = SMALL ? 16 : 64, BMO = SMALL ? 16 : 64;
+  constexpr int NST = (SMALL ? READY_ZCHUNK_SMALL : READY_ZCHUNK_LARGE) / 128;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   __shared__ int s_last;
+  __shared__ int s_acc[READY_ACC_LDS];
+  __shared__ uint32_t s_tk;
   const int g = blockIdx.x, G = gridDim.x;
+  // the accept indices are requested with the magic word, and staged in LDS
+  // before the state tiles
+  constexpr int APT = READY_ACC_LDS / 256;
+  int accv[APT];
+#pragma unroll
+  for (int k = 0; k < APT; ++k) {
+    const int b = threadIdx.x + 256 * k;
+    accv[k] = b < a.B ? a.accept_idx[b] : 0;
+  }
   if (a.counters[0] != a.magic) {
     // the workspace was not prepared for this plan: touch nothing else
     if (g == 0 && threadIdx.x == 0 && a.dev_status) *a.dev_status = READY_ERR_WORKSPACE_UNINIT;
     return;
   }
-  // the first state tile is issued before the Z items, so the state stream
-  // starts at once
-  TileRegs<RR> r0, r1;
-  const int rank = g;
-  if (g < a.g_s && rank < a.n_s) tile_issue<RR>(a, rank, r0);
-  for (int j = 0;; ++j) {
-    const int q = z_of(a, g, G, j);
-    if (q < 0) break;
-    z_item<BM, BM == 16 ? 5 : 3>(a, q, smem);
+  // a.nxcd is 8 when G is a multiple of 8 (the same number of workgroups on
+  // each XCD), else 1.  The hardware hands consecutive workgroups to
+  // consecutive XCDs, so the workgroups g with one value of g % 8 share an
+  // XCD and its L2.
+  const int nx = a.nxcd, xs = nx == 8 ? 3 : 0;  // nx = 1 << xs
+  const int x = g & (nx - 1), li = g >> xs, per = G >> xs;
+  const int nrbz = cdiv_d(a.R, BMZ), ncbz = cdiv_d(a.Nz, 64), tiles = nrbz * ncbz;
+  auto has_z = [&](int w) {
+    const int xw = w & (nx - 1);
+    return (w >> xs) < ((a.ksplit - xw + nx - 1) >> xs) * tiles;
+  };
+  {
+    const int nkx = (a.ksplit - x + nx - 1) >> xs;
+    for (int i = li; i < nkx * tiles; i += per) {
+      const int ks = x + nx * (i / tiles), rem = i % tiles;
+      z_item<BMZ, NST>(a, ks, rem / nrbz, rem % nrbz, smem);
+    }
   }
-  if (g < a.g_s) {
-    if (rank + a.g_s < a.n_s) tile_issue<RR>(a, rank + a.g_s, r1);
-    s_phase<RR>(a, rank, r0, r1, smem);
-  } else {
-    for (int j = g - a.g_s; j < a.n_a; j += a.g_t) mlp1_item<RR, BM, BM>(a, j, smem);
+#pragma unroll
+  for (int k = 0; k < APT; ++k) s_acc[threadIdx.x + 256 * k] = accv[k];
+  __syncthreads();
+  s_phase<RR>(a, g, G, smem, s_acc, &s_tk, has_z);
+  for (int j = g; j < a.n_a; j += G) mlp1_item<RR, BMZ, BMO>(a, j, smem);
+  {
+    const int nrbo = cdiv_d(a.R, BMO), ncb = cdiv_d(a.d, READY_OCOLS);
+    const int ncx = (ncb - x + nx - 1) >> xs;  // column blocks of XCD x
+    for (int i = li; i < nrbo * ncx; i += per) mlp2_item<BMO>(a, i / ncx, x + nx * (i % ncx), smem);
   }
-  for (int o = g; o < a.n_o; o += G) mlp2_item<BM>(a, o, smem);
 
   // the last workgroup to finish clears the counters (two-level count)
   __syncthreads();
@@ -865,13 +947,14 @@ __global__ void k_ws_init(uint32_t* counters, int n, uint32_t magic) {
 // ---------------------------------------------------------------- launchers
 
 size_t ready_reader_lds(int r, int F, int Nz, int small) {
-  const int BM = small ? 16 : 64;
+  const int BMZ = small ? 16 : 64, BMO = small ? 16 : 64;
   const int NB = (r + 15) / 16;
-  const size_t z_bytes = (size_t)3 * BM * 68 * 4 + (size_t)4 * BM * 4;
-  const size_t s_bytes = (size_t)r * (READY_TILE + 8) * 2 + (size_t)READY_TILE * r * 2 + 4 * (4 * NB * r * 16 + 4);
+  const size_t z_bytes = (size_t)(BMZ + 64) * 256 + 16;
+  const size_t s_bytes = (size_t)READY_TILE_ELEMS * 2 + (size_t)r * (READY_TILE + 8) * 2 + (size_t)READY_TILE * r * 2 +
+                         4 * (4 * NB * r * 16 + 4);
   const int Fs = ((F + 31) & ~31) + 8;
   const size_t a_bytes = (size_t)16 * Nz * 4 + (size_t)16 * Fs * 2 + 4 * 16 + 16;
-  const size_t sa = (size_t)BM * (256 + 8) * 2, so = (size_t)BM * 68 * 4;
+  const size_t sa = (size_t)BMO * (256 + 8) * 2, so = (size_t)BMO * (READY_OCOLS + 4) * 4;
   const size_t o_bytes = (sa > so ? sa : so) + 16;
   size_t m = z_bytes;
   if (s_bytes > m) m = s_bytes;
@@ -885,8 +968,8 @@ hipError_t ready_launch_reader(const FastArgs& a, int small, int grid, hipStream
   const size_t lds = ready_reader_lds(a.r, a.F, a.Nz, small);
 #define READY_READER_CASE(RRV)                                                   \
   do {                                                                           \
-    if (small) READY_LAUNCH((k_reader<RRV, 16>), g, block, lds, s, ev, a);       \
-    else READY_LAUNCH((k_reader<RRV, 64>), g, block, lds, s, ev, a);             \
+    if (small) READY_LAUNCH((k_reader<RRV, 1>), g, block, lds, s, ev, a);        \
+    else READY_LAUNCH((k_reader<RRV, 0>), g, block, lds, s, ev, a);              \
   } while (0)
   switch (a.r) {
     case 8: READY_READER_CASE(8); break;
@@ -904,8 +987,8 @@ int ready_reader_per_cu(int r, int small, size_t lds) {
   hipError_t e = hipSuccess;
 #define READY_OCC_CASE(RRV)                                                                              \
   do {                                                                                                   \
-    if (small) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, k_reader<RRV, 16>, 256, lds);      \
-    else e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, k_reader<RRV, 64>, 256, lds);            \
+    if (small) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, k_reader<RRV, 1>, 256, lds);       \
+    else e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, k_reader<RRV, 0>, 256, lds);             \
   } while (0)
   switch (r) {
     case 8: READY_OCC_CASE(8); break;

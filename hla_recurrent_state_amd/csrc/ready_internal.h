@@ -66,25 +66,30 @@ struct FastArgs {
   int32_t* dev_status;             // or null
   float* zpart;                    // [ksplit][R][Nz]
   float* hss;                      // [ksplit][R]
+  float* zfin;                     // [R][Nz]: z summed over the K chunks (before 1 / rms(h))
   float* pmat;                     // [B M][r][r]
   float* ell;                      // [B M]
   uint16_t* abuf;                  // [R][Hm] bf16
   uint32_t* seq_invalid;           // [B]
   // Counters, READY_CTR_STRIDE words apart: [0] the workspace magic,
   // [1] abort flag, [2 .. 2 + READY_DONE_GROUPS] workgroups finished per
-  // group and overall, then the Z items done per row tile of z, the S items
-  // done per 16 rows, the A items done per row tile of out.  The last
-  // workgroup to finish clears all of them except the magic.
+  // group and overall, then the Z items done per tile of z, the finished
+  // tiles of z per row block, the S items done per 16 rows, the A items done
+  // per row tile of out, the state-tile tickets.  The last workgroup to
+  // finish clears all of them except the magic.
   uint32_t* counters;
   int n_counters;                  // words
   uint32_t magic;
   uint32_t* abort_flag;
   uint32_t* done;                  // [READY_DONE_GROUPS + 1]
-  uint32_t* zdone;                 // [cdiv(R, BMZ)]
+  uint32_t* zcnt;                  // [cdiv(R, BMZ) * cdiv(Nz, 64)]: Z items done per tile of z
+  uint32_t* zdone;                 // [cdiv(R, BMZ)]: tiles of zfin complete per row block
   uint32_t* sdone;                 // [cdiv(R, 16)]
-  uint32_t* adone;                 // [cdiv(R, OBM)]
+  uint32_t* adone;                 // [cdiv(R, BMO)]
+  uint32_t* tk;                    // [ntg]: state-tile tickets drawn per group of workgroups
+  int ntg;                         // ticket groups: workgroup g draws the tiles t with t % ntg == g % ntg
   int n_z, n_s, n_a, n_o;          // work items per kind
-  int g_s, g_t;                    // workgroups that run S items; the rest (g_t) run A items
+  int nxcd;                        // 8: items dealt to XCDs round robin; 1: no XCD affinity
   int B, P, n, M, H, r, d, F, Hm, R, Nz, shared, ksplit, kchunk, act;
   float state_eps, h_eps;
 };
@@ -94,8 +99,14 @@ struct FastArgs {
 #define READY_CTR_STRIDE 32        // counters sit 128 bytes apart
 #define READY_DONE_GROUPS 16
 #define READY_WS_MAGIC 0x52454459u // "READY"
-#define READY_ZCHUNK_SMALL 640     // K chunk of a Z item, at most 16 rows (160 per wave)
-#define READY_ZCHUNK_LARGE 384     // K chunk of a Z item, 64-row tiles (96 per wave)
+// k_reader tiles: z in BMZ x 64 tiles over K chunks of READY_ZCHUNK_* (a
+// multiple of 128), out in BMO x READY_OCOLS tiles; BMZ = BMO = 16 for at
+// most 16 rows, else 64
+#define READY_ZCHUNK_SMALL 384
+#define READY_ZCHUNK_LARGE 640
+#define READY_OCOLS 128
+#define READY_TICKET_GROUPS 32    // state-tile ticket counters
+#define READY_ACC_LDS 1024        // accept indices staged in LDS
 
 enum { EPI_PARTIAL = 0, EPI_BIAS_ACT = 1, EPI_RESID = 2 };
 
