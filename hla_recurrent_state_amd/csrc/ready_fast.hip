@@ -121,6 +121,29 @@ __device__ bool wait_count(const uint32_t* c, uint32_t want, uint32_t* abort_fla
   }
 }
 
+// Poll two counters at once until *c1 >= w1 and *c2 >= w2 (same bounds and
+// failure reporting as wait_count).
+__device__ bool wait_count2(const uint32_t* c1, uint32_t w1, const uint32_t* c2, uint32_t w2, uint32_t* abort_flag,
+                            int32_t* dev_status) {
+  int nap = 0;
+  for (int it = 0;; ++it) {
+    const uint32_t v1 = ld_coh_u32(c1), v2 = ld_coh_u32(c2);
+    if (v1 >= w1 && v2 >= w2) return true;
+    if ((it & 15) == 15 && ld_coh_u32(abort_flag) != 0) return false;
+    if (it >= SPIN_LIMIT) {
+      st_coh_u32(abort_flag, 1u);
+      if (dev_status) st_coh_u32(dev_status, (uint32_t)READY_ERR_SYNC_TIMEOUT);
+      return false;
+    }
+    switch (nap) {
+      case 0: __builtin_amdgcn_s_sleep(4); break;
+      case 1: __builtin_amdgcn_s_sleep(8); break;
+      default: __builtin_amdgcn_s_sleep(16); break;
+    }
+    if (nap < 2) ++nap;
+  }
+}
+
 // Thread 0 waits for *c >= want; the whole workgroup learns the outcome.
 __device__ bool wg_wait(const uint32_t* c, uint32_t want, const FastArgs& a, int* s_flag) {
   if (threadIdx.x == 0) *s_flag = wait_count(c, want, a.abort_flag, a.dev_status) ? 1 : 0;
@@ -600,9 +623,12 @@ __device__ __forceinline__ void mlp1_item(const FastArgs& a, int item, unsigned 
     bq[s] = (cv && kk < F) ? *(const u32x4*)(wrow + kk) : u32x4{0u, 0u, 0u, 0u};
   }
 
-  bool ok = wg_wait(ctr(a.zdone, row0 / BMZ), (uint32_t)cdiv_d(Nz, 64), a, s_flag);
   const int b0 = row0 / a.n, b1 = (row0 + rows - 1) / a.n;
-  if (!wg_wait(ctr(a.sdone, rb), (uint32_t)(a.M * (b1 - b0 + 1)), a, s_flag)) ok = false;
+  if (threadIdx.x == 0)
+    *s_flag = wait_count2(ctr(a.zdone, row0 / BMZ), (uint32_t)cdiv_d(Nz, 64), ctr(a.sdone, rb),
+                          (uint32_t)(a.M * (b1 - b0 + 1)), a.abort_flag, a.dev_status) ? 1 : 0;
+  __syncthreads();
+  const bool ok = *s_flag != 0;
 
   // ---- one trip to memory: z of the 16 rows, the sums of squares of h,
   // and the P rows and log-RMS of this thread's first f item.  An f item is
