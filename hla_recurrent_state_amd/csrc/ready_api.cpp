@@ -41,7 +41,7 @@ struct readyPlan {
   int fast;
   int small;     // fast path: at most 16 rows (16-row tiles; 64 otherwise)
   int n_z, n_s, n_a, n_o, n_counters;
-  int c_zcnt, c_zdone, c_sdone, c_adone, c_tk;  // first counter slot of each group
+  int c_zcnt, c_zdone, c_sdone, c_adone, c_tk, c_aq, c_oq;  // first counter slot of each group
   size_t lds;
   GemmPlan gz, g1, g2;
   size_t off_zpart, off_hss, off_f, off_a, off_flags, off_pmat, off_ell, off_ctr, ws_bytes;
@@ -158,7 +158,9 @@ readyStatus readyPlanCreate(const readyShape* shape, const int32_t* layer_ids, r
     p->c_sdone = (int)(p->c_zdone + nrbz);
     p->c_adone = (int)(p->c_sdone + nrb16);
     p->c_tk = (int)(p->c_adone + nrbo);
-    p->n_counters = (int)(READY_CTR_STRIDE * (p->c_tk + READY_TICKET_GROUPS));
+    p->c_aq = p->c_tk + READY_TICKET_GROUPS;
+    p->c_oq = p->c_aq + 8;
+    p->n_counters = (int)(READY_CTR_STRIDE * (p->c_oq + 8));
   } else {
     // query GEMM: matrix cores for bf16 h and weights; K split so that about
     // 256 (matrix cores) or 512 (VALU) workgroups run
@@ -334,6 +336,8 @@ readyStatus run_reader(const readyPlan* plan, const readyStates* states, const i
     a.sdone = ctr + READY_CTR_STRIDE * plan->c_sdone;
     a.adone = ctr + READY_CTR_STRIDE * plan->c_adone;
     a.tk = ctr + READY_CTR_STRIDE * plan->c_tk;
+    a.aq = ctr + READY_CTR_STRIDE * plan->c_aq;
+    a.oq = ctr + READY_CTR_STRIDE * plan->c_oq;
     a.n_z = plan->n_z; a.n_s = plan->n_s; a.n_a = plan->n_a; a.n_o = plan->n_o;
     a.B = s.B; a.P = s.P; a.n = s.n; a.M = (int)M; a.H = s.H; a.r = s.r; a.d = (int)d; a.F = (int)F;
     a.Hm = (int)Hm; a.R = (int)R; a.Nz = plan->Nz; a.shared = s.shared_params;

@@ -636,6 +636,7 @@ __device__ __forceinline__ void mlp1_item(const FastArgs& a, int item, unsigned 
   // block (up to PS at a time) and applies it to each of their rows here.
   constexpr int CR4 = RR / 4;   // 16-byte chunks of a row of P
   constexpr int PS = RR <= 16 ? 4 : 2;  // sequences per load group
+  constexpr int RU = RR <= 8 ? 4 : (RR <= 16 ? 2 : 1);  // rows per step of the f loop
   const int nseq = b1 - b0 + 1;
   const int nmi = a.M * RR;
   u32x4 pv[PS][CR4];
@@ -692,24 +693,38 @@ __device__ __forceinline__ void mlp1_item(const FastArgs& a, int item, unsigned 
       if (e0 != tid || s0 != 0) load_p(e0, s0);
 #pragma unroll
       for (int s = 0; s < PS; ++s) {
-        if (s0 + s >= nseq) break;
         const int b = b0 + s0 + s;
-        const int ra = max(row0, b * a.n) - row0, rz = min(row0 + rows, (b + 1) * a.n) - row0;
-        for (int rr = ra; rr < rz; ++rr) {
-          float u = 0.0f;
+        // rows of sequence b in this block (none when b is past the last)
+        const int ra = max(row0, b * a.n) - row0;
+        const int rz = s0 + s < nseq ? min(row0 + rows, (b + 1) * a.n) - row0 : ra;
+        // RU rows at a time, so that their LDS reads overlap (z rows past
+        // the block's last valid row are zero and their results are dropped)
+        for (int r0 = ra; r0 < rz; r0 += RU) {
+          float u[RU];
 #pragma unroll
-          for (int c = 0; c < CR4; ++c) {
-            const float4 zv = *(const float4*)&z_s[rr * Nz + mz * RR + 4 * c];
-            u += __uint_as_float(pv[s][c].x) * zv.x + __uint_as_float(pv[s][c].y) * zv.y +
-                 __uint_as_float(pv[s][c].z) * zv.z + __uint_as_float(pv[s][c].w) * zv.w;
+          for (int q = 0; q < RU; ++q) {
+            const int rr = min(r0 + q, 15);
+            float acc = 0.0f;
+#pragma unroll
+            for (int c = 0; c < CR4; ++c) {
+              const float4 zv = *(const float4*)&z_s[rr * Nz + mz * RR + 4 * c];
+              acc += __uint_as_float(pv[s][c].x) * zv.x + __uint_as_float(pv[s][c].y) * zv.y +
+                     __uint_as_float(pv[s][c].z) * zv.z + __uint_as_float(pv[s][c].w) * zv.w;
+            }
+            u[q] = acc * s_rs[rr];
           }
-          u *= s_rs[rr];
-          fsh[rr * Fs + m * (RR + 1) + i] = f32_to_bf16_rne(u);
-          if (i == 0) fsh[rr * Fs + m * (RR + 1) + RR] = f32_to_bf16_rne(ellv[s]);
-          if (a.feat && cb == 0) {
-            float* fr = a.feat + (int64_t)(row0 + rr) * F + m * (RR + 1);
-            fr[i] = u;
-            if (i == 0) fr[RR] = ellv[s];
+#pragma unroll
+          for (int q = 0; q < RU; ++q) {
+            const int rr = r0 + q;
+            if (rr < rz) {
+              fsh[rr * Fs + m * (RR + 1) + i] = f32_to_bf16_rne(u[q]);
+              if (i == 0) fsh[rr * Fs + m * (RR + 1) + RR] = f32_to_bf16_rne(ellv[s]);
+              if (a.feat && cb == 0) {
+                float* fr = a.feat + (int64_t)(row0 + rr) * F + m * (RR + 1);
+                fr[i] = u[q];
+                if (i == 0) fr[RR] = ellv[s];
+              }
+            }
           }
         }
       }
@@ -942,11 +957,31 @@ __global__ __launch_bounds__(256, 2) void k_reader(FastArgs a) {
   for (int k = 0; k < APT; ++k) s_acc[threadIdx.x + 256 * k] = accv[k];
   __syncthreads();
   s_phase<RR>(a, g, G, smem, s_acc, &s_tk, has_z);
-  for (int j = g; j < a.n_a; j += G) mlp1_item<RR, BMZ, BMO>(a, j, smem);
+  // A items, then O items, drawn in row order from the queues of this
+  // workgroup's XCD group (A item j belongs to group j % nx, O item (rb, cb)
+  // to group cb % nx).  A ticket is drawn only when the previous item is
+  // done, so that no workgroup holds an item it cannot start yet.
   {
+    uint32_t* aq = ctr(a.aq, x);
+    uint32_t* oq = ctr(a.oq, x);
+    const int nax = (a.n_a - x + nx - 1) >> xs;
     const int nrbo = cdiv_d(a.R, BMO), ncb = cdiv_d(a.d, READY_OCOLS);
-    const int ncx = (ncb - x + nx - 1) >> xs;  // column blocks of XCD x
-    for (int i = li; i < nrbo * ncx; i += per) mlp2_item<BMO>(a, i / ncx, x + nx * (i % ncx), smem);
+    const int ncx = (ncb - x + nx - 1) >> xs;  // column blocks of XCD group x
+    const int nox = nrbo * ncx;
+    bool in_a = true;
+    for (;;) {
+      if (threadIdx.x == 0) s_tk = count_up(in_a ? aq : oq);
+      __syncthreads();
+      const uint32_t i = s_tk;
+      __syncthreads();  // every thread has read s_tk
+      if (in_a && i >= (uint32_t)nax) {
+        in_a = false;
+        continue;
+      }
+      if (!in_a && i >= (uint32_t)nox) break;
+      if (in_a) mlp1_item<RR, BMZ, BMO>(a, x + (int)(i << xs), smem);
+      else mlp2_item<BMO>(a, (int)i / ncx, x + nx * ((int)i % ncx), smem);
+    }
   }
 
   // the last workgroup to finish clears the counters (two-level count)
@@ -990,6 +1025,8 @@ size_t ready_reader_lds(int r, int F, int Nz, int small) {
 }
 
 hipError_t ready_launch_reader(const FastArgs& a, int small, int grid, hipStream_t s, StageEvents ev) {
+  // the query items walk their K chunk in the stages the variant is built for
+  if (a.kchunk != (small ? READY_ZCHUNK_SMALL : READY_ZCHUNK_LARGE)) return hipErrorInvalidValue;
   const dim3 g((unsigned)grid), block(256);
   const size_t lds = ready_reader_lds(a.r, a.F, a.Nz, small);
 #define READY_READER_CASE(RRV)                                                   \

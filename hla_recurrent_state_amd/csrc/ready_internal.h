@@ -75,8 +75,8 @@ struct FastArgs {
   // [1] abort flag, [2 .. 2 + READY_DONE_GROUPS] workgroups finished per
   // group and overall, then the Z items done per tile of z, the finished
   // tiles of z per row block, the S items done per 16 rows, the A items done
-  // per row tile of out, the state-tile tickets.  The last workgroup to
-  // finish clears all of them except the magic.
+  // per row tile of out, the state-tile tickets, the A- and O-item tickets.
+  // The last workgroup to finish clears all of them except the magic.
   uint32_t* counters;
   int n_counters;                  // words
   uint32_t magic;
@@ -87,6 +87,8 @@ struct FastArgs {
   uint32_t* sdone;                 // [cdiv(R, 16)]
   uint32_t* adone;                 // [cdiv(R, BMO)]
   uint32_t* tk;                    // [ntg]: state-tile tickets drawn per group of workgroups
+  uint32_t* aq;                    // [8]: A-item tickets per XCD group
+  uint32_t* oq;                    // [8]: O-item tickets per XCD group
   int ntg;                         // ticket groups: workgroup g draws the tiles t with t % ntg == g % ntg
   int n_z, n_s, n_a, n_o;          // work items per kind
   int nxcd;                        // 8: items dealt to XCDs round robin; 1: no XCD affinity
