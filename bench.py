@@ -372,6 +372,137 @@ def run_b1(args, hip, torch, R, synth, seed=0):
     return res
 
 
+# ---------------------------------------------------------------- other configurations
+
+def _fill_states_random(buf, seed, torch):
+    """Seeded standard-normal states scaled by 1/128 (the size of a decayed
+    delta-rule state entry), drawn on the device.  Used only to time the
+    rank configuration, whose delta-rule generation takes about a minute on
+    the host; the kernels' work does not depend on the values."""
+    g = torch.Generator(device=buf.device)
+    g.manual_seed(seed)
+    flat = buf.view(-1)
+    step = 1 << 26
+    for i in range(0, flat.numel(), step):
+        blk = flat[i:i + step]
+        blk.copy_(torch.randn(blk.numel(), generator=g, device=buf.device, dtype=torch.float32) / 128.0)
+
+
+def run_config(name, args, hip, torch, R, synth, seed=0):
+    """Cold (after a 512 MB flush) and back-to-back latency of one call of a
+    configuration, its per-stage kernel medians, and a plain device copy that
+    moves the same number of bytes (half read, half written)."""
+    from synth.device import to_device, torch_dtype
+    device = torch.device("cuda:0")
+    cfg = synth.make_shape(name)
+    random_states = name == "rank"
+    t0 = time.time()
+    inp = synth.make(cfg, seed=seed, states=not random_states)
+    dev_in = to_device(inp, device)
+    if random_states:
+        shape = (cfg.B, cfg.P, cfg.L_tot, cfg.H, 128, 128)
+        dev_in["states"] = torch.empty(shape, dtype=torch_dtype(cfg.state_dtype), device=device)
+        _fill_states_random(dev_in["states"], seed, torch)
+    log("%s inputs in %.1f s" % (name, time.time() - t0))
+    reader = R.StateReader(shape_of(R, cfg), cfg.slots)
+    stream = torch.cuda.current_stream(device).cuda_stream
+    outs = {
+        "gathered": torch.empty((cfg.B, cfg.M, 128, 128), dtype=torch_dtype(cfg.state_dtype), device=device),
+        "out": torch.empty((cfg.B, cfg.n, cfg.d), dtype=torch_dtype(cfg.act_dtype), device=device),
+        "dev_status": torch.zeros(1, dtype=torch.int32, device=device),
+    }
+    prep = Prepared(R, reader, dev_in, outs, reader.new_workspace(device), stream)
+    lib = R.load()
+    K = args.config_steps
+    flush = torch.empty(128 * 1024 * 1024, dtype=torch.float32, device=device)
+
+    def call():
+        code = lib.readyStateReader(*prep.args)
+        if code != 0:
+            raise R.ReadyError(code, name)
+
+    def timed(fn, reps):
+        starts = [hip.event() for _ in range(reps)]
+        ends = [hip.event() for _ in range(reps)]
+        for i in range(reps):
+            flush.add_(1.0)
+            hip.record(starts[i], stream)
+            fn()
+            hip.record(ends[i], stream)
+        torch.cuda.synchronize(device)
+        vals = [1000.0 * hip.ms(starts[i], ends[i]) for i in range(reps)]
+        for e in starts + ends:
+            hip.destroy(e)
+        return vals
+
+    def back_to_back(fn, reps):
+        a, b = hip.event(), hip.event()
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize(device)
+        hip.record(a, stream)
+        for _ in range(reps):
+            fn()
+        hip.record(b, stream)
+        torch.cuda.synchronize(device)
+        us = 1000.0 * hip.ms(a, b) / reps
+        hip.destroy(a)
+        hip.destroy(b)
+        return us
+
+    for _ in range(3):
+        call()
+    torch.cuda.synchronize(device)
+    cold = timed(call, K)
+    warm = back_to_back(call, K)
+    # per-stage kernel durations (events recorded by the launches themselves)
+    n = 2 * R.READY_STAGES
+    evs = [[hip.event() for _ in range(n)] for _ in range(K)]
+    for i in range(K):
+        code = lib.readyStateReaderProfiled(*prep.args, (ctypes.c_void_p * n)(*evs[i]))
+        if code != 0:
+            raise R.ReadyError(code, name + " stages")
+    torch.cuda.synchronize(device)
+    # the single-kernel path takes bf16 states, activations and weights with r <= 32
+    fast = (cfg.state_dtype, cfg.act_dtype, cfg.weight_dtype) == ("bf16",) * 3 and cfg.r <= 32
+    stage_names = ("k_reader",) if fast else ("query_gemm", "state_kernel", "mlp1", "mlp2_residual")
+    stage_idx = (1,) if fast else (0, 1, 2, 3)
+    stages = {nm: round(pct([1000.0 * hip.ms(evs[i][2 * k], evs[i][2 * k + 1]) for i in range(K)], 50), 2)
+              for nm, k in zip(stage_names, stage_idx)}
+    for row in evs:
+        for e in row:
+            hip.destroy(e)
+    if int(outs["dev_status"].item()) != 0:
+        raise RuntimeError("device status set during the %s run" % name)
+    alg = algorithmic_bytes(cfg)["total"]
+    # plain copy of the same bytes
+    half = alg // 2
+    src = torch.empty(half, dtype=torch.uint8, device=device).fill_(1)
+    dst = torch.empty_like(src)
+    copy_cold = timed(lambda: dst.copy_(src), K)
+    copy_warm = back_to_back(lambda: dst.copy_(src), K)
+    del src, dst, flush
+    p50 = pct(cold, 50)
+    res = {
+        "path": "k_reader (single persistent kernel)" if fast else "general (4 kernels)",
+        "states": "seeded normal / 128, drawn on the device" if random_states else "fp32 gated delta rule",
+        "B": cfg.B, "M": cfg.M, "r": cfg.r, "d": cfg.d, "state_dtype": cfg.state_dtype,
+        "algorithmic_bytes": alg,
+        "cold_us": {"p10": round(pct(cold, 10), 2), "p50": round(p50, 2), "p90": round(pct(cold, 90), 2)},
+        "warm_mean_us": round(warm, 2),
+        "cold_GBps": round(alg / (p50 * 1e-6) / 1e9, 1),
+        "warm_GBps": round(alg / (warm * 1e-6) / 1e9, 1),
+        "cold_frac_of_hbm_peak": round(alg / (p50 * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+        "warm_frac_of_hbm_peak": round(alg / (warm * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+        "stage_median_us": stages,
+        "same_bytes_copy": {"cold_p50_us": round(pct(copy_cold, 50), 2), "warm_mean_us": round(copy_warm, 2),
+                            "warm_GBps": round(2 * half / (copy_warm * 1e-6) / 1e9, 1)},
+    }
+    del prep, dev_in, outs
+    torch.cuda.empty_cache()
+    return res
+
+
 # ---------------------------------------------------------------- CPU oracle baseline
 
 def cpu_baseline(bat, budget_s):
@@ -432,6 +563,9 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-b1", action="store_true")
+    ap.add_argument("--configs", default="tiny,wide,rank",
+                    help="other configurations timed after the headline (comma list, or 'none')")
+    ap.add_argument("--config-steps", type=int, default=50)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run 10 plain device copies of MIB MiB (the reference for scaling the "
                          "FETCH_SIZE / WRITE_SIZE counters to bytes) and exit")
@@ -540,6 +674,10 @@ def main():
             "unfused_vs_fused_max_abs_diff": b1["unfused_vs_fused_max_abs_diff"],
             "unfused_gathered_equal": b1["gathered_equal"],
         }
+    if args.configs and args.configs != "none":
+        out["configs"] = {}
+        for name in args.configs.split(","):
+            out["configs"][name] = run_config(name, args, hip, torch, R, synth)
     ok = True
     if not args.no_cpu:
         base, rep = cpu_baseline(bat, args.cpu_budget)
