@@ -10,7 +10,9 @@
 // general (any other dtype mix or rank):
 //   0. query GEMM (split-K partial sums of z and of the squares of h)
 //   1. k_state    gather, RMS, log-RMS, T = V^T S_bar, q = U^T z,
-//                 u = T q / sqrt(d_k), packing into f
+//                 u = T q / sqrt(d_k), packing into f (VALU); for bf16
+//                 states and weights k_state_mm, the same on the matrix
+//                 cores in the order u = V^T (S_bar q) / sqrt(d_k)
 //   2. MLP layer 1
 //   3. MLP layer 2 and residual
 //   Each GEMM runs on the matrix cores when the weights are bf16 and the rows
@@ -401,8 +403,17 @@ readyStatus run_reader(const readyPlan* plan, const readyStates* states, const i
     a.dev_status = o->dev_status; a.seq_invalid = flags;
     a.zpart = zpart; a.hss = hss; a.ksz = plan->gz.ksplit; a.nz = plan->Nz;
     a.f = fbuf; a.feat = o->feat;
-    if (ready_launch_state(a, s.state_dtype, s.weight_dtype, strm, stage_events(events, 1)) != hipSuccess)
+    if (s.state_dtype == READY_BF16 && s.weight_dtype == READY_BF16) {
+      // matrix-core form: one persistent workgroup per CU walking the tiles
+      int dev = 0, cus = 0;
+      if (hipGetDevice(&dev) != hipSuccess ||
+          hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+        return READY_ERR_HIP;
+      const int grid = (int)std::min<int64_t>((int64_t)s.B * M, cus);
+      if (ready_launch_state_mm(a, grid, strm, stage_events(events, 1)) != hipSuccess) return READY_ERR_HIP;
+    } else if (ready_launch_state(a, s.state_dtype, s.weight_dtype, strm, stage_events(events, 1)) != hipSuccess) {
       return READY_ERR_HIP;
+    }
   }
   // 2. a = act(W1 f + b1)
   {

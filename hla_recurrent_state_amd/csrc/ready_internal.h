@@ -156,6 +156,9 @@ struct StageEvents {
 
 READY_HIDDEN hipError_t ready_launch_state(const StateArgs& a, int state_dt, int weight_dt, hipStream_t s,
                                            StageEvents ev);
+// bf16 states and weights: matrix-core per-state kernel, `grid` persistent
+// workgroups (at most one per CU)
+READY_HIDDEN hipError_t ready_launch_state_mm(const StateArgs& a, int grid, hipStream_t s, StageEvents ev);
 READY_HIDDEN hipError_t ready_launch_gemm(const GemmArgs& g, int x_dt, int w_dt, int out_dt, int epi,
                                           dim3 grid, size_t lds_bytes, hipStream_t s, StageEvents ev);
 // bm: rows per workgroup tile (16 or 64); weights must be bf16

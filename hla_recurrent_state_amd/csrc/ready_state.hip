@@ -179,6 +179,323 @@ __global__ __launch_bounds__(256) void k_state(StateArgs a) {
 }
 
 
+// ---------------------------------------------------------------- k_state_mm
+
+// Matrix-core form of the per-state work for bf16 states and weights with
+// r <= 128 (a multiple of 8) and n <= 16.  The readout is taken in the order
+// u_j = V^T (S_bar q_j) / sqrt(d_k): the same value as T q_j / sqrt(d_k) with
+// T = V^T S_bar, at 2 n (2 r + d_k) d_k operations per tile instead of
+// 2 r d_k (d_k + n) -- the cheaper order once r exceeds n.  All three
+// contractions run on 16 x 16 x 32 bf16 matrix instructions:
+//   q^T = z^T U      (j x c, over i)
+//   Y   = S q        (v x j, over c)
+//   u^T = Y^T V      (j x i, over v)
+// z, q and Y are fp32 values carried as two bf16 terms (hi + lo), so each
+// product is accurate to about 2^-16 of the fp32 operand; U, V and S are bf16
+// already.  U and V contract over their slow index, so each workgroup stages
+// U^T and V^T of its layer-head pair in LDS and walks the tiles in pair-major
+// order, restaging only when the pair changes.  Persistent: one workgroup of
+// 8 waves per CU; the state tile of the item two ahead is loaded into
+// registers while the current one is worked on, so every CU keeps two tiles
+// of loads in flight.
+
+namespace {
+
+constexpr int MM_THREADS = 512;
+constexpr int MM_LD = READY_TILE + 8;   // padded LDS row of 128 bf16 (272 bytes)
+constexpr int MM_CH = READY_TILE_ELEMS * 2 / 16 / MM_THREADS;  // 16-byte state chunks per thread: 4
+constexpr int MM_S = 0;                                   // state tile, rows of 16 swizzled chunks
+constexpr int MM_UT = MM_S + READY_TILE_ELEMS * 2;        // U^T [c][i]
+constexpr int MM_VT = MM_UT + READY_TILE * MM_LD * 2;     // V^T [i][v]
+constexpr int MM_ZS = MM_VT + READY_TILE * MM_LD * 2;     // z [hi, lo][j][i]
+constexpr int MM_QS = MM_ZS + 2 * 16 * MM_LD * 2;         // q^T [hi, lo][j][c]
+constexpr int MM_YT = MM_QS + 2 * 16 * MM_LD * 2;         // Y^T [hi, lo][j][v]
+constexpr int MM_SS = MM_YT + 2 * 16 * MM_LD * 2;         // per-wave sums of squares
+constexpr int MM_BYTES = MM_SS + 64;
+
+__device__ __forceinline__ uint32_t bf16_pair(float x0, float x1) {
+  return (uint32_t)f32_to_bf16_rne(x0) | ((uint32_t)f32_to_bf16_rne(x1) << 16);
+}
+
+// x as hi + lo with hi = bf16(x), lo = bf16(x - hi)
+__device__ __forceinline__ void split_bf16(float x, uint16_t& hi, uint16_t& lo) {
+  hi = f32_to_bf16_rne(x);
+  lo = f32_to_bf16_rne(x - bf16_bits_to_f32(hi));
+}
+
+// Loads of one tile (item t of the pair-major order) into registers; pa is
+// its accept index (or -1 past the end).
+__device__ __forceinline__ void mm_fetch(const StateArgs& a, int t, int T, u32x4 (&P)[MM_CH], int& pa) {
+  pa = -1;
+  if (t >= T) return;
+  const int m = t / a.B, b = t - m * a.B;
+  pa = a.accept_idx[b];
+  if (pa < 0 || pa >= a.P) return;
+  const int l = m / a.H, hh = m - l * a.H;
+  const uint16_t* src = (const uint16_t*)a.states + (int64_t)b * a.sb + (int64_t)pa * a.sp +
+                        (int64_t)a.slot[l] * a.sl + (int64_t)hh * a.sh;
+#pragma unroll
+  for (int p = 0; p < MM_CH; ++p) {
+    const int e = threadIdx.x + MM_THREADS * p;
+    P[p] = __builtin_nontemporal_load((const u32x4*)(src + (e >> 4) * READY_TILE + (e & 15) * 8));
+  }
+}
+
+// First K-split partial sums of z and of the squares of h for item t: the
+// elements (zj[k], zi[k]) of this thread.
+__device__ __forceinline__ void mm_zfetch(const StateArgs& a, int t, int T, const int (&zj)[4],
+                                          const int (&zi)[4], float (&zr)[4], float (&hr)[4]) {
+  if (t >= T) return;
+  const int m = t / a.B, b = t - m * a.B;
+  const int mz = a.shared ? 0 : m;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    if (zj[k] < a.n && zi[k] < a.r) {
+      const int64_t row = (int64_t)b * a.n + zj[k];
+      zr[k] = a.zpart[row * a.nz + mz * a.r + zi[k]];
+      hr[k] = a.hss[row];
+    }
+  }
+}
+
+// U^T and V^T of reader pair mz into LDS, zero past rank r up to rp.
+__device__ __forceinline__ void mm_stage_uv(const StateArgs& a, int mz, int rp, unsigned char* smem) {
+  uint16_t* ut = (uint16_t*)(smem + MM_UT);
+  uint16_t* vt = (uint16_t*)(smem + MM_VT);
+  const int r = a.r;
+  const uint16_t* U = (const uint16_t*)a.u + (int64_t)mz * r * READY_TILE;
+  const uint16_t* V = (const uint16_t*)a.v + (int64_t)mz * READY_TILE * r;
+  // U [i][c]: chunk (i, 8 columns) -> U^T[c .. c + 7][i]
+  for (int e = threadIdx.x; e < rp * 16; e += MM_THREADS) {
+    const int i = e >> 4, c0 = (e & 15) * 8;
+    u32x4 w = u32x4{0u, 0u, 0u, 0u};
+    if (i < r) w = *(const u32x4*)(U + (int64_t)i * READY_TILE + c0);
+    const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      ut[(c0 + 2 * k) * MM_LD + i] = (uint16_t)(ww[k] & 0xffffu);
+      ut[(c0 + 2 * k + 1) * MM_LD + i] = (uint16_t)(ww[k] >> 16);
+    }
+  }
+  // V [v][i]: chunk (v, 8 ranks) -> V^T[i .. i + 7][v]
+  const int vch = rp / 8;
+  for (int e = threadIdx.x; e < READY_TILE * vch; e += MM_THREADS) {
+    const int v = e / vch, i0 = (e - v * vch) * 8;
+    u32x4 w = u32x4{0u, 0u, 0u, 0u};
+    if (i0 < r) w = *(const u32x4*)(V + (int64_t)v * r + i0);
+    const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      vt[(i0 + 2 * k) * MM_LD + v] = (uint16_t)(ww[k] & 0xffffu);
+      vt[(i0 + 2 * k + 1) * MM_LD + v] = (uint16_t)(ww[k] >> 16);
+    }
+  }
+}
+
+// One tile: item t with its loaded chunks P and accept index pa.
+__device__ __forceinline__ void mm_tile(const StateArgs& a, int t, const u32x4 (&P)[MM_CH], int pa, int rp,
+                                        const int (&zj)[4], const int (&zi)[4], const float (&zr)[4],
+                                        const float (&hr)[4], unsigned char* smem, int& cur_mz) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lr = lane & 15, lg = lane >> 4;
+  const int m = t / a.B, b = t - m * a.B;
+  const int mz = a.shared ? 0 : m;
+  const int n = a.n, r = a.r, F = a.F;
+  const int64_t frow = (int64_t)(b * n) * F + (int64_t)m * (r + 1);
+  const int tile = b * a.M + m;
+  const bool valid = pa >= 0 && pa < a.P;
+
+  if (mz != cur_mz) {
+    __syncthreads();  // the previous tile's readout is done with V^T
+    mm_stage_uv(a, mz, rp, smem);
+    cur_mz = mz;
+  }
+
+  // ---- steps 1-2: gathered copy, sum of squares, tile into LDS ----
+  float ss = 0.0f;
+  if (valid) {
+    uint16_t* dst = (uint16_t*)a.gathered + (int64_t)tile * READY_TILE_ELEMS;
+#pragma unroll
+    for (int p = 0; p < MM_CH; ++p) {
+      const int e = tid + MM_THREADS * p;
+      const int v = e >> 4, ch = e & 15;
+      __builtin_nontemporal_store(P[p], (u32x4*)(dst + v * READY_TILE + ch * 8));
+      ss += sumsq_bf16x8(P[p]);
+      *(u32x4*)(smem + MM_S + v * 256 + ((ch ^ (v & 15)) << 4)) = P[p];
+    }
+  }
+  ss = wave_sum(ss);
+  if (lane == 0) ((float*)(smem + MM_SS))[wave] = ss;
+
+  // ---- z_j of this pair (zero outside j < n, i < r) as hi + lo ----
+  uint16_t* zs = (uint16_t*)(smem + MM_ZS);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    if (zj[k] < 16 && zi[k] < rp) {
+      float z = 0.0f;
+      if (zj[k] < n && zi[k] < r) {
+        const int64_t row = (int64_t)b * n + zj[k];
+        float zz = zr[k], hs = hr[k];
+        for (int ks = 1; ks < a.ksz; ++ks) {
+          zz += a.zpart[((int64_t)ks * a.B * n + row) * a.nz + mz * r + zi[k]];
+          hs += a.hss[(int64_t)ks * a.B * n + row];
+        }
+        z = zz * (1.0f / sqrtf(hs / (float)a.d + a.h_eps));
+      }
+      uint16_t hi, lo;
+      split_bf16(z, hi, lo);
+      zs[zj[k] * MM_LD + zi[k]] = hi;
+      zs[(16 + zj[k]) * MM_LD + zi[k]] = lo;
+    }
+  }
+  __syncthreads();
+  const float* wss = (const float*)(smem + MM_SS);
+  const float ms = (((wss[0] + wss[1]) + (wss[2] + wss[3])) + ((wss[4] + wss[5]) + (wss[6] + wss[7]))) *
+                   (1.0f / READY_TILE_ELEMS);
+  const float rms = sqrtf(ms + a.state_eps);
+
+  // ---- q^T = z^T U: wave w owns columns c in [16 w, 16 w + 16) ----
+  {
+    f32x4 acc = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    const uint16_t* ut = (const uint16_t*)(smem + MM_UT);
+    for (int ks = 0; ks < rp / 32; ++ks) {
+      const int k0 = 32 * ks + 8 * lg;
+      const u32x4 bop = *(const u32x4*)(ut + (16 * wave + lr) * MM_LD + k0);
+      const u32x4 ahi = *(const u32x4*)(zs + lr * MM_LD + k0);
+      const u32x4 alo = *(const u32x4*)(zs + (16 + lr) * MM_LD + k0);
+      acc = mfma16x16x32(ahi, bop, acc);
+      acc = mfma16x16x32(alo, bop, acc);
+    }
+    uint16_t* qs = (uint16_t*)(smem + MM_QS);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      uint16_t hi, lo;
+      split_bf16(acc[e], hi, lo);
+      qs[(4 * lg + e) * MM_LD + 16 * wave + lr] = hi;
+      qs[(16 + 4 * lg + e) * MM_LD + 16 * wave + lr] = lo;
+    }
+  }
+  __syncthreads();
+
+  // ---- Y = S q: wave w owns rows v in [16 w, 16 w + 16) ----
+  {
+    f32x4 acc = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    const uint16_t* qs = (const uint16_t*)(smem + MM_QS);
+    const int v = 16 * wave + lr;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const int ch = 4 * ks + lg;
+      const u32x4 aop = *(const u32x4*)(smem + MM_S + v * 256 + ((ch ^ (v & 15)) << 4));
+      const u32x4 bhi = *(const u32x4*)(qs + lr * MM_LD + 8 * ch);
+      const u32x4 blo = *(const u32x4*)(qs + (16 + lr) * MM_LD + 8 * ch);
+      acc = mfma16x16x32(aop, bhi, acc);
+      acc = mfma16x16x32(aop, blo, acc);
+    }
+    // lane holds Y[16 w + 4 lg + e][lr]: four neighbouring v of row lr of Y^T
+    uint16_t hi[4], lo[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) split_bf16(acc[e], hi[e], lo[e]);
+    uint16_t* yt = (uint16_t*)(smem + MM_YT);
+    const int v0 = 16 * wave + 4 * lg;
+    *(uint2*)(yt + lr * MM_LD + v0) = make_uint2((uint32_t)hi[0] | ((uint32_t)hi[1] << 16),
+                                                 (uint32_t)hi[2] | ((uint32_t)hi[3] << 16));
+    *(uint2*)(yt + (16 + lr) * MM_LD + v0) = make_uint2((uint32_t)lo[0] | ((uint32_t)lo[1] << 16),
+                                                        (uint32_t)lo[2] | ((uint32_t)lo[3] << 16));
+  }
+  __syncthreads();
+
+  // ---- u^T = Y^T V / (rms sqrt(d_k)): wave w owns ranks i in [16 w, 16 w + 16) ----
+  const float scale = 0.08838834764831845f / rms;  // 1 / (sqrt(d_k) rms), d_k = 128
+  if (16 * wave < rp) {
+    f32x4 acc = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    const uint16_t* yt = (const uint16_t*)(smem + MM_YT);
+    const uint16_t* vt = (const uint16_t*)(smem + MM_VT);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const int k0 = 32 * ks + 8 * lg;
+      const u32x4 bop = *(const u32x4*)(vt + (16 * wave + lr) * MM_LD + k0);
+      const u32x4 ahi = *(const u32x4*)(yt + lr * MM_LD + k0);
+      const u32x4 alo = *(const u32x4*)(yt + (16 + lr) * MM_LD + k0);
+      acc = mfma16x16x32(ahi, bop, acc);
+      acc = mfma16x16x32(alo, bop, acc);
+    }
+    const int i = 16 * wave + lr;
+    if (i < r) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int j = 4 * lg + e;
+        if (j < n) {
+          const float uv = valid ? acc[e] * scale : 0.0f;
+          a.f[frow + (int64_t)j * F + i] = uv;
+          if (a.feat) a.feat[frow + (int64_t)j * F + i] = uv;
+        }
+      }
+    }
+  }
+
+  // ---- log-RMS scale after the pair's readouts; validity flags ----
+  const float ell = valid ? logf(rms) : 0.0f;
+  if (tid < n) {
+    a.f[frow + (int64_t)tid * F + r] = ell;
+    if (a.feat) a.feat[frow + (int64_t)tid * F + r] = ell;
+  }
+  if (tid == 0) {
+    if (valid) {
+      if (a.logrms) a.logrms[tile] = ell;
+      if (m == 0) a.seq_invalid[b] = 0;
+    } else {
+      if (a.dev_status) a.dev_status[0] = READY_ERR_ACCEPT_IDX;
+      if (m == 0) a.seq_invalid[b] = 1;
+    }
+  }
+}
+
+}  // namespace
+
+__global__ __launch_bounds__(MM_THREADS, 1) void k_state_mm(StateArgs a) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  const int T = a.B * a.M;
+  const int G = gridDim.x, g = blockIdx.x;
+  const int t0 = (int)((int64_t)g * T / G), t1 = (int)((int64_t)(g + 1) * T / G);
+  const int rp = (a.r + 31) & ~31;
+  // this thread's elements of z: e = tid + 512 k -> (j, i) = (e / rp, e % rp)
+  int zj[4], zi[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int e = threadIdx.x + MM_THREADS * k;
+    zj[k] = e / rp;
+    zi[k] = e - zj[k] * rp;
+  }
+  float zr[4] = {0.0f, 0.0f, 0.0f, 0.0f}, hr[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  u32x4 P0[MM_CH], P1[MM_CH];
+  int pa0, pa1;
+  mm_fetch(a, t0, t1, P0, pa0);
+  mm_zfetch(a, t0, t1, zj, zi, zr, hr);
+  mm_fetch(a, t0 + 1, t1, P1, pa1);
+  int cur_mz = -1;
+  for (int t = t0; t < t1; t += 2) {
+    {
+      float z0[4], h0[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) { z0[k] = zr[k]; h0[k] = hr[k]; }
+      mm_zfetch(a, t + 1, t1, zj, zi, zr, hr);
+      const int pa = pa0;
+      mm_tile(a, t, P0, pa, rp, zj, zi, z0, h0, smem, cur_mz);
+      mm_fetch(a, t + 2, t1, P0, pa0);
+    }
+    if (t + 1 < t1) {
+      float z1[4], h1[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) { z1[k] = zr[k]; h1[k] = hr[k]; }
+      mm_zfetch(a, t + 2, t1, zj, zi, zr, hr);
+      const int pa = pa1;
+      mm_tile(a, t + 1, P1, pa, rp, zj, zi, z1, h1, smem, cur_mz);
+      mm_fetch(a, t + 3, t1, P1, pa1);
+    }
+  }
+}
+
+
 // ---------------------------------------------------------------- launchers
 
 hipError_t ready_launch_state(const StateArgs& a, int state_dt, int weight_dt, hipStream_t s,
@@ -195,3 +512,7 @@ hipError_t ready_launch_state(const StateArgs& a, int state_dt, int weight_dt, h
   return hipGetLastError();
 }
 
+hipError_t ready_launch_state_mm(const StateArgs& a, int grid, hipStream_t s, StageEvents ev) {
+  READY_LAUNCH(k_state_mm, dim3((unsigned)grid), dim3(MM_THREADS), MM_BYTES, s, ev, a);
+  return hipGetLastError();
+}

@@ -133,6 +133,35 @@ def test_long_block_and_many_rows():
     _check(synth.make(cfg, seed=13))
 
 
+# ------------------------------------------------------------ matrix-core per-state kernel (bf16, r > 32)
+
+@pytest.mark.parametrize("r", [40, 64, 96, 128])
+def test_bf16_general_ranks_many_tiles(r):
+    """bf16 states and weights with r > 32: 640 state tiles, so each
+    persistent workgroup walks two or three tiles and crosses layer-head pairs;
+    r = 40 and 96 leave part of the last 32-rank step padded.  Gain and
+    biases set."""
+    cfg = make_shape("paper", B=20, t=8, r=r, d=512, Hm=64)
+    inp = synth.make(cfg, seed=50 + r)
+    rng = np.random.default_rng(r)
+    store = synth.gen._store
+    inp.gamma = store(1.0 + 0.1 * rng.standard_normal(cfg.d), "bf16")
+    inp.b1 = store(0.2 * rng.standard_normal(cfg.Hm), "bf16")
+    inp.b2 = store(0.2 * rng.standard_normal(cfg.d), "bf16")
+    _check(inp)
+
+
+def test_bf16_general_long_block_full_rank():
+    """n = 16 positions (every row of the padded query block used), r = 128."""
+    cfg = make_shape("paper", B=3, n=16, P=16, H=4, t=20, r=128, d=384, Hm=48)
+    _check(synth.make(cfg, seed=61))
+
+
+def test_bf16_general_shared_parameters():
+    cfg = make_shape("paper", B=5, H=6, t=8, r=64, d=256, Hm=32, shared=True)
+    _check(synth.make(cfg, seed=62))
+
+
 # ------------------------------------------------------------ accept index edge cases
 
 @pytest.mark.parametrize("pattern", ["zeros", "last", "mixed"])
@@ -144,10 +173,12 @@ def test_accept_index_edges(pattern):
     _check(inp)
 
 
-def test_out_of_range_accept_index_sets_status_and_skips_sequence():
-    from tests.gpu_util import run_reader
+@pytest.mark.parametrize("r", [8, 64])
+def test_out_of_range_accept_index_sets_status_and_skips_sequence(r):
+    """r = 8 runs the single-kernel path, r = 64 the matrix-core per-state
+    kernel of the general path."""
     dev = _dev()
-    cfg = make_shape("paper", B=3, t=16)
+    cfg = make_shape("paper", B=3, t=16, r=r)
     inp = synth.make(cfg, seed=22)
     inp.accept_idx = np.array([2, 8, -1], dtype=np.int32)
     import tests.gpu_util as gu
