@@ -31,6 +31,7 @@
 
 struct GemmPlan {
   int mfma;      // matrix-core kernel
+  int big;       // matrix-core kernel with 128 x 128 tiles (k_gemm_mm)
   int bm;        // rows per tile (matrix-core kernel)
   int ksplit;    // K splits (query GEMM only)
   int kchunk;
@@ -46,7 +47,7 @@ struct readyPlan {
   int c_zcnt, c_zdone, c_sdone, c_adone, c_tk, c_aq, c_oq;  // first counter slot of each group
   size_t lds;
   GemmPlan gz, g1, g2;
-  size_t off_zpart, off_hss, off_f, off_a, off_flags, off_pmat, off_ell, off_ctr, ws_bytes;
+  size_t off_zpart, off_hss, off_f, off_a, off_g1p, off_flags, off_pmat, off_ell, off_ctr, ws_bytes;
 };
 
 namespace {
@@ -167,7 +168,15 @@ readyStatus readyPlanCreate(const readyShape* shape, const int32_t* layer_ids, r
     // query GEMM: matrix cores for bf16 h and weights; K split so that about
     // 256 (matrix cores) or 512 (VALU) workgroups run
     p->gz.mfma = (wbf && s.act_dtype == READY_BF16) ? 1 : 0;
-    if (p->gz.mfma) {
+    p->gz.big = (p->gz.mfma && p->R >= 2 * READY_GM_TILE) ? 1 : 0;
+    if (p->gz.big) {
+      const int64_t tiles = cdiv(p->Nz, READY_GM_TILE) * cdiv(p->R, READY_GM_TILE);
+      int64_t ks = std::max<int64_t>(1, cdiv(256, tiles));
+      ks = std::min<int64_t>(ks, cdiv(s.d, 8 * READY_GM_BK));
+      const int64_t kchunk = align_up((size_t)cdiv(s.d, ks), READY_GM_BK);
+      p->gz.kchunk = (int)kchunk;
+      p->gz.ksplit = (int)cdiv(s.d, kchunk);
+    } else if (p->gz.mfma) {
       p->gz.bm = p->R <= 16 ? 16 : 64;
       const int64_t tiles = cdiv(p->Nz, READY_MFMA_BN) * cdiv(std::max(p->R, 1), p->gz.bm);
       int64_t ks = std::max<int64_t>(1, cdiv(256, tiles));
@@ -188,7 +197,18 @@ readyStatus readyPlanCreate(const readyShape* shape, const int32_t* layer_ids, r
     p->g1.bm = p->R <= 16 ? 16 : 64;
     p->g1.ksplit = 1;
     p->g1.kchunk = p->F;
+    p->g1.big = (p->g1.mfma && p->R >= 2 * READY_GM_TILE) ? 1 : 0;
+    if (p->g1.big) {
+      // few output tiles (Hm columns): split K, then sum, bias and activation
+      const int64_t tiles = cdiv(s.Hm, READY_GM_TILE) * cdiv(p->R, READY_GM_TILE);
+      int64_t ks = std::max<int64_t>(1, cdiv(256, tiles));
+      ks = std::min<int64_t>(ks, cdiv(p->F, 8 * READY_GM_BK));
+      const int64_t kchunk = align_up((size_t)cdiv(p->F, ks), READY_GM_BK);
+      p->g1.kchunk = (int)kchunk;
+      p->g1.ksplit = (int)cdiv(p->F, kchunk);
+    }
     p->g2.mfma = (wbf && s.Hm % 8 == 0) ? 1 : 0;
+    p->g2.big = (p->g2.mfma && p->R >= 2 * READY_GM_TILE) ? 1 : 0;
     p->g2.bm = p->R <= 16 ? 16 : 64;
     p->g2.ksplit = 1;
     p->g2.kchunk = s.Hm;
@@ -204,6 +224,8 @@ readyStatus readyPlanCreate(const readyShape* shape, const int32_t* layer_ids, r
   p->off_f = off;     off = align_up(off + 4 * R * (p->fast ? p->Nz : p->F), 256);
   // a: bf16 on the fast path, fp32 otherwise
   p->off_a = off;     off = align_up(off + (p->fast ? 2 : 4) * R * s.Hm, 256);
+  // K-split partial sums of the first MLP layer (k_gemm_mm with ksplit > 1)
+  p->off_g1p = off;   off = align_up(off + (p->g1.ksplit > 1 ? 4 * (size_t)p->g1.ksplit * R * s.Hm : 0), 256);
   p->off_flags = off; off = align_up(off + 4 * (size_t)std::max(s.B, 1), 256);
   p->off_pmat = off;  off = align_up(off + (p->fast ? 4 * BM * s.r * s.r : 0), 256);
   p->off_ell = off;   off = align_up(off + (p->fast ? 4 * BM : 0), 256);
@@ -376,7 +398,11 @@ readyStatus run_reader(const readyPlan* plan, const readyStates* states, const i
     g.gamma = w->h_gamma; g.hss = hss; g.ypart = zpart;
     hipError_t e;
     const StageEvents ev = stage_events(events, 0);
-    if (plan->gz.mfma) {
+    if (plan->gz.big) {
+      const dim3 grid((unsigned)cdiv(plan->Nz, READY_GM_TILE), (unsigned)plan->gz.ksplit,
+                      (unsigned)cdiv(R, READY_GM_TILE));
+      e = ready_launch_gemm_mm(g, s.act_dtype, s.act_dtype, EPI_PARTIAL, grid, strm, ev);
+    } else if (plan->gz.mfma) {
       const dim3 grid((unsigned)cdiv(plan->Nz, READY_MFMA_BN), (unsigned)plan->gz.ksplit,
                       (unsigned)cdiv(R, plan->gz.bm));
       e = ready_launch_gemm_mfma(g, s.act_dtype, s.act_dtype, EPI_PARTIAL, plan->gz.bm, grid, strm, ev);
@@ -425,7 +451,16 @@ readyStatus run_reader(const readyPlan* plan, const readyStates* states, const i
     g.bias = w->b1; g.act = s.act; g.yout = abuf;
     hipError_t e;
     const StageEvents ev = stage_events(events, 2);
-    if (plan->g1.mfma) {
+    if (plan->g1.big && plan->g1.ksplit > 1) {
+      g.kchunk = plan->g1.kchunk;
+      g.ypart = (float*)((char*)workspace + plan->off_g1p);
+      const dim3 grid((unsigned)cdiv(Hm, READY_GM_TILE), (unsigned)plan->g1.ksplit, (unsigned)cdiv(R, READY_GM_TILE));
+      e = ready_launch_gemm_mm(g, READY_F32, s.act_dtype, EPI_PARTIAL, grid, strm, StageEvents{ev.start, nullptr});
+      if (e == hipSuccess) e = ready_launch_reduce_bias_act(g, plan->g1.ksplit, strm, StageEvents{nullptr, ev.stop});
+    } else if (plan->g1.big) {
+      const dim3 grid((unsigned)cdiv(Hm, READY_GM_TILE), 1u, (unsigned)cdiv(R, READY_GM_TILE));
+      e = ready_launch_gemm_mm(g, READY_F32, s.act_dtype, EPI_BIAS_ACT, grid, strm, ev);
+    } else if (plan->g1.mfma) {
       const dim3 grid((unsigned)cdiv(Hm, READY_MFMA_BN), 1u, (unsigned)cdiv(R, plan->g1.bm));
       e = ready_launch_gemm_mfma(g, READY_F32, s.act_dtype, EPI_BIAS_ACT, plan->g1.bm, grid, strm, ev);
     } else {
@@ -445,7 +480,10 @@ readyStatus run_reader(const readyPlan* plan, const readyStates* states, const i
     g.bias = w->b2; g.h = h; g.out = o->out; g.delta = o->delta; g.seq_invalid = flags; g.n = s.n;
     hipError_t e;
     const StageEvents ev = stage_events(events, 3);
-    if (plan->g2.mfma) {
+    if (plan->g2.big) {
+      const dim3 grid((unsigned)cdiv(d, READY_GM_TILE), 1u, (unsigned)cdiv(R, READY_GM_TILE));
+      e = ready_launch_gemm_mm(g, READY_F32, s.act_dtype, EPI_RESID, grid, strm, ev);
+    } else if (plan->g2.mfma) {
       const dim3 grid((unsigned)cdiv(d, READY_MFMA_BN), 1u, (unsigned)cdiv(R, plan->g2.bm));
       e = ready_launch_gemm_mfma(g, READY_F32, s.act_dtype, EPI_RESID, plan->g2.bm, grid, strm, ev);
     } else {

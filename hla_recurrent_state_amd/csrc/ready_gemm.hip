@@ -11,6 +11,8 @@
 //                LDS in fp32 and streams W with 16-byte loads (any dtypes).
 //   k_gemm_mfma  matrix cores: bf16 operands (X narrowed to bf16 when it is
 //                fp32), fp32 accumulation, 64-column tiles of 16 or 64 rows.
+#include <algorithm>
+
 #include "ready_common.h"
 
 // ---------------------------------------------------------------- k_gemm
@@ -256,6 +258,177 @@ __global__ __launch_bounds__(256) void k_gemm_mfma(GemmArgs g) {
     }
 }
 
+// ---------------------------------------------------------------- k_gemm_mm
+
+// Large-row form of k_gemm_mfma: 128 x 128 output tiles, K in steps of 32.
+// Four waves in a 2 x 2 arrangement each own a 64 x 64 block (4 x 4 blocks of
+// 16 x 16), so every operand fragment read from LDS feeds four matrix
+// instructions.  The LDS tiles are double-buffered and the next step's global
+// loads are held in registers while the current step's matrix instructions
+// run: one barrier per step.  Requires K, ldx and ldw to keep 16-byte row
+// chunks aligned.
+constexpr int GM_BM = 128, GM_BN = 128, GM_BK = 32, GM_LD = GM_BK + 8;  // 80-byte LDS rows
+
+template <typename TX, typename TO, int EPI>
+__global__ __launch_bounds__(256, 2) void k_gemm_mm(GemmArgs g) {
+  __shared__ __attribute__((aligned(16))) uint16_t sX[2][GM_BM * GM_LD];
+  __shared__ __attribute__((aligned(16))) uint16_t sW[2][GM_BN * GM_LD];
+  constexpr bool XBF = sizeof(TX) == 2;
+  constexpr int XN = XBF ? 2 : 4;  // 16-byte X chunks per thread per step
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lr = lane & 15, lg = lane >> 4;
+  const int wr = wave >> 1, wc = wave & 1;
+  const int col0 = blockIdx.x * GM_BN, ks = blockIdx.y, row0 = blockIdx.z * GM_BM;
+  const int kbeg = ks * g.kchunk;
+  const int kend = min(g.K, kbeg + g.kchunk);
+  const int nsteps = kend > kbeg ? (kend - kbeg + GM_BK - 1) / GM_BK : 0;
+  const bool want_hss = (EPI == EPI_PARTIAL) && XBF && g.hss != nullptr && blockIdx.x == 0;
+  const uint16_t* W = (const uint16_t*)g.W;
+
+  u32x4 xq[XN], wq[2];
+  float hsq[2] = {0.0f, 0.0f};
+
+  auto load = [&](int k0) {
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+      const int c = tid + 256 * it;
+      const int gn = col0 + (c >> 2), gk = k0 + (c & 3) * 8;
+      wq[it] = u32x4{0u, 0u, 0u, 0u};
+      if (gn < g.N && gk < kend) wq[it] = *(const u32x4*)(W + (int64_t)gn * g.ldw + gk);
+    }
+#pragma unroll
+    for (int it = 0; it < XN; ++it) {
+      const int c = tid + 256 * it;
+      xq[it] = u32x4{0u, 0u, 0u, 0u};
+      if (XBF) {
+        const int gr = row0 + (c >> 2), gk = k0 + (c & 3) * 8;
+        if (gr < g.R && gk < kend) xq[it] = *(const u32x4*)((const uint16_t*)g.X + (int64_t)gr * g.ldx + gk);
+      } else {
+        const int gr = row0 + (c >> 3), gk = k0 + (c & 7) * 4;
+        if (gr < g.R && gk < kend) xq[it] = *(const u32x4*)((const float*)g.X + (int64_t)gr * g.ldx + gk);
+      }
+    }
+  };
+  auto store = [&](int buf, int k0) {
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+      const int c = tid + 256 * it;
+      *(u32x4*)&sW[buf][(c >> 2) * GM_LD + (c & 3) * 8] = wq[it];
+    }
+#pragma unroll
+    for (int it = 0; it < XN; ++it) {
+      const int c = tid + 256 * it;
+      if (XBF) {
+        u32x4 v = xq[it];
+        if (want_hss || g.gamma != nullptr) {
+          float x[8];
+          Elem<uint16_t>::unpack(v, x);
+          if (want_hss) {
+            float sq = 0.0f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) sq += x[e] * x[e];
+            // the 4 chunks of one row sit in 4 consecutive lanes
+            sq += __shfl_xor(sq, 1, 64);
+            sq += __shfl_xor(sq, 2, 64);
+            hsq[it] += sq;
+          }
+          const int gk = k0 + (c & 3) * 8;
+          if (g.gamma != nullptr && gk < kend) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) x[e] *= Elem<uint16_t>::ld(g.gamma, gk + e);
+            v = pack_bf16x8(x);
+          }
+        }
+        *(u32x4*)&sX[buf][(c >> 2) * GM_LD + (c & 3) * 8] = v;
+      } else {
+        const u32x4 v = xq[it];
+        const uint32_t lo = (uint32_t)f32_to_bf16_rne(__uint_as_float(v.x)) |
+                            ((uint32_t)f32_to_bf16_rne(__uint_as_float(v.y)) << 16);
+        const uint32_t hi = (uint32_t)f32_to_bf16_rne(__uint_as_float(v.z)) |
+                            ((uint32_t)f32_to_bf16_rne(__uint_as_float(v.w)) << 16);
+        *(uint2*)&sX[buf][(c >> 3) * GM_LD + (c & 7) * 4] = make_uint2(lo, hi);
+      }
+    }
+  };
+
+  f32x4 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+  if (nsteps > 0) {
+    load(kbeg);
+    store(0, kbeg);
+  }
+  __syncthreads();
+  for (int s = 0; s < nsteps; ++s) {
+    const int buf = s & 1;
+    const int knext = kbeg + (s + 1) * GM_BK;
+    if (s + 1 < nsteps) load(knext);
+    u32x4 bop[4], aop[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) bop[j] = *(const u32x4*)&sW[buf][(64 * wc + 16 * j + lr) * GM_LD + 8 * lg];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) aop[i] = *(const u32x4*)&sX[buf][(64 * wr + 16 * i + lr) * GM_LD + 8 * lg];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = mfma16x16x32(aop[i], bop[j], acc[i][j]);
+    if (s + 1 < nsteps) store(buf ^ 1, knext);
+    __syncthreads();
+  }
+
+  if (want_hss) {
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+      const int c = tid + 256 * it;
+      const int gr = row0 + (c >> 2);
+      if ((c & 3) == 0 && gr < g.R) g.hss[(int64_t)ks * g.R + gr] = hsq[it];
+    }
+  }
+
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int col = col0 + 64 * wc + 16 * j + lr;
+    if (col >= g.N) continue;
+    float bias = 0.0f;
+    if (EPI != EPI_PARTIAL && g.bias != nullptr) bias = Elem<uint16_t>::ld(g.bias, col);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int64_t rho = row0 + 64 * wr + 16 * i + 4 * lg + e;
+        if (rho >= g.R) continue;
+        const float y = acc[i][j][e];
+        if (EPI == EPI_PARTIAL) {
+          g.ypart[((int64_t)ks * g.R + rho) * g.N + col] = y;
+        } else if (EPI == EPI_BIAS_ACT) {
+          g.yout[rho * g.N + col] = activation(y + bias, g.act);
+        } else {
+          if (g.seq_invalid[rho / g.n]) continue;
+          const float dh = y + bias;
+          const float hv = Elem<TO>::ld(g.h, rho * g.N + col);
+          Elem<TO>::st(g.out, rho * g.N + col, hv + dh);
+          if (g.delta) g.delta[rho * g.N + col] = dh;
+        }
+      }
+  }
+}
+
+// a = act(sum over K splits of the partial sums + bias), one thread per value
+__global__ __launch_bounds__(256) void k_reduce_bias_act(GemmArgs g, int ksplit) {
+  const int64_t total = (int64_t)g.R * g.N;
+  for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < total; e += (int64_t)gridDim.x * 256) {
+    float s = 0.0f;
+    for (int ks = 0; ks < ksplit; ++ks) s += g.ypart[(int64_t)ks * total + e];
+    const int col = (int)(e % g.N);
+    const float bias = g.bias != nullptr ? Elem<uint16_t>::ld(g.bias, col) : 0.0f;
+    g.yout[e] = activation(s + bias, g.act);
+  }
+}
+
 // ---------------------------------------------------------------- launchers
 template <int EPI>
 static void launch_gemm_epi(const GemmArgs& g, int x_dt, int w_dt, int out_dt, dim3 grid,
@@ -307,5 +480,27 @@ hipError_t ready_launch_gemm_mfma(const GemmArgs& g, int x_dt, int out_dt, int e
                                   hipStream_t s, StageEvents ev) {
   if (bm == 16) launch_mfma_bm<16>(g, x_dt, out_dt, epi, grid, s, ev);
   else launch_mfma_bm<64>(g, x_dt, out_dt, epi, grid, s, ev);
+  return hipGetLastError();
+}
+
+hipError_t ready_launch_gemm_mm(const GemmArgs& g, int x_dt, int out_dt, int epi, dim3 grid, hipStream_t s,
+                                StageEvents ev) {
+  const dim3 block(256);
+  if (epi == EPI_PARTIAL) {
+    if (x_dt == READY_BF16) READY_LAUNCH((k_gemm_mm<uint16_t, float, EPI_PARTIAL>), grid, block, 0, s, ev, g);
+    else READY_LAUNCH((k_gemm_mm<float, float, EPI_PARTIAL>), grid, block, 0, s, ev, g);
+  } else if (epi == EPI_BIAS_ACT) {
+    READY_LAUNCH((k_gemm_mm<float, float, EPI_BIAS_ACT>), grid, block, 0, s, ev, g);
+  } else {
+    if (out_dt == READY_BF16) READY_LAUNCH((k_gemm_mm<float, uint16_t, EPI_RESID>), grid, block, 0, s, ev, g);
+    else READY_LAUNCH((k_gemm_mm<float, float, EPI_RESID>), grid, block, 0, s, ev, g);
+  }
+  return hipGetLastError();
+}
+
+hipError_t ready_launch_reduce_bias_act(const GemmArgs& g, int ksplit, hipStream_t s, StageEvents ev) {
+  const int64_t total = (int64_t)g.R * g.N;
+  const unsigned blocks = (unsigned)std::min<int64_t>((total + 255) / 256, 4096);
+  READY_LAUNCH(k_reduce_bias_act, dim3(blocks), dim3(256), 0, s, ev, g, ksplit);
   return hipGetLastError();
 }

@@ -91,6 +91,7 @@ __global__ __launch_bounds__(256) void k_state(StateArgs a) {
   if (tid < n) {
     const int rho = b * n + tid;
     float hs = 0.0f;
+#pragma unroll 8
     for (int ks = 0; ks < a.ksz; ++ks) hs += a.hss[(int64_t)ks * rows + rho];
     s_rs[tid] = 1.0f / sqrtf(hs / (float)a.d + a.h_eps);
   }
@@ -102,6 +103,7 @@ __global__ __launch_bounds__(256) void k_state(StateArgs a) {
     const int j = e / r, i = e - j * r;
     const int64_t rho = b * n + j;
     float s = 0.0f;
+#pragma unroll 8
     for (int ks = 0; ks < a.ksz; ++ks) s += a.zpart[((int64_t)ks * rows + rho) * a.nz + mz * r + i];
     s_z[e] = s * s_rs[j];
   }
@@ -211,7 +213,8 @@ constexpr int MM_ZS = MM_VT + READY_TILE * MM_LD * 2;     // z [hi, lo][j][i]
 constexpr int MM_QS = MM_ZS + 2 * 16 * MM_LD * 2;         // q^T [hi, lo][j][c]
 constexpr int MM_YT = MM_QS + 2 * 16 * MM_LD * 2;         // Y^T [hi, lo][j][v]
 constexpr int MM_SS = MM_YT + 2 * 16 * MM_LD * 2;         // per-wave sums of squares
-constexpr int MM_BYTES = MM_SS + 64;
+constexpr int MM_ACC = MM_SS + 64;                        // accept indices of the first READY_ACC_LDS sequences
+constexpr int MM_BYTES = MM_ACC + 4 * READY_ACC_LDS;
 
 __device__ __forceinline__ uint32_t bf16_pair(float x0, float x1) {
   return (uint32_t)f32_to_bf16_rne(x0) | ((uint32_t)f32_to_bf16_rne(x1) << 16);
@@ -225,36 +228,45 @@ __device__ __forceinline__ void split_bf16(float x, uint16_t& hi, uint16_t& lo) 
 
 // Loads of one tile (item t of the pair-major order) into registers; pa is
 // its accept index (or -1 past the end).
-__device__ __forceinline__ void mm_fetch(const StateArgs& a, int t, int T, u32x4 (&P)[MM_CH], int& pa) {
-  pa = -1;
-  if (t >= T) return;
-  const int m = t / a.B, b = t - m * a.B;
-  pa = a.accept_idx[b];
-  if (pa < 0 || pa >= a.P) return;
+// Loads of one tile (item t of the pair-major order) into registers; pa is
+// its accept index, or -1 past the end.  Every load is issued whatever the
+// item (an address clamped into range stands in for a missing or invalid
+// one), so the number of loads in flight after it is the same on every path
+// and the waits for it do not drain the loads of the items behind it.
+// ACC_LDS: the accept indices are staged in LDS (B <= READY_ACC_LDS); a load
+// from global memory here would be waited for at once, together with every
+// load and store still in flight.
+template <bool ACC_LDS>
+__device__ __forceinline__ void mm_fetch(const StateArgs& a, int t, int T, u32x4 (&P)[MM_CH], int& pa,
+                                         const int* s_acc) {
+  const int tc = min(t, T - 1);
+  const int m = tc / a.B, b = tc - m * a.B;
+  const int p = ACC_LDS ? s_acc[b] : a.accept_idx[b];
+  pa = t < T ? p : -1;
+  const int pc = min(max(p, 0), a.P - 1);
   const int l = m / a.H, hh = m - l * a.H;
-  const uint16_t* src = (const uint16_t*)a.states + (int64_t)b * a.sb + (int64_t)pa * a.sp +
+  const uint16_t* src = (const uint16_t*)a.states + (int64_t)b * a.sb + (int64_t)pc * a.sp +
                         (int64_t)a.slot[l] * a.sl + (int64_t)hh * a.sh;
 #pragma unroll
-  for (int p = 0; p < MM_CH; ++p) {
-    const int e = threadIdx.x + MM_THREADS * p;
-    P[p] = __builtin_nontemporal_load((const u32x4*)(src + (e >> 4) * READY_TILE + (e & 15) * 8));
+  for (int p2 = 0; p2 < MM_CH; ++p2) {
+    const int e = threadIdx.x + MM_THREADS * p2;
+    P[p2] = __builtin_nontemporal_load((const u32x4*)(src + (e >> 4) * READY_TILE + (e & 15) * 8));
   }
 }
 
 // First K-split partial sums of z and of the squares of h for item t: the
-// elements (zj[k], zi[k]) of this thread.
+// elements (zj[k], zi[k]) of this thread (clamped into range like the tile
+// loads; values outside j < n, i < r are not used).
 __device__ __forceinline__ void mm_zfetch(const StateArgs& a, int t, int T, const int (&zj)[4],
                                           const int (&zi)[4], float (&zr)[4], float (&hr)[4]) {
-  if (t >= T) return;
-  const int m = t / a.B, b = t - m * a.B;
+  const int tc = min(t, T - 1);
+  const int m = tc / a.B, b = tc - m * a.B;
   const int mz = a.shared ? 0 : m;
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
-    if (zj[k] < a.n && zi[k] < a.r) {
-      const int64_t row = (int64_t)b * a.n + zj[k];
-      zr[k] = a.zpart[row * a.nz + mz * a.r + zi[k]];
-      hr[k] = a.hss[row];
-    }
+    const int64_t row = (int64_t)b * a.n + min(zj[k], a.n - 1);
+    zr[k] = a.zpart[row * a.nz + mz * a.r + min(zi[k], a.r - 1)];
+    hr[k] = a.hss[row];
   }
 }
 
@@ -452,6 +464,7 @@ __device__ __forceinline__ void mm_tile(const StateArgs& a, int t, const u32x4 (
 
 }  // namespace
 
+template <bool ACC_LDS>
 __global__ __launch_bounds__(MM_THREADS, 1) void k_state_mm(StateArgs a) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int T = a.B * a.M;
@@ -466,32 +479,29 @@ __global__ __launch_bounds__(MM_THREADS, 1) void k_state_mm(StateArgs a) {
     zj[k] = e / rp;
     zi[k] = e - zj[k] * rp;
   }
-  float zr[4] = {0.0f, 0.0f, 0.0f, 0.0f}, hr[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  int* s_acc = (int*)(smem + MM_ACC);
+  if (ACC_LDS)
+    for (int i = threadIdx.x; i < a.B; i += MM_THREADS) s_acc[i] = a.accept_idx[i];
+  __syncthreads();
+  // two sets of prefetched registers, one for even and one for odd items
+  // (a register copy of a value still being loaded would wait for every
+  // load in flight)
+  float z0[4] = {0.0f, 0.0f, 0.0f, 0.0f}, h0[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  float z1[4] = {0.0f, 0.0f, 0.0f, 0.0f}, h1[4] = {0.0f, 0.0f, 0.0f, 0.0f};
   u32x4 P0[MM_CH], P1[MM_CH];
   int pa0, pa1;
-  mm_fetch(a, t0, t1, P0, pa0);
-  mm_zfetch(a, t0, t1, zj, zi, zr, hr);
-  mm_fetch(a, t0 + 1, t1, P1, pa1);
+  mm_fetch<ACC_LDS>(a, t0, t1, P0, pa0, s_acc);
+  mm_zfetch(a, t0, t1, zj, zi, z0, h0);
+  mm_fetch<ACC_LDS>(a, t0 + 1, t1, P1, pa1, s_acc);
+  mm_zfetch(a, t0 + 1, t1, zj, zi, z1, h1);
   int cur_mz = -1;
   for (int t = t0; t < t1; t += 2) {
-    {
-      float z0[4], h0[4];
-#pragma unroll
-      for (int k = 0; k < 4; ++k) { z0[k] = zr[k]; h0[k] = hr[k]; }
-      mm_zfetch(a, t + 1, t1, zj, zi, zr, hr);
-      const int pa = pa0;
-      mm_tile(a, t, P0, pa, rp, zj, zi, z0, h0, smem, cur_mz);
-      mm_fetch(a, t + 2, t1, P0, pa0);
-    }
-    if (t + 1 < t1) {
-      float z1[4], h1[4];
-#pragma unroll
-      for (int k = 0; k < 4; ++k) { z1[k] = zr[k]; h1[k] = hr[k]; }
-      mm_zfetch(a, t + 2, t1, zj, zi, zr, hr);
-      const int pa = pa1;
-      mm_tile(a, t + 1, P1, pa, rp, zj, zi, z1, h1, smem, cur_mz);
-      mm_fetch(a, t + 3, t1, P1, pa1);
-    }
+    mm_tile(a, t, P0, pa0, rp, zj, zi, z0, h0, smem, cur_mz);
+    mm_fetch<ACC_LDS>(a, t + 2, t1, P0, pa0, s_acc);
+    mm_zfetch(a, t + 2, t1, zj, zi, z0, h0);
+    if (t + 1 < t1) mm_tile(a, t + 1, P1, pa1, rp, zj, zi, z1, h1, smem, cur_mz);
+    mm_fetch<ACC_LDS>(a, t + 3, t1, P1, pa1, s_acc);
+    mm_zfetch(a, t + 3, t1, zj, zi, z1, h1);
   }
 }
 
@@ -513,6 +523,9 @@ hipError_t ready_launch_state(const StateArgs& a, int state_dt, int weight_dt, h
 }
 
 hipError_t ready_launch_state_mm(const StateArgs& a, int grid, hipStream_t s, StageEvents ev) {
-  READY_LAUNCH(k_state_mm, dim3((unsigned)grid), dim3(MM_THREADS), MM_BYTES, s, ev, a);
+  if (a.B <= READY_ACC_LDS)
+    READY_LAUNCH(k_state_mm<true>, dim3((unsigned)grid), dim3(MM_THREADS), MM_BYTES, s, ev, a);
+  else
+    READY_LAUNCH(k_state_mm<false>, dim3((unsigned)grid), dim3(MM_THREADS), MM_BYTES, s, ev, a);
   return hipGetLastError();
 }

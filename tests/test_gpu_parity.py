@@ -151,6 +151,26 @@ def test_bf16_general_ranks_many_tiles(r):
     _check(inp)
 
 
+@pytest.mark.parametrize("act_dtype", ["bf16", "f32"])
+def test_bf16_general_many_rows_large_tiles(act_dtype):
+    """B n = 259 rows (three 128-row tiles, the last ragged) with bf16 states
+    and weights and r = 64: the 128 x 128 tile GEMMs of the general path
+    (query sums split over K when the activations are bf16, the first MLP
+    layer split over K with a separate sum, bias and activation), d = 1048 and
+    Hm = 200 ragged against the 32-wide K steps and 128-wide column tiles.
+    The oracle checks a sample of sequences; the gather is checked for all."""
+    cfg = make_shape("paper", B=37, t=8, r=64, d=1048, Hm=200, act_dtype=act_dtype)
+    inp = synth.make(cfg, seed=70)
+    rng = np.random.default_rng(70)
+    store = synth.gen._store
+    inp.gamma = store(1.0 + 0.1 * rng.standard_normal(cfg.d), "bf16")
+    inp.b1 = store(0.2 * rng.standard_normal(cfg.Hm), "bf16")
+    inp.b2 = store(0.2 * rng.standard_normal(cfg.d), "bf16")
+    res, ref, rep = _check(inp, seqs=[0, 17, 18, 36])
+    want = inp.buf[np.arange(cfg.B), inp.accept_idx][:, list(cfg.slots)].reshape(cfg.B, cfg.M, 128, 128)
+    assert np.array_equal(res["gathered"], want)
+
+
 def test_bf16_general_long_block_full_rank():
     """n = 16 positions (every row of the padded query block used), r = 128."""
     cfg = make_shape("paper", B=3, n=16, P=16, H=4, t=20, r=128, d=384, Hm=48)
