@@ -399,9 +399,7 @@ readyStatus run_reader(const readyPlan* plan, const readyStates* states, const i
     hipError_t e;
     const StageEvents ev = stage_events(events, 0);
     if (plan->gz.big) {
-      const dim3 grid((unsigned)cdiv(plan->Nz, READY_GM_TILE), (unsigned)plan->gz.ksplit,
-                      (unsigned)cdiv(R, READY_GM_TILE));
-      e = ready_launch_gemm_mm(g, s.act_dtype, s.act_dtype, EPI_PARTIAL, grid, strm, ev);
+      e = ready_launch_gemm_mm(g, s.act_dtype, s.act_dtype, EPI_PARTIAL, plan->gz.ksplit, strm, ev);
     } else if (plan->gz.mfma) {
       const dim3 grid((unsigned)cdiv(plan->Nz, READY_MFMA_BN), (unsigned)plan->gz.ksplit,
                       (unsigned)cdiv(R, plan->gz.bm));
@@ -454,12 +452,11 @@ readyStatus run_reader(const readyPlan* plan, const readyStates* states, const i
     if (plan->g1.big && plan->g1.ksplit > 1) {
       g.kchunk = plan->g1.kchunk;
       g.ypart = (float*)((char*)workspace + plan->off_g1p);
-      const dim3 grid((unsigned)cdiv(Hm, READY_GM_TILE), (unsigned)plan->g1.ksplit, (unsigned)cdiv(R, READY_GM_TILE));
-      e = ready_launch_gemm_mm(g, READY_F32, s.act_dtype, EPI_PARTIAL, grid, strm, StageEvents{ev.start, nullptr});
+      e = ready_launch_gemm_mm(g, READY_F32, s.act_dtype, EPI_PARTIAL, plan->g1.ksplit, strm,
+                               StageEvents{ev.start, nullptr});
       if (e == hipSuccess) e = ready_launch_reduce_bias_act(g, plan->g1.ksplit, strm, StageEvents{nullptr, ev.stop});
     } else if (plan->g1.big) {
-      const dim3 grid((unsigned)cdiv(Hm, READY_GM_TILE), 1u, (unsigned)cdiv(R, READY_GM_TILE));
-      e = ready_launch_gemm_mm(g, READY_F32, s.act_dtype, EPI_BIAS_ACT, grid, strm, ev);
+      e = ready_launch_gemm_mm(g, READY_F32, s.act_dtype, EPI_BIAS_ACT, 1, strm, ev);
     } else if (plan->g1.mfma) {
       const dim3 grid((unsigned)cdiv(Hm, READY_MFMA_BN), 1u, (unsigned)cdiv(R, plan->g1.bm));
       e = ready_launch_gemm_mfma(g, READY_F32, s.act_dtype, EPI_BIAS_ACT, plan->g1.bm, grid, strm, ev);
@@ -481,8 +478,7 @@ readyStatus run_reader(const readyPlan* plan, const readyStates* states, const i
     hipError_t e;
     const StageEvents ev = stage_events(events, 3);
     if (plan->g2.big) {
-      const dim3 grid((unsigned)cdiv(d, READY_GM_TILE), 1u, (unsigned)cdiv(R, READY_GM_TILE));
-      e = ready_launch_gemm_mm(g, READY_F32, s.act_dtype, EPI_RESID, grid, strm, ev);
+      e = ready_launch_gemm_mm(g, READY_F32, s.act_dtype, EPI_RESID, 1, strm, ev);
     } else if (plan->g2.mfma) {
       const dim3 grid((unsigned)cdiv(d, READY_MFMA_BN), 1u, (unsigned)cdiv(R, plan->g2.bm));
       e = ready_launch_gemm_mfma(g, READY_F32, s.act_dtype, EPI_RESID, plan->g2.bm, grid, strm, ev);

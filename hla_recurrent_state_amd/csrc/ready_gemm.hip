@@ -260,40 +260,50 @@ __global__ __launch_bounds__(256) void k_gemm_mfma(GemmArgs g) {
 
 // ---------------------------------------------------------------- k_gemm_mm
 
-// Large-row form of k_gemm_mfma: 128 x 128 output tiles, K in steps of 32.
-// Four waves in a 2 x 2 arrangement each own a 64 x 64 block (4 x 4 blocks of
-// 16 x 16), so every operand fragment read from LDS feeds four matrix
-// instructions.  The LDS tiles are double-buffered and the next step's global
-// loads are held in registers while the current step's matrix instructions
-// run: one barrier per step.  Requires K, ldx and ldw to keep 16-byte row
-// chunks aligned.
-constexpr int GM_BM = 128, GM_BN = 128, GM_BK = 32, GM_LD = GM_BK + 8;  // 80-byte LDS rows
+// Large-row form of k_gemm_mfma: 128 x 128 output tiles.  Four waves in a
+// 2 x 2 arrangement each own a 64 x 64 block (4 x 4 blocks of 16 x 16), so
+// every operand fragment read from LDS feeds four matrix instructions.  The
+// next K step's global loads are held in registers while the current step's
+// matrix instructions run from LDS; then the registers go to LDS between two
+// barriers.  One LDS buffer keeps three workgroups on a CU.  Requires K, ldx
+// and ldw to keep 16-byte row chunks aligned.
+constexpr int GM_BM = READY_GM_TILE, GM_BN = READY_GM_TILE;
 
-template <typename TX, typename TO, int EPI>
-__global__ __launch_bounds__(256, 2) void k_gemm_mm(GemmArgs g) {
-  __shared__ __attribute__((aligned(16))) uint16_t sX[2][GM_BM * GM_LD];
-  __shared__ __attribute__((aligned(16))) uint16_t sW[2][GM_BN * GM_LD];
+template <typename TX, typename TO, int EPI, int GM_BK>
+__device__ __forceinline__ void gemm_mm_body(const GemmArgs& g, uint16_t* sX, uint16_t* sW) {
+  constexpr int GM_LD = GM_BK + 8;                 // padded LDS row
   constexpr bool XBF = sizeof(TX) == 2;
-  constexpr int XN = XBF ? 2 : 4;  // 16-byte X chunks per thread per step
+  constexpr int CPR = GM_BK / 8;                   // 16-byte bf16 chunks per row and step
+  constexpr int XN = GM_BM * GM_BK * sizeof(TX) / 16 / 256;  // 16-byte X chunks per thread per step
+  constexpr int WN = GM_BN * GM_BK * 2 / 16 / 256;           // 16-byte W chunks per thread per step
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lr = lane & 15, lg = lane >> 4;
   const int wr = wave >> 1, wc = wave & 1;
-  const int col0 = blockIdx.x * GM_BN, ks = blockIdx.y, row0 = blockIdx.z * GM_BM;
+  // blockIdx.x runs over the output tiles, padded to a multiple of 8: the
+  // tiles are numbered column-major (row tiles inner) and each XCD takes a
+  // contiguous run of them, so the workgroups on one XCD share a few column
+  // panels of W and the row panels of X in its L2
+  const int q = xcd_remap(blockIdx.x, gridDim.x, g.tiles_c * g.tiles_r);
+  if (q < 0) return;
+  const int tc = q / g.tiles_r;
+  const int col0 = tc * GM_BN, ks = blockIdx.y, row0 = (q - tc * g.tiles_r) * GM_BM;
   const int kbeg = ks * g.kchunk;
   const int kend = min(g.K, kbeg + g.kchunk);
   const int nsteps = kend > kbeg ? (kend - kbeg + GM_BK - 1) / GM_BK : 0;
-  const bool want_hss = (EPI == EPI_PARTIAL) && XBF && g.hss != nullptr && blockIdx.x == 0;
+  const bool want_hss = (EPI == EPI_PARTIAL) && XBF && g.hss != nullptr && tc == 0;
   const uint16_t* W = (const uint16_t*)g.W;
 
-  u32x4 xq[XN], wq[2];
-  float hsq[2] = {0.0f, 0.0f};
+  u32x4 xq[XN], wq[WN];
+  float hsq[XN];
+#pragma unroll
+  for (int it = 0; it < XN; ++it) hsq[it] = 0.0f;
 
   auto load = [&](int k0) {
 #pragma unroll
-    for (int it = 0; it < 2; ++it) {
+    for (int it = 0; it < WN; ++it) {
       const int c = tid + 256 * it;
-      const int gn = col0 + (c >> 2), gk = k0 + (c & 3) * 8;
+      const int gn = col0 + c / CPR, gk = k0 + (c % CPR) * 8;
       wq[it] = u32x4{0u, 0u, 0u, 0u};
       if (gn < g.N && gk < kend) wq[it] = *(const u32x4*)(W + (int64_t)gn * g.ldw + gk);
     }
@@ -302,19 +312,19 @@ __global__ __launch_bounds__(256, 2) void k_gemm_mm(GemmArgs g) {
       const int c = tid + 256 * it;
       xq[it] = u32x4{0u, 0u, 0u, 0u};
       if (XBF) {
-        const int gr = row0 + (c >> 2), gk = k0 + (c & 3) * 8;
+        const int gr = row0 + c / CPR, gk = k0 + (c % CPR) * 8;
         if (gr < g.R && gk < kend) xq[it] = *(const u32x4*)((const uint16_t*)g.X + (int64_t)gr * g.ldx + gk);
       } else {
-        const int gr = row0 + (c >> 3), gk = k0 + (c & 7) * 4;
+        const int gr = row0 + c / (2 * CPR), gk = k0 + (c % (2 * CPR)) * 4;
         if (gr < g.R && gk < kend) xq[it] = *(const u32x4*)((const float*)g.X + (int64_t)gr * g.ldx + gk);
       }
     }
   };
-  auto store = [&](int buf, int k0) {
+  auto store = [&](int k0) {
 #pragma unroll
-    for (int it = 0; it < 2; ++it) {
+    for (int it = 0; it < WN; ++it) {
       const int c = tid + 256 * it;
-      *(u32x4*)&sW[buf][(c >> 2) * GM_LD + (c & 3) * 8] = wq[it];
+      *(u32x4*)&sW[(c / CPR) * GM_LD + (c % CPR) * 8] = wq[it];
     }
 #pragma unroll
     for (int it = 0; it < XN; ++it) {
@@ -328,26 +338,26 @@ __global__ __launch_bounds__(256, 2) void k_gemm_mm(GemmArgs g) {
             float sq = 0.0f;
 #pragma unroll
             for (int e = 0; e < 8; ++e) sq += x[e] * x[e];
-            // the 4 chunks of one row sit in 4 consecutive lanes
-            sq += __shfl_xor(sq, 1, 64);
-            sq += __shfl_xor(sq, 2, 64);
+            // the CPR chunks of one row sit in CPR consecutive lanes
+#pragma unroll
+            for (int o = 1; o < CPR; o <<= 1) sq += __shfl_xor(sq, o, 64);
             hsq[it] += sq;
           }
-          const int gk = k0 + (c & 3) * 8;
+          const int gk = k0 + (c % CPR) * 8;
           if (g.gamma != nullptr && gk < kend) {
 #pragma unroll
             for (int e = 0; e < 8; ++e) x[e] *= Elem<uint16_t>::ld(g.gamma, gk + e);
             v = pack_bf16x8(x);
           }
         }
-        *(u32x4*)&sX[buf][(c >> 2) * GM_LD + (c & 3) * 8] = v;
+        *(u32x4*)&sX[(c / CPR) * GM_LD + (c % CPR) * 8] = v;
       } else {
         const u32x4 v = xq[it];
         const uint32_t lo = (uint32_t)f32_to_bf16_rne(__uint_as_float(v.x)) |
                             ((uint32_t)f32_to_bf16_rne(__uint_as_float(v.y)) << 16);
         const uint32_t hi = (uint32_t)f32_to_bf16_rne(__uint_as_float(v.z)) |
                             ((uint32_t)f32_to_bf16_rne(__uint_as_float(v.w)) << 16);
-        *(uint2*)&sX[buf][(c >> 3) * GM_LD + (c & 7) * 4] = make_uint2(lo, hi);
+        *(uint2*)&sX[(c / (2 * CPR)) * GM_LD + (c % (2 * CPR)) * 4] = make_uint2(lo, hi);
       }
     }
   };
@@ -360,61 +370,87 @@ __global__ __launch_bounds__(256, 2) void k_gemm_mm(GemmArgs g) {
 
   if (nsteps > 0) {
     load(kbeg);
-    store(0, kbeg);
+    store(kbeg);
   }
   __syncthreads();
   for (int s = 0; s < nsteps; ++s) {
-    const int buf = s & 1;
     const int knext = kbeg + (s + 1) * GM_BK;
     if (s + 1 < nsteps) load(knext);
-    u32x4 bop[4], aop[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) bop[j] = *(const u32x4*)&sW[buf][(64 * wc + 16 * j + lr) * GM_LD + 8 * lg];
+    for (int kk = 0; kk < GM_BK / 32; ++kk) {
+      u32x4 bop[4], aop[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) aop[i] = *(const u32x4*)&sX[buf][(64 * wr + 16 * i + lr) * GM_LD + 8 * lg];
+      for (int j = 0; j < 4; ++j) bop[j] = *(const u32x4*)&sW[(64 * wc + 16 * j + lr) * GM_LD + 32 * kk + 8 * lg];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < 4; ++i) aop[i] = *(const u32x4*)&sX[(64 * wr + 16 * i + lr) * GM_LD + 32 * kk + 8 * lg];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = mfma16x16x32(aop[i], bop[j], acc[i][j]);
-    if (s + 1 < nsteps) store(buf ^ 1, knext);
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = mfma16x16x32(aop[i], bop[j], acc[i][j]);
+    }
+    if (s + 1 < nsteps) {
+      __syncthreads();  // every wave is done reading this step's tiles
+      store(knext);
+    }
     __syncthreads();
   }
 
   if (want_hss) {
 #pragma unroll
-    for (int it = 0; it < 2; ++it) {
+    for (int it = 0; it < XN; ++it) {
       const int c = tid + 256 * it;
-      const int gr = row0 + (c >> 2);
-      if ((c & 3) == 0 && gr < g.R) g.hss[(int64_t)ks * g.R + gr] = hsq[it];
+      const int gr = row0 + c / CPR;
+      if (c % CPR == 0 && gr < g.R) g.hss[(int64_t)ks * g.R + gr] = hsq[it];
     }
   }
 
+  // epilogue: rows outer (16 per lane), so the per-row work -- the validity of
+  // the row's sequence -- is done once per row, not once per value
+  float bias[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int col = col0 + 64 * wc + 16 * j + lr;
-    if (col >= g.N) continue;
-    float bias = 0.0f;
-    if (EPI != EPI_PARTIAL && g.bias != nullptr) bias = Elem<uint16_t>::ld(g.bias, col);
+    bias[j] = (EPI != EPI_PARTIAL && g.bias != nullptr && col < g.N) ? Elem<uint16_t>::ld(g.bias, col) : 0.0f;
+  }
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int64_t rho = row0 + 64 * wr + 16 * i + 4 * lg + e;
-        if (rho >= g.R) continue;
+    for (int e = 0; e < 4; ++e) {
+      const int64_t rho = row0 + 64 * wr + 16 * i + 4 * lg + e;
+      if (rho >= g.R) continue;
+      if (EPI == EPI_RESID && g.seq_invalid[rho / g.n]) continue;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int col = col0 + 64 * wc + 16 * j + lr;
+        if (col >= g.N) continue;
         const float y = acc[i][j][e];
         if (EPI == EPI_PARTIAL) {
           g.ypart[((int64_t)ks * g.R + rho) * g.N + col] = y;
         } else if (EPI == EPI_BIAS_ACT) {
-          g.yout[rho * g.N + col] = activation(y + bias, g.act);
+          g.yout[rho * g.N + col] = activation(y + bias[j], g.act);
         } else {
-          if (g.seq_invalid[rho / g.n]) continue;
-          const float dh = y + bias;
+          const float dh = y + bias[j];
           const float hv = Elem<TO>::ld(g.h, rho * g.N + col);
           Elem<TO>::st(g.out, rho * g.N + col, hv + dh);
           if (g.delta) g.delta[rho * g.N + col] = dh;
         }
       }
-  }
+    }
+}
+
+// bf16 X: K steps of 64; fp32 X (twice the staging registers per K): steps of
+// 32.  Both keep three workgroups on a CU.
+template <typename TO, int EPI>
+__global__ __launch_bounds__(256, 3) void k_gemm_mm_bx(GemmArgs g) {
+  __shared__ __attribute__((aligned(16))) uint16_t sX[GM_BM * (64 + 8)];
+  __shared__ __attribute__((aligned(16))) uint16_t sW[GM_BN * (64 + 8)];
+  gemm_mm_body<uint16_t, TO, EPI, 64>(g, sX, sW);
+}
+template <typename TO, int EPI>
+__global__ __launch_bounds__(256, 3) void k_gemm_mm_fx(GemmArgs g) {
+  __shared__ __attribute__((aligned(16))) uint16_t sX[GM_BM * (32 + 8)];
+  __shared__ __attribute__((aligned(16))) uint16_t sW[GM_BN * (32 + 8)];
+  gemm_mm_body<float, TO, EPI, 32>(g, sX, sW);
 }
 
 // a = act(sum over K splits of the partial sums + bias), one thread per value
@@ -483,17 +519,21 @@ hipError_t ready_launch_gemm_mfma(const GemmArgs& g, int x_dt, int out_dt, int e
   return hipGetLastError();
 }
 
-hipError_t ready_launch_gemm_mm(const GemmArgs& g, int x_dt, int out_dt, int epi, dim3 grid, hipStream_t s,
+hipError_t ready_launch_gemm_mm(const GemmArgs& g0, int x_dt, int out_dt, int epi, int ksplit, hipStream_t s,
                                 StageEvents ev) {
   const dim3 block(256);
+  GemmArgs g = g0;
+  g.tiles_c = (g.N + GM_BN - 1) / GM_BN;
+  g.tiles_r = (g.R + GM_BM - 1) / GM_BM;
+  const dim3 grid((unsigned)((g.tiles_c * g.tiles_r + 7) / 8 * 8), (unsigned)ksplit);
   if (epi == EPI_PARTIAL) {
-    if (x_dt == READY_BF16) READY_LAUNCH((k_gemm_mm<uint16_t, float, EPI_PARTIAL>), grid, block, 0, s, ev, g);
-    else READY_LAUNCH((k_gemm_mm<float, float, EPI_PARTIAL>), grid, block, 0, s, ev, g);
+    if (x_dt == READY_BF16) READY_LAUNCH((k_gemm_mm_bx<float, EPI_PARTIAL>), grid, block, 0, s, ev, g);
+    else READY_LAUNCH((k_gemm_mm_fx<float, EPI_PARTIAL>), grid, block, 0, s, ev, g);
   } else if (epi == EPI_BIAS_ACT) {
-    READY_LAUNCH((k_gemm_mm<float, float, EPI_BIAS_ACT>), grid, block, 0, s, ev, g);
+    READY_LAUNCH((k_gemm_mm_fx<float, EPI_BIAS_ACT>), grid, block, 0, s, ev, g);
   } else {
-    if (out_dt == READY_BF16) READY_LAUNCH((k_gemm_mm<float, uint16_t, EPI_RESID>), grid, block, 0, s, ev, g);
-    else READY_LAUNCH((k_gemm_mm<float, float, EPI_RESID>), grid, block, 0, s, ev, g);
+    if (out_dt == READY_BF16) READY_LAUNCH((k_gemm_mm_fx<uint16_t, EPI_RESID>), grid, block, 0, s, ev, g);
+    else READY_LAUNCH((k_gemm_mm_fx<float, EPI_RESID>), grid, block, 0, s, ev, g);
   }
   return hipGetLastError();
 }

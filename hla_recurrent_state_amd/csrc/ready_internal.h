@@ -137,6 +137,7 @@ struct GemmArgs {
   float* delta;                    // [R][N] or null
   const int32_t* seq_invalid;      // [R / n]
   int n;
+  int tiles_c, tiles_r;            // k_gemm_mm: column and row tiles (set by its launcher)
 };
 
 // VALU skinny GEMM tiling
@@ -162,12 +163,12 @@ READY_HIDDEN hipError_t ready_launch_state_mm(const StateArgs& a, int grid, hipS
 READY_HIDDEN hipError_t ready_launch_gemm(const GemmArgs& g, int x_dt, int w_dt, int out_dt, int epi,
                                           dim3 grid, size_t lds_bytes, hipStream_t s, StageEvents ev);
 // 128 x 128 tiles for large row counts; weights must be bf16
-READY_HIDDEN hipError_t ready_launch_gemm_mm(const GemmArgs& g, int x_dt, int out_dt, int epi, dim3 grid,
+READY_HIDDEN hipError_t ready_launch_gemm_mm(const GemmArgs& g, int x_dt, int out_dt, int epi, int ksplit,
                                              hipStream_t s, StageEvents ev);
 // yout = act(sum of ksplit partial sums in ypart + bias)
 READY_HIDDEN hipError_t ready_launch_reduce_bias_act(const GemmArgs& g, int ksplit, hipStream_t s, StageEvents ev);
 #define READY_GM_TILE 128         // k_gemm_mm tile rows and columns
-#define READY_GM_BK 32            // k_gemm_mm K step
+#define READY_GM_BK 64            // k_gemm_mm K step
 // bm: rows per workgroup tile (16 or 64); weights must be bf16
 READY_HIDDEN hipError_t ready_launch_gemm_mfma(const GemmArgs& g, int x_dt, int out_dt, int epi, int bm,
                                                dim3 grid, hipStream_t s, StageEvents ev);

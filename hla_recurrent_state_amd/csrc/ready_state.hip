@@ -197,9 +197,9 @@ __global__ __launch_bounds__(256) void k_state(StateArgs a) {
 // already.  U and V contract over their slow index, so each workgroup stages
 // U^T and V^T of its layer-head pair in LDS and walks the tiles in pair-major
 // order, restaging only when the pair changes.  Persistent: one workgroup of
-// 8 waves per CU; the state tile of the item two ahead is loaded into
-// registers while the current one is worked on, so every CU keeps two tiles
-// of loads in flight.
+// 8 waves per CU; the state tiles of the next three items are loaded into
+// registers while the current one is worked on, so every CU keeps up to
+// three tiles of loads in flight.
 
 namespace {
 
@@ -483,25 +483,29 @@ __global__ __launch_bounds__(MM_THREADS, 1) void k_state_mm(StateArgs a) {
   if (ACC_LDS)
     for (int i = threadIdx.x; i < a.B; i += MM_THREADS) s_acc[i] = a.accept_idx[i];
   __syncthreads();
-  // two sets of prefetched registers, one for even and one for odd items
-  // (a register copy of a value still being loaded would wait for every
+  // three sets of prefetched registers, for items t, t + 1 and t + 2 modulo
+  // 3 (a register copy of a value still being loaded would wait for every
   // load in flight)
-  float z0[4] = {0.0f, 0.0f, 0.0f, 0.0f}, h0[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-  float z1[4] = {0.0f, 0.0f, 0.0f, 0.0f}, h1[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-  u32x4 P0[MM_CH], P1[MM_CH];
-  int pa0, pa1;
+  float z0[4], h0[4], z1[4], h1[4], z2[4], h2[4];
+  u32x4 P0[MM_CH], P1[MM_CH], P2[MM_CH];
+  int pa0, pa1, pa2;
   mm_fetch<ACC_LDS>(a, t0, t1, P0, pa0, s_acc);
   mm_zfetch(a, t0, t1, zj, zi, z0, h0);
   mm_fetch<ACC_LDS>(a, t0 + 1, t1, P1, pa1, s_acc);
   mm_zfetch(a, t0 + 1, t1, zj, zi, z1, h1);
+  mm_fetch<ACC_LDS>(a, t0 + 2, t1, P2, pa2, s_acc);
+  mm_zfetch(a, t0 + 2, t1, zj, zi, z2, h2);
   int cur_mz = -1;
-  for (int t = t0; t < t1; t += 2) {
+  for (int t = t0; t < t1; t += 3) {
     mm_tile(a, t, P0, pa0, rp, zj, zi, z0, h0, smem, cur_mz);
-    mm_fetch<ACC_LDS>(a, t + 2, t1, P0, pa0, s_acc);
-    mm_zfetch(a, t + 2, t1, zj, zi, z0, h0);
+    mm_fetch<ACC_LDS>(a, t + 3, t1, P0, pa0, s_acc);
+    mm_zfetch(a, t + 3, t1, zj, zi, z0, h0);
     if (t + 1 < t1) mm_tile(a, t + 1, P1, pa1, rp, zj, zi, z1, h1, smem, cur_mz);
-    mm_fetch<ACC_LDS>(a, t + 3, t1, P1, pa1, s_acc);
-    mm_zfetch(a, t + 3, t1, zj, zi, z1, h1);
+    mm_fetch<ACC_LDS>(a, t + 4, t1, P1, pa1, s_acc);
+    mm_zfetch(a, t + 4, t1, zj, zi, z1, h1);
+    if (t + 2 < t1) mm_tile(a, t + 2, P2, pa2, rp, zj, zi, z2, h2, smem, cur_mz);
+    mm_fetch<ACC_LDS>(a, t + 5, t1, P2, pa2, s_acc);
+    mm_zfetch(a, t + 5, t1, zj, zi, z2, h2);
   }
 }
 
