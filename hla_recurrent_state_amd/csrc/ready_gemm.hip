@@ -46,11 +46,21 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs g) {
   for (int k0 = kbeg; k0 < kend; k0 += READY_GEMM_KSTAGE) {
     const int klen = min(READY_GEMM_KSTAGE, kend - k0);
     __syncthreads();
-    for (int e = tid; e < RB * klen; e += 256) {
-      const int rr = e / klen, kk = e - rr * klen;
-      float x = 0.0f;
-      if (rr < nrows) x = Elem<TX>::ld(g.X, (int64_t)(row0 + rr) * g.ldx + k0 + kk);
-      xs[e] = x;
+    // batches of 8 loads in flight (issued unconditionally: element 0 stands
+    // in for one out of range), then their stores
+    for (int e0 = tid; e0 < RB * klen; e0 += 8 * 256) {
+      float xv[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int e = e0 + 256 * u;
+        const int rr = e / klen, kk = e - rr * klen;
+        const bool ok = e < RB * klen && rr < nrows;
+        const float x = Elem<TX>::ld(g.X, ok ? (int64_t)(row0 + rr) * g.ldx + k0 + kk : 0);
+        xv[u] = ok ? x : 0.0f;
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (e0 + 256 * u < RB * klen) xs[e0 + 256 * u] = xv[u];
     }
     __syncthreads();
     if (want_hss) {
@@ -71,13 +81,24 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs g) {
     if (c < g.N) {
       const TW* wrow = (const TW*)g.W + (int64_t)c * g.ldw + k0;
       if (g.vec_ok) {
-        for (int kk = lic * VW; kk < klen; kk += LPC * VW) {
-          float w[VW];
-          Elem<TW>::unpack(*(const u32x4*)(wrow + kk), w);
+        // batches of 4 row chunks in flight (a clamped address stands in for
+        // a chunk past the end; it is not used)
+        for (int kk0 = lic * VW; kk0 < klen; kk0 += 4 * LPC * VW) {
+          u32x4 wv[4];
 #pragma unroll
-          for (int rr = 0; rr < RB; ++rr)
+          for (int u = 0; u < 4; ++u) wv[u] = *(const u32x4*)(wrow + min(kk0 + u * LPC * VW, klen - VW));
 #pragma unroll
-            for (int e = 0; e < VW; ++e) acc[rr] += w[e] * xs[rr * klen + kk + e];
+          for (int u = 0; u < 4; ++u) {
+            const int kk = kk0 + u * LPC * VW;
+            if (kk < klen) {
+              float w[VW];
+              Elem<TW>::unpack(wv[u], w);
+#pragma unroll
+              for (int rr = 0; rr < RB; ++rr)
+#pragma unroll
+                for (int e = 0; e < VW; ++e) acc[rr] += w[e] * xs[rr * klen + kk + e];
+            }
+          }
         }
       } else {
         for (int kk = lic; kk < klen; kk += LPC) {

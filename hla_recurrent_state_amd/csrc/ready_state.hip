@@ -112,7 +112,13 @@ __global__ __launch_bounds__(256) void k_state(StateArgs a) {
   for (int e = tid; e < n * READY_TILE; e += 256) {
     const int j = e >> 7, k = e & 127;
     float s = 0.0f;
-    for (int i = 0; i < r; ++i) s += Elem<TW>::ld(U, (int64_t)i * READY_TILE + k) * s_z[j * r + i];
+    for (int i0 = 0; i0 < r; i0 += 8) {  // r is a multiple of 8: 8 loads in flight
+      float uv[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) uv[u] = Elem<TW>::ld(U, (int64_t)(i0 + u) * READY_TILE + k);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) s += uv[u] * s_z[j * r + i0 + u];
+    }
     s_q[j][k] = s;
   }
 
