@@ -526,6 +526,14 @@ def cpu_baseline(bat, budget_s):
         t0 = time.perf_counter()
         ref = oracle_reference(inp, seqs)
         el = time.perf_counter() - t0
+        # when the sample is short, repeat it to fill the budget (the mean is reported)
+        reps = 1
+        while el < budget_s and reps < 1000:
+            t0 = time.perf_counter()
+            oracle_reference(inp, seqs)
+            el += time.perf_counter() - t0
+            reps += 1
+        el /= reps
     committed = 2 * nseq * cfg.M * 128 * 128 * esize(cfg.state_dtype)
     # parity of the GPU outputs (set 0) on the sampled sequences
     s0 = bat["set0"]
@@ -548,7 +556,8 @@ def cpu_baseline(bat, budget_s):
     rep = compare(inp, res, ref)
     base = {"value": round(committed / el / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
             "sample": "float64 numpy oracle, steps 1-5, on %d of the %d sequences of the batched "
-                      "workload (%.1f s; committed-state bytes of the sample / time)" % (nseq, cfg.B, el)}
+                      "workload, %d timed passes of %.2f s each (committed-state bytes of the sample / "
+                      "mean time)" % (nseq, cfg.B, reps, el)}
     return base, rep
 
 
@@ -656,7 +665,7 @@ def main():
 
         def summ(v):
             return {"p10": round(pct(v, 10), 2), "p50": round(pct(v, 50), 2), "p90": round(pct(v, 90), 2)}
-        best = pct(b1["fused_graph_cold_us"], 50)
+        best = min(pct(b1["fused_graph_cold_us"], 50), pct(b1["fused_eager_cold_us"], 50))
         out["b1_latency"] = {
             "workload": "paper shape: B=1, M=32 (layers 30, 62 x 16 heads), bf16 states at t=4096, n=7, "
                         "d=5120, r=8, MLP 288->256->5120",
@@ -669,7 +678,7 @@ def main():
             "unfused_torch_warm_mean": round(b1["unfused_torch_warm_us"], 2),
             "algorithmic_bytes": pbytes,
             "hbm_roofline_us": round(roof_us, 3),
-            "frac_of_hbm_roofline": round(roof_us / best, 4),
+            "frac_of_hbm_roofline": round(roof_us / best, 4),   # against the faster cold path
             "stage_median_us": b1["stage_us"],
             "unfused_vs_fused_max_abs_diff": b1["unfused_vs_fused_max_abs_diff"],
             "unfused_gathered_equal": b1["gathered_equal"],
