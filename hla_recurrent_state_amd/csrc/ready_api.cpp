@@ -461,7 +461,9 @@ readyStatus run_reader(const readyPlan* plan, const readyStates* states, const i
       const dim3 grid((unsigned)cdiv(Hm, READY_MFMA_BN), 1u, (unsigned)cdiv(R, plan->g1.bm));
       e = ready_launch_gemm_mfma(g, READY_F32, s.act_dtype, EPI_BIAS_ACT, plan->g1.bm, grid, strm, ev);
     } else {
-      const dim3 grid((unsigned)cdiv(Hm, READY_GEMM_COLS), 1u, (unsigned)cdiv(R, READY_GEMM_RB));
+      // too few workgroups for the GPU: four columns per workgroup, K split over its waves
+      g.wave_k = cdiv(Hm, READY_GEMM_COLS) * cdiv(R, READY_GEMM_RB) < 128 ? 1 : 0;
+      const dim3 grid((unsigned)cdiv(Hm, g.wave_k ? 4 : READY_GEMM_COLS), 1u, (unsigned)cdiv(R, READY_GEMM_RB));
       const size_t lds = 4 * READY_GEMM_RB * (size_t)std::min((int)F, READY_GEMM_KSTAGE);
       e = ready_launch_gemm(g, READY_F32, s.weight_dtype, s.act_dtype, EPI_BIAS_ACT, grid, lds, strm, ev);
     }
@@ -483,7 +485,8 @@ readyStatus run_reader(const readyPlan* plan, const readyStates* states, const i
       const dim3 grid((unsigned)cdiv(d, READY_MFMA_BN), 1u, (unsigned)cdiv(R, plan->g2.bm));
       e = ready_launch_gemm_mfma(g, READY_F32, s.act_dtype, EPI_RESID, plan->g2.bm, grid, strm, ev);
     } else {
-      const dim3 grid((unsigned)cdiv(d, READY_GEMM_COLS), 1u, (unsigned)cdiv(R, READY_GEMM_RB));
+      g.wave_k = cdiv(d, READY_GEMM_COLS) * cdiv(R, READY_GEMM_RB) < 128 ? 1 : 0;
+      const dim3 grid((unsigned)cdiv(d, g.wave_k ? 4 : READY_GEMM_COLS), 1u, (unsigned)cdiv(R, READY_GEMM_RB));
       const size_t lds = 4 * READY_GEMM_RB * (size_t)std::min((int)Hm, READY_GEMM_KSTAGE);
       e = ready_launch_gemm(g, READY_F32, s.weight_dtype, s.act_dtype, EPI_RESID, grid, lds, strm, ev);
     }

@@ -20,7 +20,9 @@
 // Each workgroup owns 16 output columns (4 waves x 4 groups of LPC = 16
 // lanes), READY_GEMM_RB rows and one K split.  X rows are staged in LDS in fp32
 // by passes of READY_GEMM_KSTAGE; each lane group streams its column of W
-// with 16-byte loads and keeps RB accumulators.
+// with 16-byte loads and keeps RB accumulators.  With g.wave_k (grids too
+// small to fill the GPU) a workgroup owns 4 columns instead and its four
+// waves split each column's K range, summed through LDS in wave order.
 template <typename TX, typename TW, typename TO, int EPI>
 __global__ __launch_bounds__(256) void k_gemm(GemmArgs g) {
   constexpr int RB = READY_GEMM_RB;
@@ -30,7 +32,9 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs g) {
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int grp = lane / LPC, lic = lane - grp * LPC;
-  const int c = blockIdx.x * READY_GEMM_COLS + wave * 4 + grp;
+  const int nw = g.wave_k ? 4 : 1;                   // waves sharing a column
+  const int c = g.wave_k ? blockIdx.x * 4 + grp : blockIdx.x * READY_GEMM_COLS + wave * 4 + grp;
+  const int wk = g.wave_k ? wave : 0;                // this wave's share of K
   const int ks = blockIdx.y;
   const int row0 = blockIdx.z * RB;
   const int nrows = min(RB, g.R - row0);
@@ -83,13 +87,14 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs g) {
       if (g.vec_ok) {
         // batches of 4 row chunks in flight (a clamped address stands in for
         // a chunk past the end; it is not used)
-        for (int kk0 = lic * VW; kk0 < klen; kk0 += 4 * LPC * VW) {
+        const int step = LPC * VW * nw;
+        for (int kk0 = (wk * LPC + lic) * VW; kk0 < klen; kk0 += 4 * step) {
           u32x4 wv[4];
 #pragma unroll
-          for (int u = 0; u < 4; ++u) wv[u] = *(const u32x4*)(wrow + min(kk0 + u * LPC * VW, klen - VW));
+          for (int u = 0; u < 4; ++u) wv[u] = *(const u32x4*)(wrow + min(kk0 + u * step, klen - VW));
 #pragma unroll
           for (int u = 0; u < 4; ++u) {
-            const int kk = kk0 + u * LPC * VW;
+            const int kk = kk0 + u * step;
             if (kk < klen) {
               float w[VW];
               Elem<TW>::unpack(wv[u], w);
@@ -101,7 +106,7 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs g) {
           }
         }
       } else {
-        for (int kk = lic; kk < klen; kk += LPC) {
+        for (int kk = wk * LPC + lic; kk < klen; kk += LPC * nw) {
           const float w = Elem<TW>::ld(wrow, kk);
 #pragma unroll
           for (int rr = 0; rr < RB; ++rr) acc[rr] += w * xs[rr * klen + kk];
@@ -114,6 +119,16 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs g) {
   for (int rr = 0; rr < RB; ++rr)
 #pragma unroll
     for (int off = LPC / 2; off > 0; off >>= 1) acc[rr] += __shfl_xor(acc[rr], off, 64);
+  if (g.wave_k) {
+    __shared__ float s_wk[4][4][RB];  // [wave][group][row]
+    if (lic == 0)
+#pragma unroll
+      for (int rr = 0; rr < RB; ++rr) s_wk[wave][grp][rr] = acc[rr];
+    __syncthreads();
+    if (wave == 0 && lic == 0)
+#pragma unroll
+      for (int rr = 0; rr < RB; ++rr) acc[rr] = (s_wk[0][grp][rr] + s_wk[1][grp][rr]) + (s_wk[2][grp][rr] + s_wk[3][grp][rr]);
+  }
 
   if (want_hss) {
     hsq0 = wave_sum(hsq0);
@@ -124,7 +139,7 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs g) {
     }
   }
 
-  if (lic != 0 || c >= g.N) return;
+  if (lic != 0 || c >= g.N || (g.wave_k && wave != 0)) return;
   for (int rr = 0; rr < nrows; ++rr) {
     const int64_t rho = row0 + rr;
     if (EPI == EPI_PARTIAL) {

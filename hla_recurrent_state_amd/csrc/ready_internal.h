@@ -138,6 +138,7 @@ struct GemmArgs {
   const int32_t* seq_invalid;      // [R / n]
   int n;
   int tiles_c, tiles_r;            // k_gemm_mm: column and row tiles (set by its launcher)
+  int wave_k;                      // k_gemm: 4 columns per workgroup, K split over its waves
 };
 
 // VALU skinny GEMM tiling
