@@ -389,14 +389,16 @@ def _fill_states_random(buf, seed, torch):
         blk.copy_(torch.randn(blk.numel(), generator=g, device=buf.device, dtype=torch.float32) / 128.0)
 
 
-def run_config(name, args, hip, torch, R, synth, seed=0):
+def run_config(name, args, hip, torch, R, synth, seed=0, cfg=None, random_states=None, copy_ref=True):
     """Cold (after a 512 MB flush) and back-to-back latency of one call of a
     configuration, its per-stage kernel medians, and a plain device copy that
     moves the same number of bytes (half read, half written)."""
     from synth.device import to_device, torch_dtype
     device = torch.device("cuda:0")
-    cfg = synth.make_shape(name)
-    random_states = name == "rank"
+    if cfg is None:
+        cfg = synth.make_shape(name)
+    if random_states is None:
+        random_states = name == "rank"
     t0 = time.time()
     inp = synth.make(cfg, seed=seed, states=not random_states)
     dev_in = to_device(inp, device)
@@ -464,25 +466,30 @@ def run_config(name, args, hip, torch, R, synth, seed=0):
         if code != 0:
             raise R.ReadyError(code, name + " stages")
     torch.cuda.synchronize(device)
-    # the single-kernel path takes bf16 states, activations and weights with r <= 32
-    fast = (cfg.state_dtype, cfg.act_dtype, cfg.weight_dtype) == ("bf16",) * 3 and cfg.r <= 32
+    med = [pct([1000.0 * hip.ms(evs[i][2 * k], evs[i][2 * k + 1]) for i in range(K)], 50)
+           for k in range(R.READY_STAGES)]
+    # the single-kernel path records the events of stages 0, 2 and 3 after its one
+    # kernel (stage 1), so stage 0 "starts" after stage 1 ends; the general path
+    # runs stage 0 first
+    fast = hip.ms(evs[0][3], evs[0][0]) >= 0.0
     stage_names = ("k_reader",) if fast else ("query_gemm", "state_kernel", "mlp1", "mlp2_residual")
     stage_idx = (1,) if fast else (0, 1, 2, 3)
-    stages = {nm: round(pct([1000.0 * hip.ms(evs[i][2 * k], evs[i][2 * k + 1]) for i in range(K)], 50), 2)
-              for nm, k in zip(stage_names, stage_idx)}
+    stages = {nm: round(med[k], 2) for nm, k in zip(stage_names, stage_idx)}
     for row in evs:
         for e in row:
             hip.destroy(e)
     if int(outs["dev_status"].item()) != 0:
         raise RuntimeError("device status set during the %s run" % name)
     alg = algorithmic_bytes(cfg)["total"]
-    # plain copy of the same bytes
-    half = alg // 2
-    src = torch.empty(half, dtype=torch.uint8, device=device).fill_(1)
-    dst = torch.empty_like(src)
-    copy_cold = timed(lambda: dst.copy_(src), K)
-    copy_warm = back_to_back(lambda: dst.copy_(src), K)
-    del src, dst, flush
+    if copy_ref:
+        # plain copy of the same bytes
+        half = alg // 2
+        src = torch.empty(half, dtype=torch.uint8, device=device).fill_(1)
+        dst = torch.empty_like(src)
+        copy_cold = timed(lambda: dst.copy_(src), K)
+        copy_warm = back_to_back(lambda: dst.copy_(src), K)
+        del src, dst
+    del flush
     p50 = pct(cold, 50)
     res = {
         "path": "k_reader (single persistent kernel)" if fast else "general (4 kernels)",
@@ -496,12 +503,31 @@ def run_config(name, args, hip, torch, R, synth, seed=0):
         "cold_frac_of_hbm_peak": round(alg / (p50 * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
         "warm_frac_of_hbm_peak": round(alg / (warm * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
         "stage_median_us": stages,
-        "same_bytes_copy": {"cold_p50_us": round(pct(copy_cold, 50), 2), "warm_mean_us": round(copy_warm, 2),
-                            "warm_GBps": round(2 * half / (copy_warm * 1e-6) / 1e9, 1)},
     }
+    if copy_ref:
+        res["same_bytes_copy"] = {"cold_p50_us": round(pct(copy_cold, 50), 2), "warm_mean_us": round(copy_warm, 2),
+                                  "warm_GBps": round(2 * half / (copy_warm * 1e-6) / 1e9, 1)}
     del prep, dev_in, outs
     torch.cuda.empty_cache()
     return res
+
+
+def run_sweeps(args, hip, torch, R, synth):
+    """The batched workload's shape with one parameter changed: the reader
+    rank (8 .. 128; r <= 32 takes the single-kernel path, larger ranks the
+    general path with the matrix-core readout V^T (S_bar q)), and a single
+    selected layer (2, 30 or 62: 16 layer-head pairs).  Timing only: the
+    states are drawn on the device."""
+    out = {"rank": {}, "single_layer": {}}
+    for r in (8, 16, 32, 64, 128):
+        cfg = synth.make_shape("batched", r=r)
+        out["rank"][str(r)] = run_config("batched_r%d" % r, args, hip, torch, R, synth, cfg=cfg,
+                                         random_states=True, copy_ref=False)
+    for layer in (2, 30, 62):
+        cfg = synth.make_shape("batched", layer_ids=(layer,))
+        out["single_layer"][str(layer)] = run_config("batched_layer%d" % layer, args, hip, torch, R, synth,
+                                                     cfg=cfg, random_states=True, copy_ref=False)
+    return out
 
 
 # ---------------------------------------------------------------- CPU oracle baseline
@@ -576,6 +602,7 @@ def main():
     ap.add_argument("--configs", default="tiny,wide,rank",
                     help="other configurations timed after the headline (comma list, or 'none')")
     ap.add_argument("--config-steps", type=int, default=50)
+    ap.add_argument("--no-sweeps", action="store_true", help="skip the rank and single-layer sweeps")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run 10 plain device copies of MIB MiB (the reference for scaling the "
                          "FETCH_SIZE / WRITE_SIZE counters to bytes) and exit")
@@ -689,6 +716,8 @@ def main():
         out["configs"] = {}
         for name in args.configs.split(","):
             out["configs"][name] = run_config(name, args, hip, torch, R, synth)
+    if not args.no_sweeps:
+        out["sweeps"] = run_sweeps(args, hip, torch, R, synth)
     ok = True
     if not args.no_cpu:
         base, rep = cpu_baseline(bat, args.cpu_budget)

@@ -208,7 +208,10 @@ readyStatus readyPlanCreate(const readyShape* shape, const int32_t* layer_ids, r
       p->g1.ksplit = (int)cdiv(p->F, kchunk);
     }
     p->g2.mfma = (wbf && s.Hm % 8 == 0) ? 1 : 0;
-    p->g2.big = (p->g2.mfma && p->R >= 2 * READY_GM_TILE) ? 1 : 0;
+    // 128 x 128 tiles only when there is at least one per CU (no K split
+    // here); else the 64-row kernel gives more workgroups
+    p->g2.big = (p->g2.mfma && p->R >= 2 * READY_GM_TILE &&
+                 cdiv(s.d, READY_GM_TILE) * cdiv(p->R, READY_GM_TILE) >= 256) ? 1 : 0;
     p->g2.bm = p->R <= 16 ? 16 : 64;
     p->g2.ksplit = 1;
     p->g2.kchunk = s.Hm;
