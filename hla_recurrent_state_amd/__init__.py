@@ -5,10 +5,10 @@ kernels of libready.so.  If the library is missing, loading raises
 ReadyError -- there is no fallback path.
 
 Low-level names mirror the C functions (readyPlanCreate, readyWorkspaceSize,
-readyStateReader, readyPlanDestroy, readyStatusString, readyVersion) and the C
-structs (readyShape, readyStates, readyWeights, readyOutputs).  StateReader
-wraps them for torch tensors: it forwards data_ptr() values and the current
-HIP stream.
+readyStateReader, readyVerifyStates, readyPlanDestroy, readyStatusString,
+readyVersion) and the C structs (readyShape, readyStates, readyWeights,
+readyOutputs, readyVerifyBuffer).  StateReader and verify_states wrap them for
+torch tensors: they forward data_ptr() values and the current HIP stream.
 """
 import ctypes
 import os
@@ -43,7 +43,8 @@ ACTS = {"silu": READY_ACT_SILU, "gelu_tanh": READY_ACT_GELU_TANH, "relu": READY_
 
 # Every symbol include/ready.h declares.
 EXPORTS = ("readyPlanCreate", "readyPlanDestroy", "readyWorkspaceSize", "readyWorkspaceInit",
-           "readyStateReader", "readyStateReaderProfiled", "readyStatusString", "readyVersion")
+           "readyStateReader", "readyStateReaderProfiled", "readyVerifyStates", "readyStatusString",
+           "readyVersion")
 READY_STAGES = 4
 
 
@@ -62,6 +63,11 @@ class readyShape(ctypes.Structure):
 
 
 class readyStates(ctypes.Structure):
+    _fields_ = [("base", ctypes.c_void_p), ("stride_b", ctypes.c_int64), ("stride_p", ctypes.c_int64),
+                ("stride_l", ctypes.c_int64), ("stride_h", ctypes.c_int64)]
+
+
+class readyVerifyBuffer(ctypes.Structure):
     _fields_ = [("base", ctypes.c_void_p), ("stride_b", ctypes.c_int64), ("stride_p", ctypes.c_int64),
                 ("stride_l", ctypes.c_int64), ("stride_h", ctypes.c_int64)]
 
@@ -100,6 +106,9 @@ def load():
     lib.readyStateReader.restype = ctypes.c_int
     lib.readyStateReaderProfiled.argtypes = lib.readyStateReader.argtypes + [P(ctypes.c_void_p)]
     lib.readyStateReaderProfiled.restype = ctypes.c_int
+    lib.readyVerifyStates.argtypes = [ctypes.c_int32] * 6 + [ctypes.c_void_p] * 5 + [P(readyVerifyBuffer),
+                                                                      ctypes.c_void_p]
+    lib.readyVerifyStates.restype = ctypes.c_int
     lib.readyStatusString.argtypes = [ctypes.c_int]
     lib.readyStatusString.restype = ctypes.c_char_p
     lib.readyVersion.argtypes = []
@@ -159,6 +168,36 @@ def readyStateReaderProfiled(plan, states, accept_idx, h, weights, outputs, work
 
 
 # ------------------------------------------------------------ torch wrapper
+
+def readyVerifyStates(B, P, L, H, state_dtype, kv_dtype, state_t, k, v, alpha, beta, out, stream):
+    return load().readyVerifyStates(B, P, L, H, state_dtype, kv_dtype, state_t, k, v, alpha, beta,
+                                    ctypes.byref(out), stream)
+
+
+def verify_states(state_t, k, v, alpha, beta, out, H, stream=None):
+    """Write the verify block's per-position states into `out` (torch tensors).
+
+    state_t [B][L*H][128][128]; k, v [B][P-1][L*H][128]; alpha, beta fp32
+    [B][P-1][L*H]; out [B][P][L][H][128][128] (any outer strides), the same
+    dtype as state_t.  P = out.shape[1]; L = out.shape[2] layers are written.
+    """
+    import torch
+    if out.dim() != 6 or state_t.dim() != 4:
+        raise ReadyError(READY_ERR_BAD_SHAPE, "out must be [B][P][L][H][128][128], state_t [B][L*H][128][128]")
+    B, P, L = out.shape[0], out.shape[1], out.shape[2]
+    dt = {torch.float32: READY_F32, torch.bfloat16: READY_BF16}
+    if out.dtype != state_t.dtype or state_t.dtype not in dt or (P > 1 and k.dtype not in dt):
+        raise ReadyError(READY_ERR_UNSUPPORTED_DTYPE, "verify_states dtypes")
+    st = out.stride()
+    buf = readyVerifyBuffer(base=out.data_ptr(), stride_b=st[0], stride_p=st[1], stride_l=st[2], stride_h=st[3])
+    if stream is None:
+        stream = torch.cuda.current_stream(out.device).cuda_stream
+    kv_dt = dt[k.dtype] if P > 1 else READY_F32
+    code = readyVerifyStates(B, P, L, H, dt[state_t.dtype], kv_dt, state_t.data_ptr(), _ptr(k), _ptr(v),
+                             _ptr(alpha), _ptr(beta), buf, stream)
+    if code != READY_OK:
+        raise ReadyError(code, "readyVerifyStates")
+
 
 def make_shape(B, P, n, L_tot, L_sel, H, r, d, Hm, state_dtype="bf16", act_dtype="bf16",
                weight_dtype="bf16", act="silu", shared=False, state_eps=1e-6, h_eps=1e-6,

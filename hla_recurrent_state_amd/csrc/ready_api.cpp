@@ -500,6 +500,45 @@ readyStatus run_reader(const readyPlan* plan, const readyStates* states, const i
 
 }  // namespace
 
+readyStatus readyVerifyStates(int32_t B, int32_t P, int32_t L, int32_t H, int32_t state_dtype, int32_t kv_dtype,
+                              const void* state_t, const void* k, const void* v, const float* alpha,
+                              const float* beta, const readyVerifyBuffer* out, void* stream) {
+  if (!out) return READY_ERR_NULL_POINTER;
+  if (B < 0 || P < 1 || P > 64 || L < 1 || H < 1 || (int64_t)L * H > 4096) return READY_ERR_BAD_SHAPE;
+  if (!dtype_ok(state_dtype) || !dtype_ok(kv_dtype)) return READY_ERR_UNSUPPORTED_DTYPE;
+  if (B == 0) return READY_OK;
+  if (!state_t || !out->base) return READY_ERR_NULL_POINTER;
+  if (P > 1 && (!k || !v || !alpha || !beta)) return READY_ERR_NULL_POINTER;
+  const void* vec_ptrs[] = {state_t, out->base, P > 1 ? k : nullptr, P > 1 ? v : nullptr};
+  for (const void* ptr : vec_ptrs)
+    if (ptr && !aligned16(ptr)) return READY_ERR_MISALIGNED;
+  const size_t ss = dsize(state_dtype), ks = dsize(kv_dtype);
+  const int64_t strides[4] = {out->stride_b, out->stride_p, out->stride_l, out->stride_h};
+  for (int64_t st : strides) {
+    if (st < 0) return READY_ERR_BAD_SHAPE;
+    if ((st * (int64_t)ss) % 16 != 0) return READY_ERR_MISALIGNED;
+  }
+  const int64_t M = (int64_t)L * H, steps = P - 1;
+  const int64_t span = (int64_t)(B - 1) * out->stride_b + (int64_t)(P - 1) * out->stride_p +
+                       (int64_t)(L - 1) * out->stride_l + (int64_t)(H - 1) * out->stride_h + READY_TILE_ELEMS;
+  const Range r_out = range_of(out->base, (size_t)span * ss);
+  const Range inputs[] = {range_of(state_t, (size_t)B * M * READY_TILE_ELEMS * ss),
+                          range_of(k, steps ? (size_t)B * steps * M * READY_TILE * ks : 0),
+                          range_of(v, steps ? (size_t)B * steps * M * READY_TILE * ks : 0),
+                          range_of(alpha, steps ? (size_t)B * steps * M * 4 : 0),
+                          range_of(beta, steps ? (size_t)B * steps * M * 4 : 0)};
+  for (const Range& in : inputs)
+    if (overlap(r_out, in)) return READY_ERR_ALIASING;
+  if ((int64_t)B * M > 0x7fffffff) return READY_ERR_BAD_SHAPE;
+
+  VerifyArgs a;
+  memset(&a, 0, sizeof(a));
+  a.state_t = state_t; a.k = k; a.v = v; a.alpha = alpha; a.beta = beta; a.out = out->base;
+  a.sb = out->stride_b; a.sp = out->stride_p; a.sl = out->stride_l; a.sh = out->stride_h;
+  a.B = B; a.P = P; a.M = (int)M; a.H = H;
+  return ready_launch_verify(a, state_dtype, kv_dtype, (hipStream_t)stream) == hipSuccess ? READY_OK : READY_ERR_HIP;
+}
+
 readyStatus readyWorkspaceInit(const readyPlan* plan, void* workspace, size_t workspace_bytes, void* stream) {
   if (!plan || !workspace) return READY_ERR_NULL_POINTER;
   if (((uintptr_t)workspace & 255u) != 0) return READY_ERR_MISALIGNED;

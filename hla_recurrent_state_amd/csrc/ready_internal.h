@@ -110,6 +110,20 @@ struct FastArgs {
 #define READY_TICKET_GROUPS 32    // state-tile ticket counters
 #define READY_ACC_LDS 1024        // accept indices staged in LDS
 
+// Verify-state producer: one workgroup per (sequence, pair)
+struct VerifyArgs {
+  const void* state_t;             // [B][M][128][128] state dtype
+  const void* k;                   // [B][P-1][M][128] kv dtype
+  const void* v;                   // [B][P-1][M][128] kv dtype
+  const float* alpha;              // [B][P-1][M]
+  const float* beta;               // [B][P-1][M]
+  void* out;                       // verify buffer, state dtype
+  int64_t sb, sp, sl, sh;          // its element strides
+  int B, P, M, H;
+};
+READY_HIDDEN hipError_t ready_launch_verify(const VerifyArgs& a, int state_dt, int kv_dt, hipStream_t s);
+READY_HIDDEN size_t ready_verify_lds(int P);
+
 enum { EPI_PARTIAL = 0, EPI_BIAS_ACT = 1, EPI_RESID = 2 };
 
 // Y[rho][c] = sum_k X[rho][k] W[c][k] over rows rho < R, columns c < N,

@@ -218,6 +218,47 @@ readyStatus readyStateReaderProfiled(const readyPlan* plan, const readyStates* s
                                      void* workspace, size_t workspace_bytes, void* stream,
                                      void* const* events);
 
+/*
+ * Verify buffer written by readyVerifyStates: element [b][p][l][a][v][k] at
+ * base + b*stride_b + p*stride_p + l*stride_l + a*stride_h + v*128 + k, the
+ * same layout readyStates describes for reading.
+ */
+typedef struct readyVerifyBuffer {
+  void* base;
+  int64_t stride_b, stride_p, stride_l, stride_h;
+} readyVerifyBuffer;
+
+/*
+ * Verify-state producer, the step just upstream of the gather: for every
+ * sequence b and layer-head pair m = l*H + a, write the P per-position states
+ * of the verify block into layers 0 .. L-1 of the verify buffer:
+ *   S_{t+0} = S_t                                           (a bit copy)
+ *   S_{t+p} = alpha_p S_{t+p-1} + beta_p (v_p - alpha_p S_{t+p-1} k_p) k_p^T,
+ *             p = 1 .. P-1
+ * i.e. S_{t+p-1} A_p + B_p with A_p = alpha_p (I - beta_p k_p k_p^T),
+ * B_p = beta_p v_p k_p^T: the gated delta rule (arXiv text, Appendix D.1),
+ * applied to the positions of one verify step (section 3.1 "Drafting,
+ * verification, and commitment"); Proposition 2 (Appendix A.2) writes the
+ * same states as S_t P_j + W_j.
+ *   B >= 0 (0 is a no-op), 1 <= P <= 64, L >= 1, H >= 1, L * H <= 4096.
+ *   state_dtype (S_t and the buffer) and kv_dtype (k, v): READY_F32 or
+ *   READY_BF16.  Arithmetic is fp32: the chain continues in fp32 and each
+ *   state is rounded to state_dtype (nearest even) only when stored.
+ *   state_t  device [B][L*H][128][128], value-by-key, 16-byte aligned.
+ *   k, v     device [B][P-1][L*H][128]; entry [b][p-1] drives step p.  May be
+ *            NULL when P = 1.  16-byte aligned.
+ *   alpha, beta  device fp32 [B][P-1][L*H] (decay gate and write strength);
+ *            may be NULL when P = 1.
+ *   out      the verify buffer (its base and outer strides keep every tile
+ *            16-byte aligned); written, must not overlap any input.
+ * Asynchronous on `stream`; allocates and synchronises nothing.  Returns
+ * READY_ERR_NULL_POINTER, READY_ERR_BAD_SHAPE, READY_ERR_UNSUPPORTED_DTYPE,
+ * READY_ERR_MISALIGNED, READY_ERR_ALIASING or READY_ERR_HIP.
+ */
+readyStatus readyVerifyStates(int32_t B, int32_t P, int32_t L, int32_t H, int32_t state_dtype, int32_t kv_dtype,
+                              const void* state_t, const void* k, const void* v, const float* alpha,
+                              const float* beta, const readyVerifyBuffer* out, void* stream);
+
 /* Static, human-readable name of a status code. */
 const char* readyStatusString(readyStatus status);
 

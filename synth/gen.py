@@ -254,6 +254,42 @@ def make(cfg="tiny", seed=0, states=True, nthreads=0, **overrides):
                   u=_store(u, wd), v=_store(v, wd), w1=_store(w1, wd), w2=_store(w2, wd))
 
 
+@dataclasses.dataclass
+class VerifyInputs:
+    """Inputs of one verify-state producer call (stored values)."""
+    B: int
+    P: int
+    L: int
+    H: int
+    state_dtype: str
+    kv_dtype: str
+    state_t: np.ndarray   # [B][L*H][128][128] committed states S_t
+    k: np.ndarray         # [B][P-1][L*H][128] unit-norm keys of steps 1 .. P-1
+    v: np.ndarray         # [B][P-1][L*H][128]
+    alpha: np.ndarray     # [B][P-1][L*H] fp32 decay gates
+    beta: np.ndarray      # [B][P-1][L*H] fp32 write strengths
+
+
+def make_verify(B=2, P=8, L=2, H=3, t=16, state_dtype="bf16", kv_dtype="bf16", seed=0, alpha_lo=0.9):
+    """Seeded inputs for the verify-state producer: S_t from the fp32 gated
+    delta rule run t steps from zero (stored in state_dtype), and the block's
+    steps drawn like the rule's own inputs (keys k = g / |g| with g ~ N(0, I),
+    values ~ N(0, 1), alpha ~ U(alpha_lo, 1), beta ~ U(0, 1))."""
+    cfg = _shape("verify", B=B, P=1, layer_ids=tuple(range(L)), H=H, t=t, alpha_lo=alpha_lo,
+                 state_dtype=state_dtype, act_dtype=state_dtype, weight_dtype=state_dtype)
+    buf = gdn_states(cfg, seed)                                      # [B][1][L][H][128][128]
+    st = np.ascontiguousarray(buf.reshape(B, L * H, 128, 128))
+    steps, M = P - 1, L * H
+    rng = _rng(seed, 11)
+    g = rng.standard_normal((B, steps, M, 128))
+    k = (g / np.linalg.norm(g, axis=-1, keepdims=True)).astype(np.float32)
+    v = rng.standard_normal((B, steps, M, 128), dtype=np.float32)
+    alpha = rng.uniform(alpha_lo, 1.0, (B, steps, M)).astype(np.float32)
+    beta = rng.uniform(0.0, 1.0, (B, steps, M)).astype(np.float32)
+    return VerifyInputs(B=B, P=P, L=L, H=H, state_dtype=state_dtype, kv_dtype=kv_dtype, state_t=st,
+                        k=_store(k, kv_dtype), v=_store(v, kv_dtype), alpha=alpha, beta=beta)
+
+
 def decode(x, dtype):
     """fp32 view of a stored array (bf16 bit patterns are widened)."""
     return bf16_bits_to_f32(x) if dtype == "bf16" else np.asarray(x, dtype=np.float32)

@@ -251,3 +251,78 @@ def test_workspace_init_validation():
     _, n = R.readyWorkspaceSize(plan)
     assert R.readyWorkspaceInit(plan, 1 << 40, n, None) == R.READY_OK
     R.readyPlanDestroy(plan)
+
+
+# ------------------------------------------------------------ readyVerifyStates
+
+def _verify_call(B=2, P=8, L=2, H=4, sdt=R.READY_BF16, kdt=R.READY_BF16, mutate=None):
+    """Arguments of a well-formed call on fake, disjoint, aligned addresses;
+    `mutate` breaks one of them.  A call that passed validation would launch,
+    so every case here must be rejected (or have B = 0)."""
+    lib = _lib()
+    M = L * H
+    base = 1 << 40
+    es = 2 if sdt == R.READY_BF16 else 4
+    a = {"state_t": base, "k": base + (1 << 34), "v": base + (2 << 34), "alpha": base + (3 << 34),
+         "beta": base + (4 << 34)}
+    tile = 128 * 128
+    out = R.readyVerifyBuffer(base=base + (5 << 34), stride_b=P * L * H * tile, stride_p=L * H * tile,
+                              stride_l=H * tile, stride_h=tile)
+    a["out"] = out
+    a["B"], a["P"], a["L"], a["H"], a["sdt"], a["kdt"] = B, P, L, H, sdt, kdt
+    if mutate:
+        mutate(a)
+    return lib.readyVerifyStates(a["B"], a["P"], a["L"], a["H"], a["sdt"], a["kdt"], a["state_t"], a["k"], a["v"],
+                                 a["alpha"], a["beta"], ctypes.byref(a["out"]) if a["out"] is not None else None,
+                                 None)
+
+
+def test_verify_zero_batch_is_ok():
+    assert _verify_call(B=0) == R.READY_OK
+
+
+@pytest.mark.parametrize("kw", [dict(P=0), dict(P=65), dict(L=0), dict(H=0), dict(L=64, H=65), dict(B=-1)])
+def test_verify_rejects_bad_shapes(kw):
+    assert _verify_call(**kw) == R.READY_ERR_BAD_SHAPE
+
+
+def test_verify_rejects_bad_dtype():
+    assert _verify_call(sdt=7) == R.READY_ERR_UNSUPPORTED_DTYPE
+    assert _verify_call(kdt=-1) == R.READY_ERR_UNSUPPORTED_DTYPE
+
+
+def test_verify_null_pointers():
+    for field in ("state_t", "k", "v", "alpha", "beta", "out"):
+        def m(a, field=field):
+            a[field] = None
+        assert _verify_call(mutate=m) == R.READY_ERR_NULL_POINTER, field
+
+    def m(a):
+        a["out"].base = None
+    assert _verify_call(mutate=m) == R.READY_ERR_NULL_POINTER
+
+
+def test_verify_misaligned():
+    for field in ("state_t", "k", "v"):
+        def m(a, field=field):
+            a[field] += 2
+        assert _verify_call(mutate=m) == R.READY_ERR_MISALIGNED, field
+
+    def stride(a):
+        a["out"].stride_h += 3
+    assert _verify_call(mutate=stride) == R.READY_ERR_MISALIGNED
+
+    def negative(a):
+        a["out"].stride_p = -a["out"].stride_p
+    assert _verify_call(mutate=negative) == R.READY_ERR_BAD_SHAPE
+
+
+def test_verify_aliasing():
+    for field in ("state_t", "k", "alpha"):
+        def m(a, field=field):
+            a["out"].base = a[field]
+        assert _verify_call(mutate=m) == R.READY_ERR_ALIASING, field
+
+    def inside(a):
+        a["state_t"] = a["out"].base + 7 * 128 * 128 * 2   # an input inside the buffer's span
+    assert _verify_call(mutate=inside) == R.READY_ERR_ALIASING
