@@ -530,6 +530,90 @@ def run_sweeps(args, hip, torch, R, synth):
     return out
 
 
+def run_producer(args, hip, torch, R, synth, seed=0):
+    """The verify-state producer at the batched shape (B = 64 sequences,
+    32 layer-head pairs, P = 8 positions, bf16 states, keys and values):
+    cold and back-to-back time of one call, against its algorithmic bytes
+    (S_t, k, v, alpha, beta read once; the P states written once) and a plain
+    copy of the same byte count."""
+    from synth.device import tensor
+    device = torch.device("cuda:0")
+    B, P, L, H = 64, 8, 2, 16
+    M, steps = L * H, P - 1
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    # timing inputs drawn on the device (the producer's work does not depend on
+    # the values); parity is in tests/test_gpu_verify.py
+    st = (torch.randn((B, M, 128, 128), generator=g, device=device) / 128).to(torch.bfloat16)
+    k = torch.nn.functional.normalize(torch.randn((B, steps, M, 128), generator=g, device=device), dim=-1)
+    k = k.to(torch.bfloat16)
+    v = torch.randn((B, steps, M, 128), generator=g, device=device).to(torch.bfloat16)
+    al = 0.9 + 0.1 * torch.rand((B, steps, M), generator=g, device=device)
+    be = torch.rand((B, steps, M), generator=g, device=device)
+    out = torch.empty((B, P, L, H, 128, 128), dtype=torch.bfloat16, device=device)
+    stream = torch.cuda.current_stream(device).cuda_stream
+    lib = R.load()
+    buf = R.readyVerifyBuffer(base=out.data_ptr(), stride_b=out.stride(0), stride_p=out.stride(1),
+                              stride_l=out.stride(2), stride_h=out.stride(3))
+    cargs = (B, P, L, H, R.READY_BF16, R.READY_BF16, st.data_ptr(), k.data_ptr(), v.data_ptr(), al.data_ptr(),
+             be.data_ptr(), ctypes.byref(buf), stream)
+
+    def call():
+        code = lib.readyVerifyStates(*cargs)
+        if code != 0:
+            raise R.ReadyError(code, "producer")
+
+    K = args.config_steps
+    flush = torch.empty(128 * 1024 * 1024, dtype=torch.float32, device=device)
+    for _ in range(3):
+        call()
+    torch.cuda.synchronize(device)
+    starts = [hip.event() for _ in range(K)]
+    ends = [hip.event() for _ in range(K)]
+    for i in range(K):
+        flush.add_(1.0)
+        hip.record(starts[i], stream)
+        call()
+        hip.record(ends[i], stream)
+    torch.cuda.synchronize(device)
+    cold = [1000.0 * hip.ms(starts[i], ends[i]) for i in range(K)]
+    a, b = hip.event(), hip.event()
+    hip.record(a, stream)
+    for _ in range(K):
+        call()
+    hip.record(b, stream)
+    torch.cuda.synchronize(device)
+    warm = 1000.0 * hip.ms(a, b) / K
+    alg = B * M * 128 * 128 * 2 + 2 * B * steps * M * 128 * 2 + 2 * B * steps * M * 4 + B * P * M * 128 * 128 * 2
+    half = alg // 2
+    src = torch.empty(half, dtype=torch.uint8, device=device).fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize(device)
+    hip.record(a, stream)
+    for _ in range(K):
+        dst.copy_(src)
+    hip.record(b, stream)
+    torch.cuda.synchronize(device)
+    copy_warm = 1000.0 * hip.ms(a, b) / K
+    for e in starts + ends + [a, b]:
+        hip.destroy(e)
+    p50 = pct(cold, 50)
+    return {
+        "workload": "verify-state producer: B=64, 32 layer-head pairs, P=8 positions (7 gated delta rule "
+                    "steps), bf16 states, keys and values, fp32 gates",
+        "kernel": "k_verify_states",
+        "algorithmic_bytes": alg,
+        "cold_us": {"p10": round(pct(cold, 10), 2), "p50": round(p50, 2), "p90": round(pct(cold, 90), 2)},
+        "warm_mean_us": round(warm, 2),
+        "warm_GBps": round(alg / (warm * 1e-6) / 1e9, 1),
+        "warm_frac_of_hbm_peak": round(alg / (warm * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+        "same_bytes_copy_warm_us": round(copy_warm, 2),
+        "same_bytes_copy_warm_GBps": round(2 * half / (copy_warm * 1e-6) / 1e9, 1),
+    }
+
+
 # ---------------------------------------------------------------- CPU oracle baseline
 
 def cpu_baseline(bat, budget_s):
@@ -718,6 +802,7 @@ def main():
             out["configs"][name] = run_config(name, args, hip, torch, R, synth)
     if not args.no_sweeps:
         out["sweeps"] = run_sweeps(args, hip, torch, R, synth)
+        out["producer"] = run_producer(args, hip, torch, R, synth)
     ok = True
     if not args.no_cpu:
         base, rep = cpu_baseline(bat, args.cpu_budget)
