@@ -269,3 +269,66 @@ def state_reader(buf, accept_idx, layer_ids, H, h, Wq, U, V, W1, W2,
             dh[b, j] = mlp(f[b, j], W1, b1, W2, b2, act)
     return {"G": G, "ell": ell, "T": T, "z": z, "q": q, "u": u, "f": f,
             "dh": dh, "h_new": h + dh}
+
+
+# ---------------------------------------------------------------------------
+# Several readers sharing one gather.
+# arXiv text, section 4, "Number of injections" and Table 5: the drafter may
+# carry readers in its draft layers (0, 2, 4) or in all five instead of only
+# in the final one.
+# Reading: every reader is a complete reader (steps 3-5) with its own W_q, U,
+# V, gain, W1, b1, W2, b2, fed with the draft representations h of its own
+# layer; steps 1-2 (the committed states, S_bar and ell) depend only on the
+# target's states and are the same for all of them, so they are done once.
+# ---------------------------------------------------------------------------
+
+
+def multi_reader(buf, accept_idx, layer_ids, H, hs, readers, act="silu",
+                 state_eps=1e-6, h_eps=1e-6, shared=False, seqs=None):
+    """Run steps 1-2 once and steps 3-5 for each reader, float64.
+
+    hs: list over readers of h [B][n][d] (each reader's own injection site).
+    readers: list of dicts with Wq, U, V, W1, W2 and optionally gamma, b1, b2
+    (layouts as in state_reader).
+    Returns {"G": gathered, "ell": [B][M], "readers": [per-reader dicts with
+    T, z, q, u, f, dh, h_new as in state_reader]}.
+    """
+    B = hs[0].shape[0]
+    M = len(layer_ids) * H
+    d_v, d_k = buf.shape[4], buf.shape[5]
+    if seqs is None:
+        seqs = range(B)
+    G = np.full((B, M, d_v, d_k), np.nan)
+    S_bar = np.full((B, M, d_v, d_k), np.nan)
+    ell = np.full((B, M), np.nan)
+    # steps 1-2, once
+    for b in seqs:
+        G[b] = gather_committed(buf[b:b + 1], accept_idx[b:b + 1], layer_ids, H)[0]
+        for m in range(M):
+            S_bar[b, m], ell[b, m] = prepare_state(G[b, m], state_eps)
+    # steps 3-5, per reader
+    outs = []
+    for h, w in zip(hs, readers):
+        n, d = h.shape[1], h.shape[2]
+        Wq, U, V = w["Wq"], w["U"], w["V"]
+        r = Wq.shape[0] if shared else Wq.shape[1]
+        F = M * (r + 1)
+        T = np.full((B, M, r, d_k), np.nan)
+        z = np.full((B, n, M, r), np.nan)
+        q = np.full((B, n, M, d_k), np.nan)
+        u = np.full((B, n, M, r), np.nan)
+        f = np.full((B, n, F), np.nan)
+        dh = np.full((B, n, d), np.nan)
+        for b in seqs:
+            for m in range(M):
+                T[b, m] = project_state(pair_params(V, m, shared), S_bar[b, m])
+            for j in range(n):
+                h_hat = rmsnorm(h[b, j], w.get("gamma"), h_eps)
+                for m in range(M):
+                    z[b, j, m], q[b, j, m] = query(pair_params(Wq, m, shared),
+                                                   pair_params(U, m, shared), h_hat)
+                    u[b, j, m] = readout(T[b, m], q[b, j, m], d_k)
+                f[b, j] = pack([u[b, j, m] for m in range(M)], [ell[b, m] for m in range(M)])
+                dh[b, j] = mlp(f[b, j], w["W1"], w.get("b1"), w["W2"], w.get("b2"), act)
+        outs.append({"T": T, "z": z, "q": q, "u": u, "f": f, "dh": dh, "h_new": h + dh})
+    return {"G": G, "ell": ell, "readers": outs}

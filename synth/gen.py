@@ -254,6 +254,28 @@ def make(cfg="tiny", seed=0, states=True, nthreads=0, **overrides):
                   u=_store(u, wd), v=_store(v, wd), w1=_store(w1, wd), w2=_store(w2, wd))
 
 
+def make_readers(inp, n_readers, seed=0):
+    """Weights and draft representations of n_readers readers that share the
+    committed states of `inp` (one reader per injection site).  Reader 0 is
+    inp's own (h, wq, u, v, w1, w2); the others are drawn independently with
+    the same distributions.  Returns a list of dicts of stored arrays."""
+    cfg = inp.cfg
+    M, r, d, dk, dv, F, Hm = cfg.M, cfg.r, cfg.d, cfg.d_k, cfg.d_v, cfg.F, cfg.Hm
+    pre = () if cfg.shared else (M,)
+    wd, ad = cfg.weight_dtype, cfg.act_dtype
+    out = [dict(h=inp.h, wq=inp.wq, u=inp.u, v=inp.v, w1=inp.w1, w2=inp.w2)]
+    for i in range(1, n_readers):
+        g = lambda tag: _rng(seed, 100 * i + tag)
+        out.append(dict(
+            h=_store(g(2).standard_normal((cfg.B, cfg.n, d), dtype=np.float32), ad),
+            wq=_store(g(3).standard_normal(pre + (r, d), dtype=np.float32) / np.float32(np.sqrt(d)), wd),
+            u=_store(g(4).standard_normal(pre + (r, dk), dtype=np.float32) / np.float32(np.sqrt(r)), wd),
+            v=_store(g(5).standard_normal(pre + (dv, r), dtype=np.float32) / np.float32(np.sqrt(dv)), wd),
+            w1=_store(g(6).standard_normal((Hm, F), dtype=np.float32) / np.float32(np.sqrt(F)), wd),
+            w2=_store(g(7).standard_normal((d, Hm), dtype=np.float32) / np.float32(np.sqrt(Hm)), wd)))
+    return out
+
+
 @dataclasses.dataclass
 class VerifyInputs:
     """Inputs of one verify-state producer call (stored values)."""

@@ -314,3 +314,54 @@ def test_state_reader_seq_subset_leaves_others_nan():
     part = R.state_reader(**inp, seqs=[1])
     assert np.array_equal(part["dh"][1], full["dh"][1])
     assert np.all(np.isnan(part["dh"][0])) and np.all(np.isnan(part["dh"][2]))
+
+
+# ---------------------------------------------------------------- several readers, one gather
+
+def _readers(seed, n_readers, base):
+    """Per-reader weights and h of the same shapes as `base` (_tiny_inputs)."""
+    rng = np.random.default_rng(seed)
+    readers, hs = [], []
+    for _ in range(n_readers):
+        readers.append({k: rng.standard_normal(base[k].shape) for k in ("Wq", "U", "V", "W1", "W2")})
+        hs.append(rng.standard_normal(base["h"].shape))
+    return readers, hs
+
+
+@pytest.mark.parametrize("shared", [False, True])
+def test_multi_reader_each_reader_matches_vectorised_reading(shared):
+    inp = _tiny_inputs(8, shared=shared)
+    readers, hs = _readers(9, 3, inp)
+    got = R.multi_reader(inp["buf"], inp["accept_idx"], inp["layer_ids"], inp["H"], hs, readers,
+                         shared=shared)
+    for i, (w, h) in enumerate(zip(readers, hs)):
+        want = _einsum_reader(inp["buf"], inp["accept_idx"], inp["layer_ids"], inp["H"], h, w["Wq"], w["U"],
+                              w["V"], w["W1"], w["W2"], shared=shared)
+        assert np.allclose(got["ell"], want["ell"], rtol=1e-12, atol=1e-12)
+        for key in ("T", "z", "q", "u", "f", "dh"):
+            assert np.allclose(got["readers"][i][key], want[key], rtol=1e-12, atol=1e-12), (i, key)
+        assert np.allclose(got["readers"][i]["h_new"], h + want["dh"], rtol=1e-12, atol=1e-12)
+
+
+def test_multi_reader_shares_the_gather_and_orders_readers():
+    inp = _tiny_inputs(10)
+    readers, hs = _readers(11, 3, inp)
+    args = (inp["buf"], inp["accept_idx"], inp["layer_ids"], inp["H"])
+    got = R.multi_reader(*args, hs, readers)
+    # the gathered states are the brute-force selection of the single reader
+    single = R.state_reader(*args, hs[0], readers[0]["Wq"], readers[0]["U"], readers[0]["V"],
+                            readers[0]["W1"], readers[0]["W2"])
+    assert np.array_equal(got["G"], single["G"])
+    assert np.array_equal(got["ell"], single["ell"])
+    # every ell column of every reader's f is the shared ell
+    M, r = got["ell"].shape[1], got["readers"][0]["u"].shape[3]
+    for out in got["readers"]:
+        for j in range(hs[0].shape[1]):
+            assert np.array_equal(out["f"][:, j].reshape(-1, M, r + 1)[:, :, r], got["ell"])
+    # reversing the readers reverses the outputs
+    rev = R.multi_reader(*args, hs[::-1], readers[::-1])
+    for i in range(3):
+        assert np.array_equal(rev["readers"][i]["dh"], got["readers"][2 - i]["dh"])
+    # two identical readers on identical h give identical outputs
+    twin = R.multi_reader(*args, [hs[0], hs[0]], [readers[0], readers[0]])
+    assert np.array_equal(twin["readers"][0]["dh"], twin["readers"][1]["dh"])
