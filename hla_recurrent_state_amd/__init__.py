@@ -5,10 +5,12 @@ kernels of libready.so.  If the library is missing, loading raises
 ReadyError -- there is no fallback path.
 
 Low-level names mirror the C functions (readyPlanCreate, readyWorkspaceSize,
-readyStateReader, readyVerifyStates, readyPlanDestroy, readyStatusString,
-readyVersion) and the C structs (readyShape, readyStates, readyWeights,
+readyStateReader, readyPrepSize, readyStatePrepare, readyStateApply,
+readyVerifyStates, readyPlanDestroy, readyStatusString, readyVersion) and the C structs (readyShape, readyStates, readyWeights,
 readyOutputs, readyVerifyBuffer).  StateReader and verify_states wrap them for
-torch tensors: they forward data_ptr() values and the current HIP stream.
+torch tensors: they forward data_ptr() values and the current HIP stream
+(StateReader.prepare / StateReader.apply for several readers sharing one
+gather).
 """
 import ctypes
 import os
@@ -31,6 +33,8 @@ READY_ERR_ACCEPT_IDX = 9
 READY_ERR_OUT_OF_HOST_MEMORY = 10
 READY_ERR_SYNC_TIMEOUT = 11
 READY_ERR_WORKSPACE_UNINIT = 12
+READY_ERR_UNSUPPORTED = 13
+READY_MAX_INJ = 8
 
 READY_F32 = 0
 READY_BF16 = 1
@@ -43,8 +47,8 @@ ACTS = {"silu": READY_ACT_SILU, "gelu_tanh": READY_ACT_GELU_TANH, "relu": READY_
 
 # Every symbol include/ready.h declares.
 EXPORTS = ("readyPlanCreate", "readyPlanDestroy", "readyWorkspaceSize", "readyWorkspaceInit",
-           "readyStateReader", "readyStateReaderProfiled", "readyVerifyStates", "readyStatusString",
-           "readyVersion")
+           "readyStateReader", "readyStateReaderProfiled", "readyPrepSize", "readyStatePrepare",
+           "readyStateApply", "readyVerifyStates", "readyStatusString", "readyVersion")
 READY_STAGES = 4
 
 
@@ -106,6 +110,17 @@ def load():
     lib.readyStateReader.restype = ctypes.c_int
     lib.readyStateReaderProfiled.argtypes = lib.readyStateReader.argtypes + [P(ctypes.c_void_p)]
     lib.readyStateReaderProfiled.restype = ctypes.c_int
+    lib.readyPrepSize.argtypes = [ctypes.c_void_p, ctypes.c_int32, P(ctypes.c_size_t)]
+    lib.readyPrepSize.restype = ctypes.c_int
+    lib.readyStatePrepare.argtypes = [ctypes.c_void_p, P(readyStates), ctypes.c_void_p, ctypes.c_int32,
+                                      P(readyWeights), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                      ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_size_t,
+                                      ctypes.c_void_p]
+    lib.readyStatePrepare.restype = ctypes.c_int
+    lib.readyStateApply.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
+                                    ctypes.c_void_p, P(readyWeights), P(readyOutputs), ctypes.c_void_p,
+                                    ctypes.c_size_t, ctypes.c_void_p]
+    lib.readyStateApply.restype = ctypes.c_int
     lib.readyVerifyStates.argtypes = [ctypes.c_int32] * 6 + [ctypes.c_void_p] * 5 + [P(readyVerifyBuffer),
                                                                       ctypes.c_void_p]
     lib.readyVerifyStates.restype = ctypes.c_int
@@ -165,6 +180,25 @@ def readyStateReaderProfiled(plan, states, accept_idx, h, weights, outputs, work
     ev = (ctypes.c_void_p * (2 * READY_STAGES))(*[e for e in events])
     return load().readyStateReaderProfiled(plan, ctypes.byref(states), accept_idx, h, ctypes.byref(weights),
                                            ctypes.byref(outputs), workspace, workspace_bytes, stream, ev)
+
+
+def readyPrepSize(plan, n_inj):
+    """Returns (status, bytes) of the prepared-state buffer for n_inj readers."""
+    n = ctypes.c_size_t()
+    st = load().readyPrepSize(plan, n_inj, ctypes.byref(n))
+    return st, n.value
+
+
+def readyStatePrepare(plan, states, accept_idx, n_inj, inj_weights, gathered, logrms, dev_status, prep,
+                      prep_bytes, workspace, workspace_bytes, stream):
+    """Raw call; `inj_weights` is a ctypes array of n_inj readyWeights."""
+    return load().readyStatePrepare(plan, ctypes.byref(states), accept_idx, n_inj, inj_weights, gathered,
+                                    logrms, dev_status, prep, prep_bytes, workspace, workspace_bytes, stream)
+
+
+def readyStateApply(plan, prep, n_inj, inj, h, weights, outputs, workspace, workspace_bytes, stream):
+    return load().readyStateApply(plan, prep, n_inj, inj, h, ctypes.byref(weights), ctypes.byref(outputs),
+                                  workspace, workspace_bytes, stream)
 
 
 # ------------------------------------------------------------ torch wrapper
@@ -292,3 +326,57 @@ class StateReader:
             code = readyStateReaderProfiled(*args, events)
         if code != READY_OK:
             raise ReadyError(code, "readyStateReader")
+
+    # -------------------------------------------- several readers, one gather
+
+    def prep_size(self, n_inj):
+        code, n = readyPrepSize(self.plan, n_inj)
+        if code != READY_OK:
+            raise ReadyError(code, "readyPrepSize")
+        return n
+
+    def new_prep(self, n_inj, device):
+        """A prepared-state buffer for n_inj readers."""
+        import torch
+        return torch.empty(max(self.prep_size(n_inj), 256), dtype=torch.uint8, device=device)
+
+    def prepare(self, states, accept_idx, inj_weights, gathered, prep, logrms=None, dev_status=None,
+                workspace=None, stream=None):
+        """Steps 1-3 once for len(inj_weights) readers (dicts with at least
+        u and v); fills `prep` (from new_prep) for apply()."""
+        import torch
+        if states.dim() != 6:
+            raise ReadyError(READY_ERR_BAD_SHAPE, "states must be [B][P][L_tot][H][128][128]")
+        st = states.stride()
+        sd = readyStates(base=states.data_ptr(), stride_b=st[0], stride_p=st[1], stride_l=st[2],
+                         stride_h=st[3])
+        n_inj = len(inj_weights)
+        arr = (readyWeights * max(1, n_inj))(*[
+            readyWeights(**{k: _ptr(w.get(k)) for k in ("wq", "u", "v", "h_gamma", "w1", "b1", "w2", "b2")})
+            for w in inj_weights])
+        if workspace is None:
+            workspace = self.workspace(states.device)
+        if stream is None:
+            stream = torch.cuda.current_stream(states.device).cuda_stream
+        code = readyStatePrepare(self.plan, sd, accept_idx.data_ptr(), n_inj, arr, gathered.data_ptr(),
+                                 _ptr(logrms), _ptr(dev_status), prep.data_ptr(),
+                                 prep.numel() * prep.element_size(), workspace.data_ptr(),
+                                 workspace.numel() * workspace.element_size(), stream)
+        if code != READY_OK:
+            raise ReadyError(code, "readyStatePrepare")
+
+    def apply(self, prep, n_inj, inj, h, weights, out, delta=None, feat=None, dev_status=None,
+              workspace=None, stream=None):
+        """Steps 4-5 of reader `inj` on its own h, from a prepared buffer."""
+        import torch
+        wd = readyWeights(**{k: _ptr(weights.get(k)) for k in ("wq", "u", "v", "h_gamma", "w1", "b1", "w2", "b2")})
+        od = readyOutputs(gathered=None, out=_ptr(out), logrms=None, delta=_ptr(delta), feat=_ptr(feat),
+                          dev_status=_ptr(dev_status))
+        if workspace is None:
+            workspace = self.workspace(h.device)
+        if stream is None:
+            stream = torch.cuda.current_stream(h.device).cuda_stream
+        code = readyStateApply(self.plan, prep.data_ptr(), n_inj, inj, h.data_ptr(), wd, od,
+                               workspace.data_ptr(), workspace.numel() * workspace.element_size(), stream)
+        if code != READY_OK:
+            raise ReadyError(code, "readyStateApply")

@@ -107,6 +107,7 @@ const char* readyStatusString(readyStatus st) {
     case READY_ERR_OUT_OF_HOST_MEMORY: return "READY_ERR_OUT_OF_HOST_MEMORY";
     case READY_ERR_SYNC_TIMEOUT: return "READY_ERR_SYNC_TIMEOUT";
     case READY_ERR_WORKSPACE_UNINIT: return "READY_ERR_WORKSPACE_UNINIT";
+    case READY_ERR_UNSUPPORTED: return "READY_ERR_UNSUPPORTED";
   }
   return "READY_ERR_UNKNOWN";
 }
@@ -267,6 +268,80 @@ void reader_roles(FastArgs& a, int grid) {
   a.ntg = std::min(grid, READY_TICKET_GROUPS);
 }
 
+// FastArgs fields that depend only on the plan and the workspace: sizes,
+// work-item counts, workspace arrays and counters.  One reader (n_inj = 1),
+// every item kind (READY_MODE_FULL).
+void fast_common(const readyPlan* plan, char* wsb, FastArgs& a) {
+  const readyShape& s = plan->s;
+  memset(&a, 0, sizeof(a));
+  for (int l = 0; l < s.L_sel; ++l) a.slot[l] = plan->slot[l];
+  a.zpart = (float*)(wsb + plan->off_zpart);
+  a.hss = (float*)(wsb + plan->off_hss);
+  a.zfin = (float*)(wsb + plan->off_f);
+  a.pmat = (float*)(wsb + plan->off_pmat);
+  a.ell = (float*)(wsb + plan->off_ell);
+  a.abuf = (uint16_t*)(wsb + plan->off_a);
+  a.seq_invalid = (uint32_t*)(wsb + plan->off_flags);
+  uint32_t* ctr = (uint32_t*)(wsb + plan->off_ctr);
+  a.counters = ctr; a.n_counters = plan->n_counters;
+  a.magic = READY_WS_MAGIC ^ (uint32_t)plan->n_counters;
+  a.abort_flag = ctr + READY_CTR_STRIDE;
+  a.done = ctr + 2 * READY_CTR_STRIDE;
+  a.zcnt = ctr + READY_CTR_STRIDE * plan->c_zcnt;
+  a.zdone = ctr + READY_CTR_STRIDE * plan->c_zdone;
+  a.sdone = ctr + READY_CTR_STRIDE * plan->c_sdone;
+  a.adone = ctr + READY_CTR_STRIDE * plan->c_adone;
+  a.tk = ctr + READY_CTR_STRIDE * plan->c_tk;
+  a.aq = ctr + READY_CTR_STRIDE * plan->c_aq;
+  a.oq = ctr + READY_CTR_STRIDE * plan->c_oq;
+  a.n_z = plan->n_z; a.n_s = plan->n_s; a.n_a = plan->n_a; a.n_o = plan->n_o;
+  a.B = s.B; a.P = s.P; a.n = s.n; a.M = plan->M; a.H = s.H; a.r = s.r; a.d = s.d; a.F = plan->F;
+  a.Hm = s.Hm; a.R = plan->R; a.Nz = plan->Nz; a.shared = s.shared_params;
+  a.ksplit = plan->gz.ksplit; a.kchunk = plan->gz.kchunk; a.act = s.act;
+  a.state_eps = s.state_eps; a.h_eps = s.h_eps;
+  a.mode = READY_MODE_FULL;
+  a.n_inj = 1;
+}
+
+// Launch k_reader with the grid the GPU holds at once (every wait in the
+// kernel is for a workgroup that is already running).
+readyStatus launch_fast(const readyPlan* plan, FastArgs& a, hipStream_t strm, void* const* events) {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return READY_ERR_HIP;
+  const int per_cu = std::min(2, ready_reader_per_cu(plan->s.r, plan->small, plan->lds));
+  if (per_cu < 1 || cus < 1) return READY_ERR_HIP;
+  const int grid = per_cu * cus;
+  reader_roles(a, grid);
+  if (ready_launch_reader(a, plan->small, grid, strm, stage_events(events, 1)) != hipSuccess)
+    return READY_ERR_HIP;
+  // the other stages run inside the same kernel: their marks (if any) are
+  // recorded together after it
+  for (int i = 0; events && i < 2 * READY_STAGES; ++i)
+    if ((i < 2 || i > 3) && events[i] && hipEventRecord((hipEvent_t)events[i], strm) != hipSuccess)
+      return READY_ERR_HIP;
+  return READY_OK;
+}
+
+// Layout of the prepared-state buffer of several readers: P of every reader
+// [n_inj][B M][r][r] fp32, then ell [B M] fp32, then the invalid-sequence
+// flags [B] uint32, each section 256-byte aligned.
+struct PrepLayout {
+  size_t off_p, off_ell, off_flags, bytes;
+  int64_t p_stride;  // floats per reader
+};
+PrepLayout prep_layout(const readyPlan* plan, int n_inj) {
+  PrepLayout L;
+  const size_t BM = (size_t)plan->s.B * plan->M;
+  L.p_stride = (int64_t)BM * plan->s.r * plan->s.r;
+  L.off_p = 0;
+  L.off_ell = align_up(4 * (size_t)n_inj * (size_t)L.p_stride, 256);
+  L.off_flags = align_up(L.off_ell + 4 * BM, 256);
+  L.bytes = align_up(L.off_flags + 4 * (size_t)std::max(plan->s.B, 1), 256);
+  return L;
+}
+
 readyStatus run_reader(const readyPlan* plan, const readyStates* states, const int32_t* accept_idx,
                        const void* h, const readyWeights* w, const readyOutputs* o, void* workspace,
                        size_t workspace_bytes, void* stream, void* const* events) {
@@ -334,16 +409,13 @@ readyStatus run_reader(const readyPlan* plan, const readyStates* states, const i
   float* fbuf = (float*)(wsb + plan->off_f);
   float* abuf = (float*)(wsb + plan->off_a);
   int32_t* flags = (int32_t*)(wsb + plan->off_flags);
-  float* pmat = (float*)(wsb + plan->off_pmat);
-  float* ellw = (float*)(wsb + plan->off_ell);
 
   if (plan->fast) {
     FastArgs a;
-    memset(&a, 0, sizeof(a));
+    fast_common(plan, wsb, a);
     a.states = (const uint16_t*)states->base;
     a.sb = states->stride_b; a.sp = states->stride_p; a.sl = states->stride_l; a.sh = states->stride_h;
     a.accept_idx = accept_idx;
-    for (int l = 0; l < s.L_sel; ++l) a.slot[l] = plan->slot[l];
     a.h = (const uint16_t*)h;
     a.wq = (const uint16_t*)w->wq; a.u = (const uint16_t*)w->u; a.v = (const uint16_t*)w->v;
     a.gamma = (const uint16_t*)w->h_gamma;
@@ -351,43 +423,8 @@ readyStatus run_reader(const readyPlan* plan, const readyStates* states, const i
     a.w2 = (const uint16_t*)w->w2; a.b2 = (const uint16_t*)w->b2;
     a.gathered = (uint16_t*)o->gathered; a.out = (uint16_t*)o->out;
     a.logrms = o->logrms; a.delta = o->delta; a.feat = o->feat; a.dev_status = o->dev_status;
-    a.zpart = zpart; a.hss = hss; a.zfin = (float*)(wsb + plan->off_f); a.pmat = pmat; a.ell = ellw; a.abuf = (uint16_t*)abuf;
-    a.seq_invalid = (uint32_t*)flags;
-    uint32_t* ctr = (uint32_t*)(wsb + plan->off_ctr);
-    a.counters = ctr; a.n_counters = plan->n_counters;
-    a.magic = READY_WS_MAGIC ^ (uint32_t)plan->n_counters;
-    a.abort_flag = ctr + READY_CTR_STRIDE;
-    a.done = ctr + 2 * READY_CTR_STRIDE;
-    a.zcnt = ctr + READY_CTR_STRIDE * plan->c_zcnt;
-    a.zdone = ctr + READY_CTR_STRIDE * plan->c_zdone;
-    a.sdone = ctr + READY_CTR_STRIDE * plan->c_sdone;
-    a.adone = ctr + READY_CTR_STRIDE * plan->c_adone;
-    a.tk = ctr + READY_CTR_STRIDE * plan->c_tk;
-    a.aq = ctr + READY_CTR_STRIDE * plan->c_aq;
-    a.oq = ctr + READY_CTR_STRIDE * plan->c_oq;
-    a.n_z = plan->n_z; a.n_s = plan->n_s; a.n_a = plan->n_a; a.n_o = plan->n_o;
-    a.B = s.B; a.P = s.P; a.n = s.n; a.M = (int)M; a.H = s.H; a.r = s.r; a.d = (int)d; a.F = (int)F;
-    a.Hm = (int)Hm; a.R = (int)R; a.Nz = plan->Nz; a.shared = s.shared_params;
-    a.ksplit = plan->gz.ksplit; a.kchunk = plan->gz.kchunk; a.act = s.act;
-    a.state_eps = s.state_eps; a.h_eps = s.h_eps;
-    // the grid is what the GPU holds at once: every wait in the kernel is
-    // for a workgroup that is already running
-    int dev = 0, cus = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-      return READY_ERR_HIP;
-    const int per_cu = std::min(2, ready_reader_per_cu(s.r, plan->small, plan->lds));
-    if (per_cu < 1 || cus < 1) return READY_ERR_HIP;
-    const int grid = per_cu * cus;
-    reader_roles(a, grid);
-    if (ready_launch_reader(a, plan->small, grid, strm, stage_events(events, 1)) != hipSuccess)
-      return READY_ERR_HIP;
-    // the other stages run inside the same kernel: their marks (if any) are
-    // recorded together after it
-    for (int i = 0; events && i < 2 * READY_STAGES; ++i)
-      if ((i < 2 || i > 3) && events[i] && hipEventRecord((hipEvent_t)events[i], strm) != hipSuccess)
-        return READY_ERR_HIP;
-    return READY_OK;
+    a.u_inj[0] = a.u; a.v_inj[0] = a.v;
+    return launch_fast(plan, a, strm, events);
   }
 
   const int wvw = (int)(16 / ws);
@@ -564,6 +601,134 @@ readyStatus readyStateReaderProfiled(const readyPlan* plan, const readyStates* s
                                      void* workspace, size_t workspace_bytes, void* stream,
                                      void* const* events) {
   return run_reader(plan, states, accept_idx, h, w, o, workspace, workspace_bytes, stream, events);
+}
+
+// ---------------------------------------------------------------- several readers sharing one gather
+
+readyStatus readyPrepSize(const readyPlan* plan, int32_t n_inj, size_t* bytes) {
+  if (!plan || !bytes) return READY_ERR_NULL_POINTER;
+  if (!plan->fast) return READY_ERR_UNSUPPORTED;
+  if (n_inj < 1 || n_inj > READY_MAX_INJ) return READY_ERR_BAD_SHAPE;
+  *bytes = prep_layout(plan, n_inj).bytes;
+  return READY_OK;
+}
+
+readyStatus readyStatePrepare(const readyPlan* plan, const readyStates* states, const int32_t* accept_idx,
+                              int32_t n_inj, const readyWeights* inj_weights, void* gathered, float* logrms,
+                              int32_t* dev_status, void* prep, size_t prep_bytes, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  if (!plan || !states || !inj_weights) return READY_ERR_NULL_POINTER;
+  if (!plan->fast) return READY_ERR_UNSUPPORTED;
+  if (n_inj < 1 || n_inj > READY_MAX_INJ) return READY_ERR_BAD_SHAPE;
+  const readyShape& s = plan->s;
+  if (!states->base || !accept_idx || !gathered || !prep || !workspace) return READY_ERR_NULL_POINTER;
+  for (int i = 0; i < n_inj; ++i)
+    if (!inj_weights[i].u || !inj_weights[i].v) return READY_ERR_NULL_POINTER;
+  const PrepLayout L = prep_layout(plan, n_inj);
+  if (workspace_bytes < plan->ws_bytes || prep_bytes < L.bytes) return READY_ERR_WORKSPACE_TOO_SMALL;
+  if (!aligned16(states->base) || !aligned16(gathered)) return READY_ERR_MISALIGNED;
+  for (int i = 0; i < n_inj; ++i)
+    if (!aligned16(inj_weights[i].u) || !aligned16(inj_weights[i].v)) return READY_ERR_MISALIGNED;
+  if (((uintptr_t)workspace & 255u) != 0 || ((uintptr_t)prep & 255u) != 0) return READY_ERR_MISALIGNED;
+  const int64_t strides[4] = {states->stride_b, states->stride_p, states->stride_l, states->stride_h};
+  for (int64_t st : strides) {
+    if (st < 0) return READY_ERR_BAD_SHAPE;
+    if ((st * 2) % 16 != 0) return READY_ERR_MISALIGNED;
+  }
+  const size_t M = plan->M, mz = s.shared_params ? 1 : M;
+  const int64_t span = s.B == 0 ? 0 :
+                       (int64_t)(s.B - 1) * states->stride_b + (int64_t)(s.P - 1) * states->stride_p +
+                       (int64_t)(s.L_tot - 1) * states->stride_l + (int64_t)(s.H - 1) * states->stride_h +
+                       READY_TILE_ELEMS;
+  std::vector<Range> inputs;
+  inputs.push_back(range_of(states->base, (size_t)span * 2));
+  inputs.push_back(range_of(accept_idx, (size_t)s.B * 4));
+  for (int i = 0; i < n_inj; ++i) {
+    inputs.push_back(range_of(inj_weights[i].u, mz * s.r * READY_TILE * 2));
+    inputs.push_back(range_of(inj_weights[i].v, mz * READY_TILE * s.r * 2));
+  }
+  const Range outputs[] = {range_of(gathered, (size_t)s.B * M * READY_TILE_ELEMS * 2),
+                           range_of(logrms, logrms ? (size_t)s.B * M * 4 : 0),
+                           range_of(dev_status, dev_status ? 4 : 0), range_of(prep, L.bytes),
+                           range_of(workspace, plan->ws_bytes)};
+  const int n_out = (int)(sizeof(outputs) / sizeof(outputs[0]));
+  for (int i = 0; i < n_out; ++i) {
+    for (const Range& in : inputs)
+      if (overlap(outputs[i], in)) return READY_ERR_ALIASING;
+    for (int j = i + 1; j < n_out; ++j)
+      if (overlap(outputs[i], outputs[j])) return READY_ERR_ALIASING;
+  }
+  if (s.B == 0) return READY_OK;
+
+  char* pb = (char*)prep;
+  FastArgs a;
+  fast_common(plan, (char*)workspace, a);
+  a.mode = READY_MODE_PREPARE;
+  a.n_inj = n_inj;
+  a.states = (const uint16_t*)states->base;
+  a.sb = states->stride_b; a.sp = states->stride_p; a.sl = states->stride_l; a.sh = states->stride_h;
+  a.accept_idx = accept_idx;
+  for (int i = 0; i < n_inj; ++i) {
+    a.u_inj[i] = (const uint16_t*)inj_weights[i].u;
+    a.v_inj[i] = (const uint16_t*)inj_weights[i].v;
+  }
+  a.u = a.u_inj[0]; a.v = a.v_inj[0];
+  a.gathered = (uint16_t*)gathered; a.logrms = logrms; a.dev_status = dev_status;
+  a.pmat = (float*)(pb + L.off_p); a.p_inj_stride = L.p_stride;
+  a.ell = (float*)(pb + L.off_ell);
+  a.seq_invalid = (uint32_t*)(pb + L.off_flags);
+  return launch_fast(plan, a, (hipStream_t)stream, nullptr);
+}
+
+readyStatus readyStateApply(const readyPlan* plan, const void* prep, int32_t n_inj, int32_t inj, const void* h,
+                            const readyWeights* w, const readyOutputs* o, void* workspace, size_t workspace_bytes,
+                            void* stream) {
+  if (!plan || !w || !o) return READY_ERR_NULL_POINTER;
+  if (!plan->fast) return READY_ERR_UNSUPPORTED;
+  if (n_inj < 1 || n_inj > READY_MAX_INJ || inj < 0 || inj >= n_inj) return READY_ERR_BAD_SHAPE;
+  const readyShape& s = plan->s;
+  if (!prep || !h || !w->wq || !w->w1 || !w->w2 || !o->out || !workspace) return READY_ERR_NULL_POINTER;
+  const PrepLayout L = prep_layout(plan, n_inj);
+  if (workspace_bytes < plan->ws_bytes) return READY_ERR_WORKSPACE_TOO_SMALL;
+  const void* vec_ptrs[] = {h, w->wq, w->h_gamma, w->w1, w->w2, w->b2, o->out, o->delta, o->feat};
+  for (const void* ptr : vec_ptrs)
+    if (ptr && !aligned16(ptr)) return READY_ERR_MISALIGNED;
+  if (((uintptr_t)workspace & 255u) != 0 || ((uintptr_t)prep & 255u) != 0) return READY_ERR_MISALIGNED;
+  const size_t M = plan->M, R = plan->R, F = plan->F, Hm = s.Hm, d = s.d, mz = s.shared_params ? 1 : M;
+  const Range r_h = range_of(h, R * d * 2), r_out = range_of(o->out, R * d * 2);
+  const Range inputs[] = {range_of(prep, L.bytes), range_of(w->wq, mz * s.r * d * 2),
+                          range_of(w->h_gamma, w->h_gamma ? d * 2 : 0), range_of(w->w1, Hm * F * 2),
+                          range_of(w->b1, w->b1 ? Hm * 2 : 0), range_of(w->w2, d * Hm * 2),
+                          range_of(w->b2, w->b2 ? d * 2 : 0)};
+  const Range outputs[] = {r_out, range_of(o->delta, o->delta ? R * d * 4 : 0),
+                           range_of(o->feat, o->feat ? R * F * 4 : 0),
+                           range_of(o->dev_status, o->dev_status ? 4 : 0), range_of(workspace, plan->ws_bytes)};
+  const int n_out = (int)(sizeof(outputs) / sizeof(outputs[0]));
+  for (int i = 0; i < n_out; ++i) {
+    for (const Range& in : inputs)
+      if (overlap(outputs[i], in)) return READY_ERR_ALIASING;
+    for (int j = i + 1; j < n_out; ++j)
+      if (overlap(outputs[i], outputs[j])) return READY_ERR_ALIASING;
+    if (i != 0 && overlap(outputs[i], r_h)) return READY_ERR_ALIASING;
+  }
+  // out may be h itself (in place); any other overlap with h is an error
+  if (o->out != h && overlap(r_out, r_h)) return READY_ERR_ALIASING;
+  if (s.B == 0) return READY_OK;
+
+  const char* pb = (const char*)prep;
+  FastArgs a;
+  fast_common(plan, (char*)workspace, a);
+  a.mode = READY_MODE_APPLY;
+  a.n_s = 0;  // no state tiles: P, ell and the flags come from the prepare launch
+  a.h = (const uint16_t*)h;
+  a.wq = (const uint16_t*)w->wq; a.gamma = (const uint16_t*)w->h_gamma;
+  a.w1 = (const uint16_t*)w->w1; a.b1 = (const uint16_t*)w->b1;
+  a.w2 = (const uint16_t*)w->w2; a.b2 = (const uint16_t*)w->b2;
+  a.out = (uint16_t*)o->out; a.delta = o->delta; a.feat = o->feat; a.dev_status = o->dev_status;
+  a.pmat = (float*)(pb + L.off_p) + (int64_t)inj * L.p_stride;
+  a.ell = (float*)(pb + L.off_ell);
+  a.seq_invalid = (uint32_t*)(pb + L.off_flags);
+  return launch_fast(plan, a, (hipStream_t)stream, nullptr);
 }
 
 }  // extern "C"

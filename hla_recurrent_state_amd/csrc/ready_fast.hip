@@ -390,6 +390,78 @@ __device__ __forceinline__ void tile_count(const FastArgs& a, int t) {
   for (int q = r0 / 16; q <= r1 / 16; ++q) count_up(ctr(a.sdone, q));
 }
 
+// P = V^T (S U^T) * scale for the tile in LDS (sS) and the U, V of one
+// reader in LDS (sU, sV): S U^T on the matrix cores, wave w taking rows
+// [32 w, 32 w + 32); then each lane sums V^T over its eight rows, and the
+// four waves' partials meet in s_red.  P is stored device-coherently.
+template <int RR>
+__device__ __forceinline__ void tile_project(const u32x4* sS, const uint16_t* sU, const uint16_t* sV, float* s_red,
+                                             float scale, float* P) {
+  constexpr int NB = (RR + 15) / 16;  // 16-column blocks of U^T
+  constexpr int VC = RR / 8;          // 16-byte chunks per V row
+  constexpr int LU = READY_TILE + 8;  // padded U row in LDS (bf16)
+  constexpr int WS = NB * RR * 16;    // per-wave partials of P
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lrow = lane & 15, lq = lane >> 4;
+  f32x4 acc[2][NB];
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    u32x4 sa[2];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) sa[mb] = sS[tile_slot(32 * wave + 16 * mb + lrow, 4 * ks + lq)];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const int i = 16 * nb + lrow;
+      const u32x4 ub = (i < RR) ? *(const u32x4*)&sU[i * LU + 32 * ks + 8 * lq] : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) acc[mb][nb] = mfma16x16x32(sa[mb], ub, acc[mb][nb]);
+    }
+  }
+
+  // acc[mb][nb][e] = (S U^T)[v = 32 w + 16 mb + 4 (l / 16) + e][i' = 16 nb + l % 16]
+  float part[NB][RR];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+    for (int i = 0; i < RR; ++i) part[nb][i] = 0.0f;
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int v = 32 * wave + 16 * mb + 4 * lq + e;
+      float vrow[RR];
+#pragma unroll
+      for (int c = 0; c < VC; ++c) Elem<uint16_t>::unpack(*(const u32x4*)&sV[v * RR + 8 * c], vrow + 8 * c);
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int i = 0; i < RR; ++i) part[nb][i] += vrow[i] * acc[mb][nb][e];
+    }
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+    for (int i = 0; i < RR; ++i) {
+      part[nb][i] += __shfl_xor(part[nb][i], 16, 64);
+      part[nb][i] += __shfl_xor(part[nb][i], 32, 64);
+    }
+  if (lane < 16) {
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int i = 0; i < RR; ++i) s_red[wave * WS + (nb * RR + i) * 16 + lane] = part[nb][i];
+  }
+  __syncthreads();
+  for (int e = tid; e < RR * RR; e += 256) {
+    const int i = e / RR, ip = e - (e / RR) * RR;
+    const int idx = ((ip >> 4) * RR + i) * 16 + (ip & 15);
+    st_coh_f32(P + e, ((s_red[idx] + s_red[WS + idx]) + (s_red[2 * WS + idx] + s_red[3 * WS + idx])) * scale);
+  }
+}
+
 // Process tile t whose loads were issued: copy to `gathered`, sum of
 // squares, S U^T, P, ell.  Thread 0 also publishes `pub` (a ticket) in
 // *s_pub, readable by every thread once this returns.  Tile `announce` (if >= 0) is counted as done on
@@ -401,7 +473,6 @@ template <int RR>
 __device__ __forceinline__ void tile_process(const FastArgs& a, int t, const TileRegs<RR>& R, unsigned char* smem,
                                              int announce, uint32_t* s_pub, uint32_t pub) {
   constexpr int NB = (RR + 15) / 16;  // 16-column blocks of U^T
-  constexpr int VC = RR / 8;          // 16-byte chunks per V row
   constexpr int LU = READY_TILE + 8;  // padded U row in LDS (bf16)
   constexpr int WCH = RR * 16;
   constexpr int WS = NB * RR * 16;    // per-wave partials of P
@@ -420,7 +491,8 @@ __device__ __forceinline__ void tile_process(const FastArgs& a, int t, const Til
     // No tile loads were issued, so wait explicitly before announcing.
     __syncthreads();  // every thread has read the last published ticket
     if (tid == 0) *s_pub = pub;
-    for (int e = tid; e < RR * RR; e += 256) st_coh_f32(P + e, 0.0f);
+    for (int inj = 0; inj < a.n_inj; ++inj)
+      for (int e = tid; e < RR * RR; e += 256) st_coh_f32(P + (int64_t)inj * a.p_inj_stride + e, 0.0f);
     if (tid == 0) {
       if (a.dev_status) st_coh_u32(a.dev_status, (uint32_t)READY_ERR_ACCEPT_IDX);
       if (m == 0) st_coh_u32(a.seq_invalid + b, 1u);
@@ -455,75 +527,44 @@ __device__ __forceinline__ void tile_process(const FastArgs& a, int t, const Til
   __syncthreads();
   if (tid == 0 && announce >= 0) tile_count(a, announce);
 
-  // ---- S U^T on the matrix cores; wave w takes rows [32 w, 32 w + 32) ----
-  const int lrow = lane & 15, lq = lane >> 4;
-  f32x4 acc[2][NB];
-#pragma unroll
-  for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-  for (int ks = 0; ks < 4; ++ks) {
-    u32x4 sa[2];
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb) sa[mb] = sS[tile_slot(32 * wave + 16 * mb + lrow, 4 * ks + lq)];
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      const int i = 16 * nb + lrow;
-      const u32x4 ub = (i < RR) ? *(const u32x4*)&sU[i * LU + 32 * ks + 8 * lq] : u32x4{0u, 0u, 0u, 0u};
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb) acc[mb][nb] = mfma16x16x32(sa[mb], ub, acc[mb][nb]);
-    }
-  }
-
-  // ---- P = V^T (S U^T): each lane sums over its eight rows ----
-  // acc[mb][nb][e] = (S U^T)[v = 32 w + 16 mb + 4 (l / 16) + e][i' = 16 nb + l % 16]
-  float part[NB][RR];
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-    for (int i = 0; i < RR; ++i) part[nb][i] = 0.0f;
-#pragma unroll
-  for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int v = 32 * wave + 16 * mb + 4 * lq + e;
-      float vrow[RR];
-#pragma unroll
-      for (int c = 0; c < VC; ++c) Elem<uint16_t>::unpack(*(const u32x4*)&sV[v * RR + 8 * c], vrow + 8 * c);
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-        for (int i = 0; i < RR; ++i) part[nb][i] += vrow[i] * acc[mb][nb][e];
-    }
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-    for (int i = 0; i < RR; ++i) {
-      part[nb][i] += __shfl_xor(part[nb][i], 16, 64);
-      part[nb][i] += __shfl_xor(part[nb][i], 32, 64);
-    }
-  if (lane < 16) {
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-      for (int i = 0; i < RR; ++i) s_red[wave * WS + (nb * RR + i) * 16 + lane] = part[nb][i];
-  }
-  __syncthreads();
-
   const float ms = ((s_wsum[0] + s_wsum[1]) + (s_wsum[2] + s_wsum[3])) * (1.0f / READY_TILE_ELEMS);
   const float rms = sqrtf(ms + a.state_eps);
   const float scale = 0.08838834764831845f / rms;  // 1 / (rms sqrt(d_k)), d_k = 128
-  for (int e = tid; e < RR * RR; e += 256) {
-    const int i = e / RR, ip = e - (e / RR) * RR;
-    const int idx = ((ip >> 4) * RR + i) * 16 + (ip & 15);
-    st_coh_f32(P + e, ((s_red[idx] + s_red[WS + idx]) + (s_red[2 * WS + idx] + s_red[3 * WS + idx])) * scale);
-  }
+  tile_project<RR>(sS, sU, sV, s_red, scale, P);
   if (tid == 0) {
     const float ell = logf(rms);
     st_coh_f32(a.ell + t, ell);
     if (m == 0) st_coh_u32(a.seq_invalid + b, 0u);
     if (a.logrms) a.logrms[t] = ell;
+  }
+  // further readers of the same state (prepare launches only): the tile
+  // stays in LDS, their U and V replace the first reader's.  The next
+  // reader's U and V are requested while the current one is projected.
+  if (a.n_inj > 1) {
+    const int mz = a.shared ? 0 : m;
+    u32x4 wn[TileRegs<RR>::NW];
+    auto fetch = [&](int inj) {
+      const u32x4* Ug = (const u32x4*)(a.u_inj[inj] + (int64_t)mz * RR * READY_TILE);
+      const u32x4* Vg = (const u32x4*)(a.v_inj[inj] + (int64_t)mz * READY_TILE * RR);
+#pragma unroll
+      for (int k = 0; k < TileRegs<RR>::NW; ++k) {
+        const int c = tid + 256 * k;
+        wn[k] = c < WCH ? Ug[c] : Vg[c - WCH];
+      }
+    };
+    fetch(1);
+    for (int inj = 1; inj < a.n_inj; ++inj) {
+      __syncthreads();  // every wave is done with the previous reader's U, V and partials
+#pragma unroll
+      for (int k = 0; k < TileRegs<RR>::NW; ++k) {
+        const int c = tid + 256 * k;
+        if (c < WCH) *(u32x4*)&sU[(c >> 4) * LU + 8 * (c & 15)] = wn[k];
+        else *(u32x4*)&sV[8 * (c - WCH)] = wn[k];
+      }
+      __syncthreads();
+      if (inj + 1 < a.n_inj) fetch(inj + 1);
+      tile_project<RR>(sS, sU, sV, s_red, scale, P + (int64_t)inj * a.p_inj_stride);
+    }
   }
 }
 
@@ -626,7 +667,7 @@ __device__ __forceinline__ void mlp1_item(const FastArgs& a, int item, unsigned 
   const int b0 = row0 / a.n, b1 = (row0 + rows - 1) / a.n;
   if (threadIdx.x == 0)
     *s_flag = wait_count2(ctr(a.zdone, row0 / BMZ), (uint32_t)cdiv_d(Nz, 64), ctr(a.sdone, rb),
-                          (uint32_t)(a.M * (b1 - b0 + 1)), a.abort_flag, a.dev_status) ? 1 : 0;
+                          a.n_s > 0 ? (uint32_t)(a.M * (b1 - b0 + 1)) : 0u, a.abort_flag, a.dev_status) ? 1 : 0;
   __syncthreads();
   const bool ok = *s_flag != 0;
 
@@ -928,7 +969,7 @@ __global__ __launch_bounds__(256, 2) void k_reader(FastArgs a) {
 #pragma unroll
   for (int k = 0; k < APT; ++k) {
     const int b = threadIdx.x + 256 * k;
-    accv[k] = b < a.B ? a.accept_idx[b] : 0;
+    accv[k] = (b < a.B && a.n_s > 0) ? a.accept_idx[b] : 0;  // apply launches have no accept indices
   }
   if (a.counters[0] != a.magic) {
     // the workspace was not prepared for this plan: touch nothing else
@@ -942,11 +983,14 @@ __global__ __launch_bounds__(256, 2) void k_reader(FastArgs a) {
   const int nx = a.nxcd, xs = nx == 8 ? 3 : 0;  // nx = 1 << xs
   const int x = g & (nx - 1), li = g >> xs, per = G >> xs;
   const int nrbz = cdiv_d(a.R, BMZ), ncbz = cdiv_d(a.Nz, 64), tiles = nrbz * ncbz;
+  // a prepare launch (several readers sharing one gather) has no Z, A or O
+  // items; an apply launch has no state tiles (n_s = 0)
+  const bool zao = a.mode != READY_MODE_PREPARE;
   auto has_z = [&](int w) {
     const int xw = w & (nx - 1);
-    return (w >> xs) < ((a.ksplit - xw + nx - 1) >> xs) * tiles;
+    return zao && (w >> xs) < ((a.ksplit - xw + nx - 1) >> xs) * tiles;
   };
-  {
+  if (zao) {
     const int nkx = (a.ksplit - x + nx - 1) >> xs;
     for (int i = li; i < nkx * tiles; i += per) {
       const int ks = x + nx * (i / tiles), rem = i % tiles;
@@ -961,7 +1005,7 @@ __global__ __launch_bounds__(256, 2) void k_reader(FastArgs a) {
   // workgroup's XCD group (A item j belongs to group j % nx, O item (rb, cb)
   // to group cb % nx).  A ticket is drawn only when the previous item is
   // done, so that no workgroup holds an item it cannot start yet.
-  {
+  if (zao) {
     uint32_t* aq = ctr(a.aq, x);
     uint32_t* oq = ctr(a.oq, x);
     const int nax = (a.n_a - x + nx - 1) >> xs;

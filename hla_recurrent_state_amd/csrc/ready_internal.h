@@ -36,6 +36,11 @@ struct StateArgs {
   float* feat;                     // [B*n][F] or null
 };
 
+#define READY_MODE_FULL 0
+#define READY_MODE_PREPARE 1
+#define READY_MODE_APPLY 2
+#define READY_MAX_INJ 8            // injections one prepare launch serves
+
 // Fast path (bf16 states, activations and weights; r <= 32): one persistent
 // launch, k_reader, whose workgroups run four kinds of work items:
 //   Z  query sums z = W_q (gamma h) per 64 x 64 tile and K chunk, and the
@@ -94,6 +99,17 @@ struct FastArgs {
   int nxcd;                        // 8: items dealt to XCDs round robin; 1: no XCD affinity
   int B, P, n, M, H, r, d, F, Hm, R, Nz, shared, ksplit, kchunk, act;
   float state_eps, h_eps;
+  // Several readers sharing one gather.  READY_MODE_FULL runs every item
+  // kind.  READY_MODE_PREPARE runs only the state tiles and forms one P per
+  // injection i, from u_inj[i] and v_inj[i], stored at pmat + i p_inj_stride
+  // (u_inj[0] = u, v_inj[0] = v).  READY_MODE_APPLY runs every kind but the
+  // state tiles: its A and O items read the P, ell and invalid-sequence flags
+  // a prepare launch left (pmat, ell and seq_invalid point there).
+  int mode;
+  int n_inj;                       // 1 outside READY_MODE_PREPARE
+  int64_t p_inj_stride;            // floats
+  const uint16_t* u_inj[READY_MAX_INJ];
+  const uint16_t* v_inj[READY_MAX_INJ];
 };
 
 #define READY_FAST_MAX_F 1536      // f rows of 16 positions staged in LDS

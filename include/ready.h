@@ -60,8 +60,10 @@ typedef enum readyStatus {
   READY_ERR_OUT_OF_HOST_MEMORY = 10,
   READY_ERR_SYNC_TIMEOUT = 11,      /* device-side only: a wait between work items of one launch
                                        gave up (should never happen; outputs are then invalid) */
-  READY_ERR_WORKSPACE_UNINIT = 12   /* device-side only: the workspace was not prepared by
+  READY_ERR_WORKSPACE_UNINIT = 12,  /* device-side only: the workspace was not prepared by
                                        readyWorkspaceInit for this plan; nothing was computed */
+  READY_ERR_UNSUPPORTED = 13        /* the operation is not available for this plan's dtypes and rank
+                                       (readyPrepSize, readyStatePrepare, readyStateApply) */
 } readyStatus;
 
 typedef enum readyDtype { READY_F32 = 0, READY_BF16 = 1 } readyDtype;
@@ -217,6 +219,77 @@ readyStatus readyStateReaderProfiled(const readyPlan* plan, const readyStates* s
                                      const readyWeights* weights, const readyOutputs* outputs,
                                      void* workspace, size_t workspace_bytes, void* stream,
                                      void* const* events);
+
+/*
+ * Several readers sharing one gather.  The pages compare drafters with one
+ * reader (final draft layer) and with readers injected into draft layers
+ * (0, 2, 4) or all five, each reader with its own parameters (arXiv text,
+ * section 4 "Number of injections", Table 5).  Every reader of a block reads
+ * the same committed states, and the h of a later draft layer exists only
+ * after the earlier layers have run, so the work splits in two:
+ *
+ *   readyStatePrepare  steps 1-3 once for every reader: each committed tile
+ *                      is read once, gathered, and its ell = ln rms and, for
+ *                      every reader i, P_i = V_i^T S_bar U_i^T / sqrt(d_k)
+ *                      (r x r; u = P_i z_j is T_i q_j / sqrt(d_k) with
+ *                      T_i = V_i^T S_bar and q_j = U_i^T z_j, reassociated)
+ *                      are left in a caller buffer `prep`.
+ *   readyStateApply    steps 4-5 of reader i for its own h: z = W_q,i
+ *                      RMSNorm(h), u = P_i z, f, MLP and residual.  It reads
+ *                      no state.
+ * readyStateApply(i) gives the outputs readyStateReader gives with reader i's
+ * weights and the same states (the same arithmetic in the same order).
+ * Available when readyStateReader runs as one kernel: bf16 states,
+ * activations and weights, r <= 32 (READY_ERR_UNSUPPORTED otherwise).
+ *
+ * Bytes of the prepared-state buffer for n_inj readers (1 <= n_inj <= 8):
+ * 4 (n_inj B M r^2 + B M + B) rounded up per section to 256.
+ */
+readyStatus readyPrepSize(const readyPlan* plan, int32_t n_inj, size_t* bytes);
+
+/*
+ * Steps 1-3 for n_inj readers, asynchronously on `stream`.
+ *   states, accept_idx  as for readyStateReader.
+ *   inj_weights  host array of n_inj readyWeights; only u and v are read
+ *                (device, 16-byte aligned, layouts as in readyWeights).
+ *   gathered     [B][M][d_v][d_k] bf16 (required); logrms [B][M] fp32 and
+ *                dev_status one int32 (optional), as in readyOutputs.
+ *   prep         device, 256-byte aligned, at least readyPrepSize(n_inj)
+ *                bytes; written.  Its contents are meaningful only to
+ *                readyStateApply with the same plan and n_inj.
+ *   workspace    as for readyStateReader (prepared by readyWorkspaceInit).
+ * An accept index outside [0, P) stores READY_ERR_ACCEPT_IDX in dev_status,
+ * leaves that sequence's gathered and logrms unwritten and marks the sequence
+ * in prep, so that readyStateApply leaves its out and delta unwritten.
+ * Returns READY_ERR_NULL_POINTER, READY_ERR_UNSUPPORTED, READY_ERR_BAD_SHAPE
+ * (n_inj), READY_ERR_WORKSPACE_TOO_SMALL (workspace or prep),
+ * READY_ERR_MISALIGNED, READY_ERR_ALIASING (outputs overlapping inputs or
+ * each other) or READY_ERR_HIP.  Allocates and synchronises nothing.
+ */
+readyStatus readyStatePrepare(const readyPlan* plan, const readyStates* states, const int32_t* accept_idx,
+                              int32_t n_inj, const readyWeights* inj_weights, void* gathered, float* logrms,
+                              int32_t* dev_status, void* prep, size_t prep_bytes, void* workspace,
+                              size_t workspace_bytes, void* stream);
+
+/*
+ * Steps 4-5 of reader `inj` (0 <= inj < n_inj, n_inj as given to
+ * readyStatePrepare), asynchronously on `stream`, after the prepare call on
+ * the same stream (or ordered after it).  prep is read only.
+ *   h        device [B][n][d] bf16: the draft representations at this
+ *            reader's injection site.
+ *   weights  reader inj's wq, h_gamma, w1, b1, w2, b2 (u and v are not
+ *            read: they are folded into P).
+ *   outputs  out (required; may be exactly h), delta, feat and dev_status
+ *            (optional) as in readyOutputs; gathered and logrms are ignored.
+ *   workspace  as for readyStateReader.  Calls that share a workspace must
+ *            run one after another (the same stream does that).
+ * Returns READY_ERR_NULL_POINTER, READY_ERR_UNSUPPORTED, READY_ERR_BAD_SHAPE
+ * (n_inj or inj), READY_ERR_WORKSPACE_TOO_SMALL, READY_ERR_MISALIGNED,
+ * READY_ERR_ALIASING or READY_ERR_HIP.  Allocates and synchronises nothing.
+ */
+readyStatus readyStateApply(const readyPlan* plan, const void* prep, int32_t n_inj, int32_t inj, const void* h,
+                            const readyWeights* weights, const readyOutputs* outputs, void* workspace,
+                            size_t workspace_bytes, void* stream);
 
 /*
  * Verify buffer written by readyVerifyStates: element [b][p][l][a][v][k] at
