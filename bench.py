@@ -530,6 +530,132 @@ def run_sweeps(args, hip, torch, R, synth):
     return out
 
 
+def run_multi(args, hip, torch, R, synth, seed=0):
+    """Several readers sharing one gather at the batched shape (B = 64, 32
+    layer-head pairs, r = 8, bf16): readers in draft layers (0, 2, 4) and in
+    all five (3 and 5 readers, each with its own weights and h).  Times one
+    readyStatePrepare plus one readyStateApply per reader against one
+    readyStateReader call per reader (each re-reading the states), cold (after
+    a 512 MB flush) and back to back.  Timing only: states, weights and h are
+    drawn on the device; parity is in tests/test_gpu_multi.py."""
+    device = torch.device("cuda:0")
+    cfg = synth.make_shape("batched")
+    B, P, n, d, r, Hm, M, F = cfg.B, cfg.P, cfg.n, cfg.d, cfg.r, cfg.Hm, cfg.M, cfg.F
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    bf = torch.bfloat16
+
+    def normal(shape, scale):
+        return (torch.randn(shape, generator=g, device=device) * scale).to(bf)
+
+    states = normal((B, P, cfg.L_tot, cfg.H, 128, 128), 1.0 / 128)
+    acc = torch.randint(0, P, (B,), generator=g, device=device, dtype=torch.int32)
+    reader = R.StateReader(shape_of(R, cfg), cfg.slots)
+    stream = torch.cuda.current_stream(device).cuda_stream
+    lib = R.load()
+    ws = reader.new_workspace(device)
+    st = states.stride()
+    sd = R.readyStates(base=states.data_ptr(), stride_b=st[0], stride_p=st[1], stride_l=st[2], stride_h=st[3])
+    gathered = torch.empty((B, M, 128, 128), dtype=bf, device=device)
+    status = torch.zeros(1, dtype=torch.int32, device=device)
+    flush = torch.empty(128 * 1024 * 1024, dtype=torch.float32, device=device)
+    K = args.config_steps
+    out = {"workload": "batched shape (B=64, 32 layer-head pairs, r=8, bf16), readers at several draft layers",
+           "readers": {}}
+    for n_inj in (3, 5):
+        keep = []
+        wlist, hs, outs = [], [], []
+        for i in range(n_inj):
+            w = {"wq": normal((M, r, d), d ** -0.5), "u": normal((M, r, 128), r ** -0.5),
+                 "v": normal((M, 128, r), 128 ** -0.5), "w1": normal((Hm, F), F ** -0.5),
+                 "w2": normal((d, Hm), Hm ** -0.5)}
+            wlist.append(w)
+            hs.append(normal((B, n, d), 1.0))
+            outs.append(torch.empty((B, n, d), dtype=bf, device=device))
+        keep += [wlist, hs, outs]
+        wd = [R.readyWeights(**{k: (w[k].data_ptr() if k in w else None)
+                                for k in ("wq", "u", "v", "h_gamma", "w1", "b1", "w2", "b2")}) for w in wlist]
+        od = [R.readyOutputs(gathered=gathered.data_ptr(), out=o.data_ptr(), logrms=None, delta=None, feat=None,
+                             dev_status=status.data_ptr()) for o in outs]
+        oa = [R.readyOutputs(gathered=None, out=o.data_ptr(), logrms=None, delta=None, feat=None,
+                             dev_status=status.data_ptr()) for o in outs]
+        warr = (R.readyWeights * n_inj)(*wd)
+        prep = reader.new_prep(n_inj, device)
+        keep.append(prep)
+        single_args = [(reader.plan, ctypes.byref(sd), acc.data_ptr(), hs[i].data_ptr(), ctypes.byref(wd[i]),
+                        ctypes.byref(od[i]), ws.data_ptr(), ws.numel(), stream) for i in range(n_inj)]
+        prep_args = (reader.plan, ctypes.byref(sd), acc.data_ptr(), n_inj, warr, gathered.data_ptr(), None,
+                     status.data_ptr(), prep.data_ptr(), prep.numel(), ws.data_ptr(), ws.numel(), stream)
+        apply_args = [(reader.plan, prep.data_ptr(), n_inj, i, hs[i].data_ptr(), ctypes.byref(wd[i]),
+                       ctypes.byref(oa[i]), ws.data_ptr(), ws.numel(), stream) for i in range(n_inj)]
+
+        def check(code, what):
+            if code != 0:
+                raise R.ReadyError(code, what)
+
+        def singles():
+            for a in single_args:
+                check(lib.readyStateReader(*a), "single")
+
+        def prepare():
+            check(lib.readyStatePrepare(*prep_args), "prepare")
+
+        def applies():
+            for a in apply_args:
+                check(lib.readyStateApply(*a), "apply")
+
+        def shared():
+            prepare()
+            applies()
+
+        def timed(fn, cold):
+            for _ in range(3):
+                fn()
+            torch.cuda.synchronize(device)
+            if cold:
+                vals = []
+                for _ in range(K):
+                    flush.add_(1.0)
+                    a, b = hip.event(), hip.event()
+                    hip.record(a, stream)
+                    fn()
+                    hip.record(b, stream)
+                    torch.cuda.synchronize(device)
+                    vals.append(1000.0 * hip.ms(a, b))
+                    hip.destroy(a)
+                    hip.destroy(b)
+                return pct(vals, 50)
+            a, b = hip.event(), hip.event()
+            hip.record(a, stream)
+            for _ in range(K):
+                fn()
+            hip.record(b, stream)
+            torch.cuda.synchronize(device)
+            us = 1000.0 * hip.ms(a, b) / K
+            hip.destroy(a)
+            hip.destroy(b)
+            return us
+
+        res = {
+            "separate_calls_cold_p50_us": round(timed(singles, True), 2),
+            "separate_calls_warm_us": round(timed(singles, False), 2),
+            "shared_gather_cold_p50_us": round(timed(shared, True), 2),
+            "shared_gather_warm_us": round(timed(shared, False), 2),
+            "prepare_warm_us": round(timed(prepare, False), 2),
+            "apply_warm_us_each": round(timed(applies, False) / n_inj, 2),
+        }
+        res["speedup_warm"] = round(res["separate_calls_warm_us"] / res["shared_gather_warm_us"], 3)
+        if int(status.item()) != 0:
+            raise RuntimeError("device status set during the multi-reader run")
+        out["readers"][str(n_inj)] = res
+        log("multi-reader n=%d: %s" % (n_inj, res))
+        del keep
+    reader.close()
+    del flush
+    torch.cuda.empty_cache()
+    return out
+
+
 def run_producer(args, hip, torch, R, synth, seed=0):
     """The verify-state producer at the batched shape (B = 64 sequences,
     32 layer-head pairs, P = 8 positions, bf16 states, keys and values):
@@ -803,6 +929,7 @@ def main():
     if not args.no_sweeps:
         out["sweeps"] = run_sweeps(args, hip, torch, R, synth)
         out["producer"] = run_producer(args, hip, torch, R, synth)
+        out["multi_reader"] = run_multi(args, hip, torch, R, synth)
     ok = True
     if not args.no_cpu:
         base, rep = cpu_baseline(bat, args.cpu_budget)
