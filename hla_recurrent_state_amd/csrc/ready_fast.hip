@@ -77,8 +77,8 @@ __device__ __forceinline__ u32x4 ld_coh16(const void* base, uint32_t byte_off) {
 __device__ __forceinline__ void st_coh16(void* base, uint32_t byte_off, u32x4 v) {
   __builtin_amdgcn_raw_buffer_store_b128(v, rsrc(base), byte_off, 0, SC1);
 }
-__device__ __forceinline__ float ld_coh_f32(const float* p) {
-  return __uint_as_float(__hip_atomic_load((const uint32_t*)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+__device__ __forceinline__ float ld_coh4(const void* base, uint32_t byte_off) {
+  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rsrc(base), byte_off, 0, SC1));
 }
 __device__ __forceinline__ void st_coh_f32(float* p, float v) {
   __hip_atomic_store((uint32_t*)p, __float_as_uint(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -691,10 +691,17 @@ __device__ __forceinline__ void mlp1_item(const FastArgs& a, int item, unsigned 
       const uint32_t pofs = (uint32_t)((((b * a.M + m) * RR + i) * RR) * 4);
 #pragma unroll
       for (int c = 0; c < CR4; ++c) pv[s][c] = live ? ld_coh16(a.pmat, pofs + 16 * c) : u32x4{0u, 0u, 0u, 0u};
-      ellv[s] = (live && i == 0) ? ld_coh_f32(a.ell + b * a.M + m) : 0.0f;
+      ellv[s] = (live && i == 0) ? ld_coh4(a.ell, (uint32_t)(4 * (b * a.M + m))) : 0.0f;
     }
   };
   load_p(tid, 0);
+  // the sums of squares of h (threads 0-15, one row each) travel with the
+  // other loads
+  const bool hrow = tid < 16 && tid < rows && ok;
+  float hv[16];
+#pragma unroll
+  for (int k = 0; k < 16; ++k)
+    hv[k] = (hrow && k < a.ksplit) ? ld_coh4(a.hss, (uint32_t)(4 * (k * a.R + row0 + tid))) : 0.0f;
   const int nzc = rows * (Nz / 4);
   for (int c0 = tid; c0 < 16 * (Nz / 4); c0 += 256 * 4) {
     u32x4 v[4];
@@ -711,14 +718,11 @@ __device__ __forceinline__ void mlp1_item(const FastArgs& a, int item, unsigned 
   }
   if (tid < 16) {
     float rs = 0.0f;
-    if (tid < rows && ok) {
-      float hv[16];
-#pragma unroll
-      for (int k = 0; k < 16; ++k) hv[k] = k < a.ksplit ? ld_coh_f32(a.hss + k * a.R + row0 + tid) : 0.0f;
+    if (hrow) {
       float hs = 0.0f;
 #pragma unroll
       for (int k = 0; k < 16; ++k) hs += hv[k];
-      for (int k = 16; k < a.ksplit; ++k) hs += ld_coh_f32(a.hss + k * a.R + row0 + tid);
+      for (int k = 16; k < a.ksplit; ++k) hs += ld_coh4(a.hss, (uint32_t)(4 * (k * a.R + row0 + tid)));
       rs = 1.0f / sqrtf(hs / (float)a.d + a.h_eps);
     }
     s_rs[tid] = rs;
@@ -865,7 +869,8 @@ __device__ __forceinline__ void mlp2_item(const FastArgs& a, int rb, int cb, uns
   for (int k = 0; k < EPT; ++k) {
     const int c = tid + 256 * k;
     const int rr = c / CPR;
-    inv[k] = (c < BM * CPR && rr < rows) ? ld_coh_u32(a.seq_invalid + (row0 + rr) / a.n) : 1u;
+    inv[k] = (c < BM * CPR && rr < rows) ? __float_as_uint(ld_coh4(a.seq_invalid, (uint32_t)(4 * ((row0 + rr) / a.n))))
+                                         : 1u;
   }
 
   f32x4 acc[BM / 16][2];
@@ -886,12 +891,24 @@ __device__ __forceinline__ void mlp2_item(const FastArgs& a, int rb, int cb, uns
                                             : u32x4{0u, 0u, 0u, 0u};
         }
     }
-    __syncthreads();
-    for (int c = tid; c < BM * (KT / 8); c += 256) {
+    // the pass's a chunks are all requested before the first is parked in
+    // LDS: one trip to memory per pass instead of one per chunk
+    constexpr int ACH = BM * (KT / 8) / 256;  // 16-byte chunks per thread
+    static_assert(BM * (KT / 8) % 256 == 0, "whole chunks per thread");
+    u32x4 av[ACH];
+#pragma unroll
+    for (int j = 0; j < ACH; ++j) {
+      const int c = tid + 256 * j;
       const int rr = c / (KT / 8), kc = (c - rr * (KT / 8)) * 8;
-      u32x4 v = u32x4{0u, 0u, 0u, 0u};
-      if (rr < rows && kc < klen) v = ld_coh16(a.abuf, (uint32_t)(2 * ((row0 + rr) * a.Hm + kb + kc)));
-      *(u32x4*)&sA[rr * LA + kc] = v;
+      av[j] = (rr < rows && kc < klen) ? ld_coh16(a.abuf, (uint32_t)(2 * ((row0 + rr) * a.Hm + kb + kc)))
+                                       : u32x4{0u, 0u, 0u, 0u};
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < ACH; ++j) {
+      const int c = tid + 256 * j;
+      const int rr = c / (KT / 8), kc = (c - rr * (KT / 8)) * 8;
+      *(u32x4*)&sA[rr * LA + kc] = av[j];
     }
     __syncthreads();
 #pragma unroll
