@@ -469,7 +469,7 @@ __device__ __forceinline__ void tile_project(const u32x4* sS, const uint16_t* sU
 // in-order completion of the memory counter they are complete once every
 // wave has waited for this tile's data (the barrier after the LDS copy).
 // This tile's own stores are complete after the caller's next such wait.
-template <int RR>
+template <int RR, bool MULTI>
 __device__ __forceinline__ void tile_process(const FastArgs& a, int t, const TileRegs<RR>& R, unsigned char* smem,
                                              int announce, uint32_t* s_pub, uint32_t pub) {
   constexpr int NB = (RR + 15) / 16;  // 16-column blocks of U^T
@@ -491,7 +491,7 @@ __device__ __forceinline__ void tile_process(const FastArgs& a, int t, const Til
     // No tile loads were issued, so wait explicitly before announcing.
     __syncthreads();  // every thread has read the last published ticket
     if (tid == 0) *s_pub = pub;
-    for (int inj = 0; inj < a.n_inj; ++inj)
+    for (int inj = 0; inj < (MULTI ? a.n_inj : 1); ++inj)
       for (int e = tid; e < RR * RR; e += 256) st_coh_f32(P + (int64_t)inj * a.p_inj_stride + e, 0.0f);
     if (tid == 0) {
       if (a.dev_status) st_coh_u32(a.dev_status, (uint32_t)READY_ERR_ACCEPT_IDX);
@@ -540,7 +540,7 @@ __device__ __forceinline__ void tile_process(const FastArgs& a, int t, const Til
   // further readers of the same state (prepare launches only): the tile
   // stays in LDS, their U and V replace the first reader's.  The next
   // reader's U and V are requested while the current one is projected.
-  if (a.n_inj > 1) {
+  if (MULTI && a.n_inj > 1) {
     const int mz = a.shared ? 0 : m;
     u32x4 wn[TileRegs<RR>::NW];
     auto fetch = [&](int inj) {
@@ -578,7 +578,7 @@ __device__ __forceinline__ void tile_process(const FastArgs& a, int t, const Til
 // waiting for it never waits for tile data.  The tile processed two turns
 // back is announced while a tile is processed; the last two at the end.
 // has_z(w) tells whether workgroup w runs Z items.
-template <int RR, typename HasZ>
+template <int RR, bool MULTI, typename HasZ>
 __device__ __forceinline__ void s_phase(const FastArgs& a, int g, int G, unsigned char* smem, const int* s_acc,
                                         uint32_t* s_tk, HasZ has_z) {
   const int tid = threadIdx.x;
@@ -607,7 +607,7 @@ __device__ __forceinline__ void s_phase(const FastArgs& a, int g, int G, unsigne
   if (t1 >= 0) tile_issue<RR>(a, t1, r1, s_acc);
   int h1 = -1, h2 = -1;  // tiles processed one and two turns back
   while (t0 >= 0) {
-    tile_process<RR>(a, t0, r0, smem, h2, s_tk, pend);
+    tile_process<RR, MULTI>(a, t0, r0, smem, h2, s_tk, pend);
     const uint32_t i2 = *s_tk;
     h2 = h1;
     h1 = t0;
@@ -970,7 +970,7 @@ __device__ __forceinline__ void mlp2_item(const FastArgs& a, int rb, int cb, uns
 // then its O items.  Items of one kind are dealt to the workgroups in order
 // (Z items and O items per XCD: the K chunks ks with ks % nxcd == x, and the
 // column blocks cb with cb % nxcd == x, go to the workgroups on XCD x).
-template <int RR, int SMALL>
+template <int RR, int SMALL, int MODE>
 __global__ __launch_bounds__(256, 2) void k_reader(FastArgs a) {
   constexpr int BMZ = SMALL ? 16 : 64, BMO = SMALL ? 16 : 64;
   constexpr int NST = (SMALL ? READY_ZCHUNK_SMALL : READY_ZCHUNK_LARGE) / 128;
@@ -986,7 +986,7 @@ __global__ __launch_bounds__(256, 2) void k_reader(FastArgs a) {
 #pragma unroll
   for (int k = 0; k < APT; ++k) {
     const int b = threadIdx.x + 256 * k;
-    accv[k] = (b < a.B && a.n_s > 0) ? a.accept_idx[b] : 0;  // apply launches have no accept indices
+    accv[k] = (MODE != READY_MODE_APPLY && b < a.B) ? a.accept_idx[b] : 0;  // apply launches have none
   }
   if (a.counters[0] != a.magic) {
     // the workspace was not prepared for this plan: touch nothing else
@@ -1002,12 +1002,12 @@ __global__ __launch_bounds__(256, 2) void k_reader(FastArgs a) {
   const int nrbz = cdiv_d(a.R, BMZ), ncbz = cdiv_d(a.Nz, 64), tiles = nrbz * ncbz;
   // a prepare launch (several readers sharing one gather) has no Z, A or O
   // items; an apply launch has no state tiles (n_s = 0)
-  const bool zao = a.mode != READY_MODE_PREPARE;
+  constexpr bool zao = MODE != READY_MODE_PREPARE;
   auto has_z = [&](int w) {
     const int xw = w & (nx - 1);
     return zao && (w >> xs) < ((a.ksplit - xw + nx - 1) >> xs) * tiles;
   };
-  if (zao) {
+  if constexpr (zao) {
     const int nkx = (a.ksplit - x + nx - 1) >> xs;
     for (int i = li; i < nkx * tiles; i += per) {
       const int ks = x + nx * (i / tiles), rem = i % tiles;
@@ -1017,12 +1017,12 @@ __global__ __launch_bounds__(256, 2) void k_reader(FastArgs a) {
 #pragma unroll
   for (int k = 0; k < APT; ++k) s_acc[threadIdx.x + 256 * k] = accv[k];
   __syncthreads();
-  s_phase<RR>(a, g, G, smem, s_acc, &s_tk, has_z);
+  if (MODE != READY_MODE_APPLY) s_phase<RR, MODE == READY_MODE_PREPARE>(a, g, G, smem, s_acc, &s_tk, has_z);
   // A items, then O items, drawn in row order from the queues of this
   // workgroup's XCD group (A item j belongs to group j % nx, O item (rb, cb)
   // to group cb % nx).  A ticket is drawn only when the previous item is
   // done, so that no workgroup holds an item it cannot start yet.
-  if (zao) {
+  if constexpr (zao) {
     uint32_t* aq = ctr(a.aq, x);
     uint32_t* oq = ctr(a.oq, x);
     const int nax = (a.n_a - x + nx - 1) >> xs;
@@ -1090,10 +1090,19 @@ hipError_t ready_launch_reader(const FastArgs& a, int small, int grid, hipStream
   if (a.kchunk != (small ? READY_ZCHUNK_SMALL : READY_ZCHUNK_LARGE)) return hipErrorInvalidValue;
   const dim3 g((unsigned)grid), block(256);
   const size_t lds = ready_reader_lds(a.r, a.F, a.Nz, small);
-#define READY_READER_CASE(RRV)                                                   \
-  do {                                                                           \
-    if (small) READY_LAUNCH((k_reader<RRV, 1>), g, block, lds, s, ev, a);        \
-    else READY_LAUNCH((k_reader<RRV, 0>), g, block, lds, s, ev, a);              \
+#define READY_READER_MODE(RRV, SM)                                                          \
+  do {                                                                                      \
+    if (a.mode == READY_MODE_PREPARE)                                                       \
+      READY_LAUNCH((k_reader<RRV, SM, READY_MODE_PREPARE>), g, block, lds, s, ev, a);       \
+    else if (a.mode == READY_MODE_APPLY)                                                    \
+      READY_LAUNCH((k_reader<RRV, SM, READY_MODE_APPLY>), g, block, lds, s, ev, a);         \
+    else                                                                                    \
+      READY_LAUNCH((k_reader<RRV, SM, READY_MODE_FULL>), g, block, lds, s, ev, a);          \
+  } while (0)
+#define READY_READER_CASE(RRV)             \
+  do {                                     \
+    if (small) READY_READER_MODE(RRV, 1);  \
+    else READY_READER_MODE(RRV, 0);        \
   } while (0)
   switch (a.r) {
     case 8: READY_READER_CASE(8); break;
@@ -1102,17 +1111,31 @@ hipError_t ready_launch_reader(const FastArgs& a, int small, int grid, hipStream
     default: READY_READER_CASE(32); break;
   }
 #undef READY_READER_CASE
+#undef READY_READER_MODE
   return hipGetLastError();
 }
 
-// Workgroups of k_reader that one CU holds at once (0 on error).
+// Workgroups of k_reader that one CU holds at once, the least over the three
+// modes (0 on error).
 int ready_reader_per_cu(int r, int small, size_t lds) {
-  int nb = 0;
+  int nb = 1 << 20;
   hipError_t e = hipSuccess;
-#define READY_OCC_CASE(RRV)                                                                              \
-  do {                                                                                                   \
-    if (small) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, k_reader<RRV, 1>, 256, lds);       \
-    else e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, k_reader<RRV, 0>, 256, lds);             \
+#define READY_OCC_ONE(KERNEL)                                                     \
+  do {                                                                            \
+    int n1 = 0;                                                                   \
+    if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n1, KERNEL, 256, lds); \
+    nb = n1 < nb ? n1 : nb;                                                       \
+  } while (0)
+#define READY_OCC_SM(RRV, SM)                                          \
+  do {                                                                 \
+    READY_OCC_ONE((k_reader<RRV, SM, READY_MODE_FULL>));               \
+    READY_OCC_ONE((k_reader<RRV, SM, READY_MODE_PREPARE>));            \
+    READY_OCC_ONE((k_reader<RRV, SM, READY_MODE_APPLY>));              \
+  } while (0)
+#define READY_OCC_CASE(RRV)            \
+  do {                                 \
+    if (small) READY_OCC_SM(RRV, 1);   \
+    else READY_OCC_SM(RRV, 0);         \
   } while (0)
   switch (r) {
     case 8: READY_OCC_CASE(8); break;
@@ -1121,6 +1144,8 @@ int ready_reader_per_cu(int r, int small, size_t lds) {
     default: READY_OCC_CASE(32); break;
   }
 #undef READY_OCC_CASE
+#undef READY_OCC_SM
+#undef READY_OCC_ONE
   return e == hipSuccess ? nb : 0;
 }
 
