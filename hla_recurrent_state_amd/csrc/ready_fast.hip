@@ -2,28 +2,32 @@
 // and weights, rank r <= 32.  One persistent launch, k_reader.
 //
 // Its grid is two workgroups per CU, which the register and LDS budget of
-// the kernel lets the GPU hold at the same time.  Work is assigned
-// statically to three groups of workgroups:
-//   workers   (the first g_w): Z items, a BM x 64 tile of the partial sums
-//             z = W_q (gamma h) over one K chunk plus the sums of squares of
-//             h for RMSNorm(h_j) (step 4, query); then the A items of the
-//             early rows, 16 rows x 64 columns of a: f_j = [P z_j / rms(h_j),
-//             ell] per pair (u_j = T q_j / sqrt(d_k) with T = V^T S_bar and
-//             q_j = U^T z_j, reassociated through P), a = act(W1 f + b1)
-//             (step 4 readout, step 5); then the O items of the early row
-//             blocks, a BM x 64 tile of out = h + W2 a + b2 (step 5); then the
-//             A items of the late rows.
-//   streamers (the next g_s): the state tiles t = s, s + g_s, ...: fused
-//             gather at the accept index into the caller's buffer, mean
-//             square, log-RMS and P = V^T S_bar U^T / sqrt(d_k), an r x r
-//             matrix (steps 1-3); two tiles are in flight while one is
-//             processed.  Then O items of the late row blocks.
-//   the rest: O items of the late row blocks only.
-// "Late" rows belong to sequences whose tiles are among the last two turns
-// of the streamers; their MLP runs after the stream, everything else while
-// it runs.  Z and S items never wait; A items wait for Z and S items; O
-// items wait for A items, and a worker finishes its early A items before it
-// takes an O item.  With every workgroup resident at once each wait ends.
+// the kernel lets the GPU hold at the same time.  Every workgroup runs four
+// kinds of work item, in this order:
+//   Z  the query sums: a BM x 64 tile of the partial sums z = W_q (gamma h)
+//      over one K chunk, plus the sums of squares of h for RMSNorm(h_j)
+//      (step 4); the item that completes a tile's last chunk sums the chunks
+//      in chunk order.  Only the first workgroups of each XCD have Z items.
+//   S  the state tiles, drawn through ticket counters in sequence order:
+//      fused gather at the accept index into the caller's buffer, mean
+//      square, log-RMS and P = V^T S_bar U^T / sqrt(d_k), an r x r matrix
+//      (steps 1-3; u_j = T q_j / sqrt(d_k) with T = V^T S_bar and
+//      q_j = U^T z_j is P z_j).  Two tiles are in flight while one is
+//      processed.
+//   A  16 rows x 64 columns of a: f_j = [P z_j / rms(h_j), ell] per pair,
+//      a = act(W1 f + b1) (step 4 readout, step 5), drawn in row order from
+//      a queue per XCD group once the workgroup has no tile left.
+//   O  a BM x 128 tile of out = h + W2 a + b2 (step 5), drawn the same way
+//      once the A queue is empty.
+// Z and S items never wait; A items wait for the Z and S items of their
+// rows; O items wait for the A items of their rows.  With every workgroup
+// resident at once each wait ends.
+//
+// Several readers sharing one gather use two more forms of the same kernel
+// (the MODE template parameter): a prepare launch runs only the S items and
+// forms one P per reader from the same tile in LDS; an apply launch runs
+// only the Z, A and O items of one reader, reading the P, ell and
+// invalid-sequence flags a prepare launch left.
 //
 // The K chunks of the Z items, and the column blocks of the O items, are
 // dealt to the XCDs round robin (the hardware hands workgroup g to XCD
