@@ -254,11 +254,13 @@ def make(cfg="tiny", seed=0, states=True, nthreads=0, **overrides):
                   u=_store(u, wd), v=_store(v, wd), w1=_store(w1, wd), w2=_store(w2, wd))
 
 
-def make_readers(inp, n_readers, seed=0):
+def make_readers(inp, n_readers, seed=0, extras=False):
     """Weights and draft representations of n_readers readers that share the
     committed states of `inp` (one reader per injection site).  Reader 0 is
     inp's own (h, wq, u, v, w1, w2); the others are drawn independently with
-    the same distributions.  Returns a list of dicts of stored arrays."""
+    the same distributions.  With extras, every reader also gets a gain
+    gamma ~ N(1, 0.1^2) and biases b1, b2 ~ N(0, 0.1^2) (reader 0's drawn
+    here too).  Returns a list of dicts of stored arrays."""
     cfg = inp.cfg
     M, r, d, dk, dv, F, Hm = cfg.M, cfg.r, cfg.d, cfg.d_k, cfg.d_v, cfg.F, cfg.Hm
     pre = () if cfg.shared else (M,)
@@ -273,6 +275,12 @@ def make_readers(inp, n_readers, seed=0):
             v=_store(g(5).standard_normal(pre + (dv, r), dtype=np.float32) / np.float32(np.sqrt(dv)), wd),
             w1=_store(g(6).standard_normal((Hm, F), dtype=np.float32) / np.float32(np.sqrt(F)), wd),
             w2=_store(g(7).standard_normal((d, Hm), dtype=np.float32) / np.float32(np.sqrt(Hm)), wd)))
+    if extras:
+        for i, rd in enumerate(out):
+            g = lambda tag: _rng(seed, 100 * i + tag)
+            rd["gamma"] = _store(1.0 + 0.1 * g(8).standard_normal(d, dtype=np.float32), wd)
+            rd["b1"] = _store(0.1 * g(9).standard_normal(Hm, dtype=np.float32), wd)
+            rd["b2"] = _store(0.1 * g(10).standard_normal(d, dtype=np.float32), wd)
     return out
 
 

@@ -34,6 +34,9 @@ def _say(*a):
 
 def _reader_dev(rd, cfg, device):
     w = {k: tensor(rd[k], cfg.weight_dtype, device) for k in ("wq", "u", "v", "w1", "w2")}
+    for src, dst in (("gamma", "h_gamma"), ("b1", "b1"), ("b2", "b2")):
+        if src in rd:
+            w[dst] = tensor(rd[src], cfg.weight_dtype, device)
     return tensor(rd["h"], cfg.act_dtype, device), w
 
 
@@ -95,6 +98,10 @@ def _oracle(inp, readers, seqs):
     ws = [{"Wq": orc.decode(rd["wq"], cfg.weight_dtype), "U": orc.decode(rd["u"], cfg.weight_dtype),
            "V": orc.decode(rd["v"], cfg.weight_dtype), "W1": orc.decode(rd["w1"], cfg.weight_dtype),
            "W2": orc.decode(rd["w2"], cfg.weight_dtype)} for rd in readers]
+    for w, rd in zip(ws, readers):
+        for k in ("gamma", "b1", "b2"):
+            if k in rd:
+                w[k] = orc.decode(rd[k], cfg.weight_dtype)
     ref = orc.multi_reader(buf, inp.accept_idx[seqs], list(cfg.slots), cfg.H, hs, ws, act=cfg.act,
                            state_eps=cfg.state_eps, h_eps=cfg.h_eps, shared=cfg.shared)
     out = []
@@ -105,13 +112,14 @@ def _oracle(inp, readers, seqs):
     return out
 
 
-def _check(inp, n_readers, seqs=None, seed=5):
+def _check(inp, n_readers, seqs=None, seed=5, extras=False):
     from tests.gpu_util import compare
     dev = _dev()
     cfg = inp.cfg
     seqs = list(range(cfg.B)) if seqs is None else list(seqs)
-    _say("multi case", cfg.name, "B", cfg.B, "M", cfg.M, "r", cfg.r, "readers", n_readers)
-    readers = synth.make_readers(inp, n_readers, seed=seed)
+    _say("multi case", cfg.name, "B", cfg.B, "M", cfg.M, "r", cfg.r, "readers", n_readers, "act", cfg.act,
+         "shared", cfg.shared, "extras", extras)
+    readers = synth.make_readers(inp, n_readers, seed=seed, extras=extras)
     res = _run_multi(inp, readers, dev)
     refs = _oracle(inp, readers, seqs)
     for i in range(n_readers):
@@ -133,6 +141,16 @@ def test_batched_sample_five_readers():
 @pytest.mark.parametrize("r", [16, 24])
 def test_ranks_two_readers(r):
     _check(synth.make("paper", seed=4, r=r, B=3), 2)
+
+
+def test_gain_biases_and_gelu():
+    # every reader with its own RMSNorm gain and MLP biases, GELU (tanh form)
+    _check(synth.make("paper", seed=14, B=3, act="gelu_tanh"), 3, extras=True)
+
+
+def test_shared_reader_parameters_relu():
+    # one W_q, U, V per reader shared by all pairs, ReLU
+    _check(synth.make("paper", seed=15, B=2, shared=True, act="relu"), 2, extras=True)
 
 
 def test_rank_32_is_unsupported():
