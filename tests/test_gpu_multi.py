@@ -143,6 +143,12 @@ def test_ranks_two_readers(r):
     _check(synth.make("paper", seed=4, r=r, B=3), 2)
 
 
+@pytest.mark.parametrize("n_readers", [1, 8])
+def test_one_and_the_most_readers(n_readers):
+    # a single reader through prepare/apply, and the most readers one prepare serves
+    _check(synth.make("paper", seed=16, B=2), n_readers)
+
+
 def test_gain_biases_and_gelu():
     # every reader with its own RMSNorm gain and MLP biases, GELU (tanh form)
     _check(synth.make("paper", seed=14, B=3, act="gelu_tanh"), 3, extras=True)
