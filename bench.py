@@ -586,7 +586,7 @@ def run_multi(args, hip, torch, R, synth, seed=0):
                         ctypes.byref(od[i]), ws.data_ptr(), ws.numel(), stream) for i in range(n_inj)]
         prep_args = (reader.plan, ctypes.byref(sd), acc.data_ptr(), n_inj, warr, gathered.data_ptr(), None,
                      status.data_ptr(), prep.data_ptr(), prep.numel(), ws.data_ptr(), ws.numel(), stream)
-        apply_args = [(reader.plan, prep.data_ptr(), n_inj, i, hs[i].data_ptr(), ctypes.byref(wd[i]),
+        apply_args = [(reader.plan, prep.data_ptr(), prep.numel(), n_inj, i, hs[i].data_ptr(), ctypes.byref(wd[i]),
                        ctypes.byref(oa[i]), ws.data_ptr(), ws.numel(), stream) for i in range(n_inj)]
 
         def check(code, what):

@@ -117,9 +117,9 @@ def load():
                                       ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_size_t,
                                       ctypes.c_void_p]
     lib.readyStatePrepare.restype = ctypes.c_int
-    lib.readyStateApply.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
-                                    ctypes.c_void_p, P(readyWeights), P(readyOutputs), ctypes.c_void_p,
-                                    ctypes.c_size_t, ctypes.c_void_p]
+    lib.readyStateApply.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32,
+                                    ctypes.c_int32, ctypes.c_void_p, P(readyWeights), P(readyOutputs),
+                                    ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
     lib.readyStateApply.restype = ctypes.c_int
     lib.readyVerifyStates.argtypes = [ctypes.c_int32] * 6 + [ctypes.c_void_p] * 5 + [P(readyVerifyBuffer),
                                                                       ctypes.c_void_p]
@@ -196,9 +196,9 @@ def readyStatePrepare(plan, states, accept_idx, n_inj, inj_weights, gathered, lo
                                     logrms, dev_status, prep, prep_bytes, workspace, workspace_bytes, stream)
 
 
-def readyStateApply(plan, prep, n_inj, inj, h, weights, outputs, workspace, workspace_bytes, stream):
-    return load().readyStateApply(plan, prep, n_inj, inj, h, ctypes.byref(weights), ctypes.byref(outputs),
-                                  workspace, workspace_bytes, stream)
+def readyStateApply(plan, prep, prep_bytes, n_inj, inj, h, weights, outputs, workspace, workspace_bytes, stream):
+    return load().readyStateApply(plan, prep, prep_bytes, n_inj, inj, h, ctypes.byref(weights),
+                                  ctypes.byref(outputs), workspace, workspace_bytes, stream)
 
 
 # ------------------------------------------------------------ torch wrapper
@@ -376,7 +376,8 @@ class StateReader:
             workspace = self.workspace(h.device)
         if stream is None:
             stream = torch.cuda.current_stream(h.device).cuda_stream
-        code = readyStateApply(self.plan, prep.data_ptr(), n_inj, inj, h.data_ptr(), wd, od,
-                               workspace.data_ptr(), workspace.numel() * workspace.element_size(), stream)
+        code = readyStateApply(self.plan, prep.data_ptr(), prep.numel() * prep.element_size(), n_inj, inj,
+                               h.data_ptr(), wd, od, workspace.data_ptr(),
+                               workspace.numel() * workspace.element_size(), stream)
         if code != READY_OK:
             raise ReadyError(code, "readyStateApply")

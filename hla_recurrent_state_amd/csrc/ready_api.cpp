@@ -680,16 +680,16 @@ readyStatus readyStatePrepare(const readyPlan* plan, const readyStates* states, 
   return launch_fast(plan, a, (hipStream_t)stream, nullptr);
 }
 
-readyStatus readyStateApply(const readyPlan* plan, const void* prep, int32_t n_inj, int32_t inj, const void* h,
-                            const readyWeights* w, const readyOutputs* o, void* workspace, size_t workspace_bytes,
-                            void* stream) {
+readyStatus readyStateApply(const readyPlan* plan, const void* prep, size_t prep_bytes, int32_t n_inj, int32_t inj,
+                            const void* h, const readyWeights* w, const readyOutputs* o, void* workspace,
+                            size_t workspace_bytes, void* stream) {
   if (!plan || !w || !o) return READY_ERR_NULL_POINTER;
   if (!plan->fast) return READY_ERR_UNSUPPORTED;
   if (n_inj < 1 || n_inj > READY_MAX_INJ || inj < 0 || inj >= n_inj) return READY_ERR_BAD_SHAPE;
   const readyShape& s = plan->s;
   if (!prep || !h || !w->wq || !w->w1 || !w->w2 || !o->out || !workspace) return READY_ERR_NULL_POINTER;
   const PrepLayout L = prep_layout(plan, n_inj);
-  if (workspace_bytes < plan->ws_bytes) return READY_ERR_WORKSPACE_TOO_SMALL;
+  if (workspace_bytes < plan->ws_bytes || prep_bytes < L.bytes) return READY_ERR_WORKSPACE_TOO_SMALL;
   const void* vec_ptrs[] = {h, w->wq, w->h_gamma, w->w1, w->w2, w->b2, o->out, o->delta, o->feat};
   for (const void* ptr : vec_ptrs)
     if (ptr && !aligned16(ptr)) return READY_ERR_MISALIGNED;

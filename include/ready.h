@@ -274,7 +274,8 @@ readyStatus readyStatePrepare(const readyPlan* plan, const readyStates* states, 
 /*
  * Steps 4-5 of reader `inj` (0 <= inj < n_inj, n_inj as given to
  * readyStatePrepare), asynchronously on `stream`, after the prepare call on
- * the same stream (or ordered after it).  prep is read only.
+ * the same stream (or ordered after it).  prep (prep_bytes, at least
+ * readyPrepSize(n_inj)) is read only.
  *   h        device [B][n][d] bf16: the draft representations at this
  *            reader's injection site.
  *   weights  reader inj's wq, h_gamma, w1, b1, w2, b2 (u and v are not
@@ -284,12 +285,12 @@ readyStatus readyStatePrepare(const readyPlan* plan, const readyStates* states, 
  *   workspace  as for readyStateReader.  Calls that share a workspace must
  *            run one after another (the same stream does that).
  * Returns READY_ERR_NULL_POINTER, READY_ERR_UNSUPPORTED, READY_ERR_BAD_SHAPE
- * (n_inj or inj), READY_ERR_WORKSPACE_TOO_SMALL, READY_ERR_MISALIGNED,
+ * (n_inj or inj), READY_ERR_WORKSPACE_TOO_SMALL (workspace or prep), READY_ERR_MISALIGNED,
  * READY_ERR_ALIASING or READY_ERR_HIP.  Allocates and synchronises nothing.
  */
-readyStatus readyStateApply(const readyPlan* plan, const void* prep, int32_t n_inj, int32_t inj, const void* h,
-                            const readyWeights* weights, const readyOutputs* outputs, void* workspace,
-                            size_t workspace_bytes, void* stream);
+readyStatus readyStateApply(const readyPlan* plan, const void* prep, size_t prep_bytes, int32_t n_inj, int32_t inj,
+                            const void* h, const readyWeights* weights, const readyOutputs* outputs,
+                            void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Verify buffer written by readyVerifyStates: element [b][p][l][a][v][k] at

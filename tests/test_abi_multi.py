@@ -131,8 +131,9 @@ def _apply_args(shape, n_inj=3, inj=1):
     F = M * (r + 1)
     w = R.readyWeights(wq=f.alloc(M * r * d * 2), w1=f.alloc(Hm * F * 2), w2=f.alloc(d * Hm * 2))
     o = R.readyOutputs(out=f.alloc(B * n * d * 2))
-    return dict(plan=plan, prep=f.alloc(prep_bytes), n_inj=n_inj, inj=inj, h=f.alloc(B * n * d * 2), weights=w,
-                outputs=o, workspace=f.alloc(ws_bytes), workspace_bytes=ws_bytes, stream=None)
+    return dict(plan=plan, prep=f.alloc(prep_bytes), prep_bytes=prep_bytes, n_inj=n_inj, inj=inj,
+                h=f.alloc(B * n * d * 2), weights=w, outputs=o, workspace=f.alloc(ws_bytes), workspace_bytes=ws_bytes,
+                stream=None)
 
 
 def _apply(shape, mutate=None, **kw):
@@ -167,6 +168,7 @@ def test_apply_argument_errors():
     for m in (set_("inj", 3), set_("inj", -1), set_("n_inj", 0), set_("n_inj", R.READY_MAX_INJ + 1)):
         assert _apply(_shape(), mutate=m) == R.READY_ERR_BAD_SHAPE
     assert _apply(_shape(), mutate=set_("workspace_bytes", 256)) == R.READY_ERR_WORKSPACE_TOO_SMALL
+    assert _apply(_shape(), mutate=set_("prep_bytes", 256)) == R.READY_ERR_WORKSPACE_TOO_SMALL
 
     def mis_h(a):
         a["h"] += 2
