@@ -244,11 +244,11 @@ def stage_breakdown(hip, lib, sets, R, stream, torch, device, reps):
     return out
 
 
-def shape_of(R, cfg, B=None):
+def shape_of(R, cfg, B=None, path="fused"):
     return R.make_shape(B=cfg.B if B is None else B, P=cfg.P, n=cfg.n, L_tot=cfg.L_tot, L_sel=cfg.L_sel,
                         H=cfg.H, r=cfg.r, d=cfg.d, Hm=cfg.Hm, state_dtype=cfg.state_dtype,
                         act_dtype=cfg.act_dtype, weight_dtype=cfg.weight_dtype, act=cfg.act,
-                        shared=cfg.shared, state_eps=cfg.state_eps, h_eps=cfg.h_eps)
+                        shared=cfg.shared, state_eps=cfg.state_eps, h_eps=cfg.h_eps, path=path)
 
 
 # ---------------------------------------------------------------- B = 1 latency
@@ -348,7 +348,25 @@ def run_b1(args, hip, torch, R, synth, seed=0):
     res["fused_graph_cold_us"] = timed(g.replay, True, K)
     res["fused_graph_warm_us"] = back_to_back(g.replay, K)
 
-    # unfused comparator
+    # the library's unfused path on the same inputs: four launches (query sums;
+    # gather, RMS, log-RMS, readout; MLP layer 1; MLP layer 2 and residual)
+    ureader = R.StateReader(shape_of(R, cfg, path="unfused"), cfg.slots)
+    uouts = {"gathered": torch.empty_like(s0.keep[1]["gathered"]), "out": torch.empty_like(s0.keep[1]["out"]),
+             "dev_status": torch.zeros(1, dtype=torch.int32, device=device)}
+    uprep = Prepared(R, ureader, s0.keep[0], uouts, ureader.new_workspace(device), stream)
+
+    def ucall():
+        code = lib.readyStateReader(*uprep.args)
+        if code != 0:
+            raise R.ReadyError(code, "b1 unfused")
+
+    for _ in range(10):
+        ucall()
+    torch.cuda.synchronize(device)
+    res["library_unfused_cold_us"] = timed(ucall, True, K)
+    res["library_unfused_warm_us"] = back_to_back(ucall, K)
+
+    # unfused PyTorch comparator
     dev_in = dict(s0.keep[0])
     w = dev_in["weights"]
     dev_in["_slots"] = torch.tensor(list(cfg.slots), device=device)
@@ -369,6 +387,12 @@ def run_b1(args, hip, torch, R, synth, seed=0):
     diff = (ours - ref_out.float()).abs().max().item()
     res["unfused_vs_fused_max_abs_diff"] = diff
     res["gathered_equal"] = bool(torch.equal(gath2.view(torch.int16), s0.keep[1]["gathered"].view(torch.int16)))
+    res["library_unfused_vs_fused_max_abs_diff"] = (uouts["out"].float() - ours).abs().max().item()
+    res["library_unfused_gathered_equal"] = bool(torch.equal(uouts["gathered"].view(torch.int16),
+                                                             s0.keep[1]["gathered"].view(torch.int16)))
+    if int(uouts["dev_status"].item()) != 0:
+        raise RuntimeError("device status set during the unfused B = 1 run")
+    ureader.close()
     res["cfg"] = cfg
     return res
 
@@ -913,6 +937,8 @@ def main():
             "fused_eager_cold": summ(b1["fused_eager_cold_us"]),
             "fused_graph_warm_mean": round(b1["fused_graph_warm_us"], 2),
             "fused_eager_warm_mean": round(b1["fused_eager_warm_us"], 2),
+            "library_unfused_cold": summ(b1["library_unfused_cold_us"]),
+            "library_unfused_warm_mean": round(b1["library_unfused_warm_us"], 2),
             "unfused_torch_cold": summ(b1["unfused_torch_cold_us"]),
             "unfused_torch_warm_mean": round(b1["unfused_torch_warm_us"], 2),
             "algorithmic_bytes": pbytes,
@@ -921,6 +947,8 @@ def main():
             "stage_median_us": b1["stage_us"],
             "unfused_vs_fused_max_abs_diff": b1["unfused_vs_fused_max_abs_diff"],
             "unfused_gathered_equal": b1["gathered_equal"],
+            "library_unfused_vs_fused_max_abs_diff": b1["library_unfused_vs_fused_max_abs_diff"],
+            "library_unfused_gathered_equal": b1["library_unfused_gathered_equal"],
         }
     if args.configs and args.configs != "none":
         out["configs"] = {}

@@ -44,6 +44,9 @@ READY_ACT_RELU = 2
 
 DTYPES = {"f32": READY_F32, "bf16": READY_BF16}
 ACTS = {"silu": READY_ACT_SILU, "gelu_tanh": READY_ACT_GELU_TANH, "relu": READY_ACT_RELU}
+READY_PATH_FUSED = 0
+READY_PATH_UNFUSED = 1
+PATHS = {"fused": READY_PATH_FUSED, "unfused": READY_PATH_UNFUSED}
 
 # Every symbol include/ready.h declares.
 EXPORTS = ("readyPlanCreate", "readyPlanDestroy", "readyWorkspaceSize", "readyWorkspaceInit",
@@ -63,7 +66,7 @@ class readyShape(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in
                 ("B", "P", "n", "L_tot", "L_sel", "H", "d_k", "d_v", "r", "d", "Hm",
                  "state_dtype", "act_dtype", "weight_dtype", "act", "shared_params")] + \
-               [("state_eps", ctypes.c_float), ("h_eps", ctypes.c_float)]
+               [("state_eps", ctypes.c_float), ("h_eps", ctypes.c_float), ("path", ctypes.c_int32)]
 
 
 class readyStates(ctypes.Structure):
@@ -235,11 +238,11 @@ def verify_states(state_t, k, v, alpha, beta, out, H, stream=None):
 
 def make_shape(B, P, n, L_tot, L_sel, H, r, d, Hm, state_dtype="bf16", act_dtype="bf16",
                weight_dtype="bf16", act="silu", shared=False, state_eps=1e-6, h_eps=1e-6,
-               d_k=128, d_v=128):
+               d_k=128, d_v=128, path="fused"):
     return readyShape(B=B, P=P, n=n, L_tot=L_tot, L_sel=L_sel, H=H, d_k=d_k, d_v=d_v, r=r, d=d, Hm=Hm,
                       state_dtype=DTYPES[state_dtype], act_dtype=DTYPES[act_dtype],
                       weight_dtype=DTYPES[weight_dtype], act=ACTS[act], shared_params=int(bool(shared)),
-                      state_eps=state_eps, h_eps=h_eps)
+                      state_eps=state_eps, h_eps=h_eps, path=PATHS[path])
 
 
 def _ptr(t):

@@ -80,6 +80,7 @@ readyStatus validate_shape(const readyShape& s, const int32_t* layer_ids) {
   if (s.r < 8 || s.r > 128 || s.r % 8 != 0) return READY_ERR_BAD_SHAPE;
   if (s.d < 8 || s.d % 8 != 0 || s.Hm < 1 || s.Hm > 4096) return READY_ERR_BAD_SHAPE;
   if (s.shared_params != 0 && s.shared_params != 1) return READY_ERR_BAD_SHAPE;
+  if (s.path != READY_PATH_FUSED && s.path != READY_PATH_UNFUSED) return READY_ERR_BAD_SHAPE;
   if (!(s.state_eps >= 0.0f) || !(s.h_eps >= 0.0f)) return READY_ERR_BAD_SHAPE;
   for (int l = 0; l < s.L_sel; ++l)
     if (layer_ids[l] < 0 || layer_ids[l] >= s.L_tot) return READY_ERR_LAYER_ID_RANGE;
@@ -142,7 +143,7 @@ readyStatus readyPlanCreate(const readyShape* shape, const int32_t* layer_ids, r
   const bool fits = allbf && s.r <= 32 && p->F % 8 == 0 && p->F <= READY_FAST_MAX_F && s.Hm % 8 == 0 &&
                     p->Nz <= READY_FAST_MAX_NZ && small_ws;
   p->lds = fits ? ready_reader_lds(s.r, p->F, p->Nz, p->small) : 0;
-  p->fast = (fits && p->lds <= 80 * 1024) ? 1 : 0;  // two workgroups per CU
+  p->fast = (fits && p->lds <= 80 * 1024 && s.path == READY_PATH_FUSED) ? 1 : 0;  // two workgroups per CU
 
   if (p->fast) {
     // work items of k_reader

@@ -68,6 +68,16 @@ typedef enum readyStatus {
 
 typedef enum readyDtype { READY_F32 = 0, READY_BF16 = 1 } readyDtype;
 
+/*
+ * Kernel path.  READY_PATH_FUSED runs the whole call as one persistent kernel
+ * where it can (bf16 states, activations and weights, r <= 32) and as four
+ * launches otherwise.  READY_PATH_UNFUSED always runs the four launches
+ * (query sums; gather, RMS, log-RMS, projection and readout; first MLP layer;
+ * second MLP layer and residual): a comparator and a debugging aid with the
+ * same outputs and tolerance.
+ */
+typedef enum readyPath { READY_PATH_FUSED = 0, READY_PATH_UNFUSED = 1 } readyPath;
+
 /* Activation of the bottleneck MLP (the pages do not name it; SiLU default). */
 typedef enum readyAct { READY_ACT_SILU = 0, READY_ACT_GELU_TANH = 1, READY_ACT_RELU = 2 } readyAct;
 
@@ -93,6 +103,7 @@ typedef struct readyShape {
   int32_t shared_params;   /* 0: W_q, U, V stacked per pair; 1: one set for all pairs */
   float state_eps;         /* added to mean(S^2); the pages are silent, 1e-6 suggested */
   float h_eps;             /* added to mean(h^2) in RMSNorm(h); 1e-6 suggested */
+  int32_t path;            /* readyPath: READY_PATH_FUSED (0, default) or READY_PATH_UNFUSED */
 } readyShape;
 
 /*

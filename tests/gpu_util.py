@@ -20,12 +20,12 @@ def tol_for(cfg):
     return 1e-4 if fp32 else 1e-2
 
 
-def reader_shape(cfg, B=None):
+def reader_shape(cfg, B=None, path="fused"):
     from hla_recurrent_state_amd import make_shape
     return make_shape(B=cfg.B if B is None else B, P=cfg.P, n=cfg.n, L_tot=cfg.L_tot, L_sel=cfg.L_sel,
                       H=cfg.H, r=cfg.r, d=cfg.d, Hm=cfg.Hm, state_dtype=cfg.state_dtype,
                       act_dtype=cfg.act_dtype, weight_dtype=cfg.weight_dtype, act=cfg.act,
-                      shared=cfg.shared, state_eps=cfg.state_eps, h_eps=cfg.h_eps)
+                      shared=cfg.shared, state_eps=cfg.state_eps, h_eps=cfg.h_eps, path=path)
 
 
 def alloc_outputs(cfg, device, B=None):
@@ -41,13 +41,13 @@ def alloc_outputs(cfg, device, B=None):
     }
 
 
-def run_reader(inp, device, dev_inputs=None, inplace=False):
+def run_reader(inp, device, dev_inputs=None, inplace=False, path="fused"):
     """One call; returns host copies of all outputs plus the device status."""
     import torch
     from hla_recurrent_state_amd import StateReader
     cfg = inp.cfg
     d = dev_inputs if dev_inputs is not None else to_device(inp, device)
-    reader = StateReader(reader_shape(cfg), cfg.slots)
+    reader = StateReader(reader_shape(cfg, path=path), cfg.slots)
     o = alloc_outputs(cfg, device)
     if inplace:
         o["out"] = d["h"].clone()

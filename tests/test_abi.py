@@ -70,6 +70,21 @@ def test_plan_rejects_bad_shapes(kw, code):
     assert not plan.value
 
 
+def test_plan_path_selector():
+    _lib()
+    st, _ = R.readyPlanCreate(_shape(path="fused"), [0, 1])
+    assert st == R.READY_OK
+    bad = _shape()
+    bad.path = 2
+    assert R.readyPlanCreate(bad, [0, 1])[0] == R.READY_ERR_BAD_SHAPE
+    # the unfused path never takes the single kernel, so the shared-gather
+    # entry points (which need it) report it as unsupported
+    st, plan = R.readyPlanCreate(_shape(path="unfused"), [0, 1])
+    assert st == R.READY_OK and R.readyPrepSize(plan, 2)[0] == R.READY_ERR_UNSUPPORTED
+    st, plan = R.readyPlanCreate(_shape(path="fused"), [0, 1])
+    assert st == R.READY_OK and R.readyPrepSize(plan, 2)[0] == R.READY_OK
+
+
 def test_plan_rejects_bad_dtype_and_activation():
     _lib()
     s = _shape()

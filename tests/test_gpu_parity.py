@@ -29,11 +29,11 @@ def _say(*a):
     sys.stdout.flush()
 
 
-def _check(inp, seqs=None, inplace=False, expect_ok=True):
+def _check(inp, seqs=None, inplace=False, expect_ok=True, path="fused"):
     from tests.gpu_util import compare, oracle_reference, run_reader
     dev = _dev()
-    _say("case", inp.cfg.name, "B", inp.cfg.B, "M", inp.cfg.M, "r", inp.cfg.r, inp.cfg.state_dtype)
-    res = run_reader(inp, dev, inplace=inplace)
+    _say("case", inp.cfg.name, "B", inp.cfg.B, "M", inp.cfg.M, "r", inp.cfg.r, inp.cfg.state_dtype, path)
+    res = run_reader(inp, dev, inplace=inplace, path=path)
     ref = oracle_reference(inp, seqs)
     rep = compare(inp, res, ref)
     _say("  report", rep)
@@ -58,6 +58,24 @@ def test_wide_heads():
 
 def test_batched():
     _check(synth.make("batched", seed=1))
+
+
+# ------------------------------------------------------------ the unfused path (four launches)
+
+def test_paper_shape_unfused_path():
+    _check(synth.make("paper", seed=1), path="unfused")
+
+
+def test_batched_unfused_path_matches_fused():
+    # the four-launch path on the single-kernel path's workload: within
+    # tolerance of the oracle, the gather bit-identical to the single kernel's,
+    # log-RMS equal up to the order of the sum of squares (8 waves against 4)
+    from tests.gpu_util import run_reader
+    inp = synth.make("batched", seed=2)
+    res_u, _, _ = _check(inp, seqs=[0, 31, 63], path="unfused")
+    res_f = run_reader(inp, _dev())
+    assert np.array_equal(res_u["gathered"], res_f["gathered"])
+    assert np.max(np.abs(res_u["logrms"] - res_f["logrms"])) <= 1e-6 * max(1.0, np.max(np.abs(res_f["logrms"])))
 
 
 def test_rank_ablation_sampled():
