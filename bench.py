@@ -397,6 +397,79 @@ def run_b1(args, hip, torch, R, synth, seed=0):
     return res
 
 
+# ---------------------------------------------------------------- step 1 alone
+
+def run_gather(args, hip, torch, R, synth, seed=0):
+    """readyGather (step 1 alone: the committed states into the caller's
+    buffer) at the paper shape (B = 1, 32 pairs, bf16: 1 MiB read + 1 MiB
+    written) and the batched shape (B = 64: 64 MiB + 64 MiB), cold (after a
+    512 MB update) and back to back, with the states drawn on the device.  The
+    pages time the same operator on their hardware as context."""
+    device = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(device).cuda_stream
+    lib = R.load()
+    flush = torch.empty(128 * 1024 * 1024, dtype=torch.float32, device=device)
+    K = args.config_steps
+    res = {}
+    for name in ("paper", "batched"):
+        cfg = synth.make_shape(name)
+        states = torch.empty((cfg.B, cfg.P, cfg.L_tot, cfg.H, 128, 128), dtype=torch.bfloat16, device=device)
+        _fill_states_random(states, seed, torch)
+        g = torch.Generator(device=device)
+        g.manual_seed(seed)
+        acc = torch.randint(0, cfg.P, (cfg.B,), generator=g, device=device, dtype=torch.int32)
+        gathered = torch.empty((cfg.B, cfg.M, 128, 128), dtype=torch.bfloat16, device=device)
+        status = torch.zeros(1, dtype=torch.int32, device=device)
+        reader = R.StateReader(shape_of(R, cfg), cfg.slots)
+        st = states.stride()
+        sd = R.readyStates(base=states.data_ptr(), stride_b=st[0], stride_p=st[1], stride_l=st[2], stride_h=st[3])
+        gargs = (reader.plan, ctypes.byref(sd), acc.data_ptr(), gathered.data_ptr(), status.data_ptr(), stream)
+
+        def call():
+            code = lib.readyGather(*gargs)
+            if code != 0:
+                raise R.ReadyError(code, "gather")
+
+        for _ in range(5):
+            call()
+        torch.cuda.synchronize(device)
+        cold = []
+        for _ in range(K):
+            flush.add_(1.0)
+            a, b = hip.event(), hip.event()
+            hip.record(a, stream)
+            call()
+            hip.record(b, stream)
+            torch.cuda.synchronize(device)
+            cold.append(1000.0 * hip.ms(a, b))
+            hip.destroy(a)
+            hip.destroy(b)
+        a, b = hip.event(), hip.event()
+        hip.record(a, stream)
+        for _ in range(K):
+            call()
+        hip.record(b, stream)
+        torch.cuda.synchronize(device)
+        warm = 1000.0 * hip.ms(a, b) / K
+        hip.destroy(a)
+        hip.destroy(b)
+        if int(status.item()) != 0:
+            raise RuntimeError("device status set during the gather run")
+        nbytes = 2 * cfg.B * cfg.M * 128 * 128 * 2
+        res[name] = {"B": cfg.B, "M": cfg.M, "bytes_read_plus_written": nbytes,
+                     "cold_us": {"p10": round(pct(cold, 10), 2), "p50": round(pct(cold, 50), 2),
+                                 "p90": round(pct(cold, 90), 2)},
+                     "warm_mean_us": round(warm, 2),
+                     "warm_GBps": round(nbytes / (warm * 1e-6) / 1e9, 1),
+                     "warm_frac_of_hbm_peak": round(nbytes / (warm * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+        reader.close()
+        del states, gathered
+    del flush
+    torch.cuda.empty_cache()
+    res["kernel"] = "k_gather"
+    return res
+
+
 # ---------------------------------------------------------------- other configurations
 
 def _fill_states_random(buf, seed, torch):
@@ -950,6 +1023,8 @@ def main():
             "library_unfused_vs_fused_max_abs_diff": b1["library_unfused_vs_fused_max_abs_diff"],
             "library_unfused_gathered_equal": b1["library_unfused_gathered_equal"],
         }
+    if not args.no_b1:
+        out["gather_only"] = run_gather(args, hip, torch, R, synth)
     if args.configs and args.configs != "none":
         out["configs"] = {}
         for name in args.configs.split(","):

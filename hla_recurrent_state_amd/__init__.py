@@ -5,7 +5,7 @@ kernels of libready.so.  If the library is missing, loading raises
 ReadyError -- there is no fallback path.
 
 Low-level names mirror the C functions (readyPlanCreate, readyWorkspaceSize,
-readyStateReader, readyPrepSize, readyStatePrepare, readyStateApply,
+readyStateReader, readyGather, readyPrepSize, readyStatePrepare, readyStateApply,
 readyVerifyStates, readyPlanDestroy, readyStatusString, readyVersion) and the C structs (readyShape, readyStates, readyWeights,
 readyOutputs, readyVerifyBuffer).  StateReader and verify_states wrap them for
 torch tensors: they forward data_ptr() values and the current HIP stream
@@ -50,7 +50,7 @@ PATHS = {"fused": READY_PATH_FUSED, "unfused": READY_PATH_UNFUSED}
 
 # Every symbol include/ready.h declares.
 EXPORTS = ("readyPlanCreate", "readyPlanDestroy", "readyWorkspaceSize", "readyWorkspaceInit",
-           "readyStateReader", "readyStateReaderProfiled", "readyPrepSize", "readyStatePrepare",
+           "readyStateReader", "readyStateReaderProfiled", "readyGather", "readyPrepSize", "readyStatePrepare",
            "readyStateApply", "readyVerifyStates", "readyStatusString", "readyVersion")
 READY_STAGES = 4
 
@@ -113,6 +113,9 @@ def load():
     lib.readyStateReader.restype = ctypes.c_int
     lib.readyStateReaderProfiled.argtypes = lib.readyStateReader.argtypes + [P(ctypes.c_void_p)]
     lib.readyStateReaderProfiled.restype = ctypes.c_int
+    lib.readyGather.argtypes = [ctypes.c_void_p, P(readyStates), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                ctypes.c_void_p]
+    lib.readyGather.restype = ctypes.c_int
     lib.readyPrepSize.argtypes = [ctypes.c_void_p, ctypes.c_int32, P(ctypes.c_size_t)]
     lib.readyPrepSize.restype = ctypes.c_int
     lib.readyStatePrepare.argtypes = [ctypes.c_void_p, P(readyStates), ctypes.c_void_p, ctypes.c_int32,
@@ -183,6 +186,11 @@ def readyStateReaderProfiled(plan, states, accept_idx, h, weights, outputs, work
     ev = (ctypes.c_void_p * (2 * READY_STAGES))(*[e for e in events])
     return load().readyStateReaderProfiled(plan, ctypes.byref(states), accept_idx, h, ctypes.byref(weights),
                                            ctypes.byref(outputs), workspace, workspace_bytes, stream, ev)
+
+
+def readyGather(plan, states, accept_idx, gathered, dev_status, stream):
+    """Raw call of step 1 alone.  Returns status."""
+    return load().readyGather(plan, ctypes.byref(states), accept_idx, gathered, dev_status, stream)
 
 
 def readyPrepSize(plan, n_inj):
@@ -329,6 +337,20 @@ class StateReader:
             code = readyStateReaderProfiled(*args, events)
         if code != READY_OK:
             raise ReadyError(code, "readyStateReader")
+
+    def gather(self, states, accept_idx, gathered, dev_status=None, stream=None):
+        """Step 1 alone: the committed states into `gathered`."""
+        import torch
+        if states.dim() != 6:
+            raise ReadyError(READY_ERR_BAD_SHAPE, "states must be [B][P][L_tot][H][128][128]")
+        st = states.stride()
+        sd = readyStates(base=states.data_ptr(), stride_b=st[0], stride_p=st[1], stride_l=st[2],
+                         stride_h=st[3])
+        if stream is None:
+            stream = torch.cuda.current_stream(states.device).cuda_stream
+        code = readyGather(self.plan, sd, accept_idx.data_ptr(), gathered.data_ptr(), _ptr(dev_status), stream)
+        if code != READY_OK:
+            raise ReadyError(code, "readyGather")
 
     # -------------------------------------------- several readers, one gather
 

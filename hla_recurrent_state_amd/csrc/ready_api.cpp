@@ -604,6 +604,43 @@ readyStatus readyStateReaderProfiled(const readyPlan* plan, const readyStates* s
   return run_reader(plan, states, accept_idx, h, w, o, workspace, workspace_bytes, stream, events);
 }
 
+// ---------------------------------------------------------------- step 1 alone
+
+readyStatus readyGather(const readyPlan* plan, const readyStates* states, const int32_t* accept_idx, void* gathered,
+                        int32_t* dev_status, void* stream) {
+  if (!plan || !states) return READY_ERR_NULL_POINTER;
+  const readyShape& s = plan->s;
+  if (s.B == 0) return READY_OK;
+  if (!states->base || !accept_idx || !gathered) return READY_ERR_NULL_POINTER;
+  const size_t ss = dsize(s.state_dtype);
+  if (!aligned16(states->base) || !aligned16(gathered)) return READY_ERR_MISALIGNED;
+  const int64_t strides[4] = {states->stride_b, states->stride_p, states->stride_l, states->stride_h};
+  for (int64_t st : strides) {
+    if (st < 0) return READY_ERR_BAD_SHAPE;
+    if ((st * (int64_t)ss) % 16 != 0) return READY_ERR_MISALIGNED;
+  }
+  const size_t M = plan->M;
+  const int64_t span = (int64_t)(s.B - 1) * states->stride_b + (int64_t)(s.P - 1) * states->stride_p +
+                       (int64_t)(s.L_tot - 1) * states->stride_l + (int64_t)(s.H - 1) * states->stride_h +
+                       READY_TILE_ELEMS;
+  const Range r_states = range_of(states->base, (size_t)span * ss);
+  const Range r_acc = range_of(accept_idx, (size_t)s.B * 4);
+  const Range r_gath = range_of(gathered, (size_t)s.B * M * READY_TILE_ELEMS * ss);
+  const Range r_st = range_of(dev_status, dev_status ? 4 : 0);
+  if (overlap(r_gath, r_states) || overlap(r_gath, r_acc) || overlap(r_gath, r_st) || overlap(r_st, r_states) ||
+      overlap(r_st, r_acc))
+    return READY_ERR_ALIASING;
+  GatherArgs a;
+  memset(&a, 0, sizeof(a));
+  a.states = states->base;
+  a.sb = states->stride_b; a.sp = states->stride_p; a.sl = states->stride_l; a.sh = states->stride_h;
+  a.accept_idx = accept_idx;
+  for (int l = 0; l < s.L_sel; ++l) a.slot[l] = plan->slot[l];
+  a.B = s.B; a.P = s.P; a.M = (int)M; a.H = s.H; a.esize = (int)ss;
+  a.gathered = gathered; a.dev_status = dev_status;
+  return ready_launch_gather(a, (hipStream_t)stream) == hipSuccess ? READY_OK : READY_ERR_HIP;
+}
+
 // ---------------------------------------------------------------- several readers sharing one gather
 
 readyStatus readyPrepSize(const readyPlan* plan, int32_t n_inj, size_t* bytes) {

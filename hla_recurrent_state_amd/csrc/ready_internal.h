@@ -126,6 +126,19 @@ struct FastArgs {
 #define READY_TICKET_GROUPS 32    // state-tile ticket counters
 #define READY_ACC_LDS 1024        // accept indices staged in LDS
 
+// Step 1 alone: one workgroup per (sequence, pair) tile
+struct GatherArgs {
+  const void* states;
+  int64_t sb, sp, sl, sh;          // element strides of the verify buffer
+  const int32_t* accept_idx;       // [B]
+  int32_t slot[READY_MAX_LSEL];
+  int B, P, M, H;
+  int esize;                       // bytes per state element (2 or 4)
+  void* gathered;                  // [B][M][128][128]
+  int32_t* dev_status;             // or null
+};
+READY_HIDDEN hipError_t ready_launch_gather(const GatherArgs& a, hipStream_t s);
+
 // Verify-state producer: one workgroup per (sequence, pair)
 struct VerifyArgs {
   const void* state_t;             // [B][M][128][128] state dtype

@@ -232,6 +232,26 @@ readyStatus readyStateReaderProfiled(const readyPlan* plan, const readyStates* s
                                      void* const* events);
 
 /*
+ * Step 1 alone: gathered[b][m] = states[b][accept_idx[b]][layer_ids[l]][a]
+ * (m = l H + a) for every sequence and selected layer-head pair, a bit copy
+ * into the caller's preallocated buffer (arXiv text, section 3.2 "Avoiding
+ * redundant data movement"; section 3.1 "Drafting, verification, and
+ * commitment").  readyStateReader does the same copy fused with the later
+ * steps; this entry point is for callers that want only the committed states.
+ *   states, accept_idx  as for readyStateReader (plan's B, P, L_tot, H,
+ *                       layer slots and state_dtype).
+ *   gathered   [B][M][d_v][d_k] in state_dtype, 16-byte aligned; must not
+ *              overlap the states, accept_idx or dev_status.
+ *   dev_status one int32 or NULL: an accept index outside [0, P) stores
+ *              READY_ERR_ACCEPT_IDX there and leaves that sequence's tiles.
+ * Asynchronous on `stream`; allocates and synchronises nothing.  Returns
+ * READY_ERR_NULL_POINTER, READY_ERR_BAD_SHAPE (negative stride),
+ * READY_ERR_MISALIGNED, READY_ERR_ALIASING or READY_ERR_HIP.
+ */
+readyStatus readyGather(const readyPlan* plan, const readyStates* states, const int32_t* accept_idx, void* gathered,
+                        int32_t* dev_status, void* stream);
+
+/*
  * Several readers sharing one gather.  The pages compare drafters with one
  * reader (final draft layer) and with readers injected into draft layers
  * (0, 2, 4) or all five, each reader with its own parameters (arXiv text,

@@ -341,3 +341,61 @@ def test_verify_aliasing():
     def inside(a):
         a["state_t"] = a["out"].base + 7 * 128 * 128 * 2   # an input inside the buffer's span
     assert _verify_call(mutate=inside) == R.READY_ERR_ALIASING
+
+
+# ---------------------------------------------------------------- step 1 alone (readyGather)
+
+def _gather_call(shape, mutate=None):
+    _lib()
+    st, plan = R.readyPlanCreate(shape, [0, 1])
+    assert st == R.READY_OK
+    f = _Fake(shape)
+    B, P, L, H = shape.B, shape.P, shape.L_tot, shape.H
+    M = shape.L_sel * H
+    tile = 128 * 128
+    es = 2 if shape.state_dtype == R.READY_BF16 else 4
+    args = dict(plan=plan,
+                states=R.readyStates(base=f.alloc(max(B, 1) * P * L * H * tile * es), stride_b=P * L * H * tile,
+                                     stride_p=L * H * tile, stride_l=H * tile, stride_h=tile),
+                accept_idx=f.alloc(4 * max(B, 1)), gathered=f.alloc(max(B, 1) * M * tile * es),
+                dev_status=f.alloc(4), stream=None)
+    if mutate:
+        mutate(args)
+    code = R.readyGather(**args)
+    R.readyPlanDestroy(plan)
+    return code
+
+
+def test_gather_validation():
+    assert _gather_call(_shape(B=0)) == R.READY_OK
+
+    def set_(k, v):
+        def f(a):
+            a[k] = v
+        return f
+
+    def null_states(a):
+        a["states"].base = None
+
+    for m in (set_("accept_idx", None), set_("gathered", None), null_states):
+        assert _gather_call(_shape(), mutate=m) == R.READY_ERR_NULL_POINTER
+
+    def mis_gathered(a):
+        a["gathered"] += 8
+
+    def mis_stride(a):
+        a["states"].stride_l += 1
+
+    def neg_stride(a):
+        a["states"].stride_b = -a["states"].stride_b
+    assert _gather_call(_shape(), mutate=mis_gathered) == R.READY_ERR_MISALIGNED
+    assert _gather_call(_shape(), mutate=mis_stride) == R.READY_ERR_MISALIGNED
+    assert _gather_call(_shape(), mutate=neg_stride) == R.READY_ERR_BAD_SHAPE
+
+    def gathered_in_states(a):
+        a["gathered"] = a["states"].base + 4 * 128 * 128 * 2
+
+    def status_in_gathered(a):
+        a["dev_status"] = a["gathered"] + 64
+    assert _gather_call(_shape(), mutate=gathered_in_states) == R.READY_ERR_ALIASING
+    assert _gather_call(_shape(), mutate=status_in_gathered) == R.READY_ERR_ALIASING
