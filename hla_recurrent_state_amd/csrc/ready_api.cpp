@@ -25,7 +25,6 @@
 
 #include <algorithm>
 #include <new>
-#include <vector>
 
 #include "ready_internal.h"
 
@@ -678,12 +677,13 @@ readyStatus readyStatePrepare(const readyPlan* plan, const readyStates* states, 
                        (int64_t)(s.B - 1) * states->stride_b + (int64_t)(s.P - 1) * states->stride_p +
                        (int64_t)(s.L_tot - 1) * states->stride_l + (int64_t)(s.H - 1) * states->stride_h +
                        READY_TILE_ELEMS;
-  std::vector<Range> inputs;
-  inputs.push_back(range_of(states->base, (size_t)span * 2));
-  inputs.push_back(range_of(accept_idx, (size_t)s.B * 4));
+  Range inputs[2 + 2 * READY_MAX_INJ];  // (no host allocation on the call path)
+  int n_in = 0;
+  inputs[n_in++] = range_of(states->base, (size_t)span * 2);
+  inputs[n_in++] = range_of(accept_idx, (size_t)s.B * 4);
   for (int i = 0; i < n_inj; ++i) {
-    inputs.push_back(range_of(inj_weights[i].u, mz * s.r * READY_TILE * 2));
-    inputs.push_back(range_of(inj_weights[i].v, mz * READY_TILE * s.r * 2));
+    inputs[n_in++] = range_of(inj_weights[i].u, mz * s.r * READY_TILE * 2);
+    inputs[n_in++] = range_of(inj_weights[i].v, mz * READY_TILE * s.r * 2);
   }
   const Range outputs[] = {range_of(gathered, (size_t)s.B * M * READY_TILE_ELEMS * 2),
                            range_of(logrms, logrms ? (size_t)s.B * M * 4 : 0),
@@ -691,8 +691,8 @@ readyStatus readyStatePrepare(const readyPlan* plan, const readyStates* states, 
                            range_of(workspace, plan->ws_bytes)};
   const int n_out = (int)(sizeof(outputs) / sizeof(outputs[0]));
   for (int i = 0; i < n_out; ++i) {
-    for (const Range& in : inputs)
-      if (overlap(outputs[i], in)) return READY_ERR_ALIASING;
+    for (int k = 0; k < n_in; ++k)
+      if (overlap(outputs[i], inputs[k])) return READY_ERR_ALIASING;
     for (int j = i + 1; j < n_out; ++j)
       if (overlap(outputs[i], outputs[j])) return READY_ERR_ALIASING;
   }
