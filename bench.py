@@ -888,7 +888,16 @@ def cpu_baseline(bat, budget_s):
            "logrms": extra["logrms"].cpu().numpy(), "delta": extra["delta"].cpu().numpy(),
            "feat": extra["feat"].cpu().numpy(), "dev_status": int(outs["dev_status"].item())}
     rep = compare(inp, res, ref)
+    model = ""
+    try:
+        for line in open("/proc/cpuinfo", encoding="utf-8"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
     base = {"value": round(committed / el / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "cpu_model": model, "host_cores_available": len(os.sched_getaffinity(0)),
             "sample": "float64 numpy oracle, steps 1-5, on %d of the %d sequences of the batched "
                       "workload, %d timed passes of %.2f s each (committed-state bytes of the sample / "
                       "mean time)" % (nseq, cfg.B, reps, el)}
