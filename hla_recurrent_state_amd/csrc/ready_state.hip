@@ -88,24 +88,35 @@ __global__ __launch_bounds__(256) void k_state(StateArgs a) {
   if (lane == 0) s_wsum[wave] = ss;
 
   // ---- step 4 (query side): z_j and q_j of this pair ----
-  if (tid < n) {
-    const int rho = b * n + tid;
+  // The K-split partial sums are spread over several lanes per value, so
+  // that few loads per lane stand between the query launch and this one:
+  // 32 lanes per row for the sums of squares of h, 4 per value of z; the
+  // lanes of one value are consecutive and meet through shuffles (a fixed
+  // order, so the result does not depend on timing).
+  for (int t32 = tid; t32 < 32 * n; t32 += 256) {  // whole groups of 32 lanes
+    const int j = t32 >> 5, part = t32 & 31;
+    const int rho = b * n + j;
     float hs = 0.0f;
-#pragma unroll 8
-    for (int ks = 0; ks < a.ksz; ++ks) hs += a.hss[(int64_t)ks * rows + rho];
-    s_rs[tid] = 1.0f / sqrtf(hs / (float)a.d + a.h_eps);
+#pragma unroll 4
+    for (int ks = part; ks < a.ksz; ks += 32) hs += a.hss[(int64_t)ks * rows + rho];
+#pragma unroll
+    for (int o = 1; o < 32; o <<= 1) hs += __shfl_xor(hs, o, 64);
+    if (part == 0) s_rs[j] = 1.0f / sqrtf(hs / (float)a.d + a.h_eps);
   }
   __syncthreads();
   const float ms = ((s_wsum[0] + s_wsum[1]) + (s_wsum[2] + s_wsum[3])) * (1.0f / READY_TILE_ELEMS);
   const float rms = sqrtf(ms + a.state_eps);
   const float inv_rms = 1.0f / rms;
-  for (int e = tid; e < n * r; e += 256) {
+  for (int e4 = tid; e4 < 4 * n * r; e4 += 256) {  // 4 n r is a multiple of 4: whole groups of 4 lanes
+    const int e = e4 >> 2, part = e4 & 3;
     const int j = e / r, i = e - j * r;
     const int64_t rho = b * n + j;
     float s = 0.0f;
-#pragma unroll 8
-    for (int ks = 0; ks < a.ksz; ++ks) s += a.zpart[((int64_t)ks * rows + rho) * a.nz + mz * r + i];
-    s_z[e] = s * s_rs[j];
+#pragma unroll 4
+    for (int ks = part; ks < a.ksz; ks += 4) s += a.zpart[((int64_t)ks * rows + rho) * a.nz + mz * r + i];
+    s += __shfl_xor(s, 1, 64);
+    s += __shfl_xor(s, 2, 64);
+    if (part == 0) s_z[e] = s * s_rs[j];
   }
   __syncthreads();
   const void* U = (const char*)a.u + (int64_t)mz * r * READY_TILE * sizeof(TW);
