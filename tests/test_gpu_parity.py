@@ -249,6 +249,13 @@ def test_out_of_range_accept_index_sets_status_and_skips_sequence(r):
 
 # ------------------------------------------------------------ properties
 
+def test_fast_path_large_batch():
+    # 512 sequences (16384 state tiles, 3584 draft rows): many tiles per
+    # workgroup and many row blocks of the query and MLP items; the oracle
+    # checks sequences across the batch
+    _check(synth.make(make_shape("batched", B=512, t=8), seed=35), seqs=[0, 1, 255, 300, 511])
+
+
 def test_in_place_output():
     _check(synth.make(make_shape("paper", B=2, t=16), seed=31), inplace=True)
 
