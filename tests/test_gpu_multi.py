@@ -224,3 +224,23 @@ def test_prepare_then_apply_repeated_calls():
     for i in range(3):
         for key in ("out", "delta", "feat"):
             assert np.array_equal(a[i][key], b[i][key]), (i, key)
+
+
+def test_producer_feeds_several_readers():
+    # verify-state producer -> prepare -> apply per reader, against the
+    # oracle's multi_reader on the produced states
+    from tests.gpu_util import compare
+    from tests.test_gpu_verify import _bits, _run as run_producer
+    dev = _dev()
+    cfg = synth.make_shape("paper", B=3, H=4, t=12)
+    inp = synth.make(cfg, seed=43)
+    vi = synth.make_verify(B=cfg.B, P=cfg.P, L=cfg.L_tot, H=cfg.H, t=12, seed=44)
+    buf = run_producer(vi, dev)
+    inp.buf = _bits(buf, "bf16").reshape(cfg.B, cfg.P, cfg.L_tot, cfg.H, 128, 128)
+    readers = synth.make_readers(inp, 3, seed=45)
+    res = _run_multi(inp, readers, dev)
+    refs = _oracle(inp, readers, list(range(cfg.B)))
+    for i in range(3):
+        rep = compare(inp, res[i], refs[i])
+        _say("  reader", i, rep)
+        assert rep["ok"], (i, rep)
