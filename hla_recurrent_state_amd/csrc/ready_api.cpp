@@ -310,7 +310,11 @@ readyStatus launch_fast(const readyPlan* plan, FastArgs& a, hipStream_t strm, vo
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     return READY_ERR_HIP;
-  const int per_cu = std::min(2, ready_reader_per_cu(plan->s.r, plan->small, plan->lds));
+  // prepare launches (state tiles only, no waits between workgroups) take a
+  // third workgroup per CU for more tiles in flight where registers allow
+  // (r <= 16)
+  const int cap = (a.mode == READY_MODE_PREPARE && plan->s.r <= 16) ? 3 : 2;
+  const int per_cu = std::min(cap, ready_reader_per_cu(plan->s.r, plan->small, plan->lds, a.mode));
   if (per_cu < 1 || cus < 1) return READY_ERR_HIP;
   const int grid = per_cu * cus;
   reader_roles(a, grid);

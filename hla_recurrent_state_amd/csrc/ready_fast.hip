@@ -975,7 +975,7 @@ __device__ __forceinline__ void mlp2_item(const FastArgs& a, int rb, int cb, uns
 // (Z items and O items per XCD: the K chunks ks with ks % nxcd == x, and the
 // column blocks cb with cb % nxcd == x, go to the workgroups on XCD x).
 template <int RR, int SMALL, int MODE>
-__global__ __launch_bounds__(256, 2) void k_reader(FastArgs a) {
+__global__ __launch_bounds__(256, (MODE == READY_MODE_PREPARE && RR <= 16) ? 3 : 2) void k_reader(FastArgs a) {
   constexpr int BMZ = SMALL ? 16 : 64, BMO = SMALL ? 16 : 64;
   constexpr int NST = (SMALL ? READY_ZCHUNK_SMALL : READY_ZCHUNK_LARGE) / 128;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
@@ -1119,9 +1119,9 @@ hipError_t ready_launch_reader(const FastArgs& a, int small, int grid, hipStream
   return hipGetLastError();
 }
 
-// Workgroups of k_reader that one CU holds at once, the least over the three
-// modes (0 on error).
-int ready_reader_per_cu(int r, int small, size_t lds) {
+// Workgroups of k_reader in launch mode `mode` that one CU holds at once (0 on
+// error).
+int ready_reader_per_cu(int r, int small, size_t lds, int mode) {
   int nb = 1 << 20;
   hipError_t e = hipSuccess;
 #define READY_OCC_ONE(KERNEL)                                                     \
@@ -1130,11 +1130,11 @@ int ready_reader_per_cu(int r, int small, size_t lds) {
     if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n1, KERNEL, 256, lds); \
     nb = n1 < nb ? n1 : nb;                                                       \
   } while (0)
-#define READY_OCC_SM(RRV, SM)                                          \
-  do {                                                                 \
-    READY_OCC_ONE((k_reader<RRV, SM, READY_MODE_FULL>));               \
-    READY_OCC_ONE((k_reader<RRV, SM, READY_MODE_PREPARE>));            \
-    READY_OCC_ONE((k_reader<RRV, SM, READY_MODE_APPLY>));              \
+#define READY_OCC_SM(RRV, SM)                                                               \
+  do {                                                                                      \
+    if (mode == READY_MODE_PREPARE) READY_OCC_ONE((k_reader<RRV, SM, READY_MODE_PREPARE>)); \
+    else if (mode == READY_MODE_APPLY) READY_OCC_ONE((k_reader<RRV, SM, READY_MODE_APPLY>)); \
+    else READY_OCC_ONE((k_reader<RRV, SM, READY_MODE_FULL>));                               \
   } while (0)
 #define READY_OCC_CASE(RRV)            \
   do {                                 \

@@ -220,4 +220,4 @@ READY_HIDDEN hipError_t ready_launch_gemm_mfma(const GemmArgs& g, int x_dt, int 
 READY_HIDDEN hipError_t ready_launch_reader(const FastArgs& a, int small, int grid, hipStream_t s, StageEvents ev);
 READY_HIDDEN hipError_t ready_launch_ws_init(uint32_t* counters, int n_counters, uint32_t magic, hipStream_t s);
 READY_HIDDEN size_t ready_reader_lds(int r, int F, int Nz, int small);
-READY_HIDDEN int ready_reader_per_cu(int r, int small, size_t lds);
+READY_HIDDEN int ready_reader_per_cu(int r, int small, size_t lds, int mode);
