@@ -684,9 +684,12 @@ __device__ __forceinline__ void mlp1_item(const FastArgs& a, int item, unsigned 
   constexpr int RU = RR <= 8 ? 4 : (RR <= 16 ? 2 : 1);  // rows per step of the f loop
   const int nseq = b1 - b0 + 1;
   const int nmi = a.M * RR;
-  u32x4 pv[PS][CR4];
-  float ellv[PS];
-  auto load_p = [&](int e, int s0) {
+  // at r <= 8 the P rows of a thread's second f item (e = tid + 256) come
+  // in the same trip as its first, into a second register set
+  constexpr bool PRE2 = RR <= 8;
+  u32x4 pv[PS][CR4], pv2[PRE2 ? PS : 1][PRE2 ? CR4 : 1];
+  float ellv[PS], ellv2[PRE2 ? PS : 1];
+  auto load_p_into = [&](int e, int s0, auto& dst, auto& del) {
     const int m = e / RR, i = e - (e / RR) * RR;
 #pragma unroll
     for (int s = 0; s < PS; ++s) {
@@ -694,11 +697,13 @@ __device__ __forceinline__ void mlp1_item(const FastArgs& a, int item, unsigned 
       const bool live = e < nmi && s0 + s < nseq && ok;
       const uint32_t pofs = (uint32_t)((((b * a.M + m) * RR + i) * RR) * 4);
 #pragma unroll
-      for (int c = 0; c < CR4; ++c) pv[s][c] = live ? ld_coh16(a.pmat, pofs + 16 * c) : u32x4{0u, 0u, 0u, 0u};
-      ellv[s] = (live && i == 0) ? ld_coh4(a.ell, (uint32_t)(4 * (b * a.M + m))) : 0.0f;
+      for (int c = 0; c < CR4; ++c) dst[s][c] = live ? ld_coh16(a.pmat, pofs + 16 * c) : u32x4{0u, 0u, 0u, 0u};
+      del[s] = (live && i == 0) ? ld_coh4(a.ell, (uint32_t)(4 * (b * a.M + m))) : 0.0f;
     }
   };
+  auto load_p = [&](int e, int s0) { load_p_into(e, s0, pv, ellv); };
   load_p(tid, 0);
+  if constexpr (PRE2) load_p_into(tid + 256, 0, pv2, ellv2);
   // the sums of squares of h (threads 0-15, one row each) travel with the
   // other loads
   const bool hrow = tid < 16 && tid < rows && ok;
@@ -739,7 +744,20 @@ __device__ __forceinline__ void mlp1_item(const FastArgs& a, int item, unsigned 
     const int m = e0 / RR, i = e0 - (e0 / RR) * RR;
     const int mz = a.shared ? 0 : m;
     for (int s0 = 0; s0 < nseq; s0 += PS) {
-      if (e0 != tid || s0 != 0) load_p(e0, s0);
+      if constexpr (PRE2) {
+        if (e0 == tid + 256 && s0 == 0) {
+#pragma unroll
+          for (int s = 0; s < PS; ++s) {
+#pragma unroll
+            for (int c = 0; c < CR4; ++c) pv[s][c] = pv2[s][c];
+            ellv[s] = ellv2[s];
+          }
+        } else if (e0 != tid || s0 != 0) {
+          load_p(e0, s0);
+        }
+      } else if (e0 != tid || s0 != 0) {
+        load_p(e0, s0);
+      }
 #pragma unroll
       for (int s = 0; s < PS; ++s) {
         const int b = b0 + s0 + s;
@@ -976,7 +994,8 @@ __device__ __forceinline__ void mlp2_item(const FastArgs& a, int rb, int cb, uns
 // column blocks cb with cb % nxcd == x, go to the workgroups on XCD x).
 template <int RR, int SMALL, int MODE>
 __global__ __launch_bounds__(256, (MODE == READY_MODE_PREPARE && RR <= 16) ? 3 : 2) void k_reader(FastArgs a) {
-  constexpr int BMZ = SMALL ? 16 : 64, BMO = SMALL ? 16 : 64;
+  constexpr int BMZ = SMALL ? 16 : READY_BMZ_LARGE;
+  constexpr int BMO = SMALL ? 16 : (MODE == READY_MODE_APPLY ? READY_BMO_APPLY : READY_BMO_LARGE);
   constexpr int NST = (SMALL ? READY_ZCHUNK_SMALL : READY_ZCHUNK_LARGE) / 128;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   __shared__ int s_last;
@@ -1073,7 +1092,9 @@ __global__ void k_ws_init(uint32_t* counters, int n, uint32_t magic) {
 // ---------------------------------------------------------------- launchers
 
 size_t ready_reader_lds(int r, int F, int Nz, int small) {
-  const int BMZ = small ? 16 : 64, BMO = small ? 16 : 64;
+  // the O item's area is sized for the larger of the two large-row forms
+  const int BMZ = small ? 16 : READY_BMZ_LARGE;
+  const int BMO = small ? 16 : (READY_BMO_APPLY > READY_BMO_LARGE ? READY_BMO_APPLY : READY_BMO_LARGE);
   const int NB = (r + 15) / 16;
   const size_t z_bytes = (size_t)(BMZ + 64) * 256 + 16;
   const size_t s_bytes = (size_t)READY_TILE_ELEMS * 2 + (size_t)r * (READY_TILE + 8) * 2 + (size_t)READY_TILE * r * 2 +

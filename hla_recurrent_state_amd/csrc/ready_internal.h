@@ -119,7 +119,11 @@ struct FastArgs {
 #define READY_WS_MAGIC 0x52454459u // "READY"
 // k_reader tiles: z in BMZ x 64 tiles over K chunks of READY_ZCHUNK_* (a
 // multiple of 128), out in BMO x READY_OCOLS tiles; BMZ = BMO = 16 for at
-// most 16 rows, else 64
+// most 16 rows, else READY_BMZ_LARGE and READY_BMO_LARGE (READY_BMO_APPLY in
+// apply launches, which have no state stream for short O items to overlap)
+#define READY_BMZ_LARGE 64
+#define READY_BMO_LARGE 32
+#define READY_BMO_APPLY 64
 #define READY_ZCHUNK_SMALL 384
 #define READY_ZCHUNK_LARGE 640
 #define READY_OCOLS 128
@@ -216,7 +220,7 @@ READY_HIDDEN hipError_t ready_launch_reduce_bias_act(const GemmArgs& g, int kspl
 // bm: rows per workgroup tile (16 or 64); weights must be bf16
 READY_HIDDEN hipError_t ready_launch_gemm_mfma(const GemmArgs& g, int x_dt, int out_dt, int epi, int bm,
                                                dim3 grid, hipStream_t s, StageEvents ev);
-// fast path; small: at most 16 rows (16-row tiles), else 64-row tiles
+// fast path; small: at most 16 rows (16-row tiles), else the large tiles
 READY_HIDDEN hipError_t ready_launch_reader(const FastArgs& a, int small, int grid, hipStream_t s, StageEvents ev);
 READY_HIDDEN hipError_t ready_launch_ws_init(uint32_t* counters, int n_counters, uint32_t magic, hipStream_t s);
 READY_HIDDEN size_t ready_reader_lds(int r, int F, int Nz, int small);
