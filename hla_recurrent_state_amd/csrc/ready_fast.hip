@@ -835,8 +835,8 @@ __device__ __forceinline__ void mlp1_item(const FastArgs& a, int item, unsigned 
 
 // ---------------------------------------------------------------- O items
 
-// Rows [BM rb, BM rb + BM) and columns [128 cb, 128 cb + 128) of out; wave w
-// computes columns 128 cb + 32 w .. + 31.  The W2 rows of the lane's two
+// Rows [BM rb, BM rb + BM) and columns [OC cb, OC cb + OC) of out (OC =
+// READY_OCOLS); wave w computes columns OC cb + (OC / 4) w .. + OC / 4 - 1.  The W2 rows of the lane's two
 // columns and the tile's h values are loaded before waiting; after the A
 // items of the rows are counted, the a rows are staged in LDS by passes of
 // 256 values of K (device-coherent loads) for the matrix instructions.  The
@@ -845,6 +845,8 @@ __device__ __forceinline__ void mlp1_item(const FastArgs& a, int item, unsigned 
 template <int BM>
 __device__ __forceinline__ void mlp2_item(const FastArgs& a, int rb, int cb, unsigned char* smem) {
   constexpr int OC = READY_OCOLS, KT = 256, LA = KT + 8, LO = OC + 4;
+  constexpr int WCOL = OC / 4, H2 = WCOL / 16;  // columns per wave, 16-column blocks per wave
+  static_assert(WCOL % 16 == 0, "whole 16-column blocks per wave");
   constexpr int SA = BM * LA * 2, SO = BM * LO * 4;
   uint16_t* sA = (uint16_t*)smem;   // [BM][LA]
   float* sO = (float*)smem;         // [BM][LO], after the K passes
@@ -854,17 +856,17 @@ __device__ __forceinline__ void mlp2_item(const FastArgs& a, int rb, int cb, uns
   const int lr = lane & 15, lg = lane >> 4;
   const int row0 = rb * BM, col0 = cb * OC;
   const int rows = min(BM, a.R - row0);
-  int colv[2];
-  bool cv[2];
+  int colv[H2];
+  bool cv[H2];
 #pragma unroll
-  for (int h2 = 0; h2 < 2; ++h2) {
-    colv[h2] = col0 + 32 * wave + 16 * h2 + lr;
+  for (int h2 = 0; h2 < H2; ++h2) {
+    colv[h2] = col0 + WCOL * wave + 16 * h2 + lr;
     cv[h2] = colv[h2] < a.d;
   }
 
-  u32x4 bq[2][KT / 32];
+  u32x4 bq[H2][KT / 32];
 #pragma unroll
-  for (int h2 = 0; h2 < 2; ++h2)
+  for (int h2 = 0; h2 < H2; ++h2)
 #pragma unroll
     for (int s = 0; s < KT / 32; ++s) {
       const int kk = 32 * s + 8 * lg;
@@ -895,17 +897,17 @@ __device__ __forceinline__ void mlp2_item(const FastArgs& a, int rb, int cb, uns
                                          : 1u;
   }
 
-  f32x4 acc[BM / 16][2];
+  f32x4 acc[BM / 16][H2];
 #pragma unroll
   for (int i = 0; i < BM / 16; ++i)
 #pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2) acc[i][h2] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int h2 = 0; h2 < H2; ++h2) acc[i][h2] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
   for (int kb = 0; kb < a.Hm; kb += KT) {
     const int klen = min(KT, a.Hm - kb);
     if (kb > 0) {
 #pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2)
+      for (int h2 = 0; h2 < H2; ++h2)
 #pragma unroll
         for (int s = 0; s < KT / 32; ++s) {
           const int kk = 32 * s + 8 * lg;
@@ -940,7 +942,7 @@ __device__ __forceinline__ void mlp2_item(const FastArgs& a, int rb, int cb, uns
         for (int i = 0; i < BM / 16; ++i) {
           const u32x4 aop = *(const u32x4*)&sA[(16 * i + lr) * LA + 32 * s + 8 * lg];
 #pragma unroll
-          for (int h2 = 0; h2 < 2; ++h2) acc[i][h2] = mfma16x16x32(aop, bq[h2][s], acc[i][h2]);
+          for (int h2 = 0; h2 < H2; ++h2) acc[i][h2] = mfma16x16x32(aop, bq[h2][s], acc[i][h2]);
         }
       }
     }
@@ -950,9 +952,9 @@ __device__ __forceinline__ void mlp2_item(const FastArgs& a, int rb, int cb, uns
 #pragma unroll
   for (int i = 0; i < BM / 16; ++i)
 #pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2)
+    for (int h2 = 0; h2 < H2; ++h2)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) sO[(16 * i + 4 * lg + e) * LO + 32 * wave + 16 * h2 + lr] = acc[i][h2][e];
+      for (int e = 0; e < 4; ++e) sO[(16 * i + 4 * lg + e) * LO + WCOL * wave + 16 * h2 + lr] = acc[i][h2][e];
   __syncthreads();
 #pragma unroll
   for (int k = 0; k < EPT; ++k) {
