@@ -125,6 +125,22 @@ def test_bf16_fast_path_ragged(r, rows):
     _check(inp)
 
 
+@pytest.mark.parametrize("slots,B", [((4, 1, 3), 2), ((4, 1, 3), 5), ((4, 1, 3, 0, 2), 5)])
+def test_bf16_fast_path_many_pairs_rank_8(slots, B):
+    """r = 8 with 48 or 80 layer-head pairs: more (pair, output) items of f
+    than threads in a workgroup (384 or 640 against 256), so threads build
+    two or three of them, at 14 rows (one 16-row tile) and 35 rows (a ragged
+    32-row block of out)."""
+    cfg = make_shape("paper", B=B, n=7, H=16, L_tot=5, slots=slots, t=12, r=8, d=1048, Hm=72)
+    assert cfg.M * cfg.r > 256
+    from hla_recurrent_state_amd import StateReader
+    from tests.gpu_util import reader_shape
+    sr = StateReader(reader_shape(cfg), cfg.slots)
+    sr.prep_size(1)  # raises unless the plan takes the single-kernel path
+    sr.close()
+    _check(synth.make(cfg, seed=60 + len(slots) + B))
+
+
 @pytest.mark.parametrize("act", ["gelu_tanh", "relu"])
 def test_bf16_fast_path_activations(act):
     cfg = make_shape("paper", B=2, t=12, act=act)
