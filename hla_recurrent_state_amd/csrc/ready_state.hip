@@ -272,19 +272,19 @@ __device__ __forceinline__ void mm_fetch(const StateArgs& a, int t, int T, u32x4
 }
 
 // First K-split partial sums of z and of the squares of h for item t: the
-// elements (zj[k], zi[k]) of this thread (clamped into range like the tile
-// loads; values outside j < n, i < r are not used).
-__device__ __forceinline__ void mm_zfetch(const StateArgs& a, int t, int T, const int (&zj)[4],
-                                          const int (&zi)[4], float (&zr)[4], float (&hr)[4]) {
+// four elements (zj, zi .. zi + 3) of this thread, one 16-byte load, and the
+// sum of squares of row zj (clamped into range like the tile loads; values
+// outside j < n, i < r are not used).  r is a multiple of 8, so the four
+// elements lie in one row and one aligned 16-byte chunk.
+__device__ __forceinline__ void mm_zfetch(const StateArgs& a, int t, int T, int zj, int zi, float (&zr)[4],
+                                          float& hr) {
   const int tc = min(t, T - 1);
   const int m = tc / a.B, b = tc - m * a.B;
   const int mz = a.shared ? 0 : m;
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const int64_t row = (int64_t)b * a.n + min(zj[k], a.n - 1);
-    zr[k] = a.zpart[row * a.nz + mz * a.r + min(zi[k], a.r - 1)];
-    hr[k] = a.hss[row];
-  }
+  const int64_t row = (int64_t)b * a.n + min(zj, a.n - 1);
+  const float4 v = *(const float4*)(a.zpart + row * a.nz + mz * a.r + min(zi, a.r - 4));
+  zr[0] = v.x; zr[1] = v.y; zr[2] = v.z; zr[3] = v.w;
+  hr = a.hss[row];
 }
 
 // U^T and V^T of reader pair mz into LDS, zero past rank r up to rp.
@@ -323,8 +323,8 @@ __device__ __forceinline__ void mm_stage_uv(const StateArgs& a, int mz, int rp, 
 
 // One tile: item t with its loaded chunks P and accept index pa.
 __device__ __forceinline__ void mm_tile(const StateArgs& a, int t, const u32x4 (&P)[MM_CH], int pa, int rp,
-                                        const int (&zj)[4], const int (&zi)[4], const float (&zr)[4],
-                                        const float (&hr)[4], unsigned char* smem, int& cur_mz) {
+                                        int zj, int zi, const float (&zr)[4], float hr, unsigned char* smem,
+                                        int& cur_mz) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lr = lane & 15, lg = lane >> 4;
   const int m = t / a.B, b = t - m * a.B;
@@ -358,24 +358,28 @@ __device__ __forceinline__ void mm_tile(const StateArgs& a, int t, const u32x4 (
 
   // ---- z_j of this pair (zero outside j < n, i < r) as hi + lo ----
   uint16_t* zs = (uint16_t*)(smem + MM_ZS);
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    if (zj[k] < 16 && zi[k] < rp) {
-      float z = 0.0f;
-      if (zj[k] < n && zi[k] < r) {
-        const int64_t row = (int64_t)b * n + zj[k];
-        float zz = zr[k], hs = hr[k];
-        for (int ks = 1; ks < a.ksz; ++ks) {
-          zz += a.zpart[((int64_t)ks * a.B * n + row) * a.nz + mz * r + zi[k]];
-          hs += a.hss[(int64_t)ks * a.B * n + row];
-        }
-        z = zz * (1.0f / sqrtf(hs / (float)a.d + a.h_eps));
+  if (zj < 16 && zi < rp) {
+    float z[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (zj < n && zi < r) {
+      const int64_t row = (int64_t)b * n + zj;
+      float zz[4] = {zr[0], zr[1], zr[2], zr[3]};
+      float hs = hr;
+      for (int ks = 1; ks < a.ksz; ++ks) {
+        const float4 v = *(const float4*)(a.zpart + ((int64_t)ks * a.B * n + row) * a.nz + mz * r + zi);
+        zz[0] += v.x; zz[1] += v.y; zz[2] += v.z; zz[3] += v.w;
+        hs += a.hss[(int64_t)ks * a.B * n + row];
       }
-      uint16_t hi, lo;
-      split_bf16(z, hi, lo);
-      zs[zj[k] * MM_LD + zi[k]] = hi;
-      zs[(16 + zj[k]) * MM_LD + zi[k]] = lo;
+      const float rs = 1.0f / sqrtf(hs / (float)a.d + a.h_eps);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) z[e] = zz[e] * rs;
     }
+    uint16_t hi[4], lo[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) split_bf16(z[e], hi[e], lo[e]);
+    *(uint2*)(zs + zj * MM_LD + zi) = make_uint2((uint32_t)hi[0] | ((uint32_t)hi[1] << 16),
+                                                 (uint32_t)hi[2] | ((uint32_t)hi[3] << 16));
+    *(uint2*)(zs + (16 + zj) * MM_LD + zi) = make_uint2((uint32_t)lo[0] | ((uint32_t)lo[1] << 16),
+                                                        (uint32_t)lo[2] | ((uint32_t)lo[3] << 16));
   }
   __syncthreads();
   const float* wss = (const float*)(smem + MM_SS);
@@ -488,14 +492,9 @@ __global__ __launch_bounds__(MM_THREADS, 1) void k_state_mm(StateArgs a) {
   const int G = gridDim.x, g = blockIdx.x;
   const int t0 = (int)((int64_t)g * T / G), t1 = (int)((int64_t)(g + 1) * T / G);
   const int rp = (a.r + 31) & ~31;
-  // this thread's elements of z: e = tid + 512 k -> (j, i) = (e / rp, e % rp)
-  int zj[4], zi[4];
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const int e = threadIdx.x + MM_THREADS * k;
-    zj[k] = e / rp;
-    zi[k] = e - zj[k] * rp;
-  }
+  // this thread's elements of z: row zj, ranks zi .. zi + 3 (rp / 4 threads
+  // per row; 16 rows need at most 512 threads since rp <= 128)
+  const int zj = threadIdx.x / (rp / 4), zi = 4 * (threadIdx.x - zj * (rp / 4));
   int* s_acc = (int*)(smem + MM_ACC);
   if (ACC_LDS)
     for (int i = threadIdx.x; i < a.B; i += MM_THREADS) s_acc[i] = a.accept_idx[i];
@@ -503,7 +502,7 @@ __global__ __launch_bounds__(MM_THREADS, 1) void k_state_mm(StateArgs a) {
   // three sets of prefetched registers, for items t, t + 1 and t + 2 modulo
   // 3 (a register copy of a value still being loaded would wait for every
   // load in flight)
-  float z0[4], h0[4], z1[4], h1[4], z2[4], h2[4];
+  float z0[4], z1[4], z2[4], h0, h1, h2;
   u32x4 P0[MM_CH], P1[MM_CH], P2[MM_CH];
   int pa0, pa1, pa2;
   mm_fetch<ACC_LDS>(a, t0, t1, P0, pa0, s_acc);
