@@ -667,6 +667,8 @@ __device__ __forceinline__ void mlp1_item(const FastArgs& a, int item, unsigned 
     const int kk = 32 * s + 8 * lg;
     bq[s] = (cv && kk < F) ? *(const u32x4*)(wrow + kk) : u32x4{0u, 0u, 0u, 0u};
   }
+  // the bias of this lane's column, with the W1 rows (before the wait)
+  const float bias = (cv && a.b1) ? Elem<uint16_t>::ld(a.b1, col) : 0.0f;
 
   const int b0 = row0 / a.n, b1 = (row0 + rows - 1) / a.n;
   if (threadIdx.x == 0)
@@ -819,7 +821,6 @@ __device__ __forceinline__ void mlp1_item(const FastArgs& a, int item, unsigned 
   }
   // a in bf16: lanes l and l + 1 hold neighbouring columns; the even lane
   // stores the pair as one 32-bit word
-  const float bias = (cv && a.b1) ? Elem<uint16_t>::ld(a.b1, col) : 0.0f;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     const uint32_t mine = f32_to_bf16_rne(activation(acc[e] + bias, a.act));
@@ -873,9 +874,14 @@ __device__ __forceinline__ void mlp2_item(const FastArgs& a, int rb, int cb, uns
       bq[h2][s] = (cv[h2] && kk < a.Hm) ? *(const u32x4*)(a.w2 + (int64_t)colv[h2] * a.Hm + kk) : u32x4{0u, 0u, 0u, 0u};
     }
 
-  // the epilogue's h chunks (BM rows x 16 chunks of 8 values)
+  // the epilogue's h chunks (BM rows x CPR chunks of 8 values), and the b2
+  // chunk of this thread's columns (the same for each of its chunks, since
+  // 256 is a multiple of CPR)
   constexpr int CPR = OC / 8;
   constexpr int EPT = (BM * CPR + 255) / 256;
+  static_assert(256 % CPR == 0, "one column chunk per thread");
+  const int gcb = col0 + (tid % CPR) * 8;
+  const u32x4 b2q = (a.b2 != nullptr && gcb < a.d) ? *(const u32x4*)(a.b2 + gcb) : u32x4{0u, 0u, 0u, 0u};
   u32x4 hq[EPT];
 #pragma unroll
   for (int k = 0; k < EPT; ++k) {
@@ -969,7 +975,7 @@ __device__ __forceinline__ void mlp2_item(const FastArgs& a, int rb, int cb, uns
     dv[4] = d1.x; dv[5] = d1.y; dv[6] = d1.z; dv[7] = d1.w;
     if (a.b2) {
       float bb[8];
-      Elem<uint16_t>::unpack(*(const u32x4*)(a.b2 + gc), bb);
+      Elem<uint16_t>::unpack(b2q, bb);
 #pragma unroll
       for (int e = 0; e < 8; ++e) dv[e] += bb[e];
     }
