@@ -315,31 +315,44 @@ __device__ __forceinline__ void z_item(const FastArgs& a, int ks, int cb, int rb
   __syncthreads();
   if (*s_flag) {
     // every chunk of the tile is stored (each item waited for its stores
-    // before counting): sum them in chunk order, up to 8 chunks per trip
-    constexpr int KG = 8;
+    // before counting): sum them in chunk order.  The loads of all of this
+    // thread's RBT chunks, KG K chunks at a time, are issued before any is
+    // summed, so a group costs one trip to memory (KG * RBT = 32 or 16 loads)
+    constexpr int KG = RBT == 1 ? 16 : 8;
+    float4 sum[RBT];
+    bool live[RBT];
+    uint32_t off[RBT];
 #pragma unroll
     for (int q = 0; q < RBT; ++q) {
       const int c = tid + 256 * q;
       const int rr = c >> 4, c4 = (c & 15) * 4;
       const int row = rb * BMZ + rr, col = cb * 64 + c4;
-      if (row < a.R && col < a.Nz) {
-        float4 sum = make_float4(0.f, 0.f, 0.f, 0.f);
-        for (int k0 = 0; k0 < a.ksplit; k0 += KG) {
-          u32x4 v[KG];
-#pragma unroll
-          for (int k = 0; k < KG; ++k)
-            v[k] = k0 + k < a.ksplit ? ld_coh16(a.zpart, (uint32_t)(4 * (((k0 + k) * a.R + row) * a.Nz + col)))
-                                     : u32x4{0u, 0u, 0u, 0u};
-#pragma unroll
-          for (int k = 0; k < KG; ++k) {
-            sum.x += __uint_as_float(v[k].x); sum.y += __uint_as_float(v[k].y);
-            sum.z += __uint_as_float(v[k].z); sum.w += __uint_as_float(v[k].w);
-          }
-        }
-        st_coh16(a.zfin, (uint32_t)(4 * (row * a.Nz + col)),
-                 u32x4{__float_as_uint(sum.x), __float_as_uint(sum.y), __float_as_uint(sum.z), __float_as_uint(sum.w)});
-      }
+      live[q] = row < a.R && col < a.Nz;
+      off[q] = live[q] ? (uint32_t)(row * a.Nz + col) : 0u;
+      sum[q] = make_float4(0.f, 0.f, 0.f, 0.f);
     }
+    for (int k0 = 0; k0 < a.ksplit; k0 += KG) {
+      u32x4 v[RBT][KG];
+#pragma unroll
+      for (int q = 0; q < RBT; ++q)
+#pragma unroll
+        for (int k = 0; k < KG; ++k)
+          v[q][k] = (live[q] && k0 + k < a.ksplit)
+                        ? ld_coh16(a.zpart, (uint32_t)(4 * ((k0 + k) * a.R * a.Nz + off[q])))
+                        : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int q = 0; q < RBT; ++q)
+#pragma unroll
+        for (int k = 0; k < KG; ++k) {
+          sum[q].x += __uint_as_float(v[q][k].x); sum[q].y += __uint_as_float(v[q][k].y);
+          sum[q].z += __uint_as_float(v[q][k].z); sum[q].w += __uint_as_float(v[q][k].w);
+        }
+    }
+#pragma unroll
+    for (int q = 0; q < RBT; ++q)
+      if (live[q])
+        st_coh16(a.zfin, 4 * off[q], u32x4{__float_as_uint(sum[q].x), __float_as_uint(sum[q].y),
+                                           __float_as_uint(sum[q].z), __float_as_uint(sum[q].w)});
     wait_mem();
     __syncthreads();
     if (tid == 0) count_up(ctr(a.zdone, rb));
