@@ -146,9 +146,10 @@ readyStatus readyPlanCreate(const readyShape* shape, const int32_t* layer_ids, r
 
   if (p->fast) {
     // work items of k_reader
-    // the counters per row block of out are sized for the finer of the two
-    // large-row forms (apply launches use READY_BMO_APPLY)
-    const int bmz = p->small ? 16 : READY_BMZ_LARGE;
+    // the counters per row block of z and of out are sized for the finer of
+    // the two large-row forms (apply launches use READY_BMZ_APPLY and
+    // READY_BMO_APPLY)
+    const int bmz = p->small ? 16 : std::min(READY_BMZ_LARGE, READY_BMZ_APPLY);
     const int bmo = p->small ? 16 : std::min(READY_BMO_LARGE, READY_BMO_APPLY);
     const int64_t rows = std::max(p->R, 1);
     const int64_t nrbz = cdiv(rows, bmz), ncbz = cdiv(p->Nz, 64), nrb16 = cdiv(rows, 16), nrbo = cdiv(rows, bmo);

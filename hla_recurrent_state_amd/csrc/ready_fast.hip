@@ -1015,7 +1015,7 @@ __device__ __forceinline__ void mlp2_item(const FastArgs& a, int rb, int cb, uns
 // column blocks cb with cb % nxcd == x, go to the workgroups on XCD x).
 template <int RR, int SMALL, int MODE>
 __global__ __launch_bounds__(256, (MODE == READY_MODE_PREPARE && RR <= 16) ? 3 : 2) void k_reader(FastArgs a) {
-  constexpr int BMZ = SMALL ? 16 : READY_BMZ_LARGE;
+  constexpr int BMZ = SMALL ? 16 : (MODE == READY_MODE_APPLY ? READY_BMZ_APPLY : READY_BMZ_LARGE);
   constexpr int BMO = SMALL ? 16 : (MODE == READY_MODE_APPLY ? READY_BMO_APPLY : READY_BMO_LARGE);
   constexpr int NST = (SMALL ? READY_ZCHUNK_SMALL : READY_ZCHUNK_LARGE) / 128;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
@@ -1114,7 +1114,7 @@ __global__ void k_ws_init(uint32_t* counters, int n, uint32_t magic) {
 
 size_t ready_reader_lds(int r, int F, int Nz, int small) {
   // the O item's area is sized for the larger of the two large-row forms
-  const int BMZ = small ? 16 : READY_BMZ_LARGE;
+  const int BMZ = small ? 16 : (READY_BMZ_APPLY > READY_BMZ_LARGE ? READY_BMZ_APPLY : READY_BMZ_LARGE);
   const int BMO = small ? 16 : (READY_BMO_APPLY > READY_BMO_LARGE ? READY_BMO_APPLY : READY_BMO_LARGE);
   const int NB = (r + 15) / 16;
   const size_t z_bytes = (size_t)(BMZ + 64) * 256 + 16;

@@ -119,9 +119,12 @@ struct FastArgs {
 #define READY_WS_MAGIC 0x52454459u // "READY"
 // k_reader tiles: z in BMZ x 64 tiles over K chunks of READY_ZCHUNK_* (a
 // multiple of 128), out in BMO x READY_OCOLS tiles; BMZ = BMO = 16 for at
-// most 16 rows, else READY_BMZ_LARGE and READY_BMO_LARGE (READY_BMO_APPLY in
-// apply launches, which have no state stream for short O items to overlap)
+// most 16 rows, else READY_BMZ_LARGE and READY_BMO_LARGE.  Apply launches
+// use READY_BMZ_APPLY and READY_BMO_APPLY: with no state stream beside them,
+// more query items spread the query sums over more workgroups, and fewer,
+// larger output items cost less than shorter ones would save
 #define READY_BMZ_LARGE 64
+#define READY_BMZ_APPLY 32
 #define READY_BMO_LARGE 32
 #define READY_BMO_APPLY 64
 #define READY_ZCHUNK_SMALL 384
