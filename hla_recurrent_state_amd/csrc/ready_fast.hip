@@ -850,12 +850,12 @@ __device__ __forceinline__ void mlp1_item(const FastArgs& a, int item, unsigned 
 // ---------------------------------------------------------------- O items
 
 // Rows [BM rb, BM rb + BM) and columns [OC cb, OC cb + OC) of out (OC =
-// READY_OCOLS); wave w computes columns OC cb + (OC / 4) w .. + OC / 4 - 1.  The W2 rows of the lane's two
-// columns and the tile's h values are loaded before waiting; after the A
-// items of the rows are counted, the a rows are staged in LDS by passes of
-// 256 values of K (device-coherent loads) for the matrix instructions.  The
-// epilogue goes through LDS so that h, out and delta move in 16-byte row
-// chunks.
+// READY_OCOLS); wave w computes columns OC cb + (OC / 4) w .. + OC / 4 - 1,
+// 16 at a time.  The W2 rows of the lane's columns, the tile's h values and
+// the b2 chunk are loaded before waiting; after the A items of the rows are
+// counted, the a rows are staged in LDS by passes of 256 values of K
+// (device-coherent loads) for the matrix instructions.  The epilogue goes
+// through LDS so that h, out and delta move in 16-byte row chunks.
 template <int BM>
 __device__ __forceinline__ void mlp2_item(const FastArgs& a, int rb, int cb, unsigned char* smem) {
   constexpr int OC = READY_OCOLS, KT = 256, LA = KT + 8, LO = OC + 4;
