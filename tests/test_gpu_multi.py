@@ -143,6 +143,14 @@ def test_ranks_two_readers(r):
     _check(synth.make("paper", seed=4, r=r, B=3), 2)
 
 
+def test_several_row_blocks_ragged():
+    # 77 rows: the apply launch's query sums in three 32-row tiles (the last
+    # one ragged) and its output in two 64-row tiles, against the one-reader
+    # launch's 64-row query tiles and 32-row output tiles
+    inp = synth.make("paper", seed=17, B=11)
+    _check(inp, 2, seqs=[0, 5, 10])
+
+
 @pytest.mark.parametrize("n_readers", [1, 8])
 def test_one_and_the_most_readers(n_readers):
     # a single reader through prepare/apply, and the most readers one prepare serves
