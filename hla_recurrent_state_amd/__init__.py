@@ -264,7 +264,9 @@ class StateReader:
     reader(states, accept_idx, h, weights, gathered, out, logrms=None,
            delta=None, feat=None, dev_status=None, workspace=None)
     A workspace passed in must come from new_workspace() (or have been
-    prepared with init_workspace()); by default the reader keeps its own.
+    prepared with init_workspace()); by default the reader keeps its own, one
+    per (device, stream), prepared on that stream: calls on different streams
+    never share synchronisation counters.
     `states` is a tensor [B][P][L_tot][H][128][128] (any outer strides with a
     contiguous tile) and `weights` a dict with keys wq, u, v, w1, w2 and
     optionally h_gamma, b1, b2.  Raises ReadyError on a non-zero status.
@@ -279,7 +281,7 @@ class StateReader:
         st, self.workspace_bytes = readyWorkspaceSize(self.plan)
         if st != READY_OK:
             raise ReadyError(st, "readyWorkspaceSize")
-        self._ws = None
+        self._ws = {}
 
     def close(self):
         if getattr(self, "plan", None):
@@ -308,11 +310,19 @@ class StateReader:
         if code != READY_OK:
             raise ReadyError(code, "readyWorkspaceInit")
 
-    def workspace(self, device):
+    def workspace(self, device, stream=None):
+        """The reader's own workspace for `device` and `stream` (the current
+        stream when None), prepared on that stream when first made."""
         import torch
-        if self._ws is None or self._ws.device != torch.device(device):
-            self._ws = self.new_workspace(device)
-        return self._ws
+        device = torch.device(device)
+        if stream is None:
+            stream = torch.cuda.current_stream(device).cuda_stream
+        key = (str(device), int(stream or 0))
+        ws = self._ws.get(key)
+        if ws is None:
+            ws = self.new_workspace(device, stream)
+            self._ws[key] = ws
+        return ws
 
     def __call__(self, states, accept_idx, h, weights, gathered, out, logrms=None, delta=None,
                  feat=None, dev_status=None, workspace=None, stream=None, events=None):
@@ -325,10 +335,10 @@ class StateReader:
         wd = readyWeights(**{k: _ptr(weights.get(k)) for k in ("wq", "u", "v", "h_gamma", "w1", "b1", "w2", "b2")})
         od = readyOutputs(gathered=_ptr(gathered), out=_ptr(out), logrms=_ptr(logrms), delta=_ptr(delta),
                           feat=_ptr(feat), dev_status=_ptr(dev_status))
-        if workspace is None:
-            workspace = self.workspace(h.device)
         if stream is None:
             stream = torch.cuda.current_stream(h.device).cuda_stream
+        if workspace is None:
+            workspace = self.workspace(h.device, stream)
         args = (self.plan, sd, accept_idx.data_ptr(), h.data_ptr(), wd, od, workspace.data_ptr(),
                 workspace.numel() * workspace.element_size(), stream)
         if events is None:
@@ -379,10 +389,10 @@ class StateReader:
         arr = (readyWeights * max(1, n_inj))(*[
             readyWeights(**{k: _ptr(w.get(k)) for k in ("wq", "u", "v", "h_gamma", "w1", "b1", "w2", "b2")})
             for w in inj_weights])
-        if workspace is None:
-            workspace = self.workspace(states.device)
         if stream is None:
             stream = torch.cuda.current_stream(states.device).cuda_stream
+        if workspace is None:
+            workspace = self.workspace(states.device, stream)
         code = readyStatePrepare(self.plan, sd, accept_idx.data_ptr(), n_inj, arr, gathered.data_ptr(),
                                  _ptr(logrms), _ptr(dev_status), prep.data_ptr(),
                                  prep.numel() * prep.element_size(), workspace.data_ptr(),
@@ -397,10 +407,10 @@ class StateReader:
         wd = readyWeights(**{k: _ptr(weights.get(k)) for k in ("wq", "u", "v", "h_gamma", "w1", "b1", "w2", "b2")})
         od = readyOutputs(gathered=None, out=_ptr(out), logrms=None, delta=_ptr(delta), feat=_ptr(feat),
                           dev_status=_ptr(dev_status))
-        if workspace is None:
-            workspace = self.workspace(h.device)
         if stream is None:
             stream = torch.cuda.current_stream(h.device).cuda_stream
+        if workspace is None:
+            workspace = self.workspace(h.device, stream)
         code = readyStateApply(self.plan, prep.data_ptr(), prep.numel() * prep.element_size(), n_inj, inj,
                                h.data_ptr(), wd, od, workspace.data_ptr(),
                                workspace.numel() * workspace.element_size(), stream)

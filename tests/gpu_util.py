@@ -41,8 +41,10 @@ def alloc_outputs(cfg, device, B=None):
     }
 
 
-def run_reader(inp, device, dev_inputs=None, inplace=False, path="fused"):
-    """One call; returns host copies of all outputs plus the device status."""
+def run_reader(inp, device, dev_inputs=None, inplace=False, path="fused", debug=True):
+    """One call; returns host copies of all outputs plus the device status.
+    With debug=False the optional logrms, delta and feat outputs are not
+    passed (the configuration the benchmark times) and come back as None."""
     import torch
     from hla_recurrent_state_amd import StateReader
     cfg = inp.cfg
@@ -54,15 +56,19 @@ def run_reader(inp, device, dev_inputs=None, inplace=False, path="fused"):
         h_arg = o["out"]
     else:
         h_arg = d["h"]
+    if debug:
+        dbg = dict(logrms=o["logrms"], delta=o["delta"], feat=o["feat"])
+    else:
+        dbg = dict(logrms=None, delta=None, feat=None)
     reader(d["states"], d["accept_idx"], h_arg, d["weights"], o["gathered"], o["out"],
-           logrms=o["logrms"], delta=o["delta"], feat=o["feat"], dev_status=o["dev_status"])
+           dev_status=o["dev_status"], **dbg)
     torch.cuda.synchronize(device)
     res = {
         "gathered": to_numpy_bits(o["gathered"], cfg.state_dtype),
         "out": to_numpy_bits(o["out"], cfg.act_dtype),
-        "logrms": o["logrms"].cpu().numpy(),
-        "delta": o["delta"].cpu().numpy(),
-        "feat": o["feat"].cpu().numpy(),
+        "logrms": o["logrms"].cpu().numpy() if debug else None,
+        "delta": o["delta"].cpu().numpy() if debug else None,
+        "feat": o["feat"].cpu().numpy() if debug else None,
         "dev_status": int(o["dev_status"].item()),
     }
     reader.close()
@@ -105,6 +111,9 @@ def compare(inp, res, ref, tol=None):
     got_bits = res["gathered"][seqs]
     rep["gather_bitexact"] = bool(np.array_equal(got_bits.view(np.uint8), want_bits.view(np.uint8)))
     rep["gather_oracle_equal"] = bool(np.array_equal(_decode(got_bits, cfg.state_dtype), ref["G"]))
+    if res["logrms"] is None:
+        # the timed configuration: no debug outputs, so only gathered and out
+        return _compare_out(cfg, res, ref, rep, tol)
     # 2. log-RMS
     ell = res["logrms"][seqs].astype(np.float64)
     rep["logrms_err"] = float(np.max(np.abs(ell - ref["ell"]) / np.maximum(1.0, np.abs(ref["ell"]))))
@@ -126,5 +135,25 @@ def compare(inp, res, ref, tol=None):
     rep["dev_status"] = res["dev_status"]
     rep["ok"] = (rep["gather_bitexact"] and rep["gather_oracle_equal"] and rep["logrms_err"] <= 1e-5
                  and rep["feat_rel"] <= tol and rep["dh_rel"] <= tol and rep["out_excess"] <= 0.0
+                 and rep["dev_status"] == 0)
+    return rep
+
+
+def _compare_out(cfg, res, ref, rep, tol):
+    """gathered (already in rep) and out = RNE(h + Delta h_ref) within one
+    ulp plus tol times max|Delta h_ref|."""
+    from oracle import reader as orc
+    seqs = ref["seqs"]
+    scale = max(np.max(np.abs(ref["dh"])), 1e-30)
+    out = _decode(res["out"][seqs], cfg.act_dtype)
+    if cfg.act_dtype == "bf16":
+        want = orc.round_to_bf16(ref["h_new"])
+        ulp = np.ldexp(1.0, np.frexp(np.abs(want))[1] - 8)
+    else:
+        want = ref["h_new"]
+        ulp = np.ldexp(1.0, np.frexp(np.abs(want))[1] - 24)
+    rep["out_excess"] = float(np.max(np.abs(out - want) - ulp - tol * scale))
+    rep["dev_status"] = res["dev_status"]
+    rep["ok"] = (rep["gather_bitexact"] and rep["gather_oracle_equal"] and rep["out_excess"] <= 0.0
                  and rep["dev_status"] == 0)
     return rep

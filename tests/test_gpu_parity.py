@@ -29,11 +29,12 @@ def _say(*a):
     sys.stdout.flush()
 
 
-def _check(inp, seqs=None, inplace=False, expect_ok=True, path="fused"):
+def _check(inp, seqs=None, inplace=False, expect_ok=True, path="fused", debug=True):
     from tests.gpu_util import compare, oracle_reference, run_reader
     dev = _dev()
-    _say("case", inp.cfg.name, "B", inp.cfg.B, "M", inp.cfg.M, "r", inp.cfg.r, inp.cfg.state_dtype, path)
-    res = run_reader(inp, dev, inplace=inplace, path=path)
+    _say("case", inp.cfg.name, "B", inp.cfg.B, "M", inp.cfg.M, "r", inp.cfg.r, inp.cfg.state_dtype, path,
+         "debug outputs" if debug else "no debug outputs")
+    res = run_reader(inp, dev, inplace=inplace, path=path, debug=debug)
     ref = oracle_reference(inp, seqs)
     rep = compare(inp, res, ref)
     _say("  report", rep)
@@ -58,6 +59,16 @@ def test_wide_heads():
 
 def test_batched():
     _check(synth.make("batched", seed=1))
+
+
+@pytest.mark.parametrize("name", ["paper", "batched"])
+def test_timed_configuration_without_debug_outputs(name):
+    """The call exactly as the benchmark times it: logrms, delta and feat
+    are NULL.  gathered is bit-exact and out is within one bf16 ulp of
+    RNE(h + Delta h_ref) plus the tolerance, at the full shapes (short state
+    histories, t = 64: the values change, the launch does not)."""
+    cfg = make_shape(name, t=64)
+    _check(synth.make(cfg, seed=21), debug=False)
 
 
 # ------------------------------------------------------------ the unfused path (four launches)
@@ -201,6 +212,34 @@ def test_bf16_general_many_rows_large_tiles(act_dtype):
     inp.b1 = store(0.2 * rng.standard_normal(cfg.Hm), "bf16")
     inp.b2 = store(0.2 * rng.standard_normal(cfg.d), "bf16")
     res, ref, rep = _check(inp, seqs=[0, 17, 18, 36])
+    want = inp.buf[np.arange(cfg.B), inp.accept_idx][:, list(cfg.slots)].reshape(cfg.B, cfg.M, 128, 128)
+    assert np.array_equal(res["gathered"], want)
+
+
+@pytest.mark.parametrize("path", ["fused", "unfused"])
+def test_rank_32_at_the_paper_pair_count(path):
+    """r = 32 with the pages' 32 layer-head pairs (arXiv section 4.4,
+    Table 3) at the batched shape, on the path the default plan takes and on
+    the four-launch path (the matrix-core per-state kernel at exactly
+    r = 32).  The oracle checks a sample of sequences; the gather is checked
+    for all."""
+    from hla_recurrent_state_amd import READY_ERR_UNSUPPORTED, ReadyError, StateReader
+    from tests.gpu_util import reader_shape
+    cfg = make_shape("batched", t=16, r=32)
+    assert cfg.M == 32
+    sr = StateReader(reader_shape(cfg, path=path), cfg.slots)
+    try:
+        sr.prep_size(1)
+        single = True
+    except ReadyError as e:
+        assert e.code == READY_ERR_UNSUPPORTED
+        single = False
+    sr.close()
+    if path == "unfused":
+        assert not single
+    _say("r = 32, M = 32:", "single kernel" if single else "four launches")
+    inp = synth.make(cfg, seed=33)
+    res, ref, rep = _check(inp, seqs=[0, 1, 31, 62, 63], path=path)
     want = inp.buf[np.arange(cfg.B), inp.accept_idx][:, list(cfg.slots)].reshape(cfg.B, cfg.M, 128, 128)
     assert np.array_equal(res["gathered"], want)
 
@@ -420,3 +459,4 @@ def test_repeated_calls_on_one_workspace():
               "feat": np.zeros((cfg.B, cfg.n, cfg.F), np.float32), "dev_status": 0},
         __import__("tests.gpu_util", fromlist=["oracle_reference"]).oracle_reference(inp))
     assert rep["gather_bitexact"] and rep["dh_rel"] <= rep["tol"] and rep["logrms_err"] <= 1e-5, rep
+    assert rep["out_excess"] <= 0.0, rep
