@@ -7,7 +7,8 @@ ReadyError -- there is no fallback path.
 Low-level names mirror the C functions (readyPlanCreate, readyWorkspaceSize,
 readyStateReader, readyGather, readyPrepSize, readyStatePrepare, readyStateApply,
 readyVerifyStates, readyPlanDestroy, readyStatusString, readyVersion) and the C structs (readyShape, readyStates, readyWeights,
-readyOutputs, readyVerifyBuffer).  StateReader and verify_states wrap them for
+readyOutputs, readyVerifyBuffer), plus readyStateReaderStatic, the form with
+no workspace argument for callers that cannot allocate.  StateReader and verify_states wrap them for
 torch tensors: they forward data_ptr() values and the current HIP stream
 (StateReader.prepare / StateReader.apply for several readers sharing one
 gather).
@@ -34,6 +35,9 @@ READY_ERR_OUT_OF_HOST_MEMORY = 10
 READY_ERR_SYNC_TIMEOUT = 11
 READY_ERR_WORKSPACE_UNINIT = 12
 READY_ERR_UNSUPPORTED = 13
+READY_ERR_STATIC_SCRATCH_TOO_SMALL = 14
+READY_STATIC_SCRATCH_BYTES = 16 << 20
+READY_STATIC_COUNTER_BYTES = 64 << 10
 READY_MAX_INJ = 8
 
 READY_F32 = 0
@@ -50,7 +54,7 @@ PATHS = {"fused": READY_PATH_FUSED, "unfused": READY_PATH_UNFUSED}
 
 # Every symbol include/ready.h declares.
 EXPORTS = ("readyPlanCreate", "readyPlanDestroy", "readyWorkspaceSize", "readyWorkspaceInit",
-           "readyStateReader", "readyStateReaderProfiled", "readyGather", "readyPrepSize", "readyStatePrepare",
+           "readyStateReader", "readyStateReaderProfiled", "readyStateReaderStatic", "readyGather", "readyPrepSize", "readyStatePrepare",
            "readyStateApply", "readyVerifyStates", "readyStatusString", "readyVersion")
 READY_STAGES = 4
 
@@ -113,6 +117,9 @@ def load():
     lib.readyStateReader.restype = ctypes.c_int
     lib.readyStateReaderProfiled.argtypes = lib.readyStateReader.argtypes + [P(ctypes.c_void_p)]
     lib.readyStateReaderProfiled.restype = ctypes.c_int
+    lib.readyStateReaderStatic.argtypes = [ctypes.c_void_p, P(readyStates), ctypes.c_void_p, ctypes.c_void_p,
+                                           P(readyWeights), P(readyOutputs), ctypes.c_void_p]
+    lib.readyStateReaderStatic.restype = ctypes.c_int
     lib.readyGather.argtypes = [ctypes.c_void_p, P(readyStates), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                 ctypes.c_void_p]
     lib.readyGather.restype = ctypes.c_int
@@ -186,6 +193,12 @@ def readyStateReaderProfiled(plan, states, accept_idx, h, weights, outputs, work
     ev = (ctypes.c_void_p * (2 * READY_STAGES))(*[e for e in events])
     return load().readyStateReaderProfiled(plan, ctypes.byref(states), accept_idx, h, ctypes.byref(weights),
                                            ctypes.byref(outputs), workspace, workspace_bytes, stream, ev)
+
+
+def readyStateReaderStatic(plan, states, accept_idx, h, weights, outputs, stream):
+    """Raw call of the form with the library's static scratch (no workspace)."""
+    return load().readyStateReaderStatic(plan, ctypes.byref(states), accept_idx, h, ctypes.byref(weights),
+                                         ctypes.byref(outputs), stream)
 
 
 def readyGather(plan, states, accept_idx, gathered, dev_status, stream):
@@ -347,6 +360,25 @@ class StateReader:
             code = readyStateReaderProfiled(*args, events)
         if code != READY_OK:
             raise ReadyError(code, "readyStateReader")
+
+    def call_static(self, states, accept_idx, h, weights, gathered, out, logrms=None, delta=None, feat=None,
+                    dev_status=None, stream=None):
+        """As __call__, through readyStateReaderStatic: no workspace, the
+        library's static per-device scratch instead."""
+        import torch
+        if states.dim() != 6:
+            raise ReadyError(READY_ERR_BAD_SHAPE, "states must be [B][P][L_tot][H][128][128]")
+        st = states.stride()
+        sd = readyStates(base=states.data_ptr(), stride_b=st[0], stride_p=st[1], stride_l=st[2],
+                         stride_h=st[3])
+        wd = readyWeights(**{k: _ptr(weights.get(k)) for k in ("wq", "u", "v", "h_gamma", "w1", "b1", "w2", "b2")})
+        od = readyOutputs(gathered=_ptr(gathered), out=_ptr(out), logrms=_ptr(logrms), delta=_ptr(delta),
+                          feat=_ptr(feat), dev_status=_ptr(dev_status))
+        if stream is None:
+            stream = torch.cuda.current_stream(h.device).cuda_stream
+        code = readyStateReaderStatic(self.plan, sd, accept_idx.data_ptr(), h.data_ptr(), wd, od, stream)
+        if code != READY_OK:
+            raise ReadyError(code, "readyStateReaderStatic")
 
     def gather(self, states, accept_idx, gathered, dev_status=None, stream=None):
         """Step 1 alone: the committed states into `gathered`."""

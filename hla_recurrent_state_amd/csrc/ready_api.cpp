@@ -108,6 +108,7 @@ const char* readyStatusString(readyStatus st) {
     case READY_ERR_SYNC_TIMEOUT: return "READY_ERR_SYNC_TIMEOUT";
     case READY_ERR_WORKSPACE_UNINIT: return "READY_ERR_WORKSPACE_UNINIT";
     case READY_ERR_UNSUPPORTED: return "READY_ERR_UNSUPPORTED";
+    case READY_ERR_STATIC_SCRATCH_TOO_SMALL: return "READY_ERR_STATIC_SCRATCH_TOO_SMALL";
   }
   return "READY_ERR_UNKNOWN";
 }
@@ -272,10 +273,23 @@ void reader_roles(FastArgs& a, int grid) {
   a.ntg = std::min(grid, READY_TICKET_GROUPS);
 }
 
-// FastArgs fields that depend only on the plan and the workspace: sizes,
-// work-item counts, workspace arrays and counters.  One reader (n_inj = 1),
+// The scratch of a call held in a caller's workspace: the arrays at the
+// plan's offsets, the counters at off_ctr, stamped with the plan's magic word.
+WsView workspace_view(const readyPlan* plan, void* workspace) {
+  WsView v;
+  v.data = (char*)workspace;
+  v.ctr = (uint32_t*)((char*)workspace + plan->off_ctr);
+  v.magic = READY_WS_MAGIC ^ (uint32_t)plan->n_counters;
+  v.data_bytes = plan->off_ctr;
+  v.ctr_bytes = plan->ws_bytes - plan->off_ctr;
+  return v;
+}
+
+// FastArgs fields that depend only on the plan and the scratch: sizes,
+// work-item counts, scratch arrays and counters.  One reader (n_inj = 1),
 // every item kind (READY_MODE_FULL).
-void fast_common(const readyPlan* plan, char* wsb, FastArgs& a) {
+void fast_common(const readyPlan* plan, const WsView& view, FastArgs& a) {
+  char* wsb = view.data;
   const readyShape& s = plan->s;
   memset(&a, 0, sizeof(a));
   for (int l = 0; l < s.L_sel; ++l) a.slot[l] = plan->slot[l];
@@ -286,9 +300,9 @@ void fast_common(const readyPlan* plan, char* wsb, FastArgs& a) {
   a.ell = (float*)(wsb + plan->off_ell);
   a.abuf = (uint16_t*)(wsb + plan->off_a);
   a.seq_invalid = (uint32_t*)(wsb + plan->off_flags);
-  uint32_t* ctr = (uint32_t*)(wsb + plan->off_ctr);
+  uint32_t* ctr = view.ctr;
   a.counters = ctr; a.n_counters = plan->n_counters;
-  a.magic = READY_WS_MAGIC ^ (uint32_t)plan->n_counters;
+  a.magic = view.magic;
   a.abort_flag = ctr + READY_CTR_STRIDE;
   a.done = ctr + 2 * READY_CTR_STRIDE;
   a.zcnt = ctr + READY_CTR_STRIDE * plan->c_zcnt;
@@ -350,15 +364,21 @@ PrepLayout prep_layout(const readyPlan* plan, int n_inj) {
   return L;
 }
 
-readyStatus run_reader(const readyPlan* plan, const readyStates* states, const int32_t* accept_idx,
-                       const void* h, const readyWeights* w, const readyOutputs* o, void* workspace,
-                       size_t workspace_bytes, void* stream, void* const* events) {
+}  // namespace
+
+// `sv` is the scratch when the library supplies it (the static per-device
+// array); with sv == nullptr the caller's workspace is checked and used.
+readyStatus ready_run_reader(const readyPlan* plan, const readyStates* states, const int32_t* accept_idx,
+                             const void* h, const readyWeights* w, const readyOutputs* o, void* workspace,
+                             size_t workspace_bytes, void* stream, void* const* events, const WsView* sv,
+                             WsResolve resolve) {
   if (!plan || !states || !w || !o) return READY_ERR_NULL_POINTER;
   const readyShape& s = plan->s;
   if (!states->base || !accept_idx || !h || !w->wq || !w->u || !w->v || !w->w1 || !w->w2 ||
-      !o->gathered || !o->out || !workspace)
+      !o->gathered || !o->out || (!sv && !workspace))
     return READY_ERR_NULL_POINTER;
-  if (workspace_bytes < plan->ws_bytes) return READY_ERR_WORKSPACE_TOO_SMALL;
+  if (!sv && workspace_bytes < plan->ws_bytes) return READY_ERR_WORKSPACE_TOO_SMALL;
+  WsView view = sv ? *sv : workspace_view(plan, workspace);
 
   const size_t ss = dsize(s.state_dtype), as = dsize(s.act_dtype), ws = dsize(s.weight_dtype);
   // alignment: 16 bytes for everything read or written with vector accesses
@@ -366,7 +386,7 @@ readyStatus run_reader(const readyPlan* plan, const readyStates* states, const i
                             o->gathered, o->out, o->delta, o->feat};
   for (const void* ptr : vec_ptrs)
     if (ptr && !aligned16(ptr)) return READY_ERR_MISALIGNED;
-  if (((uintptr_t)workspace & 255u) != 0) return READY_ERR_MISALIGNED;
+  if (!sv && ((uintptr_t)workspace & 255u) != 0) return READY_ERR_MISALIGNED;
   const int64_t strides[4] = {states->stride_b, states->stride_p, states->stride_l, states->stride_h};
   for (int64_t st : strides) {
     if (st < 0) return READY_ERR_BAD_SHAPE;
@@ -383,7 +403,8 @@ readyStatus run_reader(const readyPlan* plan, const readyStates* states, const i
   const Range r_gath = range_of(o->gathered, (size_t)s.B * M * READY_TILE_ELEMS * ss);
   const Range r_h = range_of(h, R * d * as);
   const Range r_out = range_of(o->out, R * d * as);
-  const Range r_ws = range_of(workspace, plan->ws_bytes);
+  const Range r_ws = range_of(view.data, view.data_bytes);
+  const Range r_ctr = range_of(view.ctr, view.ctr_bytes);
   const Range r_acc = range_of(accept_idx, (size_t)s.B * 4);
   const size_t mz = s.shared_params ? 1 : M;
   const Range inputs[] = {
@@ -395,7 +416,7 @@ readyStatus run_reader(const readyPlan* plan, const readyStates* states, const i
   const Range outputs[] = {r_gath, r_out, range_of(o->logrms, o->logrms ? (size_t)s.B * M * 4 : 0),
                            range_of(o->delta, o->delta ? R * d * 4 : 0),
                            range_of(o->feat, o->feat ? R * F * 4 : 0),
-                           range_of(o->dev_status, o->dev_status ? 4 : 0), r_ws};
+                           range_of(o->dev_status, o->dev_status ? 4 : 0), r_ws, r_ctr};
   const int n_out = (int)(sizeof(outputs) / sizeof(outputs[0]));
   for (int i = 0; i < n_out; ++i) {
     for (const Range& in : inputs)
@@ -411,7 +432,11 @@ readyStatus run_reader(const readyPlan* plan, const readyStates* states, const i
   if (s.B == 0) return READY_OK;
 
   hipStream_t strm = (hipStream_t)stream;
-  char* wsb = (char*)workspace;
+  if (resolve) {
+    const readyStatus rs = resolve(&view, strm);
+    if (rs != READY_OK) return rs;
+  }
+  char* wsb = view.data;
   float* zpart = (float*)(wsb + plan->off_zpart);
   float* hss = (float*)(wsb + plan->off_hss);
   float* fbuf = (float*)(wsb + plan->off_f);
@@ -420,7 +445,7 @@ readyStatus run_reader(const readyPlan* plan, const readyStates* states, const i
 
   if (plan->fast) {
     FastArgs a;
-    fast_common(plan, wsb, a);
+    fast_common(plan, view, a);
     a.states = (const uint16_t*)states->base;
     a.sb = states->stride_b; a.sp = states->stride_p; a.sl = states->stride_l; a.sh = states->stride_h;
     a.accept_idx = accept_idx;
@@ -499,7 +524,7 @@ readyStatus run_reader(const readyPlan* plan, const readyStates* states, const i
     const StageEvents ev = stage_events(events, 2);
     if (plan->g1.big && plan->g1.ksplit > 1) {
       g.kchunk = plan->g1.kchunk;
-      g.ypart = (float*)((char*)workspace + plan->off_g1p);
+      g.ypart = (float*)(wsb + plan->off_g1p);
       e = ready_launch_gemm_mm(g, READY_F32, s.act_dtype, EPI_PARTIAL, plan->g1.ksplit, strm,
                                StageEvents{ev.start, nullptr});
       if (e == hipSuccess) e = ready_launch_reduce_bias_act(g, plan->g1.ksplit, strm, StageEvents{nullptr, ev.stop});
@@ -543,7 +568,10 @@ readyStatus run_reader(const readyPlan* plan, const readyStates* states, const i
   return READY_OK;
 }
 
-}  // namespace
+void ready_plan_scratch_needs(const readyPlan* plan, size_t* data_bytes, size_t* ctr_bytes) {
+  *data_bytes = plan->off_ctr;
+  *ctr_bytes = plan->ws_bytes - plan->off_ctr;
+}
 
 readyStatus readyVerifyStates(int32_t B, int32_t P, int32_t L, int32_t H, int32_t state_dtype, int32_t kv_dtype,
                               const void* state_t, const void* k, const void* v, const float* alpha,
@@ -600,7 +628,7 @@ readyStatus readyStateReader(const readyPlan* plan, const readyStates* states,
                              const int32_t* accept_idx, const void* h,
                              const readyWeights* w, const readyOutputs* o,
                              void* workspace, size_t workspace_bytes, void* stream) {
-  return run_reader(plan, states, accept_idx, h, w, o, workspace, workspace_bytes, stream, nullptr);
+  return ready_run_reader(plan, states, accept_idx, h, w, o, workspace, workspace_bytes, stream, nullptr, nullptr, nullptr);
 }
 
 readyStatus readyStateReaderProfiled(const readyPlan* plan, const readyStates* states,
@@ -608,7 +636,7 @@ readyStatus readyStateReaderProfiled(const readyPlan* plan, const readyStates* s
                                      const readyWeights* w, const readyOutputs* o,
                                      void* workspace, size_t workspace_bytes, void* stream,
                                      void* const* events) {
-  return run_reader(plan, states, accept_idx, h, w, o, workspace, workspace_bytes, stream, events);
+  return ready_run_reader(plan, states, accept_idx, h, w, o, workspace, workspace_bytes, stream, events, nullptr, nullptr);
 }
 
 // ---------------------------------------------------------------- step 1 alone
@@ -708,7 +736,7 @@ readyStatus readyStatePrepare(const readyPlan* plan, const readyStates* states, 
 
   char* pb = (char*)prep;
   FastArgs a;
-  fast_common(plan, (char*)workspace, a);
+  fast_common(plan, workspace_view(plan, workspace), a);
   a.mode = READY_MODE_PREPARE;
   a.n_inj = n_inj;
   a.states = (const uint16_t*)states->base;
@@ -763,7 +791,7 @@ readyStatus readyStateApply(const readyPlan* plan, const void* prep, size_t prep
 
   const char* pb = (const char*)prep;
   FastArgs a;
-  fast_common(plan, (char*)workspace, a);
+  fast_common(plan, workspace_view(plan, workspace), a);
   a.mode = READY_MODE_APPLY;
   a.n_s = 0;  // no state tiles: P, ell and the flags come from the prepare launch
   a.h = (const uint16_t*)h;

@@ -226,5 +226,36 @@ READY_HIDDEN hipError_t ready_launch_gemm_mfma(const GemmArgs& g, int x_dt, int 
 // fast path; small: at most 16 rows (16-row tiles), else the large tiles
 READY_HIDDEN hipError_t ready_launch_reader(const FastArgs& a, int small, int grid, hipStream_t s, StageEvents ev);
 READY_HIDDEN hipError_t ready_launch_ws_init(uint32_t* counters, int n_counters, uint32_t magic, hipStream_t s);
+
+// Where a call's scratch lives: `data` holds every scratch array at the plan's
+// offsets (data_bytes of them), `ctr` the synchronisation counters (ctr_bytes),
+// whose first word must equal `magic`.  For a caller's workspace both sit in
+// it (the counters at the end, the magic tied to the plan); the no-allocation
+// entry point places them in the library's static per-device array.
+struct WsView {
+  char* data;
+  uint32_t* ctr;
+  uint32_t magic;
+  size_t data_bytes, ctr_bytes;
+};
+
+// Called once the arguments of a call have passed validation and before
+// anything is enqueued: fills in the final scratch view (for the static array:
+// its device address on the current device, cleared counters on first use).
+typedef readyStatus (*WsResolve)(WsView* view, hipStream_t stream);
+
+extern "C" {
+// readyStateReader with the scratch given by `sv` (sv == nullptr: the caller's
+// workspace, validated as readyStateReader documents).  With `resolve`, the
+// aliasing checks use sv's ranges as given and `resolve` then supplies the
+// view the launches use.
+READY_HIDDEN readyStatus ready_run_reader(const readyPlan* plan, const readyStates* states,
+                                          const int32_t* accept_idx, const void* h, const readyWeights* w,
+                                          const readyOutputs* o, void* workspace, size_t workspace_bytes,
+                                          void* stream, void* const* events, const WsView* sv,
+                                          WsResolve resolve);
+// Scratch bytes a plan's calls use: the arrays, then the counters
+READY_HIDDEN void ready_plan_scratch_needs(const readyPlan* plan, size_t* data_bytes, size_t* ctr_bytes);
+}
 READY_HIDDEN size_t ready_reader_lds(int r, int F, int Nz, int small);
 READY_HIDDEN int ready_reader_per_cu(int r, int small, size_t lds, int mode);

@@ -62,8 +62,12 @@ typedef enum readyStatus {
                                        gave up (should never happen; outputs are then invalid) */
   READY_ERR_WORKSPACE_UNINIT = 12,  /* device-side only: the workspace was not prepared by
                                        readyWorkspaceInit for this plan; nothing was computed */
-  READY_ERR_UNSUPPORTED = 13        /* the operation is not available for this plan's dtypes and rank
-                                       (readyPrepSize, readyStatePrepare, readyStateApply) */
+  READY_ERR_UNSUPPORTED = 13,       /* the operation is not available for this plan's dtypes and rank
+                                       (readyPrepSize, readyStatePrepare, readyStateApply), or
+                                       readyStateReaderStatic's first call on a device was made
+                                       while its stream was capturing */
+  READY_ERR_STATIC_SCRATCH_TOO_SMALL = 14 /* readyStateReaderStatic: the plan needs more scratch than
+                                       the library's static per-device array holds */
 } readyStatus;
 
 typedef enum readyDtype { READY_F32 = 0, READY_BF16 = 1 } readyDtype;
@@ -230,6 +234,40 @@ readyStatus readyStateReaderProfiled(const readyPlan* plan, const readyStates* s
                                      const readyWeights* weights, const readyOutputs* outputs,
                                      void* workspace, size_t workspace_bytes, void* stream,
                                      void* const* events);
+
+/*
+ * For callers that cannot allocate device memory -- code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc: the same
+ * computation as readyStateReader (same kernels, bitwise the same outputs),
+ * with no workspace argument.  Its scratch is a static device array of
+ * READY_STATIC_SCRATCH_BYTES that the library holds on every GPU it runs on
+ * until the process ends: the first READY_STATIC_COUNTER_BYTES hold the
+ * synchronisation counters, the rest the arrays readyWorkspaceSize counts.
+ *   Arguments, layouts, ownership and device-side errors as for
+ *   readyStateReader.
+ *   READY_ERR_STATIC_SCRATCH_TOO_SMALL: the plan's arrays need more than
+ *   READY_STATIC_SCRATCH_BYTES - READY_STATIC_COUNTER_BYTES bytes, or its
+ *   counters more than READY_STATIC_COUNTER_BYTES (readyWorkspaceSize gives
+ *   their sum; every plan whose workspace is at most 15 MiB fits).  Nothing
+ *   is launched.
+ *   The first call on a device looks up the array's address on that device
+ *   (READY_ERR_HIP on failure) and enqueues, on `stream` before the reader,
+ *   a small kernel that clears the counters.  That first call must not be
+ *   made while `stream` is capturing a graph (READY_ERR_UNSUPPORTED); later
+ *   calls may be captured.
+ *   Every call on one device shares that device's array, which keeps the
+ *   last call's contents; each call leaves the counters cleared, so calls
+ *   one after another (one stream, or streams ordered by events) may use any
+ *   plans.  Calls that overlap in time on one device race on the array and
+ *   give wrong results.
+ * Allocates nothing (no hipMalloc, hipFree or allocating library call) and
+ * never synchronises.
+ */
+#define READY_STATIC_SCRATCH_BYTES (16u << 20)
+#define READY_STATIC_COUNTER_BYTES (64u << 10)
+readyStatus readyStateReaderStatic(const readyPlan* plan, const readyStates* states,
+                                   const int32_t* accept_idx, const void* h,
+                                   const readyWeights* weights, const readyOutputs* outputs, void* stream);
 
 /*
  * Step 1 alone: gathered[b][m] = states[b][accept_idx[b]][layer_ids[l]][a]

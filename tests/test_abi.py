@@ -138,7 +138,7 @@ class _Fake:
         return p
 
 
-def _call(shape, layer_ids=(0, 1), mutate=None):
+def _call(shape, layer_ids=(0, 1), mutate=None, static=False):
     _lib()
     st, plan = R.readyPlanCreate(shape, list(layer_ids))
     assert st == R.READY_OK
@@ -159,7 +159,11 @@ def _call(shape, layer_ids=(0, 1), mutate=None):
                 weights=w, outputs=o, workspace=f.alloc(ws_bytes), workspace_bytes=ws_bytes, stream=None)
     if mutate:
         mutate(args)
-    code = R.readyStateReader(**args)
+    if static:
+        code = R.readyStateReaderStatic(args["plan"], args["states"], args["accept_idx"], args["h"],
+                                        args["weights"], args["outputs"], args["stream"])
+    else:
+        code = R.readyStateReader(**args)
     R.readyPlanDestroy(plan)
     return code
 
@@ -399,3 +403,50 @@ def test_gather_validation():
         a["dev_status"] = a["gathered"] + 64
     assert _gather_call(_shape(), mutate=gathered_in_states) == R.READY_ERR_ALIASING
     assert _gather_call(_shape(), mutate=status_in_gathered) == R.READY_ERR_ALIASING
+
+
+# ------------------------------------------------------------ readyStateReaderStatic (no workspace)
+
+def test_static_entry_validates_before_touching_the_device():
+    """The no-workspace form checks its arguments like readyStateReader; no
+    case here reaches the device lookup (B = 0 is a valid no-op)."""
+    assert _call(_shape(B=0), static=True) == R.READY_OK
+
+    def null(field):
+        def f(a):
+            if field.startswith("o."):
+                setattr(a["outputs"], field[2:], None)
+            else:
+                a[field] = None
+        return f
+    for field in ("accept_idx", "h", "o.gathered", "o.out"):
+        assert _call(_shape(), mutate=null(field), static=True) == R.READY_ERR_NULL_POINTER, field
+
+    def mis(a):
+        a["h"] += 2
+    assert _call(_shape(), mutate=mis, static=True) == R.READY_ERR_MISALIGNED
+
+    def alias(a):
+        a["outputs"].out = a["weights"].w2
+    assert _call(_shape(), mutate=alias, static=True) == R.READY_ERR_ALIASING
+    _lib()
+    assert R.load().readyStateReaderStatic(None, None, None, None, None, None, None) == R.READY_ERR_NULL_POINTER
+
+
+def test_static_entry_rejects_plans_beyond_the_array():
+    """Plans whose scratch exceeds the static array are refused with their
+    own status, before any argument is looked at; plans that fit are not."""
+    _lib()
+    big = R.make_shape(B=256, P=8, n=7, L_tot=3, L_sel=3, H=16, r=128, d=5120, Hm=256)
+    st, plan = R.readyPlanCreate(big, [0, 1, 2])
+    assert st == R.READY_OK
+    assert R.readyWorkspaceSize(plan)[1] > R.READY_STATIC_SCRATCH_BYTES
+    assert R.load().readyStateReaderStatic(plan, None, None, None, None, None, None) == \
+        R.READY_ERR_STATIC_SCRATCH_TOO_SMALL
+    R.readyPlanDestroy(plan)
+    batched = R.make_shape(B=64, P=8, n=7, L_tot=2, L_sel=2, H=16, r=8, d=5120, Hm=256)
+    st, plan = R.readyPlanCreate(batched, [0, 1])
+    assert R.readyWorkspaceSize(plan)[1] <= R.READY_STATIC_SCRATCH_BYTES - R.READY_STATIC_COUNTER_BYTES
+    assert R.load().readyStateReaderStatic(plan, None, None, None, None, None, None) == R.READY_ERR_NULL_POINTER
+    R.readyPlanDestroy(plan)
+    assert R.readyStatusString(R.READY_ERR_STATIC_SCRATCH_TOO_SMALL) == "READY_ERR_STATIC_SCRATCH_TOO_SMALL"
