@@ -43,7 +43,7 @@ struct readyPlan {
   int fast;
   int small;     // fast path: at most 16 rows (16-row tiles; 64 otherwise)
   int n_z, n_s, n_a, n_o, n_counters;
-  int c_zcnt, c_zdone, c_sdone, c_adone, c_tk, c_aq, c_oq;  // first counter slot of each group
+  int c_zcnt, c_zdone, c_sdone, c_adone, c_tk, c_zq, c_aq, c_oq, c_arx, c_arg;  // first counter slot of each group
   size_t lds;
   GemmPlan gz, g1, g2;
   size_t off_zpart, off_hss, off_f, off_a, off_g1p, off_flags, off_pmat, off_ell, off_ctr, ws_bytes;
@@ -140,8 +140,17 @@ readyStatus readyPlanCreate(const readyShape* shape, const int32_t* layer_ids, r
                         (int64_t)p->R * s.Hm * 2 < (1LL << 31) &&
                         fks * p->R * p->Nz * 4 < (1LL << 31);
   p->small = p->R <= 16 ? 1 : 0;
-  const bool fits = allbf && s.r <= 32 && p->F % 8 == 0 && p->F <= READY_FAST_MAX_F && s.Hm % 8 == 0 &&
+  bool fits = allbf && s.r <= 32 && p->F % 8 == 0 && p->F <= READY_FAST_MAX_F && s.Hm % 8 == 0 &&
                     p->Nz <= READY_FAST_MAX_NZ && small_ws;
+  {
+    // per-XCD queue lengths of the Z and O items (the A items are fewer)
+    const int64_t bmz = p->small ? 16 : std::min(READY_BMZ_LARGE, READY_BMZ_APPLY);
+    const int64_t bmo = p->small ? 16 : std::min(READY_BMO_LARGE, READY_BMO_APPLY);
+    const int64_t rows = std::max(p->R, 1);
+    const int64_t zq = cdiv(fks, 8) * cdiv(rows, bmz) * cdiv(p->Nz, 64);
+    const int64_t oq = cdiv(rows, bmo) * cdiv(cdiv(s.d, READY_OCOLS), 8);
+    if (zq >= (1 << 24) || oq >= (1 << 24)) fits = false;
+  }
   p->lds = fits ? ready_reader_lds(s.r, p->F, p->Nz, p->small) : 0;
   p->fast = (fits && p->lds <= 80 * 1024 && s.path == READY_PATH_FUSED) ? 1 : 0;  // two workgroups per CU
 
@@ -157,6 +166,8 @@ readyStatus readyPlanCreate(const readyShape* shape, const int32_t* layer_ids, r
     p->gz.ksplit = (int)fks;
     p->gz.kchunk = (int)zchunk;
     p->n_z = (int)(nrbz * ncbz * fks);
+    // items are claimed as (queue << 24) | index: each per-XCD queue holds
+    // fewer than 2^24 (checked below, with the other limits of the path)
     p->n_s = s.B * p->M;
     p->n_a = (int)(nrb16 * cdiv(s.Hm, 64));
     p->n_o = (int)(nrbo * cdiv(s.d, READY_OCOLS));
@@ -167,9 +178,12 @@ readyStatus readyPlanCreate(const readyShape* shape, const int32_t* layer_ids, r
     p->c_sdone = (int)(p->c_zdone + nrbz);
     p->c_adone = (int)(p->c_sdone + nrb16);
     p->c_tk = (int)(p->c_adone + nrbo);
-    p->c_aq = p->c_tk + READY_TICKET_GROUPS;
+    p->c_zq = p->c_tk + READY_TICKET_GROUPS;
+    p->c_aq = p->c_zq + 8;
     p->c_oq = p->c_aq + 8;
-    p->n_counters = (int)(READY_CTR_STRIDE * (p->c_oq + 8));
+    p->c_arx = p->c_oq + 8;
+    p->c_arg = p->c_arx + 8;
+    p->n_counters = (int)(READY_CTR_STRIDE * (p->c_arg + READY_TICKET_GROUPS));
   } else {
     // query GEMM: matrix cores for bf16 h and weights; K split so that about
     // 256 (matrix cores) or 512 (VALU) workgroups run
@@ -266,13 +280,6 @@ StageEvents stage_events(void* const* events, int i) {
   return ev;
 }
 
-// Items are dealt to the 8 XCDs round robin when the grid allows it; the
-// state tiles are drawn through READY_TICKET_GROUPS ticket counters.
-void reader_roles(FastArgs& a, int grid) {
-  a.nxcd = (grid % 8 == 0) ? 8 : 1;
-  a.ntg = std::min(grid, READY_TICKET_GROUPS);
-}
-
 // The scratch of a call held in a caller's workspace: the arrays at the
 // plan's offsets, the counters at off_ctr, stamped with the plan's magic word.
 WsView workspace_view(const readyPlan* plan, void* workspace) {
@@ -310,6 +317,9 @@ void fast_common(const readyPlan* plan, const WsView& view, FastArgs& a) {
   a.sdone = ctr + READY_CTR_STRIDE * plan->c_sdone;
   a.adone = ctr + READY_CTR_STRIDE * plan->c_adone;
   a.tk = ctr + READY_CTR_STRIDE * plan->c_tk;
+  a.zq = ctr + READY_CTR_STRIDE * plan->c_zq;
+  a.arr_x = ctr + READY_CTR_STRIDE * plan->c_arx;
+  a.arr_g = ctr + READY_CTR_STRIDE * plan->c_arg;
   a.aq = ctr + READY_CTR_STRIDE * plan->c_aq;
   a.oq = ctr + READY_CTR_STRIDE * plan->c_oq;
   a.n_z = plan->n_z; a.n_s = plan->n_s; a.n_a = plan->n_a; a.n_o = plan->n_o;
@@ -335,7 +345,6 @@ readyStatus launch_fast(const readyPlan* plan, FastArgs& a, hipStream_t strm, vo
   const int per_cu = std::min(cap, ready_reader_per_cu(plan->s.r, plan->small, plan->lds, a.mode));
   if (per_cu < 1 || cus < 1) return READY_ERR_HIP;
   const int grid = per_cu * cus;
-  reader_roles(a, grid);
   if (ready_launch_reader(a, plan->small, grid, strm, stage_events(events, 1)) != hipSuccess)
     return READY_ERR_HIP;
   // the other stages run inside the same kernel: their marks (if any) are

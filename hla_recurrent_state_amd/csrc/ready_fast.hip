@@ -1,13 +1,12 @@
 // Fast path of the ReaDy state reader for gfx950: bf16 states, activations
 // and weights, rank r <= 32.  One persistent launch, k_reader.
 //
-// Its grid is two workgroups per CU, which the register and LDS budget of
-// the kernel lets the GPU hold at the same time.  Every workgroup runs four
-// kinds of work item, in this order:
+// Its grid is two workgroups per CU.  Workgroups run four kinds of work
+// item, in this order:
 //   Z  the query sums: a BM x 64 tile of the partial sums z = W_q (gamma h)
 //      over one K chunk, plus the sums of squares of h for RMSNorm(h_j)
 //      (step 4); the item that completes a tile's last chunk sums the chunks
-//      in chunk order.  Only the first workgroups of each XCD have Z items.
+//      in chunk order.
 //   S  the state tiles, drawn through ticket counters in sequence order:
 //      fused gather at the accept index into the caller's buffer, mean
 //      square, log-RMS and P = V^T S_bar U^T / sqrt(d_k), an r x r matrix
@@ -15,13 +14,14 @@
 //      q_j = U^T z_j is P z_j).  Two tiles are in flight while one is
 //      processed.
 //   A  16 rows x 64 columns of a: f_j = [P z_j / rms(h_j), ell] per pair,
-//      a = act(W1 f + b1) (step 4 readout, step 5), drawn in row order from
-//      a queue per XCD group once the workgroup has no tile left.
-//   O  a BM x 128 tile of out = h + W2 a + b2 (step 5), drawn the same way
-//      once the A queue is empty.
-// Z and S items never wait; A items wait for the Z and S items of their
-// rows; O items wait for the A items of their rows.  With every workgroup
-// resident at once each wait ends.
+//      a = act(W1 f + b1) (step 4 readout, step 5), in row order.
+//   O  a BM x 128 tile of out = h + W2 a + b2 (step 5), in row order.
+// Every item is claimed from a counter (see "claiming work items"): no item
+// belongs to a workgroup by its index, and the launch completes whatever
+// part of its grid is resident at a time.  Z and S items never wait; A items
+// wait for the Z and S items of their rows; O items wait for the A items of
+// their rows; a workgroup waits only for items that running workgroups hold
+// or will take before they wait themselves.
 //
 // Several readers sharing one gather use two more forms of the same kernel
 // (the MODE template parameter): a prepare launch runs only the S items and
@@ -29,10 +29,10 @@
 // only the Z, A and O items of one reader, reading the P, ell and
 // invalid-sequence flags a prepare launch left.
 //
-// The K chunks of the Z items, and the column blocks of the O items, are
-// dealt to the XCDs round robin (the hardware hands workgroup g to XCD
-// g % 8), so the h and W_q columns of a chunk, and the W2 rows of a column
-// block, are read from HBM once and then served by that XCD's L2.
+// The K chunks of the Z items, and the column blocks of the O items, sit in
+// per-XCD queues that the workgroups running on that XCD (hardware XCC id)
+// draw from, so the h and W_q columns of a chunk, and the W2 rows of a
+// column block, are read from HBM once and then served by that XCD's L2.
 //
 // Cross-workgroup data (z partial sums, P, ell, the invalid-sequence flags,
 // a) is written with device-coherent stores (sc1), made complete with a wait
@@ -155,6 +155,72 @@ __device__ bool wg_wait(const uint32_t* c, uint32_t want, const FastArgs& a, int
   const bool ok = *s_flag != 0;
   __syncthreads();
   return ok;
+}
+
+// ---- claiming work items
+//
+// Items sit in queue sets: the Z, A and O items in 8 queues each (one per
+// XCD), the state tiles in READY_TICKET_GROUPS ticket groups.  A workgroup
+// marks its arrival in its homes -- its XCD (flag arr_x) and its ticket group
+// g % READY_TICKET_GROUPS (flag arr_g) -- at start, and claims from its home
+// queue of each kind until that queue is exhausted; it takes every item of
+// its home Z queue and ticket group before any item that waits.  A home
+// whose flag is still clear when a workgroup is about to take its first A
+// item is an orphan: no workgroup of this launch has run there yet (other
+// kernels hold that XCD, say, so the grid is only partly resident).  That
+// workgroup then claims and runs the orphan's Z items and tiles itself, and
+// drains the orphan XCDs' A and O queues after its own.  So every wait is for
+// items that running workgroups hold or will take before they wait
+// themselves, and every item runs.  In a launch whose grid is all resident
+// every flag is set by then, and the check costs the flag loads that travel
+// with the first A claim.
+
+constexpr uint32_t NO_ITEM = 0xffffffffu;
+
+// XCD (0..7) of the running wave
+__device__ __forceinline__ int hw_xcc() {
+  uint32_t x;
+  asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(x));
+  return (int)(x & 7u);
+}
+
+// Thread 0 claims an item of queue x for the workgroup; every thread gets
+// its index, or NO_ITEM when the queue is exhausted.
+__device__ __forceinline__ uint32_t claim_one(uint32_t* qctr, int x, uint32_t size, uint32_t* s_bc) {
+  if (threadIdx.x == 0) {
+    const uint32_t i = count_up(ctr(qctr, x));
+    *s_bc = i < size ? i : NO_ITEM;
+  }
+  __syncthreads();
+  const uint32_t r = *s_bc;
+  __syncthreads();
+  return r;
+}
+
+// One trip of wave 0: lane 0 claims from `claim` (count_up) unless it is
+// null; lanes l < n
+// read the arrival flag flag(l).  Every thread gets the claim's raw result
+// (in *claimed) and the mask of clear flags.  s_bc: 3 words of LDS.
+template <typename Flag>
+__device__ __forceinline__ uint64_t arrival_check(uint32_t* claim, int n, Flag flag, uint32_t* claimed,
+                                                  uint32_t* s_bc) {
+  const int tid = threadIdx.x;
+  if (tid < 64) {
+    uint32_t i = NO_ITEM;
+    if (tid == 0 && claim != nullptr) i = count_up(claim);
+    const bool clear = tid < n && ld_coh_u32(flag(tid)) == 0u;
+    const uint64_t m = __ballot(clear);
+    if (tid == 0) {
+      s_bc[0] = i;
+      s_bc[1] = (uint32_t)m;
+      s_bc[2] = (uint32_t)(m >> 32);
+    }
+  }
+  __syncthreads();
+  *claimed = s_bc[0];
+  const uint64_t m = (uint64_t)s_bc[1] | ((uint64_t)s_bc[2] << 32);
+  __syncthreads();
+  return m;
 }
 
 }  // namespace
@@ -480,15 +546,19 @@ __device__ __forceinline__ void tile_project(const u32x4* sS, const uint16_t* sU
 }
 
 // Process tile t whose loads were issued: copy to `gathered`, sum of
-// squares, S U^T, P, ell.  Thread 0 also publishes `pub` (a ticket) in
-// *s_pub, readable by every thread once this returns.  Tile `announce` (if >= 0) is counted as done on
+// squares, S U^T, P, ell.  Thread 0 also publishes the tile of the next
+// ticket in *s_pub, readable by every thread once this returns.  Tile `announce` (if >= 0) is counted as done on
 // the way: its stores were issued before this tile's loads, and with the
 // in-order completion of the memory counter they are complete once every
 // wave has waited for this tile's data (the barrier after the LDS copy).
 // This tile's own stores are complete after the caller's next such wait.
 template <int RR, bool MULTI>
 __device__ __forceinline__ void tile_process(const FastArgs& a, int t, const TileRegs<RR>& R, unsigned char* smem,
-                                             int announce, uint32_t* s_pub, uint32_t pub) {
+                                             int announce, uint32_t* s_pub, uint32_t raw, int q, uint32_t nt) {
+  // thread 0: the tile of ticket `raw` of group q (NO_ITEM when the group is
+  // exhausted), published after the first barrier below, so that only wave 0
+  // waits for the ticket's trip
+  auto pub_of = [&]() { return raw < nt ? (uint32_t)(q + READY_TICKET_GROUPS * (int)raw) : NO_ITEM; };
   constexpr int NB = (RR + 15) / 16;  // 16-column blocks of U^T
   constexpr int LU = READY_TILE + 8;  // padded U row in LDS (bf16)
   constexpr int WCH = RR * 16;
@@ -507,7 +577,7 @@ __device__ __forceinline__ void tile_process(const FastArgs& a, int t, const Til
     // out-of-range accept index: flag it and leave this sequence's outputs.
     // No tile loads were issued, so wait explicitly before announcing.
     __syncthreads();  // every thread has read the last published ticket
-    if (tid == 0) *s_pub = pub;
+    if (tid == 0) *s_pub = pub_of();
     for (int inj = 0; inj < (MULTI ? a.n_inj : 1); ++inj)
       for (int e = tid; e < RR * RR; e += 256) st_coh_f32(P + (int64_t)inj * a.p_inj_stride + e, 0.0f);
     if (tid == 0) {
@@ -523,7 +593,7 @@ __device__ __forceinline__ void tile_process(const FastArgs& a, int t, const Til
 
   u32x4* dst = (u32x4*)(a.gathered + (int64_t)t * READY_TILE_ELEMS);
   __syncthreads();  // the previous tile is done with the LDS area and the last published ticket
-  if (tid == 0) *s_pub = pub;
+  if (tid == 0) *s_pub = pub_of();
   float ss = 0.0f;
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
@@ -585,54 +655,48 @@ __device__ __forceinline__ void tile_process(const FastArgs& a, int t, const Til
   }
 }
 
-// The S items of workgroup g: the tiles t = q + ntg i (q = g % ntg), i a
-// ticket.  In each group the workgroups without Z items take tickets
-// 0 .. 2 k - 1 two by two, in order, without asking (k of them); every other
-// ticket is drawn from counter q (offset by 2 k), so that a workgroup that
-// started late, after Z items, simply draws fewer.  Two tiles are in flight
-// while one is processed, and the ticket of the one after them is in flight
-// too: it is requested before the loads of the tile it follows, so that
-// waiting for it never waits for tile data.  The tile processed two turns
-// back is announced while a tile is processed; the last two at the end.
-// has_z(w) tells whether workgroup w runs Z items.
-template <int RR, bool MULTI, typename HasZ>
-__device__ __forceinline__ void s_phase(const FastArgs& a, int g, int G, unsigned char* smem, const int* s_acc,
-                                        uint32_t* s_tk, HasZ has_z) {
+// Ticket i of group q is tile q + G i (G = READY_TICKET_GROUPS); group q
+// holds group_tiles(q) tickets.
+__device__ __forceinline__ uint32_t group_tiles(const FastArgs& a, int q) {
+  return (uint32_t)((a.n_s - q + READY_TICKET_GROUPS - 1) / READY_TICKET_GROUPS);
+}
+
+// The S items of one workgroup: the tiles of the tickets it draws from group
+// q until the group is exhausted, the first two in one draw.  Two tiles are
+// in flight while one is processed, and the ticket of the one after them is
+// in flight too: it is requested before the loads of the tile it follows, so
+// that waiting for it never waits for tile data.  The tile processed two
+// turns back is announced while a tile is processed; the last two at the
+// end.
+template <int RR, bool MULTI>
+__device__ __forceinline__ void s_phase(const FastArgs& a, int q, unsigned char* smem, const int* s_acc,
+                                        uint32_t* s_tk) {
+  constexpr int NQ = READY_TICKET_GROUPS;
   const int tid = threadIdx.x;
-  const int nq = a.ntg, q = g % nq, j = g / nq, nj = (G - q + nq - 1) / nq;
-  const uint32_t nt = (uint32_t)((a.n_s - q + nq - 1) / nq);
+  const uint32_t nt = group_tiles(a, q);
   uint32_t* tk = ctr(a.tk, q);
-  int nzr = 0, nzall = 0;
-  for (int jj = 0; jj < nj; ++jj)
-    if (!has_z(q + nq * jj)) {
-      nzr += jj < j ? 1 : 0;
-      ++nzall;
-    }
-  const uint32_t base = 2u * (uint32_t)nzall;
-  uint32_t i0 = 2u * (uint32_t)nzr;
-  if (has_z(g)) {
-    if (tid == 0) *s_tk = base + __hip_atomic_fetch_add(tk, 2u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __syncthreads();
-    i0 = *s_tk;
-  }
-  int t0 = i0 < nt ? q + nq * (int)i0 : -1;
-  int t1 = i0 + 1 < nt ? q + nq * (int)(i0 + 1) : -1;
-  uint32_t pend = 0xffffffffu;  // thread 0: the ticket after t1
-  if (tid == 0 && t1 >= 0) pend = base + count_up(tk);
+  if (tid == 0) *s_tk = __hip_atomic_fetch_add(tk, 2u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  const uint32_t i0 = *s_tk;
+  __syncthreads();
+  int t0 = i0 < nt ? q + NQ * (int)i0 : -1;
+  int t1 = i0 + 1 < nt ? q + NQ * (int)(i0 + 1) : -1;
+  uint32_t pend = NO_ITEM;  // thread 0: the ticket after t1
+  if (tid == 0 && t1 >= 0) pend = count_up(tk);
   TileRegs<RR> r0, r1;
   if (t0 >= 0) tile_issue<RR>(a, t0, r0, s_acc);
   if (t1 >= 0) tile_issue<RR>(a, t1, r1, s_acc);
   int h1 = -1, h2 = -1;  // tiles processed one and two turns back
   while (t0 >= 0) {
-    tile_process<RR, MULTI>(a, t0, r0, smem, h2, s_tk, pend);
-    const uint32_t i2 = *s_tk;
+    tile_process<RR, MULTI>(a, t0, r0, smem, h2, s_tk, pend, q, nt);
+    const int t2 = (int)*s_tk;
     h2 = h1;
     h1 = t0;
     t0 = t1;
     r0 = r1;
-    t1 = (t0 >= 0 && i2 < nt) ? q + nq * (int)i2 : -1;
-    pend = 0xffffffffu;
-    if (tid == 0 && t1 >= 0) pend = base + count_up(tk);
+    t1 = t0 >= 0 ? t2 : -1;
+    pend = NO_ITEM;
+    if (tid == 0 && t1 >= 0) pend = count_up(tk);
     if (t1 >= 0) tile_issue<RR>(a, t1, r1, s_acc);
   }
   wait_mem();
@@ -1008,90 +1072,166 @@ __device__ __forceinline__ void mlp2_item(const FastArgs& a, int rb, int cb, uns
 
 // ---------------------------------------------------------------- k_reader
 
-// Two workgroups of four waves per CU: at most 256 registers per lane.
-// Every workgroup runs its Z items, then its state tiles, then its A items,
-// then its O items.  Items of one kind are dealt to the workgroups in order
-// (Z items and O items per XCD: the K chunks ks with ks % nxcd == x, and the
-// column blocks cb with cb % nxcd == x, go to the workgroups on XCD x).
+// Item k of Z queue x: K chunk ks = x + 8 (k / tiles), then the tile's column
+// block and row block.
+template <int BMZ, int NST>
+__device__ __forceinline__ void z_run(const FastArgs& a, int x, uint32_t k, unsigned char* smem) {
+  const int nrbz = cdiv_d(a.R, BMZ), ncbz = cdiv_d(a.Nz, 64), tiles = nrbz * ncbz;
+  const int ks = x + 8 * ((int)k / tiles), rem = (int)k - ((int)k / tiles) * tiles;
+  z_item<BMZ, NST>(a, ks, rem / nrbz, rem - (rem / nrbz) * nrbz, smem);
+}
+
+// Tile t alone (an orphan group's): gather, statistics and projection, then
+// counted.
+template <int RR, bool MULTI>
+__device__ __forceinline__ void s_single(const FastArgs& a, int t, unsigned char* smem, const int* s_acc,
+                                         uint32_t* s_tk) {
+  TileRegs<RR> r;
+  tile_issue<RR>(a, t, r, s_acc);
+  tile_process<RR, MULTI>(a, t, r, smem, -1, s_tk, NO_ITEM, 0, 0u);
+  wait_mem();
+  __syncthreads();
+  if (threadIdx.x == 0) tile_count(a, t);
+  __syncthreads();
+}
+
+// Two workgroups of four waves per CU: at most 256 registers per lane.  A
+// workgroup takes Z items from its XCD's queue, then state tiles from its
+// ticket group, then A items, then O items, each kind until its home queue
+// is exhausted (items of queue x share operands: K chunks ks % 8 == x, A
+// items j % 8 == x, column blocks cb % 8 == x), with the orphan checks
+// described with claim_one before its first A item, its first O item and its
+// end.  The first Z claim and the arrival marks ride on the launch's first
+// trip to memory.
 template <int RR, int SMALL, int MODE>
 __global__ __launch_bounds__(256, (MODE == READY_MODE_PREPARE && RR <= 16) ? 3 : 2) void k_reader(FastArgs a) {
   constexpr int BMZ = SMALL ? 16 : (MODE == READY_MODE_APPLY ? READY_BMZ_APPLY : READY_BMZ_LARGE);
   constexpr int BMO = SMALL ? 16 : (MODE == READY_MODE_APPLY ? READY_BMO_APPLY : READY_BMO_LARGE);
   constexpr int NST = (SMALL ? READY_ZCHUNK_SMALL : READY_ZCHUNK_LARGE) / 128;
+  // a prepare launch (several readers sharing one gather) has no Z, A or O
+  // items; an apply launch has no state tiles (n_s = 0)
+  constexpr bool zao = MODE != READY_MODE_PREPARE;
+  constexpr bool has_s = MODE != READY_MODE_APPLY;
+  constexpr bool multi = MODE == READY_MODE_PREPARE;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   __shared__ int s_last;
   __shared__ int s_acc[READY_ACC_LDS];
-  __shared__ uint32_t s_tk;
+  __shared__ uint32_t s_tk[3];
+  const int tid = threadIdx.x;
   const int g = blockIdx.x, G = gridDim.x;
+  const int xcc = hw_xcc(), home_g = g % READY_TICKET_GROUPS;
+  uint32_t zfirst = NO_ITEM;
+  if (tid == 0) {
+    if constexpr (zao) zfirst = count_up(ctr(a.zq, xcc));
+    st_coh_u32(ctr(a.arr_x, xcc), 1u);
+    st_coh_u32(ctr(a.arr_g, home_g), 1u);
+  }
   // the accept indices are requested with the magic word, and staged in LDS
   // before the state tiles
   constexpr int APT = READY_ACC_LDS / 256;
   int accv[APT];
 #pragma unroll
   for (int k = 0; k < APT; ++k) {
-    const int b = threadIdx.x + 256 * k;
+    const int b = tid + 256 * k;
     accv[k] = (MODE != READY_MODE_APPLY && b < a.B) ? a.accept_idx[b] : 0;  // apply launches have none
   }
   if (a.counters[0] != a.magic) {
-    // the workspace was not prepared for this plan: touch nothing else
-    if (g == 0 && threadIdx.x == 0 && a.dev_status) *a.dev_status = READY_ERR_WORKSPACE_UNINIT;
+    // the workspace was not prepared for this plan: touch nothing else (the
+    // claim and marks above changed counter words of the workspace only)
+    if (g == 0 && tid == 0 && a.dev_status) *a.dev_status = READY_ERR_WORKSPACE_UNINIT;
     return;
   }
-  // a.nxcd is 8 when G is a multiple of 8 (the same number of workgroups on
-  // each XCD), else 1.  The hardware hands consecutive workgroups to
-  // consecutive XCDs, so the workgroups g with one value of g % 8 share an
-  // XCD and its L2.
-  const int nx = a.nxcd, xs = nx == 8 ? 3 : 0;  // nx = 1 << xs
-  const int x = g & (nx - 1), li = g >> xs, per = G >> xs;
-  const int nrbz = cdiv_d(a.R, BMZ), ncbz = cdiv_d(a.Nz, 64), tiles = nrbz * ncbz;
-  // a prepare launch (several readers sharing one gather) has no Z, A or O
-  // items; an apply launch has no state tiles (n_s = 0)
-  constexpr bool zao = MODE != READY_MODE_PREPARE;
-  auto has_z = [&](int w) {
-    const int xw = w & (nx - 1);
-    return zao && (w >> xs) < ((a.ksplit - xw + nx - 1) >> xs) * tiles;
-  };
+
+  // queue sizes
+  const int ztiles = cdiv_d(a.R, BMZ) * cdiv_d(a.Nz, 64);
+  const int ncb = cdiv_d(a.d, READY_OCOLS), nrbo = cdiv_d(a.R, BMO);
+  auto z_size = [&](int x) { return (uint32_t)(((a.ksplit - x + 7) >> 3) * ztiles); };
+  auto a_size = [&](int x) { return (uint32_t)((a.n_a - x + 7) >> 3); };
+  auto o_size = [&](int x) { return (uint32_t)(nrbo * ((ncb - x + 7) >> 3)); };
+
   if constexpr (zao) {
-    const int nkx = (a.ksplit - x + nx - 1) >> xs;
-    for (int i = li; i < nkx * tiles; i += per) {
-      const int ks = x + nx * (i / tiles), rem = i % tiles;
-      z_item<BMZ, NST>(a, ks, rem / nrbz, rem % nrbz, smem);
+    if (tid == 0) s_tk[0] = zfirst;
+    __syncthreads();
+    uint32_t i = s_tk[0];
+    __syncthreads();
+    const uint32_t zs = z_size(xcc);
+    while (i < zs) {
+      z_run<BMZ, NST>(a, xcc, i, smem);
+      i = claim_one(a.zq, xcc, zs, s_tk);
     }
   }
 #pragma unroll
-  for (int k = 0; k < APT; ++k) s_acc[threadIdx.x + 256 * k] = accv[k];
+  for (int k = 0; k < APT; ++k) s_acc[tid + 256 * k] = accv[k];
   __syncthreads();
-  if (MODE != READY_MODE_APPLY) s_phase<RR, MODE == READY_MODE_PREPARE>(a, g, G, smem, s_acc, &s_tk, has_z);
-  // A items, then O items, drawn in row order from the queues of this
-  // workgroup's XCD group (A item j belongs to group j % nx, O item (rb, cb)
-  // to group cb % nx).  A ticket is drawn only when the previous item is
-  // done, so that no workgroup holds an item it cannot start yet.
+  if constexpr (has_s) s_phase<RR, multi>(a, home_g, smem, s_acc, s_tk);
+
   if constexpr (zao) {
-    uint32_t* aq = ctr(a.aq, x);
-    uint32_t* oq = ctr(a.oq, x);
-    const int nax = (a.n_a - x + nx - 1) >> xs;
-    const int nrbo = cdiv_d(a.R, BMO), ncb = cdiv_d(a.d, READY_OCOLS);
-    const int ncx = (ncb - x + nx - 1) >> xs;  // column blocks of XCD group x
-    const int nox = nrbo * ncx;
-    bool in_a = true;
-    for (;;) {
-      if (threadIdx.x == 0) s_tk = count_up(in_a ? aq : oq);
-      __syncthreads();
-      const uint32_t i = s_tk;
-      __syncthreads();  // every thread has read s_tk
-      if (in_a && i >= (uint32_t)nax) {
-        in_a = false;
+    // before the first A item: the arrival flags of the XCDs (lanes 0-7) and
+    // ticket groups (lanes 8..), read in the trip of the first A claim
+    constexpr int NF = has_s ? 8 + READY_TICKET_GROUPS : 8;
+    auto flag = [&](int l) { return l < 8 ? ctr(a.arr_x, l) : ctr(a.arr_g, l - 8); };
+    uint32_t first;
+    const uint64_t orph = arrival_check(ctr(a.aq, xcc), NF, flag, &first, s_tk);
+    const uint32_t orph_x = (uint32_t)(orph & 0xffu);
+    if (orph != 0) {
+      // orphans (a partly resident grid only): their Z items and tiles
+      for (uint64_t m = orph; m != 0; m &= m - 1) {
+        const int k = __ffsll((unsigned long long)m) - 1;
+        if (k < 8) {
+          for (uint32_t i; (i = claim_one(a.zq, k, z_size(k), s_tk)) != NO_ITEM;) z_run<BMZ, NST>(a, k, i, smem);
+        } else if constexpr (has_s) {
+          const int q = k - 8;
+          for (uint32_t i; (i = claim_one(a.tk, q, group_tiles(a, q), s_tk)) != NO_ITEM;)
+            s_single<RR, multi>(a, q + READY_TICKET_GROUPS * (int)i, smem, s_acc, s_tk);
+        }
+      }
+    }
+    // A items in row order from the home queue, then from orphan XCDs' (A
+    // item j in queue j % 8); an item is claimed only when the previous one
+    // is done, so that no workgroup holds an item it cannot start yet
+    for (uint32_t qs = orph_x | (1u << xcc), x = (uint32_t)xcc, i = first; qs != 0;) {
+      const uint32_t na = a_size((int)x);
+      if (i >= na) {
+        qs &= ~(1u << x);
+        if (qs == 0) break;
+        x = (uint32_t)(__ffs(qs) - 1);
+        i = claim_one(a.aq, (int)x, a_size((int)x), s_tk);
         continue;
       }
-      if (!in_a && i >= (uint32_t)nox) break;
-      if (in_a) mlp1_item<RR, BMZ, BMO>(a, x + (int)(i << xs), smem);
-      else mlp2_item<BMO>(a, (int)i / ncx, x + nx * ((int)i % ncx), smem);
+      mlp1_item<RR, BMZ, BMO>(a, (int)x + 8 * (int)i, smem);
+      i = claim_one(a.aq, (int)x, na, s_tk);
+    }
+    // O items likewise (O item (rb, cb) in queue cb % 8)
+    for (uint32_t qs = orph_x | (1u << xcc), x = (uint32_t)xcc, i = claim_one(a.oq, xcc, o_size(xcc), s_tk);
+         qs != 0;) {
+      const uint32_t no = o_size((int)x);
+      if (i >= no) {
+        qs &= ~(1u << x);
+        if (qs == 0) break;
+        x = (uint32_t)(__ffs(qs) - 1);
+        i = claim_one(a.oq, (int)x, o_size((int)x), s_tk);
+        continue;
+      }
+      const int ncx = (ncb - (int)x + 7) >> 3;  // column blocks of queue x
+      mlp2_item<BMO>(a, (int)i / ncx, (int)x + 8 * ((int)i % ncx), smem);
+      i = claim_one(a.oq, (int)x, no, s_tk);
+    }
+  } else {
+    // a prepare launch, before finishing: tiles of ticket groups no
+    // workgroup has arrived in
+    auto flag = [&](int l) { return ctr(a.arr_g, l); };
+    uint32_t none;
+    const uint64_t orph = arrival_check(nullptr, READY_TICKET_GROUPS, flag, &none, s_tk);
+    for (uint64_t m = orph; m != 0; m &= m - 1) {
+      const int q = __ffsll((unsigned long long)m) - 1;
+      for (uint32_t i; (i = claim_one(a.tk, q, group_tiles(a, q), s_tk)) != NO_ITEM;)
+        s_single<RR, multi>(a, q + READY_TICKET_GROUPS * (int)i, smem, s_acc, s_tk);
     }
   }
 
   // the last workgroup to finish clears the counters (two-level count)
   __syncthreads();
-  if (threadIdx.x == 0) {
+  if (tid == 0) {
     int last = 0;
     const int grp = g % READY_DONE_GROUPS;
     const int in_grp = (G - grp + READY_DONE_GROUPS - 1) / READY_DONE_GROUPS;
@@ -1101,7 +1241,7 @@ __global__ __launch_bounds__(256, (MODE == READY_MODE_PREPARE && RR <= 16) ? 3 :
   }
   __syncthreads();
   if (s_last) {
-    for (int i = READY_CTR_STRIDE + threadIdx.x; i < a.n_counters; i += 256) a.counters[i] = 0u;
+    for (int i = READY_CTR_STRIDE + tid; i < a.n_counters; i += 256) a.counters[i] = 0u;
   }
 }
 

@@ -80,7 +80,8 @@ struct FastArgs {
   // [1] abort flag, [2 .. 2 + READY_DONE_GROUPS] workgroups finished per
   // group and overall, then the Z items done per tile of z, the finished
   // tiles of z per row block, the S items done per 16 rows, the A items done
-  // per row tile of out, the state-tile tickets, the A- and O-item tickets.
+  // per row tile of out, the state-tile tickets, the Z-, A- and O-item
+  // claim counters, the arrival flags per XCD and per ticket group.
   // The last workgroup to finish clears all of them except the magic.
   uint32_t* counters;
   int n_counters;                  // words
@@ -91,12 +92,14 @@ struct FastArgs {
   uint32_t* zdone;                 // [cdiv(R, BMZ)]: tiles of zfin complete per row block
   uint32_t* sdone;                 // [cdiv(R, 16)]
   uint32_t* adone;                 // [cdiv(R, BMO)]
-  uint32_t* tk;                    // [ntg]: state-tile tickets drawn per group of workgroups
-  uint32_t* aq;                    // [8]: A-item tickets per XCD group
-  uint32_t* oq;                    // [8]: O-item tickets per XCD group
-  int ntg;                         // ticket groups: workgroup g draws the tiles t with t % ntg == g % ntg
+  uint32_t* tk;                    // [READY_TICKET_GROUPS]: state-tile tickets drawn per group (tiles t with
+                                   // t % READY_TICKET_GROUPS == group)
+  uint32_t* zq;                    // [8]: Z items claimed per XCD queue
+  uint32_t* arr_x;                 // [8]: a workgroup of the launch has run on XCD x
+  uint32_t* arr_g;                 // [READY_TICKET_GROUPS]: a workgroup of the launch has ticket group q as home
+  uint32_t* aq;                    // [8]: A items claimed per XCD queue
+  uint32_t* oq;                    // [8]: O items claimed per XCD queue
   int n_z, n_s, n_a, n_o;          // work items per kind
-  int nxcd;                        // 8: items dealt to XCDs round robin; 1: no XCD affinity
   int B, P, n, M, H, r, d, F, Hm, R, Nz, shared, ksplit, kchunk, act;
   float state_eps, h_eps;
   // Several readers sharing one gather.  READY_MODE_FULL runs every item

@@ -209,6 +209,15 @@ readyStatus readyWorkspaceInit(const readyPlan* plan, void* workspace, size_t wo
  * need separate workspaces).  The enqueued work
  * allocates nothing and synchronises nothing, so it may be captured into a
  * HIP graph.  Returns READY_ERR_HIP if a launch fails.
+ * Calls on different streams (each with its own workspace) may run at the
+ * same time as each other and as other kernels: the single-kernel path
+ * claims all of its work items from counters in the workspace and never
+ * needs its whole grid resident at once, so a launch completes whatever part
+ * of the GPU it gets.  Its waits between work items are bounded all the same:
+ * should one last about half a second (never expected), the call stops
+ * waiting, its outputs are invalid and READY_ERR_SYNC_TIMEOUT is stored in
+ * outputs->dev_status -- the only place this failure shows, so callers that
+ * need to detect it pass a status word.
  */
 readyStatus readyStateReader(const readyPlan* plan, const readyStates* states,
                              const int32_t* accept_idx, const void* h,

@@ -460,3 +460,49 @@ def test_repeated_calls_on_one_workspace():
         __import__("tests.gpu_util", fromlist=["oracle_reference"]).oracle_reference(inp))
     assert rep["gather_bitexact"] and rep["dh_rel"] <= rep["tol"] and rep["logrms_err"] <= 1e-5, rep
     assert rep["out_excess"] <= 0.0, rep
+
+
+def test_two_concurrent_calls_on_two_streams():
+    """Two batched calls at once, each on its own stream with its own
+    workspace and buffers: the work items of each launch are claimed from
+    its own counters and a launch never needs its whole grid resident at
+    once, so both complete, and each gives bit for bit the outputs of the
+    same call made alone."""
+    from hla_recurrent_state_amd import StateReader
+    import tests.gpu_util as gu
+    from synth.device import to_numpy_bits
+    dev = _dev()
+    cfg = make_shape("batched", t=16)
+    inps = [synth.make(cfg, seed=s) for s in (81, 82)]
+    reader = StateReader(gu.reader_shape(cfg), cfg.slots)
+    streams = [torch.cuda.Stream(dev), torch.cuda.Stream(dev)]
+    ds = [synth.device.to_device(inp, dev) for inp in inps]
+    wss = [reader.new_workspace(dev, st.cuda_stream) for st in streams]
+    torch.cuda.synchronize()
+
+    def call(k, o, stream):
+        d = ds[k]
+        reader(d["states"], d["accept_idx"], d["h"], d["weights"], o["gathered"], o["out"],
+               dev_status=o["dev_status"], workspace=wss[k], stream=stream.cuda_stream)
+
+    alone = []
+    for k in range(2):
+        o = gu.alloc_outputs(cfg, dev)
+        call(k, o, streams[k])
+        torch.cuda.synchronize()
+        alone.append(o)
+    together = [gu.alloc_outputs(cfg, dev) for _ in range(2)]
+    for k in range(2):
+        call(k, together[k], streams[k])   # both enqueued before either is waited for
+    torch.cuda.synchronize()
+    for k in range(2):
+        _say("stream", k, "status", int(together[k]["dev_status"].item()))
+        assert int(together[k]["dev_status"].item()) == 0
+        for key, dt in (("out", cfg.act_dtype), ("gathered", cfg.state_dtype)):
+            assert np.array_equal(to_numpy_bits(together[k][key], dt), to_numpy_bits(alone[k][key], dt)), key
+    rep = gu.compare(inps[0], {"gathered": to_numpy_bits(together[0]["gathered"], cfg.state_dtype),
+                               "out": to_numpy_bits(together[0]["out"], cfg.act_dtype), "logrms": None,
+                               "delta": None, "feat": None, "dev_status": 0},
+                     gu.oracle_reference(inps[0], seqs=[0, 31, 63]))
+    assert rep["ok"], rep
+    reader.close()
