@@ -43,7 +43,7 @@ struct readyPlan {
   int fast;
   int small;     // fast path: at most 16 rows (16-row tiles; 64 otherwise)
   int n_z, n_s, n_a, n_o, n_counters;
-  int c_zcnt, c_zdone, c_sdone, c_adone, c_tk, c_zq, c_aq, c_oq, c_arx, c_arg;  // first counter slot of each group
+  int c_zcnt, c_zdone, c_sdone, c_adone, c_tk, c_zq, c_aq, c_oq, c_arx;  // first counter slot of each group
   size_t lds;
   GemmPlan gz, g1, g2;
   size_t off_zpart, off_hss, off_f, off_a, off_g1p, off_flags, off_pmat, off_ell, off_ctr, ws_bytes;
@@ -182,8 +182,7 @@ readyStatus readyPlanCreate(const readyShape* shape, const int32_t* layer_ids, r
     p->c_aq = p->c_zq + 8;
     p->c_oq = p->c_aq + 8;
     p->c_arx = p->c_oq + 8;
-    p->c_arg = p->c_arx + 8;
-    p->n_counters = (int)(READY_CTR_STRIDE * (p->c_arg + READY_TICKET_GROUPS));
+    p->n_counters = (int)(READY_CTR_STRIDE * (p->c_arx + 8));
   } else {
     // query GEMM: matrix cores for bf16 h and weights; K split so that about
     // 256 (matrix cores) or 512 (VALU) workgroups run
@@ -319,7 +318,6 @@ void fast_common(const readyPlan* plan, const WsView& view, FastArgs& a) {
   a.tk = ctr + READY_CTR_STRIDE * plan->c_tk;
   a.zq = ctr + READY_CTR_STRIDE * plan->c_zq;
   a.arr_x = ctr + READY_CTR_STRIDE * plan->c_arx;
-  a.arr_g = ctr + READY_CTR_STRIDE * plan->c_arg;
   a.aq = ctr + READY_CTR_STRIDE * plan->c_aq;
   a.oq = ctr + READY_CTR_STRIDE * plan->c_oq;
   a.n_z = plan->n_z; a.n_s = plan->n_s; a.n_a = plan->n_a; a.n_o = plan->n_o;

@@ -95,6 +95,20 @@ __device__ __forceinline__ uint32_t ld_coh_u32(const void* p) {
 }
 // All memory operations of this thread issued so far are complete.
 __device__ __forceinline__ void wait_mem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// The value is in registers here: a load producing it may not be sunk past
+// this point (into a later trip).
+__device__ __forceinline__ void pin(u32x4& v) { asm volatile("" : "+v"(v)); }
+__device__ __forceinline__ void pin(float& v) { asm volatile("" : "+v"(v)); }
+// Loads for a trip of many: always issued, at offset 0 when `live` is false
+// (the caller never uses such a value).  A branch around a load, or a use of
+// the value right after it, makes the compiler wait for the load there and
+// splits the trip.
+__device__ __forceinline__ u32x4 ld_coh16_at(bool live, const void* base, uint32_t byte_off) {
+  return ld_coh16(base, live ? byte_off : 0u);
+}
+__device__ __forceinline__ float ld_coh4_at(bool live, const void* base, uint32_t byte_off) {
+  return ld_coh4(base, live ? byte_off : 0u);
+}
 __device__ __forceinline__ uint32_t count_up(uint32_t* c) {
   return __hip_atomic_fetch_add(c, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -159,21 +173,23 @@ __device__ bool wg_wait(const uint32_t* c, uint32_t want, const FastArgs& a, int
 
 // ---- claiming work items
 //
-// Items sit in queue sets: the Z, A and O items in 8 queues each (one per
-// XCD), the state tiles in READY_TICKET_GROUPS ticket groups.  A workgroup
-// marks its arrival in its homes -- its XCD (flag arr_x) and its ticket group
-// g % READY_TICKET_GROUPS (flag arr_g) -- at start, and claims from its home
-// queue of each kind until that queue is exhausted; it takes every item of
-// its home Z queue and ticket group before any item that waits.  A home
-// whose flag is still clear when a workgroup is about to take its first A
-// item is an orphan: no workgroup of this launch has run there yet (other
-// kernels hold that XCD, say, so the grid is only partly resident).  That
-// workgroup then claims and runs the orphan's Z items and tiles itself, and
-// drains the orphan XCDs' A and O queues after its own.  So every wait is for
-// items that running workgroups hold or will take before they wait
-// themselves, and every item runs.  In a launch whose grid is all resident
-// every flag is set by then, and the check costs the flag loads that travel
-// with the first A claim.
+// Items sit in queue sets with one queue per XCD: the Z items (K chunks ks
+// with ks % 8 == x), the state tiles (t % 8 == x, through a ticket counter),
+// the A items (j % 8 == x) and the O items (column blocks cb % 8 == x).  A
+// workgroup marks its arrival on its XCD (the hardware XCC id; flag arr_x)
+// at start and claims from its XCD's queue of each kind until that queue is
+// exhausted; it takes every item of its XCD's Z queue and ticket group
+// before any item that waits.  An XCD whose flag is still clear when a
+// workgroup is about to take its first A item is an orphan: no workgroup of
+// this launch has run there yet (other kernels hold it, say, so the grid is
+// only partly resident).  That workgroup then claims and runs the orphan's Z
+// items and tiles itself, and drains the orphan's A and O queues after its
+// own.  So every wait is for items that running workgroups hold or will take
+// before they wait themselves, and every item runs.  In a launch whose grid
+// is all resident every flag is set by then, and the check costs the flag
+// loads that travel with the first A claim.  (Each XCD has as many Z items as
+// the others, so the tiles, shared by all the workgroups of an XCD, are
+// balanced too.)
 
 constexpr uint32_t NO_ITEM = 0xffffffffu;
 
@@ -662,7 +678,10 @@ __device__ __forceinline__ uint32_t group_tiles(const FastArgs& a, int q) {
 }
 
 // The S items of one workgroup: the tiles of the tickets it draws from group
-// q until the group is exhausted, the first two in one draw.  Two tiles are
+// q until the group is exhausted, the first two in one trip: a pair of
+// consecutive tickets when the launch has at least two tiles per workgroup,
+// else two tickets drawn one by one (so that scarce tiles spread over more
+// workgroups).  Two tiles are
 // in flight while one is processed, and the ticket of the one after them is
 // in flight too: it is requested before the loads of the tile it follows, so
 // that waiting for it never waits for tile data.  The tile processed two
@@ -675,12 +694,23 @@ __device__ __forceinline__ void s_phase(const FastArgs& a, int q, unsigned char*
   const int tid = threadIdx.x;
   const uint32_t nt = group_tiles(a, q);
   uint32_t* tk = ctr(a.tk, q);
-  if (tid == 0) *s_tk = __hip_atomic_fetch_add(tk, 2u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const bool pair = a.n_s >= 2 * (int)gridDim.x;
+  if (tid == 0) {
+    if (pair) {
+      const uint32_t i = __hip_atomic_fetch_add(tk, 2u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      s_tk[0] = i;
+      s_tk[1] = i + 1;
+    } else {
+      const uint32_t i = count_up(tk), j = count_up(tk);
+      s_tk[0] = i;
+      s_tk[1] = j;
+    }
+  }
   __syncthreads();
-  const uint32_t i0 = *s_tk;
+  const uint32_t i0 = s_tk[0], i1 = s_tk[1];
   __syncthreads();
   int t0 = i0 < nt ? q + NQ * (int)i0 : -1;
-  int t1 = i0 + 1 < nt ? q + NQ * (int)(i0 + 1) : -1;
+  int t1 = (t0 >= 0 && i1 < nt) ? q + NQ * (int)i1 : -1;
   uint32_t pend = NO_ITEM;  // thread 0: the ticket after t1
   if (tid == 0 && t1 >= 0) pend = count_up(tk);
   TileRegs<RR> r0, r1;
@@ -776,11 +806,24 @@ __device__ __forceinline__ void mlp1_item(const FastArgs& a, int item, unsigned 
       const bool live = e < nmi && s0 + s < nseq && ok;
       const uint32_t pofs = (uint32_t)((((b * a.M + m) * RR + i) * RR) * 4);
 #pragma unroll
-      for (int c = 0; c < CR4; ++c) dst[s][c] = live ? ld_coh16(a.pmat, pofs + 16 * c) : u32x4{0u, 0u, 0u, 0u};
-      del[s] = (live && i == 0) ? ld_coh4(a.ell, (uint32_t)(4 * (b * a.M + m))) : 0.0f;
+      // (rows of sequences past the block's last, and ell of outputs i > 0,
+      // are loaded from offset 0 and never used)
+      for (int c = 0; c < CR4; ++c) dst[s][c] = ld_coh16_at(live, a.pmat, pofs + 16 * c);
+      del[s] = ld_coh4_at(live && i == 0, a.ell, (uint32_t)(4 * (b * a.M + m)));
     }
   };
   auto load_p = [&](int e, int s0) { load_p_into(e, s0, pv, ellv); };
+  // z of the 16 rows: 16 Nz / 4 chunks of 16 bytes, ZC per thread in the
+  // trip (all of them for Nz <= 256), the rest after it
+  constexpr int ZC = 4;
+  const int nzc = rows * (Nz / 4), nzall = 16 * (Nz / 4);
+  u32x4 zv[ZC];
+#pragma unroll
+  for (int j = 0; j < ZC; ++j) {
+    const int c = tid + 256 * j;
+    zv[j] = ld_coh16_at(c < nzc && ok, a.zfin, (uint32_t)(4 * (row0 * Nz + 4 * c)));  // rows past the block's
+                                                                                      // last are never used
+  }
   load_p(tid, 0);
   if constexpr (PRE2) load_p_into(tid + 256, 0, pv2, ellv2);
   // the sums of squares of h (threads 0-15, one row each) travel with the
@@ -789,27 +832,37 @@ __device__ __forceinline__ void mlp1_item(const FastArgs& a, int item, unsigned 
   float hv[16];
 #pragma unroll
   for (int k = 0; k < 16; ++k)
-    hv[k] = (hrow && k < a.ksplit) ? ld_coh4(a.hss, (uint32_t)(4 * (k * a.R + row0 + tid))) : 0.0f;
-  const int nzc = rows * (Nz / 4);
-  for (int c0 = tid; c0 < 16 * (Nz / 4); c0 += 256 * 4) {
-    u32x4 v[4];
+    hv[k] = ld_coh4_at(hrow && k < a.ksplit, a.hss, (uint32_t)(4 * (k * a.R + row0 + tid)));
+  // every load of the trip is in flight before this wait; the pins keep the
+  // compiler from sinking any of them into a later trip
+  wait_mem();
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int c = c0 + 256 * j;
-      v[j] = (c < nzc && ok) ? ld_coh16(a.zfin, (uint32_t)(4 * (row0 * Nz + 4 * c))) : u32x4{0u, 0u, 0u, 0u};
-    }
+  for (int j = 0; j < ZC; ++j) pin(zv[j]);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int c = c0 + 256 * j;
-      if (c < 16 * (Nz / 4)) *(u32x4*)&z_s[4 * c] = v[j];
+  for (int s = 0; s < PS; ++s) {
+#pragma unroll
+    for (int c = 0; c < CR4; ++c) {
+      pin(pv[s][c]);
+      if constexpr (PRE2) pin(pv2[s][c]);
     }
+    pin(ellv[s]);
+    if constexpr (PRE2) pin(ellv2[s]);
   }
+#pragma unroll
+  for (int k = 0; k < 16; ++k) pin(hv[k]);
+#pragma unroll
+  for (int j = 0; j < ZC; ++j) {
+    const int c = tid + 256 * j;
+    if (c < nzall) *(u32x4*)&z_s[4 * c] = zv[j];
+  }
+  for (int c = tid + 256 * ZC; c < nzall; c += 256)
+    *(u32x4*)&z_s[4 * c] = (c < nzc && ok) ? ld_coh16(a.zfin, (uint32_t)(4 * (row0 * Nz + 4 * c))) : u32x4{0u, 0u, 0u, 0u};
   if (tid < 16) {
     float rs = 0.0f;
     if (hrow) {
       float hs = 0.0f;
 #pragma unroll
-      for (int k = 0; k < 16; ++k) hs += hv[k];
+      for (int k = 0; k < 16; ++k) hs += k < a.ksplit ? hv[k] : 0.0f;
       for (int k = 16; k < a.ksplit; ++k) hs += ld_coh4(a.hss, (uint32_t)(4 * (k * a.R + row0 + tid)));
       rs = 1.0f / sqrtf(hs / (float)a.d + a.h_eps);
     }
@@ -1119,12 +1172,11 @@ __global__ __launch_bounds__(256, (MODE == READY_MODE_PREPARE && RR <= 16) ? 3 :
   __shared__ uint32_t s_tk[3];
   const int tid = threadIdx.x;
   const int g = blockIdx.x, G = gridDim.x;
-  const int xcc = hw_xcc(), home_g = g % READY_TICKET_GROUPS;
+  const int xcc = hw_xcc(), home_g = xcc;  // ticket group x is drawn on XCD x
   uint32_t zfirst = NO_ITEM;
   if (tid == 0) {
     if constexpr (zao) zfirst = count_up(ctr(a.zq, xcc));
     st_coh_u32(ctr(a.arr_x, xcc), 1u);
-    st_coh_u32(ctr(a.arr_g, home_g), 1u);
   }
   // the accept indices are requested with the magic word, and staged in LDS
   // before the state tiles
@@ -1166,25 +1218,18 @@ __global__ __launch_bounds__(256, (MODE == READY_MODE_PREPARE && RR <= 16) ? 3 :
   if constexpr (has_s) s_phase<RR, multi>(a, home_g, smem, s_acc, s_tk);
 
   if constexpr (zao) {
-    // before the first A item: the arrival flags of the XCDs (lanes 0-7) and
-    // ticket groups (lanes 8..), read in the trip of the first A claim
-    constexpr int NF = has_s ? 8 + READY_TICKET_GROUPS : 8;
-    auto flag = [&](int l) { return l < 8 ? ctr(a.arr_x, l) : ctr(a.arr_g, l - 8); };
+    // before the first A item: the arrival flags of the XCDs, read in the
+    // trip of the first A claim
+    auto flag = [&](int l) { return ctr(a.arr_x, l); };
     uint32_t first;
-    const uint64_t orph = arrival_check(ctr(a.aq, xcc), NF, flag, &first, s_tk);
-    const uint32_t orph_x = (uint32_t)(orph & 0xffu);
-    if (orph != 0) {
-      // orphans (a partly resident grid only): their Z items and tiles
-      for (uint64_t m = orph; m != 0; m &= m - 1) {
-        const int k = __ffsll((unsigned long long)m) - 1;
-        if (k < 8) {
-          for (uint32_t i; (i = claim_one(a.zq, k, z_size(k), s_tk)) != NO_ITEM;) z_run<BMZ, NST>(a, k, i, smem);
-        } else if constexpr (has_s) {
-          const int q = k - 8;
-          for (uint32_t i; (i = claim_one(a.tk, q, group_tiles(a, q), s_tk)) != NO_ITEM;)
-            s_single<RR, multi>(a, q + READY_TICKET_GROUPS * (int)i, smem, s_acc, s_tk);
-        }
-      }
+    const uint32_t orph_x = (uint32_t)arrival_check(ctr(a.aq, xcc), 8, flag, &first, s_tk);
+    // orphan XCDs (a partly resident grid only): their Z items and tiles
+    for (uint32_t m = orph_x; m != 0; m &= m - 1) {
+      const int x = __ffs(m) - 1;
+      for (uint32_t i; (i = claim_one(a.zq, x, z_size(x), s_tk)) != NO_ITEM;) z_run<BMZ, NST>(a, x, i, smem);
+      if constexpr (has_s)
+        for (uint32_t i; (i = claim_one(a.tk, x, group_tiles(a, x), s_tk)) != NO_ITEM;)
+          s_single<RR, multi>(a, x + READY_TICKET_GROUPS * (int)i, smem, s_acc, s_tk);
     }
     // A items in row order from the home queue, then from orphan XCDs' (A
     // item j in queue j % 8); an item is claimed only when the previous one
@@ -1219,7 +1264,7 @@ __global__ __launch_bounds__(256, (MODE == READY_MODE_PREPARE && RR <= 16) ? 3 :
   } else {
     // a prepare launch, before finishing: tiles of ticket groups no
     // workgroup has arrived in
-    auto flag = [&](int l) { return ctr(a.arr_g, l); };
+    auto flag = [&](int l) { return ctr(a.arr_x, l); };
     uint32_t none;
     const uint64_t orph = arrival_check(nullptr, READY_TICKET_GROUPS, flag, &none, s_tk);
     for (uint64_t m = orph; m != 0; m &= m - 1) {

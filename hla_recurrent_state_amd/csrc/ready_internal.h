@@ -81,7 +81,7 @@ struct FastArgs {
   // group and overall, then the Z items done per tile of z, the finished
   // tiles of z per row block, the S items done per 16 rows, the A items done
   // per row tile of out, the state-tile tickets, the Z-, A- and O-item
-  // claim counters, the arrival flags per XCD and per ticket group.
+  // claim counters, the arrival flags per XCD.
   // The last workgroup to finish clears all of them except the magic.
   uint32_t* counters;
   int n_counters;                  // words
@@ -93,10 +93,9 @@ struct FastArgs {
   uint32_t* sdone;                 // [cdiv(R, 16)]
   uint32_t* adone;                 // [cdiv(R, BMO)]
   uint32_t* tk;                    // [READY_TICKET_GROUPS]: state-tile tickets drawn per group (tiles t with
-                                   // t % READY_TICKET_GROUPS == group)
+                                   // t % READY_TICKET_GROUPS == group; group x is drawn on XCD x)
   uint32_t* zq;                    // [8]: Z items claimed per XCD queue
   uint32_t* arr_x;                 // [8]: a workgroup of the launch has run on XCD x
-  uint32_t* arr_g;                 // [READY_TICKET_GROUPS]: a workgroup of the launch has ticket group q as home
   uint32_t* aq;                    // [8]: A items claimed per XCD queue
   uint32_t* oq;                    // [8]: O items claimed per XCD queue
   int n_z, n_s, n_a, n_o;          // work items per kind
@@ -133,7 +132,7 @@ struct FastArgs {
 #define READY_ZCHUNK_SMALL 384
 #define READY_ZCHUNK_LARGE 640
 #define READY_OCOLS 128
-#define READY_TICKET_GROUPS 32    // state-tile ticket counters
+#define READY_TICKET_GROUPS 8     // state-tile ticket counters, one per XCD
 #define READY_ACC_LDS 1024        // accept indices staged in LDS
 
 // Step 1 alone: one workgroup per (sequence, pair) tile
