@@ -18,8 +18,13 @@ b1_latency single-block latency at the paper shape (B = 1), eager and
            graph-replayed, cache-cold and warm, next to an unfused PyTorch
            eager composition of the same five steps.
 cpu_baseline  the float64 oracle on a bounded sample of the batched
-           workload, on the host (1 thread), with a parity check of the GPU
-           outputs on that sample.
+           workload, on the host with its BLAS on every core this process may
+           use (`cores` is the thread count the BLAS reports), with a parity
+           check of the GPU outputs on that sample; plus a one-thread run of
+           the paper shape (B = 1).
+operators  the pages report the gather and the reader as two operators:
+           the gather alone (readyGather) and the whole call, cold, at the
+           paper and wide shapes, and their difference.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
@@ -402,23 +407,26 @@ def run_b1(args, hip, torch, R, synth, seed=0):
 def run_gather(args, hip, torch, R, synth, seed=0):
     """readyGather (step 1 alone: the committed states into the caller's
     buffer) at the paper shape (B = 1, 32 pairs, bf16: 1 MiB read + 1 MiB
-    written) and the batched shape (B = 64: 64 MiB + 64 MiB), cold (after a
-    512 MB update) and back to back, with the states drawn on the device.  The
-    pages time the same operator on their hardware as context."""
+    written), the wide shape (B = 1, 96 pairs, fp32: 6 MiB + 6 MiB) and the
+    batched shape (B = 64: 64 MiB + 64 MiB), cold (after a 512 MB update) and
+    back to back, with the states drawn on the device.  The pages time the
+    same operator on their hardware as context."""
+    from synth.device import torch_dtype
     device = torch.device("cuda:0")
     stream = torch.cuda.current_stream(device).cuda_stream
     lib = R.load()
     flush = torch.empty(128 * 1024 * 1024, dtype=torch.float32, device=device)
     K = args.config_steps
     res = {}
-    for name in ("paper", "batched"):
+    for name in ("paper", "wide", "batched"):
         cfg = synth.make_shape(name)
-        states = torch.empty((cfg.B, cfg.P, cfg.L_tot, cfg.H, 128, 128), dtype=torch.bfloat16, device=device)
+        sdt = torch_dtype(cfg.state_dtype)
+        states = torch.empty((cfg.B, cfg.P, cfg.L_tot, cfg.H, 128, 128), dtype=sdt, device=device)
         _fill_states_random(states, seed, torch)
         g = torch.Generator(device=device)
         g.manual_seed(seed)
         acc = torch.randint(0, cfg.P, (cfg.B,), generator=g, device=device, dtype=torch.int32)
-        gathered = torch.empty((cfg.B, cfg.M, 128, 128), dtype=torch.bfloat16, device=device)
+        gathered = torch.empty((cfg.B, cfg.M, 128, 128), dtype=sdt, device=device)
         status = torch.zeros(1, dtype=torch.int32, device=device)
         reader = R.StateReader(shape_of(R, cfg), cfg.slots)
         st = states.stride()
@@ -455,8 +463,8 @@ def run_gather(args, hip, torch, R, synth, seed=0):
         hip.destroy(b)
         if int(status.item()) != 0:
             raise RuntimeError("device status set during the gather run")
-        nbytes = 2 * cfg.B * cfg.M * 128 * 128 * 2
-        res[name] = {"B": cfg.B, "M": cfg.M, "bytes_read_plus_written": nbytes,
+        nbytes = 2 * cfg.B * cfg.M * 128 * 128 * esize(cfg.state_dtype)
+        res[name] = {"B": cfg.B, "M": cfg.M, "state_dtype": cfg.state_dtype, "bytes_read_plus_written": nbytes,
                      "cold_us": {"p10": round(pct(cold, 10), 2), "p50": round(pct(cold, 50), 2),
                                  "p90": round(pct(cold, 90), 2)},
                      "warm_mean_us": round(warm, 2),
@@ -484,6 +492,16 @@ def _fill_states_random(buf, seed, torch):
     for i in range(0, flat.numel(), step):
         blk = flat[i:i + step]
         blk.copy_(torch.randn(blk.numel(), generator=g, device=buf.device, dtype=torch.float32) / 128.0)
+
+
+def footprint(cfg):
+    """Element counts of the state-access footprint: the committed states,
+    M d_v d_k, which do not grow with the prefix, against the key-value cache
+    a softmax-attention reader would read at the same prefix length t,
+    M t (d_k + d_v) (arXiv text, section 3.2 "State-access footprint")."""
+    st = cfg.M * cfg.d_v * cfg.d_k
+    kv = cfg.M * cfg.t * (cfg.d_k + cfg.d_v)
+    return {"t": cfg.t, "state_elements": st, "kv_cache_elements": kv, "ratio": "1 : %g" % (kv / st)}
 
 
 def run_config(name, args, hip, torch, R, synth, seed=0, cfg=None, random_states=None, copy_ref=True):
@@ -600,6 +618,7 @@ def run_config(name, args, hip, torch, R, synth, seed=0, cfg=None, random_states
         "cold_frac_of_hbm_peak": round(alg / (p50 * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
         "warm_frac_of_hbm_peak": round(alg / (warm * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
         "stage_median_us": stages,
+        "state_vs_kv": footprint(cfg),
     }
     if copy_ref:
         res["same_bytes_copy"] = {"cold_p50_us": round(pct(copy_cold, 50), 2), "warm_mean_us": round(copy_warm, 2),
@@ -839,41 +858,67 @@ def run_producer(args, hip, torch, R, synth, seed=0):
 
 # ---------------------------------------------------------------- CPU oracle baseline
 
-def cpu_baseline(bat, budget_s):
-    """Time the float64 oracle on a bounded sample of the batched workload and
-    check the GPU outputs of the same sequences against it."""
+def _blas_threads():
+    """Threads the BLAS under numpy will use, as it reports them (None if
+    threadpoolctl cannot tell)."""
+    try:
+        from threadpoolctl import threadpool_info
+    except ImportError:
+        return None
+    n = [i.get("num_threads") for i in threadpool_info() if i.get("user_api") == "blas"]
+    return max(n) if n else None
+
+
+def _time_oracle(inp, nseq_max, budget_s):
+    """Mean time of the oracle over the first nseq sequences, nseq sized so a
+    pass takes about budget_s, repeated until budget_s is spent."""
+    from tests.gpu_util import oracle_reference
+    t0 = time.perf_counter()
+    oracle_reference(inp, [0])
+    one = time.perf_counter() - t0
+    nseq = int(max(1, min(nseq_max, budget_s / max(one, 1e-3))))
+    seqs = list(range(nseq))
+    t0 = time.perf_counter()
+    ref = oracle_reference(inp, seqs)
+    el = time.perf_counter() - t0
+    reps = 1
+    while el < budget_s and reps < 1000:
+        t0 = time.perf_counter()
+        oracle_reference(inp, seqs)
+        el += time.perf_counter() - t0
+        reps += 1
+    return ref, nseq, reps, el / reps
+
+
+def cpu_baseline(bat, budget_s, synth):
+    """Time the float64 oracle on a bounded sample of the batched workload,
+    with the BLAS on every core this process may use, and check the GPU
+    outputs of the same sequences against it; then one thread on the paper
+    shape (B = 1)."""
+    import contextlib
     try:
         from threadpoolctl import threadpool_limits
     except ImportError:
         threadpool_limits = None
-    from tests.gpu_util import compare, oracle_reference
+    from tests.gpu_util import compare
     from synth.device import to_numpy_bits
-    import contextlib
     inp, cfg = bat["inp"], bat["cfg"]
-    ctx = threadpool_limits(limits=1) if threadpool_limits else contextlib.nullcontext()
+    avail = len(os.sched_getaffinity(0))
+    ctx = threadpool_limits(limits=avail) if threadpool_limits else contextlib.nullcontext()
     with ctx:
-        t0 = time.perf_counter()
-        oracle_reference(inp, [0])
-        one = time.perf_counter() - t0
-        nseq = int(max(1, min(cfg.B, budget_s / max(one, 1e-3))))
-        seqs = list(range(nseq))
-        t0 = time.perf_counter()
-        ref = oracle_reference(inp, seqs)
-        el = time.perf_counter() - t0
-        # when the sample is short, repeat it to fill the budget (the mean is reported)
-        reps = 1
-        while el < budget_s and reps < 1000:
-            t0 = time.perf_counter()
-            oracle_reference(inp, seqs)
-            el += time.perf_counter() - t0
-            reps += 1
-        el /= reps
+        threads = _blas_threads()
+        ref, nseq, reps, el = _time_oracle(inp, cfg.B, budget_s)
     committed = 2 * nseq * cfg.M * 128 * 128 * esize(cfg.state_dtype)
+    # one thread, paper shape
+    pinp = synth.make("paper", seed=0)
+    ctx1 = threadpool_limits(limits=1) if threadpool_limits else contextlib.nullcontext()
+    with ctx1:
+        threads1 = _blas_threads()
+        _, _, reps1, el1 = _time_oracle(pinp, 1, budget_s / 2)
     # parity of the GPU outputs (set 0) on the sampled sequences
     s0 = bat["set0"]
     outs = s0.keep[1]
     import torch
-    import hla_recurrent_state_amd as R
     dev = outs["out"].device
     extra = {"logrms": torch.empty((cfg.B, cfg.M), dtype=torch.float32, device=dev),
              "delta": torch.empty((cfg.B, cfg.n, cfg.d), dtype=torch.float32, device=dev),
@@ -896,11 +941,15 @@ def cpu_baseline(bat, budget_s):
                 break
     except OSError:
         pass
-    base = {"value": round(committed / el / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "cpu_model": model, "host_cores_available": len(os.sched_getaffinity(0)),
+    base = {"value": round(committed / el / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "cpu_model": model, "host_cores_available": avail,
             "sample": "float64 numpy oracle, steps 1-5, on %d of the %d sequences of the batched "
-                      "workload, %d timed passes of %.2f s each (committed-state bytes of the sample / "
-                      "mean time)" % (nseq, cfg.B, reps, el)}
+                      "workload, BLAS limited to the %d cores of this process's affinity (it reports %s "
+                      "threads), %d timed passes of %.2f s each (committed-state bytes of the sample / "
+                      "mean time)" % (nseq, cfg.B, avail, threads, reps, el),
+            "paper_one_thread": {"us_per_block": round(1e6 * el1, 1), "cores": threads1,
+                                 "sample": "the paper shape (B = 1, 32 pairs), one thread, %d timed passes"
+                                           % reps1}}
     return base, rep
 
 
@@ -912,7 +961,8 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--b1-steps", type=int, default=200)
-    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work")
+    ap.add_argument("--cpu-budget", type=float, default=10.0,
+                    help="seconds of oracle work on the batched sample (half that again at the paper shape)")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-b1", action="store_true")
     ap.add_argument("--configs", default="tiny,wide,rank",
@@ -1038,13 +1088,28 @@ def main():
         out["configs"] = {}
         for name in args.configs.split(","):
             out["configs"][name] = run_config(name, args, hip, torch, R, synth)
+    # the pages' two operators (arXiv text, section 3.2, Fig. 4): the gather
+    # alone and the reader; the fused call has no separate gather, so the
+    # reader's own share is reported as the difference of the two cold medians
+    if "gather_only" in out:
+        ops = {}
+        whole = {}
+        if "b1_latency" in out:
+            whole["paper"] = out["b1_latency"]["fused_eager_cold"]["p50"]
+        if "configs" in out and "wide" in out["configs"]:
+            whole["wide"] = out["configs"]["wide"]["cold_us"]["p50"]
+        for name, w in whole.items():
+            g = out["gather_only"][name]["cold_us"]["p50"]
+            ops[name] = {"gather_cold_p50_us": g, "reader_call_cold_p50_us": w,
+                         "reader_minus_gather_cold_p50_us": round(w - g, 2)}
+        out["operators"] = ops
     if not args.no_sweeps:
         out["sweeps"] = run_sweeps(args, hip, torch, R, synth)
         out["producer"] = run_producer(args, hip, torch, R, synth)
         out["multi_reader"] = run_multi(args, hip, torch, R, synth)
     ok = True
     if not args.no_cpu:
-        base, rep = cpu_baseline(bat, args.cpu_budget)
+        base, rep = cpu_baseline(bat, args.cpu_budget, synth)
         out["cpu_baseline"] = base
         out["parity"] = {k: rep[k] for k in ("gather_bitexact", "dh_rel", "logrms_err", "feat_rel", "ok")}
         ok = rep["ok"]
