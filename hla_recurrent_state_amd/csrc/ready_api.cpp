@@ -93,7 +93,7 @@ extern "C" {
 int32_t readyVersion(void) { return READY_VERSION; }
 
 const char* readyStatusString(readyStatus st) {
-  switch (st) {
+  switch (static_cast<int>(st)) {
     case READY_OK: return "READY_OK";
     case READY_ERR_NULL_POINTER: return "READY_ERR_NULL_POINTER";
     case READY_ERR_BAD_SHAPE: return "READY_ERR_BAD_SHAPE";

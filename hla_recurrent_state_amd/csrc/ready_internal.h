@@ -259,5 +259,23 @@ READY_HIDDEN readyStatus ready_run_reader(const readyPlan* plan, const readyStat
 // Scratch bytes a plan's calls use: the arrays, then the counters
 READY_HIDDEN void ready_plan_scratch_needs(const readyPlan* plan, size_t* data_bytes, size_t* ctr_bytes);
 }
-READY_HIDDEN size_t ready_reader_lds(int r, int F, int Nz, int small);
+// dynamic LDS bytes of a k_reader launch: the largest of its item kinds' areas
+inline size_t ready_reader_lds(int r, int F, int Nz, int small) {
+  // the O item's area is sized for the larger of the two large-row forms
+  const int BMZ = small ? 16 : (READY_BMZ_APPLY > READY_BMZ_LARGE ? READY_BMZ_APPLY : READY_BMZ_LARGE);
+  const int BMO = small ? 16 : (READY_BMO_APPLY > READY_BMO_LARGE ? READY_BMO_APPLY : READY_BMO_LARGE);
+  const int NB = (r + 15) / 16;
+  const size_t z_bytes = (size_t)(BMZ + 64) * 256 + 16;
+  const size_t s_bytes = (size_t)READY_TILE_ELEMS * 2 + (size_t)r * (READY_TILE + 8) * 2 + (size_t)READY_TILE * r * 2 +
+                         4 * (4 * NB * r * 16 + 4);
+  const int Fs = ((F + 31) & ~31) + 8;
+  const size_t a_bytes = (size_t)16 * Nz * 4 + (size_t)16 * Fs * 2 + 4 * 16 + 16;
+  const size_t sa = (size_t)BMO * (256 + 8) * 2, so = (size_t)BMO * (READY_OCOLS + 4) * 4;
+  const size_t o_bytes = (sa > so ? sa : so) + 16;
+  size_t m = z_bytes;
+  if (s_bytes > m) m = s_bytes;
+  if (a_bytes > m) m = a_bytes;
+  if (o_bytes > m) m = o_bytes;
+  return (m + 15) & ~(size_t)15;
+}
 READY_HIDDEN int ready_reader_per_cu(int r, int small, size_t lds, int mode);

@@ -66,8 +66,12 @@ typedef enum readyStatus {
                                        (readyPrepSize, readyStatePrepare, readyStateApply), or
                                        readyStateReaderStatic's first call on a device was made
                                        while its stream was capturing */
-  READY_ERR_STATIC_SCRATCH_TOO_SMALL = 14 /* readyStateReaderStatic: the plan needs more scratch than
+  READY_ERR_STATIC_SCRATCH_TOO_SMALL = 14, /* readyStateReaderStatic: the plan needs more scratch than
                                        the library's static per-device array holds */
+  /* range markers, not status codes: they make every int32_t a value of the
+     type, so that readyStatusString may be passed any code a C caller holds */
+  READY_STATUS_RANGE_MIN = -2147483647 - 1,
+  READY_STATUS_RANGE_MAX = 2147483647
 } readyStatus;
 
 typedef enum readyDtype { READY_F32 = 0, READY_BF16 = 1 } readyDtype;
