@@ -43,7 +43,7 @@ struct readyPlan {
   int fast;
   int small;     // fast path: at most 16 rows (16-row tiles; 64 otherwise)
   int n_z, n_s, n_a, n_o, n_counters;
-  int c_zcnt, c_zdone, c_sdone, c_adone, c_tk, c_zq, c_aq, c_oq, c_arx;  // first counter slot of each group
+  int c_zcnt, c_zdone, c_sdone, c_adone, c_tk, c_aq, c_oq, c_arx;  // first counter slot of each group
   size_t lds;
   GemmPlan gz, g1, g2;
   size_t off_zpart, off_hss, off_f, off_a, off_g1p, off_flags, off_pmat, off_ell, off_ctr, ws_bytes;
@@ -143,11 +143,12 @@ readyStatus readyPlanCreate(const readyShape* shape, const int32_t* layer_ids, r
   bool fits = allbf && s.r <= 32 && p->F % 8 == 0 && p->F <= READY_FAST_MAX_F && s.Hm % 8 == 0 &&
                     p->Nz <= READY_FAST_MAX_NZ && small_ws;
   {
-    // per-XCD queue lengths of the Z and O items (the A items are fewer)
+    // per-XCD queue lengths: Z items and state tiles (one queue), O items
+    // (the A items are fewer)
     const int64_t bmz = p->small ? 16 : std::min(READY_BMZ_LARGE, READY_BMZ_APPLY);
     const int64_t bmo = p->small ? 16 : std::min(READY_BMO_LARGE, READY_BMO_APPLY);
     const int64_t rows = std::max(p->R, 1);
-    const int64_t zq = cdiv(fks, 8) * cdiv(rows, bmz) * cdiv(p->Nz, 64);
+    const int64_t zq = cdiv(fks, 8) * cdiv(rows, bmz) * cdiv(p->Nz, 64) + cdiv((int64_t)s.B * p->M, 8);
     const int64_t oq = cdiv(rows, bmo) * cdiv(cdiv(s.d, READY_OCOLS), 8);
     if (zq >= (1 << 24) || oq >= (1 << 24)) fits = false;
   }
@@ -166,8 +167,7 @@ readyStatus readyPlanCreate(const readyShape* shape, const int32_t* layer_ids, r
     p->gz.ksplit = (int)fks;
     p->gz.kchunk = (int)zchunk;
     p->n_z = (int)(nrbz * ncbz * fks);
-    // items are claimed as (queue << 24) | index: each per-XCD queue holds
-    // fewer than 2^24 (checked below, with the other limits of the path)
+    // each per-XCD queue holds fewer than 2^24 items (checked above)
     p->n_s = s.B * p->M;
     p->n_a = (int)(nrb16 * cdiv(s.Hm, 64));
     p->n_o = (int)(nrbo * cdiv(s.d, READY_OCOLS));
@@ -178,8 +178,7 @@ readyStatus readyPlanCreate(const readyShape* shape, const int32_t* layer_ids, r
     p->c_sdone = (int)(p->c_zdone + nrbz);
     p->c_adone = (int)(p->c_sdone + nrb16);
     p->c_tk = (int)(p->c_adone + nrbo);
-    p->c_zq = p->c_tk + READY_TICKET_GROUPS;
-    p->c_aq = p->c_zq + 8;
+    p->c_aq = p->c_tk + READY_TICKET_GROUPS;
     p->c_oq = p->c_aq + 8;
     p->c_arx = p->c_oq + 8;
     p->n_counters = (int)(READY_CTR_STRIDE * (p->c_arx + 8));
@@ -316,7 +315,6 @@ void fast_common(const readyPlan* plan, const WsView& view, FastArgs& a) {
   a.sdone = ctr + READY_CTR_STRIDE * plan->c_sdone;
   a.adone = ctr + READY_CTR_STRIDE * plan->c_adone;
   a.tk = ctr + READY_CTR_STRIDE * plan->c_tk;
-  a.zq = ctr + READY_CTR_STRIDE * plan->c_zq;
   a.arr_x = ctr + READY_CTR_STRIDE * plan->c_arx;
   a.aq = ctr + READY_CTR_STRIDE * plan->c_aq;
   a.oq = ctr + READY_CTR_STRIDE * plan->c_oq;

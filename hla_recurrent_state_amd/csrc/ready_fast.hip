@@ -7,7 +7,7 @@
 //      over one K chunk, plus the sums of squares of h for RMSNorm(h_j)
 //      (step 4); the item that completes a tile's last chunk sums the chunks
 //      in chunk order.
-//   S  the state tiles, drawn through ticket counters in sequence order:
+//   S  the state tiles, drawn through ticket positions in sequence order:
 //      fused gather at the accept index into the caller's buffer, mean
 //      square, log-RMS and P = V^T S_bar U^T / sqrt(d_k), an r x r matrix
 //      (steps 1-3; u_j = T q_j / sqrt(d_k) with T = V^T S_bar and
@@ -33,6 +33,10 @@
 // per-XCD queues that the workgroups running on that XCD (hardware XCC id)
 // draw from, so the h and W_q columns of a chunk, and the W2 rows of a
 // column block, are read from HBM once and then served by that XCD's L2.
+// The Z items and the state tiles share one queue per XCD, Z items first:
+// a workgroup's first claim, made in the launch's first trip to memory,
+// hands it either Z items or its first tiles, so no workgroup spends a trip
+// on a claim that finds its kind of item gone.
 //
 // Cross-workgroup data (z partial sums, P, ell, the invalid-sequence flags,
 // a) is written with device-coherent stores (sc1), made complete with a wait
@@ -99,15 +103,25 @@ __device__ __forceinline__ void wait_mem() { asm volatile("s_waitcnt vmcnt(0)" :
 // this point (into a later trip).
 __device__ __forceinline__ void pin(u32x4& v) { asm volatile("" : "+v"(v)); }
 __device__ __forceinline__ void pin(float& v) { asm volatile("" : "+v"(v)); }
-// Loads for a trip of many: always issued, at offset 0 when `live` is false
-// (the caller never uses such a value).  A branch around a load, or a use of
-// the value right after it, makes the compiler wait for the load there and
-// splits the trip.
+// Loads for a trip of many: always issued; when `live` is false the offset
+// lies past the descriptor's record count, so the load returns zero and
+// moves no data.  A branch around a load, or a use of the value right after
+// it, makes the compiler wait for the load there and splits the trip.
+constexpr uint32_t DEAD_OFF = 0x80000000u;  // past 0x7fffffff records, with room for an immediate offset
 __device__ __forceinline__ u32x4 ld_coh16_at(bool live, const void* base, uint32_t byte_off) {
-  return ld_coh16(base, live ? byte_off : 0u);
+  return ld_coh16(base, live ? byte_off : DEAD_OFF);
 }
 __device__ __forceinline__ float ld_coh4_at(bool live, const void* base, uint32_t byte_off) {
-  return ld_coh4(base, live ? byte_off : 0u);
+  return ld_coh4(base, live ? byte_off : DEAD_OFF);
+}
+// The thread index, as a value the compiler cannot match with other reads
+// of it: the work items derive their lane offsets from their own copy, so
+// those are recomputed per item instead of held (and spilled) across the
+// whole kernel.
+__device__ __forceinline__ int item_tid() {
+  int t = (int)threadIdx.x;
+  asm volatile("" : "+v"(t));
+  return t;
 }
 __device__ __forceinline__ uint32_t count_up(uint32_t* c) {
   return __hip_atomic_fetch_add(c, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -220,7 +234,7 @@ __device__ __forceinline__ uint32_t claim_one(uint32_t* qctr, int x, uint32_t si
 template <typename Flag>
 __device__ __forceinline__ uint64_t arrival_check(uint32_t* claim, int n, Flag flag, uint32_t* claimed,
                                                   uint32_t* s_bc) {
-  const int tid = threadIdx.x;
+  const int tid = item_tid();
   if (tid < 64) {
     uint32_t i = NO_ITEM;
     if (tid == 0 && claim != nullptr) i = count_up(claim);
@@ -269,7 +283,7 @@ struct ZStage {
 
 template <int BMZ>
 __device__ __forceinline__ void z_stage_load(const FastArgs& a, int rb, int cb, int k0, int kend, ZStage<BMZ>& S) {
-  const int tid = threadIdx.x;
+  const int tid = item_tid();
   const int kk = k0 + 8 * (tid & 15);
   const bool kv = kk < kend;
   const u32x4 zero = u32x4{0u, 0u, 0u, 0u};
@@ -298,7 +312,7 @@ __device__ __forceinline__ void z_item(const FastArgs& a, int ks, int cb, int rb
   float* red = (float*)smem;                     // [BMZ][LD], after the stages
   int* s_flag = (int*)(smem + (BMZ + 64) * 256);
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = item_tid(), lane = tid & 63, wave = tid >> 6;
   const int lr = lane & 15, lg = lane >> 4;
   const int rbw = (wave % (RBT / WR)) * WR, cbw = (wave / (RBT / WR)) * WC;
   const int kbeg = ks * a.kchunk;
@@ -465,7 +479,7 @@ template <int RR>
 __device__ __forceinline__ void tile_issue(const FastArgs& a, int t, TileRegs<RR>& R, const int* s_acc) {
   constexpr int WCH = RR * 16;
   const int b = t / a.M, m = t - (t / a.M) * a.M;
-  const int tid = threadIdx.x;
+  const int tid = item_tid();
   const int mz = a.shared ? 0 : m;
   R.p = b < READY_ACC_LDS ? s_acc[b] : a.accept_idx[b];
   const u32x4* Ug = (const u32x4*)(a.u + (int64_t)mz * RR * READY_TILE);
@@ -500,7 +514,7 @@ __device__ __forceinline__ void tile_project(const u32x4* sS, const uint16_t* sU
   constexpr int VC = RR / 8;          // 16-byte chunks per V row
   constexpr int LU = READY_TILE + 8;  // padded U row in LDS (bf16)
   constexpr int WS = NB * RR * 16;    // per-wave partials of P
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = item_tid(), lane = tid & 63, wave = tid >> 6;
   const int lrow = lane & 15, lq = lane >> 4;
   f32x4 acc[2][NB];
 #pragma unroll
@@ -570,11 +584,15 @@ __device__ __forceinline__ void tile_project(const u32x4* sS, const uint16_t* sU
 // This tile's own stores are complete after the caller's next such wait.
 template <int RR, bool MULTI>
 __device__ __forceinline__ void tile_process(const FastArgs& a, int t, const TileRegs<RR>& R, unsigned char* smem,
-                                             int announce, uint32_t* s_pub, uint32_t raw, int q, uint32_t nt) {
-  // thread 0: the tile of ticket `raw` of group q (NO_ITEM when the group is
-  // exhausted), published after the first barrier below, so that only wave 0
-  // waits for the ticket's trip
-  auto pub_of = [&]() { return raw < nt ? (uint32_t)(q + READY_TICKET_GROUPS * (int)raw) : NO_ITEM; };
+                                             int announce, uint32_t* s_pub, uint32_t raw, int q, uint32_t zs,
+                                             uint32_t nt) {
+  // thread 0: the tile at position `raw` of queue q (NO_ITEM when that is
+  // past the queue's zs Z items and nt tickets), published after the first
+  // barrier below, so that only wave 0 waits for the claim's trip
+  auto pub_of = [&]() {
+    return (raw != NO_ITEM && raw >= zs && raw - zs < nt) ? (uint32_t)(q + READY_TICKET_GROUPS * (int)(raw - zs))
+                                                          : NO_ITEM;
+  };
   constexpr int NB = (RR + 15) / 16;  // 16-column blocks of U^T
   constexpr int LU = READY_TILE + 8;  // padded U row in LDS (bf16)
   constexpr int WCH = RR * 16;
@@ -586,7 +604,7 @@ __device__ __forceinline__ void tile_process(const FastArgs& a, int t, const Til
   float* s_wsum = s_red + 4 * WS;                        // [4]
 
   const int b = t / a.M, m = t - (t / a.M) * a.M;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = item_tid(), lane = tid & 63, wave = tid >> 6;
   float* P = a.pmat + (int64_t)t * RR * RR;
 
   if (R.p < 0 || R.p >= a.P) {
@@ -677,57 +695,50 @@ __device__ __forceinline__ uint32_t group_tiles(const FastArgs& a, int q) {
   return (uint32_t)((a.n_s - q + READY_TICKET_GROUPS - 1) / READY_TICKET_GROUPS);
 }
 
-// The S items of one workgroup: the tiles of the tickets it draws from group
-// q until the group is exhausted, the first two in one trip: a pair of
-// consecutive tickets when the launch has at least two tiles per workgroup,
-// else two tickets drawn one by one (so that scarce tiles spread over more
-// workgroups).  Two tiles are
-// in flight while one is processed, and the ticket of the one after them is
-// in flight too: it is requested before the loads of the tile it follows, so
-// that waiting for it never waits for tile data.  The tile processed two
-// turns back is announced while a tile is processed; the last two at the
-// end.
+// The S items of one workgroup: the tiles at the positions it holds and
+// claims in queue q after the queue's zs Z items (ticket i of group q is
+// position zs + i).  p0 and p1 are positions the workgroup already holds
+// (NO_ITEM for none); it claims one position at a time after them.  Two
+// tiles are in flight while one is processed, and the position after them
+// is claimed too: it is requested before the loads of the tile it follows,
+// so that waiting for it never waits for tile data.  A workgroup that starts
+// with one tile keeps one in flight.  The tile processed two turns back is
+// announced while a tile is processed; the last two at the end.
 template <int RR, bool MULTI>
-__device__ __forceinline__ void s_phase(const FastArgs& a, int q, unsigned char* smem, const int* s_acc,
-                                        uint32_t* s_tk) {
+__device__ __forceinline__ void s_phase(const FastArgs& a, int q, uint32_t zs, uint32_t p0, uint32_t p1,
+                                        unsigned char* smem, const int* s_acc, uint32_t* s_tk) {
   constexpr int NQ = READY_TICKET_GROUPS;
-  const int tid = threadIdx.x;
+  const int tid = item_tid();
   const uint32_t nt = group_tiles(a, q);
   uint32_t* tk = ctr(a.tk, q);
-  const bool pair = a.n_s >= 2 * (int)gridDim.x;
-  if (tid == 0) {
-    if (pair) {
-      const uint32_t i = __hip_atomic_fetch_add(tk, 2u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      s_tk[0] = i;
-      s_tk[1] = i + 1;
-    } else {
-      const uint32_t i = count_up(tk), j = count_up(tk);
-      s_tk[0] = i;
-      s_tk[1] = j;
-    }
-  }
-  __syncthreads();
-  const uint32_t i0 = s_tk[0], i1 = s_tk[1];
-  __syncthreads();
-  int t0 = i0 < nt ? q + NQ * (int)i0 : -1;
-  int t1 = (t0 >= 0 && i1 < nt) ? q + NQ * (int)i1 : -1;
-  uint32_t pend = NO_ITEM;  // thread 0: the ticket after t1
-  if (tid == 0 && t1 >= 0) pend = count_up(tk);
+  auto tile_at = [&](uint32_t pos) {
+    return (pos != NO_ITEM && pos >= zs && pos - zs < nt) ? q + NQ * (int)(pos - zs) : -1;
+  };
+  int t0 = tile_at(p0);
+  int t1 = t0 >= 0 ? tile_at(p1) : -1;
+  uint32_t pend = NO_ITEM;  // thread 0: the position after the newest tile
+  if (tid == 0 && t0 >= 0) pend = count_up(tk);
   TileRegs<RR> r0, r1;
   if (t0 >= 0) tile_issue<RR>(a, t0, r0, s_acc);
   if (t1 >= 0) tile_issue<RR>(a, t1, r1, s_acc);
   int h1 = -1, h2 = -1;  // tiles processed one and two turns back
   while (t0 >= 0) {
-    tile_process<RR, MULTI>(a, t0, r0, smem, h2, s_tk, pend, q, nt);
+    tile_process<RR, MULTI>(a, t0, r0, smem, h2, s_tk, pend, q, zs, nt);
     const int t2 = (int)*s_tk;
     h2 = h1;
     h1 = t0;
-    t0 = t1;
-    r0 = r1;
-    t1 = t0 >= 0 ? t2 : -1;
     pend = NO_ITEM;
-    if (tid == 0 && t1 >= 0) pend = count_up(tk);
-    if (t1 >= 0) tile_issue<RR>(a, t1, r1, s_acc);
+    if (t1 >= 0) {
+      t0 = t1;
+      r0 = r1;
+      t1 = t2;
+      if (tid == 0 && t1 >= 0) pend = count_up(tk);
+      if (t1 >= 0) tile_issue<RR>(a, t1, r1, s_acc);
+    } else {
+      t0 = t2;
+      if (tid == 0 && t0 >= 0) pend = count_up(tk);
+      if (t0 >= 0) tile_issue<RR>(a, t0, r0, s_acc);
+    }
   }
   wait_mem();
   __syncthreads();
@@ -751,7 +762,7 @@ template <int RR, int BMZ, int BMO>
 __device__ __forceinline__ void mlp1_item(const FastArgs& a, int item, unsigned char* smem) {
   const int ncb = cdiv_d(a.Hm, 64);
   const int rb = item / ncb, cb = item - (item / ncb) * ncb;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = item_tid(), lane = tid & 63, wave = tid >> 6;
   const int lr = lane & 15, lg = lane >> 4;
   const int row0 = rb * 16;
   const int rows = min(16, a.R - row0);
@@ -983,7 +994,7 @@ __device__ __forceinline__ void mlp2_item(const FastArgs& a, int rb, int cb, uns
   float* sO = (float*)smem;         // [BM][LO], after the K passes
   int* s_flag = (int*)(smem + (SA > SO ? SA : SO));
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = item_tid(), lane = tid & 63, wave = tid >> 6;
   const int lr = lane & 15, lg = lane >> 4;
   const int row0 = rb * BM, col0 = cb * OC;
   const int rows = min(BM, a.R - row0);
@@ -1141,7 +1152,7 @@ __device__ __forceinline__ void s_single(const FastArgs& a, int t, unsigned char
                                          uint32_t* s_tk) {
   TileRegs<RR> r;
   tile_issue<RR>(a, t, r, s_acc);
-  tile_process<RR, MULTI>(a, t, r, smem, -1, s_tk, NO_ITEM, 0, 0u);
+  tile_process<RR, MULTI>(a, t, r, smem, -1, s_tk, NO_ITEM, 0, 0u, 0u);
   wait_mem();
   __syncthreads();
   if (threadIdx.x == 0) tile_count(a, t);
@@ -1149,13 +1160,13 @@ __device__ __forceinline__ void s_single(const FastArgs& a, int t, unsigned char
 }
 
 // Two workgroups of four waves per CU: at most 256 registers per lane.  A
-// workgroup takes Z items from its XCD's queue, then state tiles from its
-// ticket group, then A items, then O items, each kind until its home queue
-// is exhausted (items of queue x share operands: K chunks ks % 8 == x, A
-// items j % 8 == x, column blocks cb % 8 == x), with the orphan checks
-// described with claim_one before its first A item, its first O item and its
-// end.  The first Z claim and the arrival marks ride on the launch's first
-// trip to memory.
+// workgroup takes positions of its XCD's queue (Z items, then the tickets of
+// tile group x) until the queue is exhausted, then A items, then O items,
+// each kind until its home queue is exhausted (items of queue x share
+// operands: K chunks ks % 8 == x, A items j % 8 == x, column blocks
+// cb % 8 == x), with the orphan checks described with claim_one before its
+// first A item, its first O item and its end.  The first claim and the
+// arrival marks ride on the launch's first trip to memory.
 template <int RR, int SMALL, int MODE>
 __global__ __launch_bounds__(256, (MODE == READY_MODE_PREPARE && RR <= 16) ? 3 : 2) void k_reader(FastArgs a) {
   constexpr int BMZ = SMALL ? 16 : (MODE == READY_MODE_APPLY ? READY_BMZ_APPLY : READY_BMZ_LARGE);
@@ -1170,12 +1181,16 @@ __global__ __launch_bounds__(256, (MODE == READY_MODE_PREPARE && RR <= 16) ? 3 :
   __shared__ int s_last;
   __shared__ int s_acc[READY_ACC_LDS];
   __shared__ uint32_t s_tk[3];
-  const int tid = threadIdx.x;
+  const int tid = item_tid();
   const int g = blockIdx.x, G = gridDim.x;
-  const int xcc = hw_xcc(), home_g = xcc;  // ticket group x is drawn on XCD x
-  uint32_t zfirst = NO_ITEM;
+  const int xcc = hw_xcc();  // the queue of XCD x holds its Z items, then tile group x
+  // claims take two positions at a time when the launch has at least two
+  // state tiles per workgroup (two tiles in flight from the first trip on),
+  // else one, so that scarce tiles spread over more workgroups
+  const uint32_t step = a.n_s >= 2 * G ? 2u : 1u;
+  uint32_t first = NO_ITEM;
   if (tid == 0) {
-    if constexpr (zao) zfirst = count_up(ctr(a.zq, xcc));
+    first = __hip_atomic_fetch_add(ctr(a.tk, xcc), step, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     st_coh_u32(ctr(a.arr_x, xcc), 1u);
   }
   // the accept indices are requested with the magic word, and staged in LDS
@@ -1197,25 +1212,47 @@ __global__ __launch_bounds__(256, (MODE == READY_MODE_PREPARE && RR <= 16) ? 3 :
   // queue sizes
   const int ztiles = cdiv_d(a.R, BMZ) * cdiv_d(a.Nz, 64);
   const int ncb = cdiv_d(a.d, READY_OCOLS), nrbo = cdiv_d(a.R, BMO);
-  auto z_size = [&](int x) { return (uint32_t)(((a.ksplit - x + 7) >> 3) * ztiles); };
+  auto z_size = [&](int x) { return zao ? (uint32_t)(((a.ksplit - x + 7) >> 3) * ztiles) : 0u; };
   auto a_size = [&](int x) { return (uint32_t)((a.n_a - x + 7) >> 3); };
   auto o_size = [&](int x) { return (uint32_t)(nrbo * ((ncb - x + 7) >> 3)); };
 
+  // positions [p, pe) of the home queue are this workgroup's: Z items are
+  // run in order (claiming again when they run out), the first tile
+  // positions go to the S phase
+  if (tid == 0) s_tk[0] = first;
+  __syncthreads();
+  uint32_t p = s_tk[0], pe = p + step;
+  __syncthreads();
+  const uint32_t zs = z_size(xcc);
   if constexpr (zao) {
-    if (tid == 0) s_tk[0] = zfirst;
-    __syncthreads();
-    uint32_t i = s_tk[0];
-    __syncthreads();
-    const uint32_t zs = z_size(xcc);
-    while (i < zs) {
-      z_run<BMZ, NST>(a, xcc, i, smem);
-      i = claim_one(a.zq, xcc, zs, s_tk);
+    for (;;) {
+      if (p >= pe) {
+        if (tid == 0) s_tk[0] = __hip_atomic_fetch_add(ctr(a.tk, xcc), step, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __syncthreads();
+        p = s_tk[0];
+        __syncthreads();
+        pe = p + step;
+      }
+      if (p >= zs) break;
+      z_run<BMZ, NST>(a, xcc, p, smem);
+      ++p;
     }
   }
 #pragma unroll
   for (int k = 0; k < APT; ++k) s_acc[tid + 256 * k] = accv[k];
   __syncthreads();
-  if constexpr (has_s) s_phase<RR, multi>(a, home_g, smem, s_acc, s_tk);
+  if constexpr (has_s) {
+    uint32_t p1 = p + 1 < pe ? p + 1 : NO_ITEM;
+    if (step == 2u && p1 == NO_ITEM && p >= zs && p - zs < group_tiles(a, xcc)) {
+      // the last Z item of a pair of positions was followed by one tile:
+      // claim a second, so that two tiles are in flight from the start
+      if (tid == 0) s_tk[0] = count_up(ctr(a.tk, xcc));
+      __syncthreads();
+      p1 = s_tk[0];
+      __syncthreads();
+    }
+    s_phase<RR, multi>(a, xcc, zs, p, p1, smem, s_acc, s_tk);
+  }
 
   if constexpr (zao) {
     // before the first A item: the arrival flags of the XCDs, read in the
@@ -1226,10 +1263,14 @@ __global__ __launch_bounds__(256, (MODE == READY_MODE_PREPARE && RR <= 16) ? 3 :
     // orphan XCDs (a partly resident grid only): their Z items and tiles
     for (uint32_t m = orph_x; m != 0; m &= m - 1) {
       const int x = __ffs(m) - 1;
-      for (uint32_t i; (i = claim_one(a.zq, x, z_size(x), s_tk)) != NO_ITEM;) z_run<BMZ, NST>(a, x, i, smem);
-      if constexpr (has_s)
-        for (uint32_t i; (i = claim_one(a.tk, x, group_tiles(a, x), s_tk)) != NO_ITEM;)
-          s_single<RR, multi>(a, x + READY_TICKET_GROUPS * (int)i, smem, s_acc, s_tk);
+      const uint32_t zsx = z_size(x), qx = zsx + (has_s ? group_tiles(a, x) : 0u);
+      for (uint32_t i; (i = claim_one(a.tk, x, qx, s_tk)) != NO_ITEM;) {
+        if (i < zsx) {
+          z_run<BMZ, NST>(a, x, i, smem);
+        } else if constexpr (has_s) {
+          s_single<RR, multi>(a, x + READY_TICKET_GROUPS * (int)(i - zsx), smem, s_acc, s_tk);
+        }
+      }
     }
     // A items in row order from the home queue, then from orphan XCDs' (A
     // item j in queue j % 8); an item is claimed only when the previous one

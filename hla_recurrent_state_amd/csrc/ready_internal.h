@@ -92,9 +92,9 @@ struct FastArgs {
   uint32_t* zdone;                 // [cdiv(R, BMZ)]: tiles of zfin complete per row block
   uint32_t* sdone;                 // [cdiv(R, 16)]
   uint32_t* adone;                 // [cdiv(R, BMO)]
-  uint32_t* tk;                    // [READY_TICKET_GROUPS]: state-tile tickets drawn per group (tiles t with
-                                   // t % READY_TICKET_GROUPS == group; group x is drawn on XCD x)
-  uint32_t* zq;                    // [8]: Z items claimed per XCD queue
+  uint32_t* tk;                    // [READY_TICKET_GROUPS]: positions claimed in the queue of XCD x: its Z
+                                   // items first, then the tickets of state-tile group x (tiles t with
+                                   // t % READY_TICKET_GROUPS == x)
   uint32_t* arr_x;                 // [8]: a workgroup of the launch has run on XCD x
   uint32_t* aq;                    // [8]: A items claimed per XCD queue
   uint32_t* oq;                    // [8]: O items claimed per XCD queue
