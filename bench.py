@@ -353,6 +353,34 @@ def run_b1(args, hip, torch, R, synth, seed=0):
     res["fused_graph_cold_us"] = timed(g.replay, True, K)
     res["fused_graph_warm_us"] = back_to_back(g.replay, K)
 
+    # what a graph launch costs by itself on this runtime: a one-element
+    # kernel, eager and as a one-node graph, cold like the reader
+    tiny = torch.zeros(1, device=device)
+    gt = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(cap):
+        tiny.add_(1.0)
+        torch.cuda.synchronize(device)
+        with torch.cuda.graph(gt, stream=cap):
+            tiny.add_(1.0)
+    torch.cuda.current_stream(device).wait_stream(cap)
+    torch.cuda.synchronize(device)
+    res["tiny_kernel_eager_cold_us"] = timed(lambda: tiny.add_(1.0), True, K)
+    res["tiny_kernel_graph_cold_us"] = timed(gt.replay, True, K)
+    # ten reader calls captured in one graph (as a drafter step would hold
+    # them): the per-call cost with the launch overhead paid once
+    g10 = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(cap):
+        with torch.cuda.graph(g10, stream=cap):
+            for _ in range(10):
+                code = lib.readyStateReader(*gargs)
+                if code != 0:
+                    break
+    if code != 0:
+        raise R.ReadyError(code, "capture of ten calls")
+    torch.cuda.current_stream(device).wait_stream(cap)
+    torch.cuda.synchronize(device)
+    res["fused_graph10_warm_us_per_call"] = [v / 10.0 for v in timed(g10.replay, False, max(K // 10, 10))]
+
     # the library's unfused path on the same inputs: four launches (query sums;
     # gather, RMS, log-RMS, readout; MLP layer 1; MLP layer 2 and residual)
     ureader = R.StateReader(shape_of(R, cfg, path="unfused"), cfg.slots)
@@ -1069,6 +1097,18 @@ def main():
             "fused_eager_cold": summ(b1["fused_eager_cold_us"]),
             "fused_graph_warm_mean": round(b1["fused_graph_warm_us"], 2),
             "fused_eager_warm_mean": round(b1["fused_eager_warm_us"], 2),
+            # the graph penalty is the runtime's per-launch cost: the same for a
+            # one-element kernel, and paid once for a graph of many calls
+            "graph_launch_overhead": {
+                "tiny_kernel_eager_cold_p50": round(pct(b1["tiny_kernel_eager_cold_us"], 50), 2),
+                "tiny_kernel_graph_cold_p50": round(pct(b1["tiny_kernel_graph_cold_us"], 50), 2),
+                "per_graph_launch_us": round(pct(b1["tiny_kernel_graph_cold_us"], 50)
+                                             - pct(b1["tiny_kernel_eager_cold_us"], 50), 2),
+                "fused_graph_cold_p50_minus_it": round(pct(b1["fused_graph_cold_us"], 50)
+                                                       - (pct(b1["tiny_kernel_graph_cold_us"], 50)
+                                                          - pct(b1["tiny_kernel_eager_cold_us"], 50)), 2),
+            },
+            "fused_graph10_warm_per_call": summ(b1["fused_graph10_warm_us_per_call"]),
             "library_unfused_cold": summ(b1["library_unfused_cold_us"]),
             "library_unfused_warm_mean": round(b1["library_unfused_warm_us"], 2),
             "unfused_torch_cold": summ(b1["unfused_torch_cold_us"]),
