@@ -11,8 +11,8 @@
 //      fused gather at the accept index into the caller's buffer, mean
 //      square, log-RMS and P = V^T S_bar U^T / sqrt(d_k), an r x r matrix
 //      (steps 1-3; u_j = T q_j / sqrt(d_k) with T = V^T S_bar and
-//      q_j = U^T z_j is P z_j).  Two tiles are in flight while one is
-//      processed.
+//      q_j = U^T z_j is P z_j).  One tile per workgroup is in flight
+//      at a time.
 //   A  16 rows x 64 columns of a: f_j = [P z_j / rms(h_j), ell] per pair,
 //      a = act(W1 f + b1) (step 4 readout, step 5), in row order.
 //   O  a BM x 128 tile of out = h + W2 a + b2 (step 5), in row order.
@@ -63,6 +63,8 @@
 // D[4 (l / 16) .. + 3][l % 16].  For Y = X W^T both operands are 16-byte
 // chunks of rows (X rows for A, W rows for B), so they load straight from
 // memory into registers.
+#include <type_traits>
+
 #include "ready_common.h"
 
 namespace {
@@ -695,57 +697,41 @@ __device__ __forceinline__ uint32_t group_tiles(const FastArgs& a, int q) {
   return (uint32_t)((a.n_s - q + READY_TICKET_GROUPS - 1) / READY_TICKET_GROUPS);
 }
 
-// The S items of one workgroup: the tiles at the positions it holds and
-// claims in queue q after the queue's zs Z items (ticket i of group q is
-// position zs + i).  p0 and p1 are positions the workgroup already holds
-// (NO_ITEM for none); it claims one position at a time after them.  Two
-// tiles are in flight while one is processed, and the position after them
-// is claimed too: it is requested before the loads of the tile it follows,
-// so that waiting for it never waits for tile data.  A workgroup that starts
-// with one tile keeps one in flight.  The tile processed two turns back is
-// announced while a tile is processed; the last two at the end.
+// The S items of one workgroup: the tiles at the positions it claims in
+// queue q after the queue's zs Z items (ticket i of group q is position
+// zs + i), starting with position p0 (NO_ITEM for none).  One tile is in
+// flight at a time: its loads are issued when the previous tile has been
+// processed, and the position after it is claimed before its loads, so that
+// waiting for the claim never waits for tile data.  (More tiles in flight
+// per workgroup only lengthen the memory queues once the whole grid streams:
+// the launch is then bound by bandwidth, and the deeper queues delay the
+// last tiles.)  The previous tile's stores were issued before this tile's
+// loads, so they are complete once every wave has waited for this tile's
+// data: it is announced then; the last one at the end.
 template <int RR, bool MULTI>
-__device__ __forceinline__ void s_phase(const FastArgs& a, int q, uint32_t zs, uint32_t p0, uint32_t p1,
-                                        unsigned char* smem, const int* s_acc, uint32_t* s_tk) {
+__device__ __forceinline__ void s_phase(const FastArgs& a, int q, uint32_t zs, uint32_t p0, unsigned char* smem,
+                                        const int* s_acc, uint32_t* s_tk) {
   constexpr int NQ = READY_TICKET_GROUPS;
   const int tid = item_tid();
   const uint32_t nt = group_tiles(a, q);
   uint32_t* tk = ctr(a.tk, q);
-  auto tile_at = [&](uint32_t pos) {
-    return (pos != NO_ITEM && pos >= zs && pos - zs < nt) ? q + NQ * (int)(pos - zs) : -1;
-  };
-  int t0 = tile_at(p0);
-  int t1 = t0 >= 0 ? tile_at(p1) : -1;
-  uint32_t pend = NO_ITEM;  // thread 0: the position after the newest tile
+  int t0 = (p0 != NO_ITEM && p0 >= zs && p0 - zs < nt) ? q + NQ * (int)(p0 - zs) : -1;
+  uint32_t pend = NO_ITEM;  // thread 0: the position after t0
   if (tid == 0 && t0 >= 0) pend = count_up(tk);
-  TileRegs<RR> r0, r1;
+  TileRegs<RR> r0;
   if (t0 >= 0) tile_issue<RR>(a, t0, r0, s_acc);
-  if (t1 >= 0) tile_issue<RR>(a, t1, r1, s_acc);
-  int h1 = -1, h2 = -1;  // tiles processed one and two turns back
+  int h1 = -1;  // the tile processed last turn
   while (t0 >= 0) {
-    tile_process<RR, MULTI>(a, t0, r0, smem, h2, s_tk, pend, q, zs, nt);
-    const int t2 = (int)*s_tk;
-    h2 = h1;
+    tile_process<RR, MULTI>(a, t0, r0, smem, h1, s_tk, pend, q, zs, nt);
     h1 = t0;
+    t0 = (int)*s_tk;
     pend = NO_ITEM;
-    if (t1 >= 0) {
-      t0 = t1;
-      r0 = r1;
-      t1 = t2;
-      if (tid == 0 && t1 >= 0) pend = count_up(tk);
-      if (t1 >= 0) tile_issue<RR>(a, t1, r1, s_acc);
-    } else {
-      t0 = t2;
-      if (tid == 0 && t0 >= 0) pend = count_up(tk);
-      if (t0 >= 0) tile_issue<RR>(a, t0, r0, s_acc);
-    }
+    if (tid == 0 && t0 >= 0) pend = count_up(tk);
+    if (t0 >= 0) tile_issue<RR>(a, t0, r0, s_acc);
   }
   wait_mem();
   __syncthreads();
-  if (tid == 0) {
-    if (h1 >= 0) tile_count(a, h1);
-    if (h2 >= 0) tile_count(a, h2);
-  }
+  if (tid == 0 && h1 >= 0) tile_count(a, h1);
   __syncthreads();  // the LDS area is reused by the next item
 }
 
@@ -796,9 +782,10 @@ __device__ __forceinline__ void mlp1_item(const FastArgs& a, int item, unsigned 
   const bool ok = *s_flag != 0;
 
   // ---- one trip to memory: z of the 16 rows, the sums of squares of h,
-  // and the P rows and log-RMS of this thread's first f item.  An f item is
-  // (pair m, output i): it holds row i of P[b][m] for the sequences b of this
-  // block (up to PS at a time) and applies it to each of their rows here.
+  // the P rows of this thread's first f item and the log-RMS entries it
+  // places.  An f item is (pair m, output i): it holds row i of P[b][m] for
+  // the sequences b of this block (up to PS at a time) and applies it to
+  // each of their rows here.
   constexpr int CR4 = RR / 4;   // 16-byte chunks of a row of P
   constexpr int PS = RR <= 16 ? 4 : 2;  // sequences per load group
   constexpr int RU = RR <= 8 ? 4 : (RR <= 16 ? 2 : 1);  // rows per step of the f loop
@@ -808,8 +795,7 @@ __device__ __forceinline__ void mlp1_item(const FastArgs& a, int item, unsigned 
   // in the same trip as its first, into a second register set
   constexpr bool PRE2 = RR <= 8;
   u32x4 pv[PS][CR4], pv2[PRE2 ? PS : 1][PRE2 ? CR4 : 1];
-  float ellv[PS], ellv2[PRE2 ? PS : 1];
-  auto load_p_into = [&](int e, int s0, auto& dst, auto& del) {
+  auto load_p_into = [&](int e, int s0, auto& dst) {
     const int m = e / RR, i = e - (e / RR) * RR;
 #pragma unroll
     for (int s = 0; s < PS; ++s) {
@@ -817,13 +803,28 @@ __device__ __forceinline__ void mlp1_item(const FastArgs& a, int item, unsigned 
       const bool live = e < nmi && s0 + s < nseq && ok;
       const uint32_t pofs = (uint32_t)((((b * a.M + m) * RR + i) * RR) * 4);
 #pragma unroll
-      // (rows of sequences past the block's last, and ell of outputs i > 0,
-      // are loaded from offset 0 and never used)
       for (int c = 0; c < CR4; ++c) dst[s][c] = ld_coh16_at(live, a.pmat, pofs + 16 * c);
-      del[s] = ld_coh4_at(live && i == 0, a.ell, (uint32_t)(4 * (b * a.M + m)));
     }
   };
-  auto load_p = [&](int e, int s0) { load_p_into(e, s0, pv, ellv); };
+  auto load_p = [&](int e, int s0) { load_p_into(e, s0, pv); };
+  // the ell columns of f: (row, pair) entries e = tid + 256 j of the 16 x M
+  // of them, EL per thread in the trip, the rest after it
+  constexpr int EL = 2;
+  const int nel = 16 * a.M;
+  auto ell_of = [&](int e, bool& live, int& fofs) {
+    const int rr = e / a.M, m = e - (e / a.M) * a.M;
+    live = e < nel && rr < rows && ok;
+    fofs = rr * Fs + m * (RR + 1) + RR;
+    return (uint32_t)(4 * (((row0 + rr) / a.n) * a.M + m));
+  };
+  float ev[EL];
+#pragma unroll
+  for (int j = 0; j < EL; ++j) {
+    bool live;
+    int fofs;
+    const uint32_t off = ell_of(tid + 256 * j, live, fofs);
+    ev[j] = ld_coh4_at(live, a.ell, off);
+  }
   // z of the 16 rows: 16 Nz / 4 chunks of 16 bytes, ZC per thread in the
   // trip (all of them for Nz <= 256), the rest after it
   constexpr int ZC = 4;
@@ -832,11 +833,10 @@ __device__ __forceinline__ void mlp1_item(const FastArgs& a, int item, unsigned 
 #pragma unroll
   for (int j = 0; j < ZC; ++j) {
     const int c = tid + 256 * j;
-    zv[j] = ld_coh16_at(c < nzc && ok, a.zfin, (uint32_t)(4 * (row0 * Nz + 4 * c)));  // rows past the block's
-                                                                                      // last are never used
+    zv[j] = ld_coh16_at(c < nzc && ok, a.zfin, (uint32_t)(4 * (row0 * Nz + 4 * c)));
   }
   load_p(tid, 0);
-  if constexpr (PRE2) load_p_into(tid + 256, 0, pv2, ellv2);
+  if constexpr (PRE2) load_p_into(tid + 256, 0, pv2);
   // the sums of squares of h (threads 0-15, one row each) travel with the
   // other loads
   const bool hrow = tid < 16 && tid < rows && ok;
@@ -856,9 +856,9 @@ __device__ __forceinline__ void mlp1_item(const FastArgs& a, int item, unsigned 
       pin(pv[s][c]);
       if constexpr (PRE2) pin(pv2[s][c]);
     }
-    pin(ellv[s]);
-    if constexpr (PRE2) pin(ellv2[s]);
   }
+#pragma unroll
+  for (int j = 0; j < EL; ++j) pin(ev[j]);
 #pragma unroll
   for (int k = 0; k < 16; ++k) pin(hv[k]);
 #pragma unroll
@@ -883,66 +883,89 @@ __device__ __forceinline__ void mlp1_item(const FastArgs& a, int item, unsigned 
   for (int e = tid; e < 2 * Fs; e += 256) ((u32x4*)fsh)[e] = u32x4{0u, 0u, 0u, 0u};
   __syncthreads();
 
-  for (int e0 = tid; e0 < nmi; e0 += 256) {
-    const int m = e0 / RR, i = e0 - (e0 / RR) * RR;
-    const int mz = a.shared ? 0 : m;
-    for (int s0 = 0; s0 < nseq; s0 += PS) {
-      if constexpr (PRE2) {
-        if (e0 == tid + 256 && s0 == 0) {
+  const bool want_feat = a.feat != nullptr && cb == 0;
+  float* feat0 = a.feat + (int64_t)row0 * F;
+  // the ell columns
 #pragma unroll
-          for (int s = 0; s < PS; ++s) {
+  for (int j = 0; j < EL; ++j) {
+    bool live;
+    int fofs;
+    ell_of(tid + 256 * j, live, fofs);
+    if (live) {
+      fsh[fofs] = f32_to_bf16_rne(ev[j]);
+      if (want_feat) feat0[fofs - (fofs / Fs) * (Fs - F)] = ev[j];
+    }
+  }
+  for (int e = tid + 256 * EL; e < nel; e += 256) {
+    bool live;
+    int fofs;
+    const uint32_t off = ell_of(e, live, fofs);
+    if (live) {
+      const float v = ld_coh4(a.ell, off);
+      fsh[fofs] = f32_to_bf16_rne(v);
+      if (want_feat) feat0[fofs - (fofs / Fs) * (Fs - F)] = v;
+    }
+  }
+  // the u columns.  Each step computes RU rows of one sequence's range; a
+  // step's rows past the range are rewritten later by the sequence they
+  // belong to (or are zero rows past the block), so they need no test.
+  auto f_loop = [&](auto feat_tag) {
+    constexpr bool FEAT = decltype(feat_tag)::value;
+    for (int e0 = tid; e0 < nmi; e0 += 256) {
+      const int m = e0 / RR, i = e0 - (e0 / RR) * RR;
+      const int mz = a.shared ? 0 : m;
+      const int fcol = m * (RR + 1) + i;
+      for (int s0 = 0; s0 < nseq; s0 += PS) {
+        if constexpr (PRE2) {
+          if (e0 == tid + 256 && s0 == 0) {
 #pragma unroll
-            for (int c = 0; c < CR4; ++c) pv[s][c] = pv2[s][c];
-            ellv[s] = ellv2[s];
+            for (int s = 0; s < PS; ++s) {
+#pragma unroll
+              for (int c = 0; c < CR4; ++c) pv[s][c] = pv2[s][c];
+            }
+          } else if (e0 != tid || s0 != 0) {
+            load_p(e0, s0);
           }
         } else if (e0 != tid || s0 != 0) {
           load_p(e0, s0);
         }
-      } else if (e0 != tid || s0 != 0) {
-        load_p(e0, s0);
-      }
 #pragma unroll
-      for (int s = 0; s < PS; ++s) {
-        const int b = b0 + s0 + s;
-        // rows of sequence b in this block (none when b is past the last)
-        const int ra = max(row0, b * a.n) - row0;
-        const int rz = s0 + s < nseq ? min(row0 + rows, (b + 1) * a.n) - row0 : ra;
-        // RU rows at a time, so that their LDS reads overlap (z rows past
-        // the block's last valid row are zero and their results are dropped)
-        for (int r0 = ra; r0 < rz; r0 += RU) {
-          float u[RU];
+        for (int s = 0; s < PS; ++s) {
+          const int b = b0 + s0 + s;
+          // rows of sequence b in this block (none when b is past the last)
+          const int ra = max(row0, b * a.n) - row0;
+          const int rz = s0 + s < nseq ? min(row0 + rows, (b + 1) * a.n) - row0 : ra;
+          for (int r0 = ra; r0 < rz; r0 += RU) {
 #pragma unroll
-          for (int q = 0; q < RU; ++q) {
-            const int rr = min(r0 + q, 15);
-            float acc = 0.0f;
+            for (int q = 0; q < RU; ++q) {
+              const int rr = min(r0 + q, 15);
+              float acc = 0.0f;
 #pragma unroll
-            for (int c = 0; c < CR4; ++c) {
-              const float4 zv = *(const float4*)&z_s[rr * Nz + mz * RR + 4 * c];
-              acc += __uint_as_float(pv[s][c].x) * zv.x + __uint_as_float(pv[s][c].y) * zv.y +
-                     __uint_as_float(pv[s][c].z) * zv.z + __uint_as_float(pv[s][c].w) * zv.w;
-            }
-            u[q] = acc * s_rs[rr];
-          }
-#pragma unroll
-          for (int q = 0; q < RU; ++q) {
-            const int rr = r0 + q;
-            if (rr < rz) {
-              fsh[rr * Fs + m * (RR + 1) + i] = f32_to_bf16_rne(u[q]);
-              if (i == 0) fsh[rr * Fs + m * (RR + 1) + RR] = f32_to_bf16_rne(ellv[s]);
-              if (a.feat && cb == 0) {
-                float* fr = a.feat + (int64_t)(row0 + rr) * F + m * (RR + 1);
-                fr[i] = u[q];
-                if (i == 0) fr[RR] = ellv[s];
+              for (int c = 0; c < CR4; ++c) {
+                const float4 zq = *(const float4*)&z_s[rr * Nz + mz * RR + 4 * c];
+                acc += __uint_as_float(pv[s][c].x) * zq.x + __uint_as_float(pv[s][c].y) * zq.y +
+                       __uint_as_float(pv[s][c].z) * zq.z + __uint_as_float(pv[s][c].w) * zq.w;
+              }
+              const float u = acc * s_rs[rr];
+              fsh[rr * Fs + fcol] = f32_to_bf16_rne(u);
+              if constexpr (FEAT) {
+                if (r0 + q < rz) feat0[rr * F + fcol] = u;
               }
             }
           }
         }
       }
     }
-  }
+  };
+  if (want_feat) f_loop(std::true_type{});
+  else f_loop(std::false_type{});
   __syncthreads();
 
-  f32x4 acc = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  // a = act(W1 f + b1) for this wave's 16 columns.  The A operands of a
+  // pass are read from LDS first (steps past F read the last step's
+  // columns: their W1 chunks are zero), then the matrix instructions run
+  // back to back, alternating between two accumulators.
+  f32x4 acc0 = f32x4{0.0f, 0.0f, 0.0f, 0.0f}, acc1 = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
   for (int k0 = 0; k0 < Fp; k0 += 32 * W1S) {
     if (k0 > 0) {
 #pragma unroll
@@ -951,15 +974,19 @@ __device__ __forceinline__ void mlp1_item(const FastArgs& a, int item, unsigned 
         bq[s] = (cv && kk < F) ? *(const u32x4*)(wrow + kk) : u32x4{0u, 0u, 0u, 0u};
       }
     }
+    u32x4 aop[W1S];
 #pragma unroll
     for (int s = 0; s < W1S; ++s) {
-      const int kb = k0 + 32 * s;
-      if (kb < Fp) {
-        const u32x4 aop = *(const u32x4*)&fsh[lr * Fs + kb + 8 * lg];
-        acc = mfma16x16x32(aop, bq[s], acc);
-      }
+      const int kb = min(k0 + 32 * s, Fp - 32);
+      aop[s] = *(const u32x4*)&fsh[lr * Fs + kb + 8 * lg];
+    }
+#pragma unroll
+    for (int s = 0; s < W1S; s += 2) {
+      acc0 = mfma16x16x32(aop[s], bq[s], acc0);
+      if (s + 1 < W1S) acc1 = mfma16x16x32(aop[s + 1], bq[s + 1], acc1);
     }
   }
+  const f32x4 acc = acc0 + acc1;
   // a in bf16: lanes l and l + 1 hold neighbouring columns; the even lane
   // stores the pair as one 32-bit word
 #pragma unroll
@@ -1184,13 +1211,9 @@ __global__ __launch_bounds__(256, (MODE == READY_MODE_PREPARE && RR <= 16) ? 3 :
   const int tid = item_tid();
   const int g = blockIdx.x, G = gridDim.x;
   const int xcc = hw_xcc();  // the queue of XCD x holds its Z items, then tile group x
-  // claims take two positions at a time when the launch has at least two
-  // state tiles per workgroup (two tiles in flight from the first trip on),
-  // else one, so that scarce tiles spread over more workgroups
-  const uint32_t step = a.n_s >= 2 * G ? 2u : 1u;
   uint32_t first = NO_ITEM;
   if (tid == 0) {
-    first = __hip_atomic_fetch_add(ctr(a.tk, xcc), step, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    first = count_up(ctr(a.tk, xcc));
     st_coh_u32(ctr(a.arr_x, xcc), 1u);
   }
   // the accept indices are requested with the magic word, and staged in LDS
@@ -1216,43 +1239,27 @@ __global__ __launch_bounds__(256, (MODE == READY_MODE_PREPARE && RR <= 16) ? 3 :
   auto a_size = [&](int x) { return (uint32_t)((a.n_a - x + 7) >> 3); };
   auto o_size = [&](int x) { return (uint32_t)(nrbo * ((ncb - x + 7) >> 3)); };
 
-  // positions [p, pe) of the home queue are this workgroup's: Z items are
-  // run in order (claiming again when they run out), the first tile
-  // positions go to the S phase
+  // position p of the home queue is this workgroup's: Z items are run
+  // (claiming the next position after each), the first tile position goes
+  // to the S phase
   if (tid == 0) s_tk[0] = first;
   __syncthreads();
-  uint32_t p = s_tk[0], pe = p + step;
+  uint32_t p = s_tk[0];
   __syncthreads();
   const uint32_t zs = z_size(xcc);
   if constexpr (zao) {
-    for (;;) {
-      if (p >= pe) {
-        if (tid == 0) s_tk[0] = __hip_atomic_fetch_add(ctr(a.tk, xcc), step, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __syncthreads();
-        p = s_tk[0];
-        __syncthreads();
-        pe = p + step;
-      }
-      if (p >= zs) break;
+    while (p < zs) {
       z_run<BMZ, NST>(a, xcc, p, smem);
-      ++p;
+      if (tid == 0) s_tk[0] = count_up(ctr(a.tk, xcc));
+      __syncthreads();
+      p = s_tk[0];
+      __syncthreads();
     }
   }
 #pragma unroll
   for (int k = 0; k < APT; ++k) s_acc[tid + 256 * k] = accv[k];
   __syncthreads();
-  if constexpr (has_s) {
-    uint32_t p1 = p + 1 < pe ? p + 1 : NO_ITEM;
-    if (step == 2u && p1 == NO_ITEM && p >= zs && p - zs < group_tiles(a, xcc)) {
-      // the last Z item of a pair of positions was followed by one tile:
-      // claim a second, so that two tiles are in flight from the start
-      if (tid == 0) s_tk[0] = count_up(ctr(a.tk, xcc));
-      __syncthreads();
-      p1 = s_tk[0];
-      __syncthreads();
-    }
-    s_phase<RR, multi>(a, xcc, zs, p, p1, smem, s_acc, s_tk);
-  }
+  if constexpr (has_s) s_phase<RR, multi>(a, xcc, zs, p, smem, s_acc, s_tk);
 
   if constexpr (zao) {
     // before the first A item: the arrival flags of the XCDs, read in the
