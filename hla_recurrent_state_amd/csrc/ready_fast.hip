@@ -577,20 +577,18 @@ __device__ __forceinline__ void tile_project(const u32x4* sS, const uint16_t* sU
   }
 }
 
-// Process tile t whose loads were issued: copy to `gathered`, sum of
-// squares, S U^T, P, ell.  Thread 0 also publishes the tile of the next
-// ticket in *s_pub, readable by every thread once this returns.  Tile `announce` (if >= 0) is counted as done on
-// the way: its stores were issued before this tile's loads, and with the
-// in-order completion of the memory counter they are complete once every
-// wave has waited for this tile's data (the barrier after the LDS copy).
-// This tile's own stores are complete after the caller's next such wait.
+// Process tile t whose loads were issued into R: copy to `gathered`, sum of
+// squares, S U^T, P, ell.  Once R's data is in LDS, the loads of the tile at
+// position `raw` of queue q (published in *s_pub, NO_ITEM when that is past
+// the queue's zs Z items and nt tickets) go out into R, after thread 0's claim
+// of the position after it (returned; tk == nullptr: no claim).  So the next
+// tile's loads overlap this tile's projection and stores, and the claim has a
+// whole turn to return.  At the end every wave waits for its stores, and the
+// tile is counted done.
 template <int RR, bool MULTI>
-__device__ __forceinline__ void tile_process(const FastArgs& a, int t, const TileRegs<RR>& R, unsigned char* smem,
-                                             int announce, uint32_t* s_pub, uint32_t raw, int q, uint32_t zs,
-                                             uint32_t nt) {
-  // thread 0: the tile at position `raw` of queue q (NO_ITEM when that is
-  // past the queue's zs Z items and nt tickets), published after the first
-  // barrier below, so that only wave 0 waits for the claim's trip
+__device__ __forceinline__ uint32_t tile_process(const FastArgs& a, int t, TileRegs<RR>& R, unsigned char* smem,
+                                                 uint32_t* s_pub, uint32_t raw, int q, uint32_t zs, uint32_t nt,
+                                                 uint32_t* tk, const int* s_acc) {
   auto pub_of = [&]() {
     return (raw != NO_ITEM && raw >= zs && raw - zs < nt) ? (uint32_t)(q + READY_TICKET_GROUPS * (int)(raw - zs))
                                                           : NO_ITEM;
@@ -609,11 +607,38 @@ __device__ __forceinline__ void tile_process(const FastArgs& a, int t, const Til
   const int tid = item_tid(), lane = tid & 63, wave = tid >> 6;
   float* P = a.pmat + (int64_t)t * RR * RR;
 
-  if (R.p < 0 || R.p >= a.P) {
-    // out-of-range accept index: flag it and leave this sequence's outputs.
-    // No tile loads were issued, so wait explicitly before announcing.
-    __syncthreads();  // every thread has read the last published ticket
-    if (tid == 0) *s_pub = pub_of();
+  const bool valid = R.p >= 0 && R.p < a.P;
+  u32x4* dst = (u32x4*)(a.gathered + (int64_t)t * READY_TILE_ELEMS);
+  __syncthreads();  // the previous tile is done with the LDS area and *s_pub
+  if (tid == 0) *s_pub = pub_of();
+  float ss = 0.0f;
+  if (valid) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int c = tid + 256 * j;
+      __builtin_nontemporal_store(R.data[j], dst + c);
+      sS[tile_slot(c >> 4, c & 15)] = R.data[j];
+      ss += sumsq_bf16x8(R.data[j]);
+    }
+#pragma unroll
+    for (int k = 0; k < TileRegs<RR>::NW; ++k) {
+      const int c = tid + 256 * k;
+      if (c < WCH) *(u32x4*)&sU[(c >> 4) * LU + 8 * (c & 15)] = R.w[k];
+      else *(u32x4*)&sV[8 * (c - WCH)] = R.w[k];
+    }
+  }
+  // ---- step 2: mean square ----
+  ss = wave_sum(ss);
+  if (lane == 0) s_wsum[wave] = ss;
+  __syncthreads();
+  // R is free: claim the position after the next tile, then issue its loads
+  const int tn = (int)*s_pub;
+  uint32_t claim = NO_ITEM;
+  if (tid == 0 && tn >= 0 && tk != nullptr) claim = count_up(tk);
+  if (tn >= 0) tile_issue<RR>(a, tn, R, s_acc);
+
+  if (!valid) {
+    // out-of-range accept index: flag it and leave this sequence's outputs
     for (int inj = 0; inj < (MULTI ? a.n_inj : 1); ++inj)
       for (int e = tid; e < RR * RR; e += 256) st_coh_f32(P + (int64_t)inj * a.p_inj_stride + e, 0.0f);
     if (tid == 0) {
@@ -623,32 +648,9 @@ __device__ __forceinline__ void tile_process(const FastArgs& a, int t, const Til
     }
     wait_mem();
     __syncthreads();
-    if (tid == 0 && announce >= 0) tile_count(a, announce);
-    return;
+    if (tid == 0) tile_count(a, t);
+    return claim;
   }
-
-  u32x4* dst = (u32x4*)(a.gathered + (int64_t)t * READY_TILE_ELEMS);
-  __syncthreads();  // the previous tile is done with the LDS area and the last published ticket
-  if (tid == 0) *s_pub = pub_of();
-  float ss = 0.0f;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int c = tid + 256 * j;
-    __builtin_nontemporal_store(R.data[j], dst + c);
-    sS[tile_slot(c >> 4, c & 15)] = R.data[j];
-    ss += sumsq_bf16x8(R.data[j]);
-  }
-#pragma unroll
-  for (int k = 0; k < TileRegs<RR>::NW; ++k) {
-    const int c = tid + 256 * k;
-    if (c < WCH) *(u32x4*)&sU[(c >> 4) * LU + 8 * (c & 15)] = R.w[k];
-    else *(u32x4*)&sV[8 * (c - WCH)] = R.w[k];
-  }
-  // ---- step 2: mean square ----
-  ss = wave_sum(ss);
-  if (lane == 0) s_wsum[wave] = ss;
-  __syncthreads();
-  if (tid == 0 && announce >= 0) tile_count(a, announce);
 
   const float ms = ((s_wsum[0] + s_wsum[1]) + (s_wsum[2] + s_wsum[3])) * (1.0f / READY_TILE_ELEMS);
   const float rms = sqrtf(ms + a.state_eps);
@@ -689,6 +691,10 @@ __device__ __forceinline__ void tile_process(const FastArgs& a, int t, const Til
       tile_project<RR>(sS, sU, sV, s_red, scale, P + (int64_t)inj * a.p_inj_stride);
     }
   }
+  wait_mem();
+  __syncthreads();
+  if (tid == 0) tile_count(a, t);
+  return claim;
 }
 
 // Ticket i of group q is tile q + G i (G = READY_TICKET_GROUPS); group q
@@ -700,14 +706,12 @@ __device__ __forceinline__ uint32_t group_tiles(const FastArgs& a, int q) {
 // The S items of one workgroup: the tiles at the positions it claims in
 // queue q after the queue's zs Z items (ticket i of group q is position
 // zs + i), starting with position p0 (NO_ITEM for none).  One tile is in
-// flight at a time: its loads are issued when the previous tile has been
-// processed, and the position after it is claimed before its loads, so that
-// waiting for the claim never waits for tile data.  (More tiles in flight
-// per workgroup only lengthen the memory queues once the whole grid streams:
-// the launch is then bound by bandwidth, and the deeper queues delay the
-// last tiles.)  The previous tile's stores were issued before this tile's
-// loads, so they are complete once every wave has waited for this tile's
-// data: it is announced then; the last one at the end.
+// flight at a time: the next tile's loads are issued once the current one's
+// data is in LDS (see tile_process), and each position is claimed a turn
+// before its loads, so that waiting for a claim never waits for tile data.
+// (More tiles in flight per workgroup only lengthen the memory queues once
+// the whole grid streams: the launch is then bound by bandwidth, and the
+// deeper queues delay the last tiles.)
 template <int RR, bool MULTI>
 __device__ __forceinline__ void s_phase(const FastArgs& a, int q, uint32_t zs, uint32_t p0, unsigned char* smem,
                                         const int* s_acc, uint32_t* s_tk) {
@@ -716,22 +720,14 @@ __device__ __forceinline__ void s_phase(const FastArgs& a, int q, uint32_t zs, u
   const uint32_t nt = group_tiles(a, q);
   uint32_t* tk = ctr(a.tk, q);
   int t0 = (p0 != NO_ITEM && p0 >= zs && p0 - zs < nt) ? q + NQ * (int)(p0 - zs) : -1;
-  uint32_t pend = NO_ITEM;  // thread 0: the position after t0
-  if (tid == 0 && t0 >= 0) pend = count_up(tk);
+  uint32_t raw = NO_ITEM;  // thread 0: the position after t0
+  if (tid == 0 && t0 >= 0) raw = count_up(tk);
   TileRegs<RR> r0;
   if (t0 >= 0) tile_issue<RR>(a, t0, r0, s_acc);
-  int h1 = -1;  // the tile processed last turn
   while (t0 >= 0) {
-    tile_process<RR, MULTI>(a, t0, r0, smem, h1, s_tk, pend, q, zs, nt);
-    h1 = t0;
+    raw = tile_process<RR, MULTI>(a, t0, r0, smem, s_tk, raw, q, zs, nt, tk, s_acc);
     t0 = (int)*s_tk;
-    pend = NO_ITEM;
-    if (tid == 0 && t0 >= 0) pend = count_up(tk);
-    if (t0 >= 0) tile_issue<RR>(a, t0, r0, s_acc);
   }
-  wait_mem();
-  __syncthreads();
-  if (tid == 0 && h1 >= 0) tile_count(a, h1);
   __syncthreads();  // the LDS area is reused by the next item
 }
 
@@ -1179,10 +1175,7 @@ __device__ __forceinline__ void s_single(const FastArgs& a, int t, unsigned char
                                          uint32_t* s_tk) {
   TileRegs<RR> r;
   tile_issue<RR>(a, t, r, s_acc);
-  tile_process<RR, MULTI>(a, t, r, smem, -1, s_tk, NO_ITEM, 0, 0u, 0u);
-  wait_mem();
-  __syncthreads();
-  if (threadIdx.x == 0) tile_count(a, t);
+  tile_process<RR, MULTI>(a, t, r, smem, s_tk, NO_ITEM, 0, 0u, 0u, nullptr, s_acc);
   __syncthreads();
 }
 
