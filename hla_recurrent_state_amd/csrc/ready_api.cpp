@@ -163,20 +163,20 @@ readyStatus readyPlanCreate(const readyShape* shape, const int32_t* layer_ids, r
     const int bmz = p->small ? 16 : std::min(READY_BMZ_LARGE, READY_BMZ_APPLY);
     const int bmo = p->small ? 16 : std::min(READY_BMO_LARGE, READY_BMO_APPLY);
     const int64_t rows = std::max(p->R, 1);
-    const int64_t nrbz = cdiv(rows, bmz), ncbz = cdiv(p->Nz, 64), nrb16 = cdiv(rows, 16), nrbo = cdiv(rows, bmo);
+    const int64_t nrbz = cdiv(rows, bmz), ncbz = cdiv(p->Nz, 64), nrba = cdiv(rows, READY_ABM), nrbo = cdiv(rows, bmo);
     p->gz.ksplit = (int)fks;
     p->gz.kchunk = (int)zchunk;
     p->n_z = (int)(nrbz * ncbz * fks);
     // each per-XCD queue holds fewer than 2^24 items (checked above)
     p->n_s = s.B * p->M;
-    p->n_a = (int)(nrb16 * cdiv(s.Hm, 64));
+    p->n_a = (int)(nrba * cdiv(s.Hm, 64));
     p->n_o = (int)(nrbo * cdiv(s.d, READY_OCOLS));
     // counter slots: magic, abort, READY_DONE_GROUPS + 1 done counts, then
     // per tile of z, per row block of z, per 16 rows, per row block of out
     p->c_zcnt = 2 + READY_DONE_GROUPS + 1;
     p->c_zdone = (int)(p->c_zcnt + nrbz * ncbz);
     p->c_sdone = (int)(p->c_zdone + nrbz);
-    p->c_adone = (int)(p->c_sdone + nrb16);
+    p->c_adone = (int)(p->c_sdone + nrba);
     p->c_tk = (int)(p->c_adone + nrbo);
     p->c_aq = p->c_tk + READY_TICKET_GROUPS;
     p->c_oq = p->c_aq + 8;

@@ -13,7 +13,7 @@
 //      (steps 1-3; u_j = T q_j / sqrt(d_k) with T = V^T S_bar and
 //      q_j = U^T z_j is P z_j).  One tile per workgroup is in flight
 //      at a time.
-//   A  16 rows x 64 columns of a: f_j = [P z_j / rms(h_j), ell] per pair,
+//   A  8 rows x 64 columns of a: f_j = [P z_j / rms(h_j), ell] per pair,
 //      a = act(W1 f + b1) (step 4 readout, step 5), in row order.
 //   O  a BM x 128 tile of out = h + W2 a + b2 (step 5), in row order.
 // Every item is claimed from a counter (see "claiming work items"): no item
@@ -502,7 +502,7 @@ __device__ __forceinline__ void tile_issue(const FastArgs& a, int t, TileRegs<RR
 __device__ __forceinline__ void tile_count(const FastArgs& a, int t) {
   const int b = t / a.M;
   const int r0 = b * a.n, r1 = b * a.n + a.n - 1;
-  for (int q = r0 / 16; q <= r1 / 16; ++q) count_up(ctr(a.sdone, q));
+  for (int q = r0 / READY_ABM; q <= r1 / READY_ABM; ++q) count_up(ctr(a.sdone, q));
 }
 
 // P = V^T (S U^T) * scale for the tile in LDS (sS) and the U, V of one
@@ -733,7 +733,8 @@ __device__ __forceinline__ void s_phase(const FastArgs& a, int q, uint32_t zs, u
 
 // ---------------------------------------------------------------- A items
 
-// Rows [16 rb, 16 rb + 16) of f and a, columns [64 cb, 64 cb + 64) of a.
+// Rows [8 rb, 8 rb + 8) of f and a (READY_ABM = 8; the matrix instructions
+// take 16-row tiles, whose upper half is zero), columns [64 cb, 64 cb + 64).
 // After the tiles of zfin of these rows and the S items of their sequences
 // are counted, one trip to memory brings z (into LDS), the sums of squares of
 // h, and the P rows and log-RMS this thread applies: f = [u = P z / rms(h),
@@ -746,13 +747,13 @@ __device__ __forceinline__ void mlp1_item(const FastArgs& a, int item, unsigned 
   const int rb = item / ncb, cb = item - (item / ncb) * ncb;
   const int tid = item_tid(), lane = tid & 63, wave = tid >> 6;
   const int lr = lane & 15, lg = lane >> 4;
-  const int row0 = rb * 16;
-  const int rows = min(16, a.R - row0);
+  const int row0 = rb * READY_ABM;
+  const int rows = min(READY_ABM, a.R - row0);
   const int F = a.F, Nz = a.Nz;
   const int Fp = (F + 31) & ~31;
   const int Fs = Fp + 8;
-  float* z_s = (float*)smem;                       // [16][Nz]
-  uint16_t* fsh = (uint16_t*)(z_s + 16 * Nz);      // [16][Fs]
+  float* z_s = (float*)smem;                       // [READY_ABM][Nz]
+  uint16_t* fsh = (uint16_t*)(z_s + READY_ABM * Nz);  // [16][Fs]: rows past READY_ABM stay zero
   float* s_rs = (float*)(fsh + 16 * Fs);           // [16]
   int* s_flag = (int*)(s_rs + 16);
 
@@ -777,7 +778,7 @@ __device__ __forceinline__ void mlp1_item(const FastArgs& a, int item, unsigned 
   __syncthreads();
   const bool ok = *s_flag != 0;
 
-  // ---- one trip to memory: z of the 16 rows, the sums of squares of h,
+  // ---- one trip to memory: z of the rows, the sums of squares of h,
   // the P rows of this thread's first f item and the log-RMS entries it
   // places.  An f item is (pair m, output i): it holds row i of P[b][m] for
   // the sequences b of this block (up to PS at a time) and applies it to
@@ -806,7 +807,7 @@ __device__ __forceinline__ void mlp1_item(const FastArgs& a, int item, unsigned 
   // the ell columns of f: (row, pair) entries e = tid + 256 j of the 16 x M
   // of them, EL per thread in the trip, the rest after it
   constexpr int EL = 2;
-  const int nel = 16 * a.M;
+  const int nel = READY_ABM * a.M;
   auto ell_of = [&](int e, bool& live, int& fofs) {
     const int rr = e / a.M, m = e - (e / a.M) * a.M;
     live = e < nel && rr < rows && ok;
@@ -821,10 +822,10 @@ __device__ __forceinline__ void mlp1_item(const FastArgs& a, int item, unsigned 
     const uint32_t off = ell_of(tid + 256 * j, live, fofs);
     ev[j] = ld_coh4_at(live, a.ell, off);
   }
-  // z of the 16 rows: 16 Nz / 4 chunks of 16 bytes, ZC per thread in the
+  // z of the rows: READY_ABM Nz / 4 chunks of 16 bytes, ZC per thread in the
   // trip (all of them for Nz <= 256), the rest after it
   constexpr int ZC = 4;
-  const int nzc = rows * (Nz / 4), nzall = 16 * (Nz / 4);
+  const int nzc = rows * (Nz / 4), nzall = READY_ABM * (Nz / 4);
   u32x4 zv[ZC];
 #pragma unroll
   for (int j = 0; j < ZC; ++j) {
@@ -934,7 +935,7 @@ __device__ __forceinline__ void mlp1_item(const FastArgs& a, int item, unsigned 
           for (int r0 = ra; r0 < rz; r0 += RU) {
 #pragma unroll
             for (int q = 0; q < RU; ++q) {
-              const int rr = min(r0 + q, 15);
+              const int rr = min(r0 + q, READY_ABM - 1);
               float acc = 0.0f;
 #pragma unroll
               for (int c = 0; c < CR4; ++c) {
@@ -1055,7 +1056,7 @@ __device__ __forceinline__ void mlp2_item(const FastArgs& a, int rb, int cb, uns
                                                    : u32x4{0u, 0u, 0u, 0u};
   }
 
-  const uint32_t want = (uint32_t)(cdiv_d(rows, 16) * cdiv_d(a.Hm, 64));
+  const uint32_t want = (uint32_t)(cdiv_d(rows, READY_ABM) * cdiv_d(a.Hm, 64));
   if (!wg_wait(ctr(a.adone, rb), want, a, s_flag)) return;
   // the invalid-sequence flags of the epilogue's rows, with the a loads
   uint32_t inv[EPT];

@@ -132,6 +132,7 @@ struct FastArgs {
 #define READY_ZCHUNK_SMALL 384
 #define READY_ZCHUNK_LARGE 640
 #define READY_OCOLS 128
+#define READY_ABM 8                // rows of an A item (and of a state-tile count)
 #define READY_TICKET_GROUPS 8     // state-tile ticket counters, one per XCD
 #define READY_ACC_LDS 1024        // accept indices staged in LDS
 
@@ -269,7 +270,7 @@ inline size_t ready_reader_lds(int r, int F, int Nz, int small) {
   const size_t s_bytes = (size_t)READY_TILE_ELEMS * 2 + (size_t)r * (READY_TILE + 8) * 2 + (size_t)READY_TILE * r * 2 +
                          4 * (4 * NB * r * 16 + 4);
   const int Fs = ((F + 31) & ~31) + 8;
-  const size_t a_bytes = (size_t)16 * Nz * 4 + (size_t)16 * Fs * 2 + 4 * 16 + 16;
+  const size_t a_bytes = (size_t)READY_ABM * Nz * 4 + (size_t)16 * Fs * 2 + 4 * 16 + 16;
   const size_t sa = (size_t)BMO * (256 + 8) * 2, so = (size_t)BMO * (READY_OCOLS + 4) * 4;
   const size_t o_bytes = (sa > so ? sa : so) + 16;
   size_t m = z_bytes;

@@ -14,6 +14,7 @@ import numpy as np
 import pytest
 
 import synth
+from tests.gpu_util import reader_shape
 from synth.device import tensor, to_device, to_numpy_bits
 
 pytestmark = pytest.mark.gpu
@@ -167,11 +168,25 @@ def test_shared_reader_parameters_relu():
     _check(synth.make("paper", seed=15, B=2, shared=True, act="relu"), 2, extras=True)
 
 
-def test_rank_32_is_unsupported():
-    # r = 32 at the paper shape runs as four kernels, so there is no P to share
+def test_rank_32_at_the_paper_pair_count_two_readers():
+    # r = 32 with the pages' 32 pairs runs as the single kernel, so its P can
+    # be shared: checked against the oracle and against single calls
+    dev = _dev()
+    inp = synth.make("paper", seed=16, r=32, B=3)
+    sr_shape = reader_shape(inp.cfg)
+    from hla_recurrent_state_amd import StateReader
+    assert StateReader(sr_shape, inp.cfg.slots).prep_size(2) > 0
+    readers, res = _check(inp, 2)
+    for i, rd in enumerate(readers):
+        single = _run_single(inp, rd, dev)
+        for key in ("gathered", "logrms", "out", "delta", "feat"):
+            assert np.array_equal(res[i][key].view(np.uint8), single[key].view(np.uint8)), (i, key)
+
+
+def test_rank_40_is_unsupported():
+    # r = 40 runs as four kernels, so there is no P to share
     from hla_recurrent_state_amd import READY_ERR_UNSUPPORTED, StateReader, ReadyError
-    from tests.gpu_util import reader_shape
-    cfg = synth.make_shape("paper", r=32)
+    cfg = synth.make_shape("paper", r=40)
     sr = StateReader(reader_shape(cfg), cfg.slots)
     with pytest.raises(ReadyError) as e:
         sr.prep_size(2)

@@ -219,8 +219,8 @@ def test_bf16_general_many_rows_large_tiles(act_dtype):
 @pytest.mark.parametrize("path", ["fused", "unfused"])
 def test_rank_32_at_the_paper_pair_count(path):
     """r = 32 with the pages' 32 layer-head pairs (arXiv section 4.4,
-    Table 3) at the batched shape, on the path the default plan takes and on
-    the four-launch path (the matrix-core per-state kernel at exactly
+    Table 3) at the batched shape, on the single kernel (the default plan)
+    and on the four-launch path (the matrix-core per-state kernel at exactly
     r = 32).  The oracle checks a sample of sequences; the gather is checked
     for all."""
     from hla_recurrent_state_amd import READY_ERR_UNSUPPORTED, ReadyError, StateReader
@@ -235,8 +235,7 @@ def test_rank_32_at_the_paper_pair_count(path):
         assert e.code == READY_ERR_UNSUPPORTED
         single = False
     sr.close()
-    if path == "unfused":
-        assert not single
+    assert single == (path == "fused")
     _say("r = 32, M = 32:", "single kernel" if single else "four launches")
     inp = synth.make(cfg, seed=33)
     res, ref, rep = _check(inp, seqs=[0, 1, 31, 62, 63], path=path)
