@@ -46,7 +46,7 @@ struct readyPlan {
   int c_zcnt, c_zdone, c_sdone, c_adone, c_tk, c_aq, c_oq, c_arx;  // first counter slot of each group
   size_t lds;
   GemmPlan gz, g1, g2;
-  size_t off_zpart, off_hss, off_f, off_a, off_g1p, off_flags, off_pmat, off_ell, off_ctr, ws_bytes;
+  size_t off_zpart, off_hss, off_rsv, off_f, off_fu, off_a, off_g1p, off_flags, off_pmat, off_ell, off_ctr, ws_bytes;
 };
 
 namespace {
@@ -138,7 +138,8 @@ readyStatus readyPlanCreate(const readyShape* shape, const int32_t* layer_ids, r
   const int64_t fks = cdiv(s.d, zchunk);
   const bool small_ws = (int64_t)s.B * p->M * s.r * s.r * 4 < (1LL << 31) &&
                         (int64_t)p->R * s.Hm * 2 < (1LL << 31) &&
-                        fks * p->R * p->Nz * 4 < (1LL << 31);
+                        fks * p->R * p->Nz * 4 < (1LL << 31) &&
+                        (int64_t)p->R * ((p->F + 31) & ~31) * 4 < (1LL << 31);
   p->small = p->R <= 16 ? 1 : 0;
   bool fits = allbf && s.r <= 32 && p->F % 8 == 0 && p->F <= READY_FAST_MAX_F && s.Hm % 8 == 0 &&
                     p->Nz <= READY_FAST_MAX_NZ && small_ws;
@@ -241,8 +242,10 @@ readyStatus readyPlanCreate(const readyShape* shape, const int32_t* layer_ids, r
   size_t off = 0;
   p->off_zpart = off; off = align_up(off + 4 * ks * R * p->Nz, 256);
   p->off_hss = off;   off = align_up(off + 4 * ks * R, 256);
+  p->off_rsv = off;   off = align_up(off + (p->fast ? 4 * R : 0), 256);
   // f on the general path, z summed over the K chunks on the fast path
   p->off_f = off;     off = align_up(off + 4 * R * (p->fast ? p->Nz : p->F), 256);
+  p->off_fu = off;    off = align_up(off + (p->fast ? 4 * R * (size_t)((p->F + 31) & ~31) : 0), 256);
   // a: bf16 on the fast path, fp32 otherwise
   p->off_a = off;     off = align_up(off + (p->fast ? 2 : 4) * R * s.Hm, 256);
   // K-split partial sums of the first MLP layer (k_gemm_mm with ksplit > 1)
@@ -300,7 +303,9 @@ void fast_common(const readyPlan* plan, const WsView& view, FastArgs& a) {
   for (int l = 0; l < s.L_sel; ++l) a.slot[l] = plan->slot[l];
   a.zpart = (float*)(wsb + plan->off_zpart);
   a.hss = (float*)(wsb + plan->off_hss);
+  a.rsv = (float*)(wsb + plan->off_rsv);
   a.zfin = (float*)(wsb + plan->off_f);
+  a.fu = (float*)(wsb + plan->off_fu);
   a.pmat = (float*)(wsb + plan->off_pmat);
   a.ell = (float*)(wsb + plan->off_ell);
   a.abuf = (uint16_t*)(wsb + plan->off_a);

@@ -155,14 +155,15 @@ __device__ bool wait_count(const uint32_t* c, uint32_t want, uint32_t* abort_fla
   }
 }
 
-// Poll two counters at once until *c1 >= w1 and *c2 >= w2 (same bounds and
-// failure reporting as wait_count).
-__device__ bool wait_count2(const uint32_t* c1, uint32_t w1, const uint32_t* c2, uint32_t w2, uint32_t* abort_flag,
-                            int32_t* dev_status) {
+// Poll two counters at once until *c1 >= w1 and (*c2 & m2) >= w2 (same
+// bounds and failure reporting as wait_count); *last2 gets *c2's last value.
+__device__ bool wait_count2(const uint32_t* c1, uint32_t w1, const uint32_t* c2, uint32_t m2, uint32_t w2,
+                            uint32_t* last2, uint32_t* abort_flag, int32_t* dev_status) {
   int nap = 0;
   for (int it = 0;; ++it) {
     const uint32_t v1 = ld_coh_u32(c1), v2 = ld_coh_u32(c2);
-    if (v1 >= w1 && v2 >= w2) return true;
+    *last2 = v2;
+    if (v1 >= w1 && (v2 & m2) >= w2) return true;
     if ((it & 15) == 15 && ld_coh_u32(abort_flag) != 0) return false;
     if (it >= SPIN_LIMIT) {
       st_coh_u32(abort_flag, 1u);
@@ -185,6 +186,34 @@ __device__ bool wg_wait(const uint32_t* c, uint32_t want, const FastArgs& a, int
   const bool ok = *s_flag != 0;
   __syncthreads();
   return ok;
+}
+
+// Thread 0 of a state tile (u path): have the query items of sequence b's
+// rows been counted done?  `known` is the count read when the tile's loads
+// were issued.  Polls at most Z_WAIT_POLLS times (about 100 us): the query
+// items are taken before any tile (they come first in every queue) and never
+// wait, so in a launch whose grid is resident they finish well within it;
+// when some XCD's workgroups have not run (other kernels hold it), the tile
+// gives up and takes the P path, so no tile ever waits on such an XCD.
+constexpr int Z_WAIT_POLLS = 256;
+__device__ bool rows_query_done(const FastArgs& a, int b, int bmz, uint32_t known) {
+  const uint32_t want = (uint32_t)((a.Nz + 63) / 64);
+  if (known >= want) return true;
+  const int r0 = b * a.n, r1 = b * a.n + a.n - 1;
+  const uint32_t* c0 = ctr(a.zdone, r0 / bmz);
+  const uint32_t* c1 = ctr(a.zdone, r1 / bmz);
+  int nap = 0;
+  for (int it = 0; it < Z_WAIT_POLLS; ++it) {
+    if (min(ld_coh_u32(c0), ld_coh_u32(c1)) >= want) return true;
+    if ((it & 15) == 15 && ld_coh_u32(a.abort_flag) != 0) return false;
+    switch (nap) {
+      case 0: __builtin_amdgcn_s_sleep(4); break;
+      case 1: __builtin_amdgcn_s_sleep(8); break;
+      default: __builtin_amdgcn_s_sleep(16); break;
+    }
+    if (nap < 2) ++nap;
+  }
+  return false;
 }
 
 // ---- claiming work items
@@ -302,7 +331,7 @@ __device__ __forceinline__ void z_stage_load(const FastArgs& a, int rb, int cb, 
   S.g = (kv && a.gamma != nullptr) ? *(const u32x4*)(a.gamma + kk) : zero;
 }
 
-template <int BMZ, int NST>
+template <int BMZ, int NST, bool RSV>
 __device__ __forceinline__ void z_item(const FastArgs& a, int ks, int cb, int rb, unsigned char* smem) {
   constexpr int RBT = BMZ / 16;                  // 16-row blocks of the tile
   constexpr int WR = RBT >= 4 ? 2 : 1;           // row blocks per wave
@@ -429,6 +458,13 @@ __device__ __forceinline__ void z_item(const FastArgs& a, int ks, int cb, int rb
       off[q] = live[q] ? (uint32_t)(row * a.Nz + col) : 0u;
       sum[q] = make_float4(0.f, 0.f, 0.f, 0.f);
     }
+    // (column block 0) the K chunks' sums of squares of the rows' h, for
+    // 1 / rms(h), travel with the first group
+    const bool hrow = RSV && cb == 0 && tid < BMZ && rb * BMZ + tid < a.R;
+    float hv[16];
+#pragma unroll
+    for (int k = 0; k < 16; ++k)
+      hv[k] = ld_coh4_at(hrow && k < a.ksplit, a.hss, (uint32_t)(4 * (k * a.R + rb * BMZ + tid)));
     for (int k0 = 0; k0 < a.ksplit; k0 += KG) {
       u32x4 v[RBT][KG];
 #pragma unroll
@@ -451,11 +487,32 @@ __device__ __forceinline__ void z_item(const FastArgs& a, int ks, int cb, int rb
       if (live[q])
         st_coh16(a.zfin, 4 * off[q], u32x4{__float_as_uint(sum[q].x), __float_as_uint(sum[q].y),
                                            __float_as_uint(sum[q].z), __float_as_uint(sum[q].w)});
+    if (RSV && hrow) {
+      // 1 / rms(h) of the rows (RMSNorm of the pages' h), from the K chunks'
+      // sums of squares that this column block's items stored, in chunk order
+      const int row = rb * BMZ + tid;
+      float hs = 0.0f;
+#pragma unroll
+      for (int k = 0; k < 16; ++k) hs += k < a.ksplit ? hv[k] : 0.0f;
+      for (int k = 16; k < a.ksplit; ++k) hs += ld_coh4(a.hss, (uint32_t)(4 * (k * a.R + row)));
+      st_coh_f32(a.rsv + row, 1.0f / sqrtf(hs / (float)a.d + a.h_eps));
+    }
     wait_mem();
     __syncthreads();
     if (tid == 0) count_up(ctr(a.zdone, rb));
   }
   __syncthreads();  // s_flag and the LDS area are reused by the next item
+}
+
+// acc + p . z over four values, rounded step by step in a fixed order: the
+// state tiles and the A items form u = P z / rms(h) with it, so f is the same
+// bit for bit whichever of them forms it.
+__device__ __forceinline__ float dot4_acc(float acc, float4 p, float4 z) {
+  float t = __fmul_rn(p.x, z.x);
+  t = __fmaf_rn(p.y, z.y, t);
+  t = __fmaf_rn(p.z, z.z, t);
+  t = __fmaf_rn(p.w, z.w, t);
+  return __fadd_rn(acc, t);
 }
 
 // ---------------------------------------------------------------- S items
@@ -474,16 +531,24 @@ struct TileRegs {
   static constexpr int NW = 2 * RR * 16 / 256;  // weight chunks per thread
   u32x4 data[8];
   u32x4 w[NW];
-  int p;  // accept index of the tile's sequence
+  int p;        // accept index of the tile's sequence
+  uint32_t zc;  // query items counted done for the tile's rows (the smaller of its row blocks' counts)
 };
 
-template <int RR>
+// UP: the counts of the query items of the sequence's rows are read in the
+// same trip (see tile_process).
+template <int RR, bool UP, int BMZ>
 __device__ __forceinline__ void tile_issue(const FastArgs& a, int t, TileRegs<RR>& R, const int* s_acc) {
   constexpr int WCH = RR * 16;
   const int b = t / a.M, m = t - (t / a.M) * a.M;
   const int tid = item_tid();
   const int mz = a.shared ? 0 : m;
   R.p = b < READY_ACC_LDS ? s_acc[b] : a.accept_idx[b];
+  if constexpr (UP) {
+    const int r0 = b * a.n, r1 = b * a.n + a.n - 1;
+    const uint32_t c0 = ld_coh_u32(ctr(a.zdone, r0 / BMZ)), c1 = ld_coh_u32(ctr(a.zdone, r1 / BMZ));
+    R.zc = min(c0, c1);
+  }
   const u32x4* Ug = (const u32x4*)(a.u + (int64_t)mz * RR * READY_TILE);
   const u32x4* Vg = (const u32x4*)(a.v + (int64_t)mz * READY_TILE * RR);
 #pragma unroll
@@ -499,10 +564,14 @@ __device__ __forceinline__ void tile_issue(const FastArgs& a, int t, TileRegs<RR
   for (int j = 0; j < 8; ++j) R.data[j] = __builtin_nontemporal_load(src + tid + 256 * j);
 }
 
-__device__ __forceinline__ void tile_count(const FastArgs& a, int t) {
+// A tile counts itself in the state-tile counters of the 8-row blocks its
+// sequence touches: 1 in the low half, and 1 in the high half too when it
+// wrote its columns of f itself (u_path).
+__device__ __forceinline__ void tile_count(const FastArgs& a, int t, bool u_path) {
   const int b = t / a.M;
   const int r0 = b * a.n, r1 = b * a.n + a.n - 1;
-  for (int q = r0 / READY_ABM; q <= r1 / READY_ABM; ++q) count_up(ctr(a.sdone, q));
+  for (int q = r0 / READY_ABM; q <= r1 / READY_ABM; ++q)
+    __hip_atomic_fetch_add(ctr(a.sdone, q), u_path ? 0x10001u : 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // P = V^T (S U^T) * scale for the tile in LDS (sS) and the U, V of one
@@ -511,7 +580,7 @@ __device__ __forceinline__ void tile_count(const FastArgs& a, int t) {
 // four waves' partials meet in s_red.  P is stored device-coherently.
 template <int RR>
 __device__ __forceinline__ void tile_project(const u32x4* sS, const uint16_t* sU, const uint16_t* sV, float* s_red,
-                                             float scale, float* P) {
+                                             float scale, float* P, float* sP = nullptr) {
   constexpr int NB = (RR + 15) / 16;  // 16-column blocks of U^T
   constexpr int VC = RR / 8;          // 16-byte chunks per V row
   constexpr int LU = READY_TILE + 8;  // padded U row in LDS (bf16)
@@ -573,7 +642,9 @@ __device__ __forceinline__ void tile_project(const u32x4* sS, const uint16_t* sU
   for (int e = tid; e < RR * RR; e += 256) {
     const int i = e / RR, ip = e - (e / RR) * RR;
     const int idx = ((ip >> 4) * RR + i) * 16 + (ip & 15);
-    st_coh_f32(P + e, ((s_red[idx] + s_red[WS + idx]) + (s_red[2 * WS + idx] + s_red[3 * WS + idx])) * scale);
+    const float pv = ((s_red[idx] + s_red[WS + idx]) + (s_red[2 * WS + idx] + s_red[3 * WS + idx])) * scale;
+    st_coh_f32(P + e, pv);
+    if (sP) sP[e] = pv;
   }
 }
 
@@ -585,7 +656,14 @@ __device__ __forceinline__ void tile_project(const u32x4* sS, const uint16_t* sU
 // tile's loads overlap this tile's projection and stores, and the claim has a
 // whole turn to return.  At the end every wave waits for its stores, and the
 // tile is counted done.
-template <int RR, bool MULTI>
+//
+// UP (one-reader launches at r >= 16, where forming f from P in the A items
+// means moving r^2 floats per (sequence, pair) again): once the query items of
+// the tile's rows are counted done (rows_query_done), the tile also forms its
+// pair's columns of f for its sequence's rows, u = P z / rms(h) and ell, into
+// fu, and counts itself with the u mark (tile_count): A items whose rows'
+// tiles all did so load f instead of forming it from P.
+template <int RR, bool MULTI, bool UP, int BMZ>
 __device__ __forceinline__ uint32_t tile_process(const FastArgs& a, int t, TileRegs<RR>& R, unsigned char* smem,
                                                  uint32_t* s_pub, uint32_t raw, int q, uint32_t zs, uint32_t nt,
                                                  uint32_t* tk, const int* s_acc) {
@@ -602,6 +680,10 @@ __device__ __forceinline__ uint32_t tile_process(const FastArgs& a, int t, TileR
   uint16_t* sV = sU + RR * LU;                           // [128][RR]
   float* s_red = (float*)(sV + READY_TILE * RR);         // [4][WS]
   float* s_wsum = s_red + 4 * WS;                        // [4]
+  float* s_P = s_wsum + 4;                               // [RR][RR]: P (u path)
+  float* s_zu = s_P + RR * RR;                           // [16][RR]: z of the sequence's rows (u path)
+  float* s_ru = s_zu + 16 * RR;                          // [16]: their 1 / rms(h)
+  float* s_el = s_ru + 16;                               // ell
 
   const int b = t / a.M, m = t - (t / a.M) * a.M;
   const int tid = item_tid(), lane = tid & 63, wave = tid >> 6;
@@ -609,8 +691,20 @@ __device__ __forceinline__ uint32_t tile_process(const FastArgs& a, int t, TileR
 
   const bool valid = R.p >= 0 && R.p < a.P;
   u32x4* dst = (u32x4*)(a.gathered + (int64_t)t * READY_TILE_ELEMS);
+  // the u path is taken on thread 0's reading of the query counts (waves may
+  // have read different counts), published with the first barrier
+  if constexpr (UP) {
+    if (tid == 0) s_pub[2] = (valid && rows_query_done(a, b, BMZ, R.zc)) ? 1u : 0u;
+  }
   __syncthreads();  // the previous tile is done with the LDS area and *s_pub
   if (tid == 0) *s_pub = pub_of();
+  const bool up = UP && s_pub[2] != 0u;
+  // u path: z of the sequence's rows for this pair, and their 1 / rms(h)
+  constexpr int RC = RR / 4;
+  const int mz = a.shared ? 0 : m;
+  const int zj = tid / RC, zk = tid - (tid / RC) * RC;
+  const u32x4 zq = ld_coh16_at(up && tid < a.n * RC, a.zfin, (uint32_t)(4 * ((b * a.n + zj) * a.Nz + mz * RR + 4 * zk)));
+  const float rq = ld_coh4_at(up && tid < a.n, a.rsv, (uint32_t)(4 * (b * a.n + tid)));
   float ss = 0.0f;
   if (valid) {
 #pragma unroll
@@ -635,7 +729,7 @@ __device__ __forceinline__ uint32_t tile_process(const FastArgs& a, int t, TileR
   const int tn = (int)*s_pub;
   uint32_t claim = NO_ITEM;
   if (tid == 0 && tn >= 0 && tk != nullptr) claim = count_up(tk);
-  if (tn >= 0) tile_issue<RR>(a, tn, R, s_acc);
+  if (tn >= 0) tile_issue<RR, UP, BMZ>(a, tn, R, s_acc);
 
   if (!valid) {
     // out-of-range accept index: flag it and leave this sequence's outputs
@@ -648,19 +742,39 @@ __device__ __forceinline__ uint32_t tile_process(const FastArgs& a, int t, TileR
     }
     wait_mem();
     __syncthreads();
-    if (tid == 0) tile_count(a, t);
+    if (tid == 0) tile_count(a, t, false);
     return claim;
   }
 
   const float ms = ((s_wsum[0] + s_wsum[1]) + (s_wsum[2] + s_wsum[3])) * (1.0f / READY_TILE_ELEMS);
   const float rms = sqrtf(ms + a.state_eps);
   const float scale = 0.08838834764831845f / rms;  // 1 / (rms sqrt(d_k)), d_k = 128
-  tile_project<RR>(sS, sU, sV, s_red, scale, P);
+  tile_project<RR>(sS, sU, sV, s_red, scale, P, up ? s_P : nullptr);
   if (tid == 0) {
     const float ell = logf(rms);
     st_coh_f32(a.ell + t, ell);
     if (m == 0) st_coh_u32(a.seq_invalid + b, 0u);
     if (a.logrms) a.logrms[t] = ell;
+    s_el[0] = ell;
+  }
+  if (up) {
+    // f of the sequence's rows for this pair: u_j = P z_j / rms(h_j), ell
+    if (tid < a.n * RC) *(u32x4*)&s_zu[zj * RR + 4 * zk] = zq;
+    if (tid < a.n) s_ru[tid] = rq;
+    __syncthreads();
+    const int Fp = (a.F + 31) & ~31;
+    for (int e = tid; e < a.n * (RR + 1); e += 256) {
+      const int j = e / (RR + 1), i = e - (e / (RR + 1)) * (RR + 1);
+      float v = s_el[0];
+      if (i < RR) {
+        float acc = 0.0f;
+#pragma unroll
+        for (int c = 0; c < RC; ++c)
+          acc = dot4_acc(acc, *(const float4*)&s_P[i * RR + 4 * c], *(const float4*)&s_zu[j * RR + 4 * c]);
+        v = __fmul_rn(acc, s_ru[j]);
+      }
+      st_coh_f32(a.fu + (int64_t)(b * a.n + j) * Fp + m * (RR + 1) + i, v);
+    }
   }
   // further readers of the same state (prepare launches only): the tile
   // stays in LDS, their U and V replace the first reader's.  The next
@@ -693,7 +807,7 @@ __device__ __forceinline__ uint32_t tile_process(const FastArgs& a, int t, TileR
   }
   wait_mem();
   __syncthreads();
-  if (tid == 0) tile_count(a, t);
+  if (tid == 0) tile_count(a, t, up);
   return claim;
 }
 
@@ -712,7 +826,7 @@ __device__ __forceinline__ uint32_t group_tiles(const FastArgs& a, int q) {
 // (More tiles in flight per workgroup only lengthen the memory queues once
 // the whole grid streams: the launch is then bound by bandwidth, and the
 // deeper queues delay the last tiles.)
-template <int RR, bool MULTI>
+template <int RR, bool MULTI, bool UP, int BMZ>
 __device__ __forceinline__ void s_phase(const FastArgs& a, int q, uint32_t zs, uint32_t p0, unsigned char* smem,
                                         const int* s_acc, uint32_t* s_tk) {
   constexpr int NQ = READY_TICKET_GROUPS;
@@ -723,9 +837,9 @@ __device__ __forceinline__ void s_phase(const FastArgs& a, int q, uint32_t zs, u
   uint32_t raw = NO_ITEM;  // thread 0: the position after t0
   if (tid == 0 && t0 >= 0) raw = count_up(tk);
   TileRegs<RR> r0;
-  if (t0 >= 0) tile_issue<RR>(a, t0, r0, s_acc);
+  if (t0 >= 0) tile_issue<RR, UP, BMZ>(a, t0, r0, s_acc);
   while (t0 >= 0) {
-    raw = tile_process<RR, MULTI>(a, t0, r0, smem, s_tk, raw, q, zs, nt, tk, s_acc);
+    raw = tile_process<RR, MULTI, UP, BMZ>(a, t0, r0, smem, s_tk, raw, q, zs, nt, tk, s_acc);
     t0 = (int)*s_tk;
   }
   __syncthreads();  // the LDS area is reused by the next item
@@ -741,7 +855,7 @@ __device__ __forceinline__ void s_phase(const FastArgs& a, int q, uint32_t zs, u
 // ell] per (row, pair), into LDS in bf16 and into `feat` in fp32.
 // Wave w computes a's columns 64 cb + 16 w .. + 15 on the matrix cores, W1
 // rows streaming straight from memory.
-template <int RR, int BMZ, int BMO>
+template <int RR, int BMZ, int BMO, bool UP>
 __device__ __forceinline__ void mlp1_item(const FastArgs& a, int item, unsigned char* smem) {
   const int ncb = cdiv_d(a.Hm, 64);
   const int rb = item / ncb, cb = item - (item / ncb) * ncb;
@@ -772,11 +886,59 @@ __device__ __forceinline__ void mlp1_item(const FastArgs& a, int item, unsigned 
   const float bias = (cv && a.b1) ? Elem<uint16_t>::ld(a.b1, col) : 0.0f;
 
   const int b0 = row0 / a.n, b1 = (row0 + rows - 1) / a.n;
-  if (threadIdx.x == 0)
-    *s_flag = wait_count2(ctr(a.zdone, row0 / BMZ), (uint32_t)cdiv_d(Nz, 64), ctr(a.sdone, rb),
-                          a.n_s > 0 ? (uint32_t)(a.M * (b1 - b0 + 1)) : 0u, a.abort_flag, a.dev_status) ? 1 : 0;
+  // the state-tile count of these rows: tiles in the low half, tiles that
+  // formed their columns of f themselves in the high half (tile_count)
+  const uint32_t want_s = a.n_s > 0 ? (uint32_t)(a.M * (b1 - b0 + 1)) : 0u;
+  if (threadIdx.x == 0) {
+    uint32_t last = 0u;
+    const bool okw = wait_count2(ctr(a.zdone, row0 / BMZ), (uint32_t)cdiv_d(Nz, 64), ctr(a.sdone, rb), 0xffffu,
+                                 want_s, &last, a.abort_flag, a.dev_status);
+    *s_flag = !okw ? 0 : ((UP && want_s > 0u && (last >> 16) >= want_s) ? 2 : 1);
+  }
   __syncthreads();
   const bool ok = *s_flag != 0;
+  const bool f_ready = UP && *s_flag == 2;  // every tile of these rows formed its columns of f
+  const bool want_feat = a.feat != nullptr && cb == 0;
+  float* feat0 = a.feat + (int64_t)row0 * F;
+
+  if (f_ready) {
+    // ---- one trip to memory: the f rows (fp32, rows Fp apart), placed in
+    // LDS in bf16 (and into `feat` in fp32)
+    constexpr int FC = 8;
+    const int cpr = Fp / 4;  // 16-byte chunks per row
+    const int nfc = rows * cpr;
+    u32x4 fv[FC];
+#pragma unroll
+    for (int j = 0; j < FC; ++j) {
+      const int c = tid + 256 * j;
+      fv[j] = ld_coh16_at(c < nfc, a.fu, (uint32_t)(4 * ((row0 + c / cpr) * Fp + 4 * (c - (c / cpr) * cpr))));
+    }
+    // f starts at zero (rows past the end, padding columns); Fs is a multiple of 8
+    for (int e = tid; e < 2 * Fs; e += 256) ((u32x4*)fsh)[e] = u32x4{0u, 0u, 0u, 0u};
+    wait_mem();
+#pragma unroll
+    for (int j = 0; j < FC; ++j) pin(fv[j]);
+    __syncthreads();
+    auto put = [&](int c, u32x4 v) {
+      const int rr = c / cpr, c0 = 4 * (c - (c / cpr) * cpr);
+      const float x[4] = {__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z), __uint_as_float(v.w)};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (c0 + e < F) {
+          fsh[rr * Fs + c0 + e] = f32_to_bf16_rne(x[e]);
+          if (want_feat) feat0[rr * F + c0 + e] = x[e];
+        }
+      }
+    };
+#pragma unroll
+    for (int j = 0; j < FC; ++j) {
+      const int c = tid + 256 * j;
+      if (c < nfc) put(c, fv[j]);
+    }
+    for (int c = tid + 256 * FC; c < nfc; c += 256)
+      put(c, ld_coh16(a.fu, (uint32_t)(4 * ((row0 + c / cpr) * Fp + 4 * (c - (c / cpr) * cpr)))));
+    __syncthreads();
+  } else {
 
   // ---- one trip to memory: z of the rows, the sums of squares of h,
   // the P rows of this thread's first f item and the log-RMS entries it
@@ -834,13 +996,19 @@ __device__ __forceinline__ void mlp1_item(const FastArgs& a, int item, unsigned 
   }
   load_p(tid, 0);
   if constexpr (PRE2) load_p_into(tid + 256, 0, pv2);
-  // the sums of squares of h (threads 0-15, one row each) travel with the
-  // other loads
-  const bool hrow = tid < 16 && tid < rows && ok;
-  float hv[16];
+  // 1 / rms(h) of the rows (threads below `rows`, one row each) travels with
+  // the other loads: at the ranks where the tiles form f, as the value the
+  // query items left in rsv; below, as the K chunks' sums of squares
+  constexpr bool RSV = RR >= READY_UPATH_MIN_R;
+  const bool hrow = tid < rows && ok;
+  float rsl = 0.0f, hv[RSV ? 1 : 16];
+  if constexpr (RSV) {
+    rsl = ld_coh4_at(hrow, a.rsv, (uint32_t)(4 * (row0 + tid)));
+  } else {
 #pragma unroll
-  for (int k = 0; k < 16; ++k)
-    hv[k] = ld_coh4_at(hrow && k < a.ksplit, a.hss, (uint32_t)(4 * (k * a.R + row0 + tid)));
+    for (int k = 0; k < 16; ++k)
+      hv[k] = ld_coh4_at(hrow && k < a.ksplit, a.hss, (uint32_t)(4 * (k * a.R + row0 + tid)));
+  }
   // every load of the trip is in flight before this wait; the pins keep the
   // compiler from sinking any of them into a later trip
   wait_mem();
@@ -856,8 +1024,12 @@ __device__ __forceinline__ void mlp1_item(const FastArgs& a, int item, unsigned 
   }
 #pragma unroll
   for (int j = 0; j < EL; ++j) pin(ev[j]);
+  if constexpr (RSV) {
+    pin(rsl);
+  } else {
 #pragma unroll
-  for (int k = 0; k < 16; ++k) pin(hv[k]);
+    for (int k = 0; k < 16; ++k) pin(hv[k]);
+  }
 #pragma unroll
   for (int j = 0; j < ZC; ++j) {
     const int c = tid + 256 * j;
@@ -865,23 +1037,20 @@ __device__ __forceinline__ void mlp1_item(const FastArgs& a, int item, unsigned 
   }
   for (int c = tid + 256 * ZC; c < nzall; c += 256)
     *(u32x4*)&z_s[4 * c] = (c < nzc && ok) ? ld_coh16(a.zfin, (uint32_t)(4 * (row0 * Nz + 4 * c))) : u32x4{0u, 0u, 0u, 0u};
-  if (tid < 16) {
-    float rs = 0.0f;
+  if constexpr (!RSV) {
     if (hrow) {
       float hs = 0.0f;
 #pragma unroll
       for (int k = 0; k < 16; ++k) hs += k < a.ksplit ? hv[k] : 0.0f;
       for (int k = 16; k < a.ksplit; ++k) hs += ld_coh4(a.hss, (uint32_t)(4 * (k * a.R + row0 + tid)));
-      rs = 1.0f / sqrtf(hs / (float)a.d + a.h_eps);
+      rsl = 1.0f / sqrtf(hs / (float)a.d + a.h_eps);
     }
-    s_rs[tid] = rs;
   }
+  if (tid < 16) s_rs[tid] = hrow ? rsl : 0.0f;
   // f starts at zero (rows past the end, padding columns); Fs is a multiple of 8
   for (int e = tid; e < 2 * Fs; e += 256) ((u32x4*)fsh)[e] = u32x4{0u, 0u, 0u, 0u};
   __syncthreads();
 
-  const bool want_feat = a.feat != nullptr && cb == 0;
-  float* feat0 = a.feat + (int64_t)row0 * F;
   // the ell columns
 #pragma unroll
   for (int j = 0; j < EL; ++j) {
@@ -939,11 +1108,19 @@ __device__ __forceinline__ void mlp1_item(const FastArgs& a, int item, unsigned 
               float acc = 0.0f;
 #pragma unroll
               for (int c = 0; c < CR4; ++c) {
+                const float4 pq = make_float4(__uint_as_float(pv[s][c].x), __uint_as_float(pv[s][c].y),
+                                              __uint_as_float(pv[s][c].z), __uint_as_float(pv[s][c].w));
                 const float4 zq = *(const float4*)&z_s[rr * Nz + mz * RR + 4 * c];
-                acc += __uint_as_float(pv[s][c].x) * zq.x + __uint_as_float(pv[s][c].y) * zq.y +
-                       __uint_as_float(pv[s][c].z) * zq.z + __uint_as_float(pv[s][c].w) * zq.w;
+                if constexpr (RR >= READY_UPATH_MIN_R) {
+                  // the same rounding as the tiles' u path (at these ranks
+                  // one-reader launches take it, and every launch of the
+                  // rank must give the same f)
+                  acc = dot4_acc(acc, pq, zq);
+                } else {
+                  acc += pq.x * zq.x + pq.y * zq.y + pq.z * zq.z + pq.w * zq.w;
+                }
               }
-              const float u = acc * s_rs[rr];
+              const float u = __fmul_rn(acc, s_rs[rr]);
               fsh[rr * Fs + fcol] = f32_to_bf16_rne(u);
               if constexpr (FEAT) {
                 if (r0 + q < rz) feat0[rr * F + fcol] = u;
@@ -957,6 +1134,7 @@ __device__ __forceinline__ void mlp1_item(const FastArgs& a, int item, unsigned 
   if (want_feat) f_loop(std::true_type{});
   else f_loop(std::false_type{});
   __syncthreads();
+  }
 
   // a = act(W1 f + b1) for this wave's 16 columns.  The A operands of a
   // pass are read from LDS first (steps past F read the last step's
@@ -1162,11 +1340,11 @@ __device__ __forceinline__ void mlp2_item(const FastArgs& a, int rb, int cb, uns
 
 // Item k of Z queue x: K chunk ks = x + 8 (k / tiles), then the tile's column
 // block and row block.
-template <int BMZ, int NST>
+template <int BMZ, int NST, bool RSV>
 __device__ __forceinline__ void z_run(const FastArgs& a, int x, uint32_t k, unsigned char* smem) {
   const int nrbz = cdiv_d(a.R, BMZ), ncbz = cdiv_d(a.Nz, 64), tiles = nrbz * ncbz;
   const int ks = x + 8 * ((int)k / tiles), rem = (int)k - ((int)k / tiles) * tiles;
-  z_item<BMZ, NST>(a, ks, rem / nrbz, rem - (rem / nrbz) * nrbz, smem);
+  z_item<BMZ, NST, RSV>(a, ks, rem / nrbz, rem - (rem / nrbz) * nrbz, smem);
 }
 
 // Tile t alone (an orphan group's): gather, statistics and projection, then
@@ -1175,8 +1353,8 @@ template <int RR, bool MULTI>
 __device__ __forceinline__ void s_single(const FastArgs& a, int t, unsigned char* smem, const int* s_acc,
                                          uint32_t* s_tk) {
   TileRegs<RR> r;
-  tile_issue<RR>(a, t, r, s_acc);
-  tile_process<RR, MULTI>(a, t, r, smem, s_tk, NO_ITEM, 0, 0u, 0u, nullptr, s_acc);
+  tile_issue<RR, false, 16>(a, t, r, s_acc);
+  tile_process<RR, MULTI, false, 16>(a, t, r, smem, s_tk, NO_ITEM, 0, 0u, 0u, nullptr, s_acc);
   __syncthreads();
 }
 
@@ -1243,7 +1421,7 @@ __global__ __launch_bounds__(256, (MODE == READY_MODE_PREPARE && RR <= 16) ? 3 :
   const uint32_t zs = z_size(xcc);
   if constexpr (zao) {
     while (p < zs) {
-      z_run<BMZ, NST>(a, xcc, p, smem);
+      z_run<BMZ, NST, RR >= READY_UPATH_MIN_R>(a, xcc, p, smem);
       if (tid == 0) s_tk[0] = count_up(ctr(a.tk, xcc));
       __syncthreads();
       p = s_tk[0];
@@ -1253,7 +1431,7 @@ __global__ __launch_bounds__(256, (MODE == READY_MODE_PREPARE && RR <= 16) ? 3 :
 #pragma unroll
   for (int k = 0; k < APT; ++k) s_acc[tid + 256 * k] = accv[k];
   __syncthreads();
-  if constexpr (has_s) s_phase<RR, multi>(a, xcc, zs, p, smem, s_acc, s_tk);
+  if constexpr (has_s) s_phase<RR, multi, MODE == READY_MODE_FULL && RR >= READY_UPATH_MIN_R, BMZ>(a, xcc, zs, p, smem, s_acc, s_tk);
 
   if constexpr (zao) {
     // before the first A item: the arrival flags of the XCDs, read in the
@@ -1267,7 +1445,7 @@ __global__ __launch_bounds__(256, (MODE == READY_MODE_PREPARE && RR <= 16) ? 3 :
       const uint32_t zsx = z_size(x), qx = zsx + (has_s ? group_tiles(a, x) : 0u);
       for (uint32_t i; (i = claim_one(a.tk, x, qx, s_tk)) != NO_ITEM;) {
         if (i < zsx) {
-          z_run<BMZ, NST>(a, x, i, smem);
+          z_run<BMZ, NST, RR >= READY_UPATH_MIN_R>(a, x, i, smem);
         } else if constexpr (has_s) {
           s_single<RR, multi>(a, x + READY_TICKET_GROUPS * (int)(i - zsx), smem, s_acc, s_tk);
         }
@@ -1285,7 +1463,7 @@ __global__ __launch_bounds__(256, (MODE == READY_MODE_PREPARE && RR <= 16) ? 3 :
         i = claim_one(a.aq, (int)x, a_size((int)x), s_tk);
         continue;
       }
-      mlp1_item<RR, BMZ, BMO>(a, (int)x + 8 * (int)i, smem);
+      mlp1_item<RR, BMZ, BMO, MODE == READY_MODE_FULL && RR >= READY_UPATH_MIN_R>(a, (int)x + 8 * (int)i, smem);
       i = claim_one(a.aq, (int)x, na, s_tk);
     }
     // O items likewise (O item (rb, cb) in queue cb % 8)

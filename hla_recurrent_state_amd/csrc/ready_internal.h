@@ -71,7 +71,9 @@ struct FastArgs {
   int32_t* dev_status;             // or null
   float* zpart;                    // [ksplit][R][Nz]
   float* hss;                      // [ksplit][R]
+  float* rsv;                       // [R]: 1 / rms(h) per row (from the items completing z column block 0)
   float* zfin;                     // [R][Nz]: z summed over the K chunks (before 1 / rms(h))
+  float* fu;                       // [R][Fp]: f rows formed by the state tiles (Fp = F rounded up to 32)
   float* pmat;                     // [B M][r][r]
   float* ell;                      // [B M]
   uint16_t* abuf;                  // [R][Hm] bf16
@@ -133,6 +135,9 @@ struct FastArgs {
 #define READY_ZCHUNK_LARGE 640
 #define READY_OCOLS 128
 #define READY_ABM 8                // rows of an A item (and of a state-tile count)
+#ifndef READY_UPATH_MIN_R
+#define READY_UPATH_MIN_R 24        // the state tiles form f themselves from this rank on
+#endif
 #define READY_TICKET_GROUPS 8     // state-tile ticket counters, one per XCD
 #define READY_ACC_LDS 1024        // accept indices staged in LDS
 
@@ -268,7 +273,7 @@ inline size_t ready_reader_lds(int r, int F, int Nz, int small) {
   const int NB = (r + 15) / 16;
   const size_t z_bytes = (size_t)(BMZ + 64) * 256 + 16;
   const size_t s_bytes = (size_t)READY_TILE_ELEMS * 2 + (size_t)r * (READY_TILE + 8) * 2 + (size_t)READY_TILE * r * 2 +
-                         4 * (4 * NB * r * 16 + 4);
+                         4 * (4 * NB * r * 16 + 4) + 4 * ((size_t)r * r + 16 * (size_t)r + 16 + 4);
   const int Fs = ((F + 31) & ~31) + 8;
   const size_t a_bytes = (size_t)READY_ABM * Nz * 4 + (size_t)16 * Fs * 2 + 4 * 16 + 16;
   const size_t sa = (size_t)BMO * (256 + 8) * 2, so = (size_t)BMO * (READY_OCOLS + 4) * 4;
