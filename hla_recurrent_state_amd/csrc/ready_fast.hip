@@ -1338,13 +1338,18 @@ __device__ __forceinline__ void mlp2_item(const FastArgs& a, int rb, int cb, uns
 
 // ---------------------------------------------------------------- k_reader
 
-// Item k of Z queue x: K chunk ks = x + 8 (k / tiles), then the tile's column
-// block and row block.
+// Item k of Z queue x.  Queue x holds the K chunks ks = x, x + 8, ... of every
+// (row block, column block) tile, row blocks outermost: the first rows' z is
+// complete (every column block, every K chunk) before any later row block's
+// item is taken, so the state tiles of the first sequences, which wait for
+// their rows' z, can start while the Z phase is still running.
 template <int BMZ, int NST, bool RSV>
 __device__ __forceinline__ void z_run(const FastArgs& a, int x, uint32_t k, unsigned char* smem) {
-  const int nrbz = cdiv_d(a.R, BMZ), ncbz = cdiv_d(a.Nz, 64), tiles = nrbz * ncbz;
-  const int ks = x + 8 * ((int)k / tiles), rem = (int)k - ((int)k / tiles) * tiles;
-  z_item<BMZ, NST, RSV>(a, ks, rem / nrbz, rem - (rem / nrbz) * nrbz, smem);
+  const int ncbz = cdiv_d(a.Nz, 64), nk = (a.ksplit - x + 7) >> 3;
+  const int per_rb = nk * ncbz;
+  const int rb = (int)k / per_rb, rem = (int)k - rb * per_rb;
+  const int kk = rem / ncbz, cb = rem - kk * ncbz;
+  z_item<BMZ, NST, RSV>(a, x + 8 * kk, cb, rb, smem);
 }
 
 // Tile t alone (an orphan group's): gather, statistics and projection, then
