@@ -615,7 +615,8 @@ def run_config(name, args, hip, torch, R, synth, seed=0, cfg=None, random_states
     # kernel (stage 1), so stage 0 "starts" after stage 1 ends; the general path
     # runs stage 0 first
     fast = hip.ms(evs[0][3], evs[0][0]) >= 0.0
-    stage_names = ("k_reader",) if fast else ("query_gemm", "state_kernel", "mlp1", "mlp2_residual")
+    kname = "k_reader_f32" if cfg.state_dtype == "f32" else "k_reader"
+    stage_names = (kname,) if fast else ("query_gemm", "state_kernel", "mlp1", "mlp2_residual")
     stage_idx = (1,) if fast else (0, 1, 2, 3)
     stages = {nm: round(med[k], 2) for nm, k in zip(stage_names, stage_idx)}
     for row in evs:
@@ -635,7 +636,7 @@ def run_config(name, args, hip, torch, R, synth, seed=0, cfg=None, random_states
     del flush
     p50 = pct(cold, 50)
     res = {
-        "path": "k_reader (single persistent kernel)" if fast else "general (4 kernels)",
+        "path": kname + " (single persistent kernel)" if fast else "general (4 kernels)",
         "states": "seeded normal / 128, drawn on the device" if random_states else "fp32 gated delta rule",
         "B": cfg.B, "M": cfg.M, "r": cfg.r, "d": cfg.d, "state_dtype": cfg.state_dtype,
         "algorithmic_bytes": alg,

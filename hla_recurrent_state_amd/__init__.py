@@ -5,7 +5,7 @@ kernels of libready.so.  If the library is missing, loading raises
 ReadyError -- there is no fallback path.
 
 Low-level names mirror the C functions (readyPlanCreate, readyWorkspaceSize,
-readyStateReader, readyGather, readyPrepSize, readyStatePrepare, readyStateApply,
+readyPlanLaunches, readyStateReader, readyGather, readyPrepSize, readyStatePrepare, readyStateApply,
 readyVerifyStates, readyPlanDestroy, readyStatusString, readyVersion) and the C structs (readyShape, readyStates, readyWeights,
 readyOutputs, readyVerifyBuffer), plus readyStateReaderStatic, the form with
 no workspace argument for callers that cannot allocate.  StateReader and verify_states wrap them for
@@ -53,7 +53,7 @@ READY_PATH_UNFUSED = 1
 PATHS = {"fused": READY_PATH_FUSED, "unfused": READY_PATH_UNFUSED}
 
 # Every symbol include/ready.h declares.
-EXPORTS = ("readyPlanCreate", "readyPlanDestroy", "readyWorkspaceSize", "readyWorkspaceInit",
+EXPORTS = ("readyPlanCreate", "readyPlanDestroy", "readyWorkspaceSize", "readyPlanLaunches", "readyWorkspaceInit",
            "readyStateReader", "readyStateReaderProfiled", "readyStateReaderStatic", "readyGather", "readyPrepSize", "readyStatePrepare",
            "readyStateApply", "readyVerifyStates", "readyStatusString", "readyVersion")
 READY_STAGES = 4
@@ -109,6 +109,8 @@ def load():
     lib.readyPlanDestroy.restype = ctypes.c_int
     lib.readyWorkspaceSize.argtypes = [ctypes.c_void_p, P(ctypes.c_size_t)]
     lib.readyWorkspaceSize.restype = ctypes.c_int
+    lib.readyPlanLaunches.argtypes = [ctypes.c_void_p, P(ctypes.c_int32)]
+    lib.readyPlanLaunches.restype = ctypes.c_int
     lib.readyWorkspaceInit.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
     lib.readyWorkspaceInit.restype = ctypes.c_int
     lib.readyStateReader.argtypes = [ctypes.c_void_p, P(readyStates), ctypes.c_void_p, ctypes.c_void_p,
@@ -171,6 +173,13 @@ def readyWorkspaceSize(plan):
     """Returns (status, bytes)."""
     n = ctypes.c_size_t()
     st = load().readyWorkspaceSize(plan, ctypes.byref(n))
+    return st, n.value
+
+
+def readyPlanLaunches(plan):
+    """Returns (status, kernel launches per readyStateReader call)."""
+    n = ctypes.c_int32()
+    st = load().readyPlanLaunches(plan, ctypes.byref(n))
     return st, n.value
 
 
@@ -294,6 +303,9 @@ class StateReader:
         st, self.workspace_bytes = readyWorkspaceSize(self.plan)
         if st != READY_OK:
             raise ReadyError(st, "readyWorkspaceSize")
+        st, self.launches = readyPlanLaunches(self.plan)
+        if st != READY_OK:
+            raise ReadyError(st, "readyPlanLaunches")
         self._ws = {}
 
     def close(self):

@@ -41,6 +41,7 @@ struct readyPlan {
   int32_t slot[READY_MAX_LSEL];
   int M, F, R, Mz, Nz;
   int fast;
+  int f32;       // fp32 single-launch path (k_reader_f32)
   int small;     // fast path: at most 16 rows (16-row tiles; 64 otherwise)
   int n_z, n_s, n_a, n_o, n_counters;
   int c_zcnt, c_zdone, c_sdone, c_adone, c_tk, c_aq, c_oq, c_arx;  // first counter slot of each group
@@ -155,6 +156,20 @@ readyStatus readyPlanCreate(const readyShape* shape, const int32_t* layer_ids, r
   }
   p->lds = fits ? ready_reader_lds(s.r, p->F, p->Nz, p->small) : 0;
   p->fast = (fits && p->lds <= 80 * 1024 && s.path == READY_PATH_FUSED) ? 1 : 0;  // two workgroups per CU
+  {
+    // fp32 states, activations and weights at serving sizes: k_reader_f32
+    // (its byte offsets into W_q, W1, W2, h and the partial sums of z are
+    // 32-bit)
+    const bool allf = s.state_dtype == READY_F32 && s.act_dtype == READY_F32 && s.weight_dtype == READY_F32;
+    const int64_t R = p->R, nks = cdiv(s.d, READY_F32_KC);
+    const bool ok = allf && s.path == READY_PATH_FUSED && R >= 1 && R <= 16 && (s.r == 8 || s.r == 16) &&
+                    s.Hm % 4 == 0 && s.Hm <= READY_F32_MAX_HM && p->F <= READY_F32_MAX_F &&
+                    R * p->Nz <= READY_F32_MAX_RNZ && (int64_t)s.B * p->M * s.r <= READY_F32_MAX_UNITS &&
+                    (int64_t)p->Nz * s.d * 4 < (1LL << 31) && nks * R * p->Nz * 4 < (1LL << 31) &&
+                    (int64_t)s.d * s.Hm * 4 < (1LL << 31) && (int64_t)s.Hm * p->F * 4 < (1LL << 31) &&
+                    R * s.d * 4 < (1LL << 31) && ready_f32_lds(s.r, p->R, p->Nz, p->F, s.Hm) <= READY_F32_MAX_LDS;
+    p->f32 = ok ? 1 : 0;
+  }
 
   if (p->fast) {
     // work items of k_reader
@@ -183,6 +198,29 @@ readyStatus readyPlanCreate(const readyShape* shape, const int32_t* layer_ids, r
     p->c_oq = p->c_aq + 8;
     p->c_arx = p->c_oq + 8;
     p->n_counters = (int)(READY_CTR_STRIDE * (p->c_arx + 8));
+  } else if (p->f32) {
+    // work items of k_reader_f32, and its counters: magic, abort,
+    // READY_DONE_GROUPS + 1 done counts, 8 claim counters each of the S and Z
+    // items, of the A items and of the O items, 8 arrival flags, the column
+    // blocks of z done, the S items done, the A items done, the Z items done
+    // per column block
+    const int64_t nks = cdiv(s.d, READY_F32_KC), ncz = cdiv(p->Nz, READY_F32_ZC);
+    p->gz.ksplit = (int)nks;
+    p->gz.kchunk = READY_F32_KC;
+    p->n_s = s.B * p->M;
+    p->n_z = (int)(ncz * nks);
+    p->n_a = (int)cdiv(s.Hm, READY_F32_AC);
+    p->n_o = (int)cdiv(s.d, READY_F32_OC);
+    p->lds = ready_f32_lds(s.r, p->R, p->Nz, p->F, s.Hm);
+    p->c_tk = 2 + READY_DONE_GROUPS + 1;
+    p->c_aq = p->c_tk + 8;
+    p->c_oq = p->c_aq + 8;
+    p->c_arx = p->c_oq + 8;
+    p->c_zdone = p->c_arx + 8;
+    p->c_sdone = p->c_zdone + 1;
+    p->c_adone = p->c_sdone + 1;
+    p->c_zcnt = p->c_adone + 1;
+    p->n_counters = (int)(READY_CTR_STRIDE * (p->c_zcnt + ncz));
   } else {
     // query GEMM: matrix cores for bf16 h and weights; K split so that about
     // 256 (matrix cores) or 512 (VALU) workgroups run
@@ -241,18 +279,20 @@ readyStatus readyPlanCreate(const readyShape* shape, const int32_t* layer_ids, r
   const size_t ks = (size_t)p->gz.ksplit;
   size_t off = 0;
   p->off_zpart = off; off = align_up(off + 4 * ks * R * p->Nz, 256);
-  p->off_hss = off;   off = align_up(off + 4 * ks * R, 256);
+  p->off_hss = off;   off = align_up(off + 4 * ks * R * (p->f32 ? (size_t)cdiv(p->Nz, READY_F32_ZC) : 1), 256);
   p->off_rsv = off;   off = align_up(off + (p->fast ? 4 * R : 0), 256);
   // f on the general path, z summed over the K chunks on the fast path
-  p->off_f = off;     off = align_up(off + 4 * R * (p->fast ? p->Nz : p->F), 256);
-  p->off_fu = off;    off = align_up(off + (p->fast ? 4 * R * (size_t)((p->F + 31) & ~31) : 0), 256);
+  p->off_f = off;     off = align_up(off + (p->f32 ? 0 : 4 * R * (p->fast ? p->Nz : p->F)), 256);
+  p->off_fu = off;
+  off = align_up(off + (p->fast ? 4 * R * (size_t)((p->F + 31) & ~31) : p->f32 ? 4 * R * (size_t)((p->F + 63) & ~63) : 0),
+                 256);
   // a: bf16 on the fast path, fp32 otherwise
   p->off_a = off;     off = align_up(off + (p->fast ? 2 : 4) * R * s.Hm, 256);
   // K-split partial sums of the first MLP layer (k_gemm_mm with ksplit > 1)
   p->off_g1p = off;   off = align_up(off + (p->g1.ksplit > 1 ? 4 * (size_t)p->g1.ksplit * R * s.Hm : 0), 256);
   p->off_flags = off; off = align_up(off + 4 * (size_t)std::max(s.B, 1), 256);
-  p->off_pmat = off;  off = align_up(off + (p->fast ? 4 * BM * s.r * s.r : 0), 256);
-  p->off_ell = off;   off = align_up(off + (p->fast ? 4 * BM : 0), 256);
+  p->off_pmat = off;  off = align_up(off + (p->fast || p->f32 ? 4 * BM * s.r * s.r : 0), 256);
+  p->off_ell = off;   off = align_up(off + (p->fast || p->f32 ? 4 * BM : 0), 256);
   p->off_ctr = off;   off = align_up(off + 4 * (size_t)p->n_counters, 256);
   p->ws_bytes = off;
   *plan = p;
@@ -267,6 +307,13 @@ readyStatus readyPlanDestroy(readyPlan* plan) {
 readyStatus readyWorkspaceSize(const readyPlan* plan, size_t* bytes) {
   if (!plan || !bytes) return READY_ERR_NULL_POINTER;
   *bytes = plan->ws_bytes;
+  return READY_OK;
+}
+
+readyStatus readyPlanLaunches(const readyPlan* plan, int32_t* launches) {
+  if (!plan || !launches) return READY_ERR_NULL_POINTER;
+  if (plan->fast || plan->f32) *launches = 1;
+  else *launches = (plan->g1.big && plan->g1.ksplit > 1) ? 5 : 4;
   return READY_OK;
 }
 
@@ -470,6 +517,64 @@ readyStatus ready_run_reader(const readyPlan* plan, const readyStates* states, c
     return launch_fast(plan, a, strm, events);
   }
 
+  if (plan->f32) {
+    F32Args a;
+    memset(&a, 0, sizeof(a));
+    a.states = (const float*)states->base;
+    a.sb = states->stride_b; a.sp = states->stride_p; a.sl = states->stride_l; a.sh = states->stride_h;
+    a.accept_idx = accept_idx;
+    for (int l = 0; l < s.L_sel; ++l) a.slot[l] = plan->slot[l];
+    a.h = (const float*)h;
+    a.wq = (const float*)w->wq; a.u = (const float*)w->u; a.v = (const float*)w->v;
+    a.gamma = (const float*)w->h_gamma;
+    a.w1 = (const float*)w->w1; a.b1 = (const float*)w->b1;
+    a.w2 = (const float*)w->w2; a.b2 = (const float*)w->b2;
+    a.gathered = (float*)o->gathered; a.out = (float*)o->out;
+    a.logrms = o->logrms; a.delta = o->delta; a.feat = o->feat; a.dev_status = o->dev_status;
+    a.zpart = zpart; a.hss = hss;
+    a.fbuf = (float*)(wsb + plan->off_fu);
+    a.pmat = (float*)(wsb + plan->off_pmat);
+    a.ell = (float*)(wsb + plan->off_ell);
+    a.abuf = abuf;
+    a.seq_invalid = (uint32_t*)flags;
+    uint32_t* ctr = view.ctr;
+    a.counters = ctr; a.n_counters = plan->n_counters; a.magic = view.magic;
+    a.abort_flag = ctr + READY_CTR_STRIDE;
+    a.done = ctr + 2 * READY_CTR_STRIDE;
+    a.lq = ctr + READY_CTR_STRIDE * plan->c_tk;
+    a.aq = ctr + READY_CTR_STRIDE * plan->c_aq;
+    a.oq = ctr + READY_CTR_STRIDE * plan->c_oq;
+    a.arr_x = ctr + READY_CTR_STRIDE * plan->c_arx;
+    a.zdone = ctr + READY_CTR_STRIDE * plan->c_zdone;
+    a.sdone = ctr + READY_CTR_STRIDE * plan->c_sdone;
+    a.adone = ctr + READY_CTR_STRIDE * plan->c_adone;
+    a.zcnt = ctr + READY_CTR_STRIDE * plan->c_zcnt;
+    a.n_s = plan->n_s; a.n_z = plan->n_z; a.n_a = plan->n_a; a.n_o = plan->n_o;
+    a.nks = plan->gz.ksplit; a.ncz = (int)cdiv(plan->Nz, READY_F32_ZC);
+    {
+      // z of all rows in at most 256 chunks of 16 bytes, each summed by
+      // 256 / nq threads over at most READY_F32_ZSUM_LOADS K chunks apiece
+      const int nq = plan->R * plan->Nz / 4;
+      a.zsum_a = (nq <= 256 && a.nks <= 64 && a.nks <= READY_F32_ZSUM_LOADS * (256 / nq)) ? 1 : 0;
+    }
+    a.B = s.B; a.P = s.P; a.n = s.n; a.M = plan->M; a.H = s.H; a.r = s.r; a.d = s.d; a.F = plan->F;
+    a.Hm = s.Hm; a.R = plan->R; a.Nz = plan->Nz; a.shared = s.shared_params; a.act = s.act;
+    a.state_eps = s.state_eps; a.h_eps = s.h_eps;
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+      return READY_ERR_HIP;
+    const int64_t items = (int64_t)a.n_s + a.n_z + a.n_a + a.n_o;
+    const int grid = (int)std::min<int64_t>(items, 2 * (int64_t)cus);
+    if (ready_launch_reader_f32(a, grid, plan->lds, strm, stage_events(events, 1)) != hipSuccess) return READY_ERR_HIP;
+    // the other stages run inside the same kernel: their marks (if any) are
+    // recorded together after it
+    for (int i = 0; events && i < 2 * READY_STAGES; ++i)
+      if ((i < 2 || i > 3) && events[i] && hipEventRecord((hipEvent_t)events[i], strm) != hipSuccess)
+        return READY_ERR_HIP;
+    return READY_OK;
+  }
+
   const int wvw = (int)(16 / ws);
   // 0. z partials and sums of squares of h
   {
@@ -626,7 +731,7 @@ readyStatus readyWorkspaceInit(const readyPlan* plan, void* workspace, size_t wo
   if (!plan || !workspace) return READY_ERR_NULL_POINTER;
   if (((uintptr_t)workspace & 255u) != 0) return READY_ERR_MISALIGNED;
   if (workspace_bytes < plan->ws_bytes) return READY_ERR_WORKSPACE_TOO_SMALL;
-  if (!plan->fast || plan->n_counters == 0) return READY_OK;  // the general path keeps no counters
+  if ((!plan->fast && !plan->f32) || plan->n_counters == 0) return READY_OK;  // the general path keeps no counters
   uint32_t* ctr = (uint32_t*)((char*)workspace + plan->off_ctr);
   if (ready_launch_ws_init(ctr, plan->n_counters, READY_WS_MAGIC ^ (uint32_t)plan->n_counters,
                            (hipStream_t)stream) != hipSuccess)

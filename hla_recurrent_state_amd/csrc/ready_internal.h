@@ -116,6 +116,91 @@ struct FastArgs {
   const uint16_t* v_inj[READY_MAX_INJ];
 };
 
+// fp32 single-launch path (fp32 states, activations and weights; at most 16
+// rows, r <= 16): one persistent launch, k_reader_f32, whose workgroups claim
+// S, Z, A and O items (see ready_f32.hip) from one counter
+struct F32Args {
+  const float* states;
+  int64_t sb, sp, sl, sh;          // element strides of the verify buffer
+  const int32_t* accept_idx;       // [B], B <= 16
+  int32_t slot[READY_MAX_LSEL];
+  const float* h;                  // [R][d]
+  const float* wq;                 // [Nz][d]
+  const float* u;                  // [Mz][r][128]
+  const float* v;                  // [Mz][128][r]
+  const float* gamma;              // [d] or null
+  const float* w1;                 // [Hm][F]
+  const float* b1;                 // [Hm] or null
+  const float* w2;                 // [d][Hm]
+  const float* b2;                 // [d] or null
+  float* gathered;                 // [B][M][128][128]
+  float* out;                      // [R][d] (may be h)
+  float* logrms;                   // [B][M] or null
+  float* delta;                    // [R][d] or null
+  float* feat;                     // [R][F] or null
+  int32_t* dev_status;             // or null
+  float* zpart;                    // [nks][R][Nz]: partial sums of W_q (gamma h) per K chunk
+  float* hss;                      // [ncz][nks][R]: partial sums of h^2 (one copy per column block of z)
+  float* fbuf;                     // [R][Fp]: f rows (Fp = F rounded up to 64), formed with z's sums
+  float* pmat;                     // [B M][r][r]
+  float* ell;                      // [B M]
+  float* abuf;                     // [R][Hm]
+  uint32_t* seq_invalid;           // [B]
+  // Counters, READY_CTR_STRIDE words apart: [0] the workspace magic, [1]
+  // abort flag, [2 .. 2 + READY_DONE_GROUPS] workgroups finished per group
+  // and overall, then per XCD the claim counters of the S and Z items, of the
+  // A items and of the O items and the arrival flags, then the finished
+  // column blocks of z, the S items done, the A items done and the Z items
+  // done per column block.  The last workgroup to finish clears all of them
+  // but the magic.
+  uint32_t* counters;
+  int n_counters;                  // words
+  uint32_t magic;
+  uint32_t* abort_flag;
+  uint32_t* done;
+  uint32_t* lq;                    // [8]: S and Z items claimed per XCD queue
+  uint32_t* aq;                    // [8]: A items claimed per XCD queue
+  uint32_t* oq;                    // [8]: O items claimed per XCD queue
+  uint32_t* arr_x;                 // [8]: a workgroup of the launch has run on XCD x
+  uint32_t* zdone;
+  uint32_t* sdone;
+  uint32_t* adone;
+  uint32_t* zcnt;                  // [ncz]
+  int n_s, n_z, n_a, n_o;          // work items per kind
+  int nks, ncz;                    // K chunks and column blocks of z
+  int zsum_a;                      // the A items sum z's K chunks and form f (no summing Z item); zdone
+                                   // then counts Z items, else the column blocks of z summed and f formed
+  int B, P, n, M, H, r, d, F, Hm, R, Nz, shared, act;
+  float state_eps, h_eps;
+};
+#define READY_F32_KC 256           // K chunk of a query item (4 waves x 64)
+#define READY_F32_ZC 64            // columns of z per query item (one per lane)
+#define READY_F32_AC 16            // columns of a per A item (4 waves x 4)
+#define READY_F32_OC 32            // columns of out per O item (2 passes of 4 waves x 4)
+#define READY_F32_MAX_F 1024       // W1 row values a lane holds: 16 x 4
+#define READY_F32_MAX_HM 512       // W2 row values a lane holds per pass: 8 x 4
+#define READY_F32_MAX_RNZ 8192     // query sums of all rows staged in LDS
+#define READY_F32_MAX_UNITS 1024   // rows of P (B M r) one A item reads, 4 per thread
+#define READY_F32_MAX_LDS (64 * 1024)
+// the A items sum z's K chunks themselves when z has at most 256 chunks of
+// 16 bytes and every thread sums at most READY_F32_ZSUM_LOADS of them
+#define READY_F32_ZSUM_LOADS 8
+// dynamic LDS bytes of a k_reader_f32 launch: the largest of its item kinds'
+// areas (rows R, rows rounded up to the 8 or 16 the kernel is built for)
+inline size_t ready_f32_lds(int r, int R, int Nz, int F, int Hm) {
+  const size_t RB = R <= 8 ? 8 : 16;
+  const size_t s_f = (size_t)r * (READY_TILE + 4) + (size_t)READY_TILE * r + 4 * 8 * (READY_TILE + 4) + 4;
+  const size_t z_f = RB * READY_F32_KC + 4 * RB * 64;
+  const size_t fa = RB * (((size_t)F + 63) & ~(size_t)63);
+  const size_t a_f = (((size_t)R * Nz + 3) & ~(size_t)3) + (fa > 1040 ? fa : 1040);
+  const size_t o_f = RB * (((size_t)Hm + 63) & ~(size_t)63) + 16;
+  size_t m = s_f;
+  if (z_f > m) m = z_f;
+  if (a_f > m) m = a_f;
+  if (o_f > m) m = o_f;
+  return 4 * m;
+}
+
 #define READY_FAST_MAX_F 1536      // f rows of 16 positions staged in LDS
 #define READY_FAST_MAX_NZ 1024     // query sums of 16 positions staged in LDS
 #define READY_CTR_STRIDE 32        // counters sit 128 bytes apart
@@ -233,6 +318,9 @@ READY_HIDDEN hipError_t ready_launch_gemm_mfma(const GemmArgs& g, int x_dt, int 
                                                dim3 grid, hipStream_t s, StageEvents ev);
 // fast path; small: at most 16 rows (16-row tiles), else the large tiles
 READY_HIDDEN hipError_t ready_launch_reader(const FastArgs& a, int small, int grid, hipStream_t s, StageEvents ev);
+// fp32 single-launch path: `grid` workgroups (two per CU at most)
+READY_HIDDEN hipError_t ready_launch_reader_f32(const F32Args& a, int grid, size_t lds, hipStream_t s,
+                                                StageEvents ev);
 READY_HIDDEN hipError_t ready_launch_ws_init(uint32_t* counters, int n_counters, uint32_t magic, hipStream_t s);
 
 // Where a call's scratch lives: `data` holds every scratch array at the plan's

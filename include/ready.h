@@ -191,6 +191,17 @@ readyStatus readyPlanDestroy(readyPlan* plan);
 readyStatus readyWorkspaceSize(const readyPlan* plan, size_t* bytes);
 
 /*
+ * Kernel launches one readyStateReader call makes with this plan, into
+ * *launches: 1 where the whole reader runs as one persistent kernel (bf16
+ * states, activations and weights with r <= 32; fp32 throughout with at most
+ * 16 rows B n and r <= 16, the serving shapes), 4 or 5 on the general path
+ * (query GEMM, per-state kernel, MLP layer 1, whose K-split form adds a
+ * reduction, MLP layer 2 with the residual).  Host only.  Returns
+ * READY_ERR_NULL_POINTER for a null argument.
+ */
+readyStatus readyPlanLaunches(const readyPlan* plan, int32_t* launches);
+
+/*
  * Prepare a workspace for use with `plan`: enqueue on `stream` a small kernel
  * that clears the synchronisation counters the state reader keeps in the
  * workspace and stamps it for this plan.  Call it once after allocating the

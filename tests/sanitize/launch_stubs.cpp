@@ -20,5 +20,6 @@ hipError_t ready_launch_gemm_mfma(const GemmArgs&, int, int, int, int, dim3, hip
   return hipErrorNoDevice;
 }
 hipError_t ready_launch_reader(const FastArgs&, int, int, hipStream_t, StageEvents) { return hipErrorNoDevice; }
+hipError_t ready_launch_reader_f32(const F32Args&, int, size_t, hipStream_t, StageEvents) { return hipErrorNoDevice; }
 hipError_t ready_launch_ws_init(uint32_t*, int, uint32_t, hipStream_t) { return hipErrorNoDevice; }
 int ready_reader_per_cu(int, int, size_t, int) { return 0; }

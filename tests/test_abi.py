@@ -265,8 +265,10 @@ def test_workspace_init_validation():
     assert R.readyWorkspaceInit(plan, (1 << 40) + 16, n, None) == R.READY_ERR_MISALIGNED
     assert R.readyWorkspaceInit(plan, 1 << 40, n - 1, None) == R.READY_ERR_WORKSPACE_TOO_SMALL
     R.readyPlanDestroy(plan)
-    # the general path keeps no counters: nothing to prepare, nothing launched
-    st, plan = R.readyPlanCreate(_shape(state_dtype="f32", act_dtype="f32", weight_dtype="f32"), [0, 1])
+    # the general path (fp32 at 21 rows) keeps no counters: nothing to
+    # prepare, nothing launched
+    st, plan = R.readyPlanCreate(_shape(B=3, state_dtype="f32", act_dtype="f32", weight_dtype="f32"), [0, 1])
+    assert R.readyPlanLaunches(plan) == (R.READY_OK, 4)
     _, n = R.readyWorkspaceSize(plan)
     assert R.readyWorkspaceInit(plan, 1 << 40, n, None) == R.READY_OK
     R.readyPlanDestroy(plan)
@@ -450,3 +452,35 @@ def test_static_entry_rejects_plans_beyond_the_array():
     assert R.load().readyStateReaderStatic(plan, None, None, None, None, None, None) == R.READY_ERR_NULL_POINTER
     R.readyPlanDestroy(plan)
     assert R.readyStatusString(R.READY_ERR_STATIC_SCRATCH_TOO_SMALL) == "READY_ERR_STATIC_SCRATCH_TOO_SMALL"
+
+
+@pytest.mark.parametrize("kw,launches", [
+    (dict(), 1),                                                    # bf16, r = 8: k_reader
+    (dict(r=32), 1),
+    (dict(r=64), 4),                                                # bf16 general path
+    (dict(path="unfused"), 4),
+    (dict(B=1, state_dtype="f32", act_dtype="f32", weight_dtype="f32"), 1),   # k_reader_f32
+    (dict(B=2, n=8, r=16, state_dtype="f32", act_dtype="f32", weight_dtype="f32"), 1),
+    (dict(B=1, state_dtype="f32", act_dtype="f32", weight_dtype="f32", path="unfused"), 4),
+    (dict(B=3, state_dtype="f32", act_dtype="f32", weight_dtype="f32"), 4),   # 21 rows
+    (dict(B=1, r=24, state_dtype="f32", act_dtype="f32", weight_dtype="f32"), 4),
+    (dict(B=1, Hm=66, state_dtype="f32", act_dtype="f32", weight_dtype="f32"), 4),
+    (dict(B=1, state_dtype="f32", act_dtype="f32", weight_dtype="bf16"), 4),
+])
+def test_plan_launch_count(kw, launches):
+    """Which shapes run as one kernel: all-bf16 with r <= 32, and all-fp32 at
+    most 16 rows with r <= 16 and Hm a multiple of 4; the rest as the
+    general path's four launches."""
+    _lib()
+    st, plan = R.readyPlanCreate(_shape(**kw), [0, 1])
+    assert st == R.READY_OK
+    assert R.readyPlanLaunches(plan) == (R.READY_OK, launches)
+    R.readyPlanDestroy(plan)
+
+
+def test_plan_launch_count_null_arguments():
+    lib = _lib()
+    st, plan = R.readyPlanCreate(_shape(), [0, 1])
+    assert lib.readyPlanLaunches(None, None) == R.READY_ERR_NULL_POINTER
+    assert lib.readyPlanLaunches(plan, None) == R.READY_ERR_NULL_POINTER
+    R.readyPlanDestroy(plan)
