@@ -200,8 +200,9 @@ readyStatus readyPlanCreate(const readyShape* shape, const int32_t* layer_ids, r
     p->n_counters = (int)(READY_CTR_STRIDE * (p->c_arx + 8));
   } else if (p->f32) {
     // work items of k_reader_f32, and its counters: magic, abort,
-    // READY_DONE_GROUPS + 1 done counts, 8 claim counters each of the S and Z
-    // items, of the A items and of the O items, 8 arrival flags, the column
+    // READY_DONE_GROUPS + 1 done counts, READY_F32_QUEUES claim counters each
+    // of the S and Z items, of the A items and of the O items and as many
+    // arrival flags, the column
     // blocks of z done, the S items done, the A items done, the Z items done
     // per column block
     const int64_t nks = cdiv(s.d, READY_F32_KC), ncz = cdiv(p->Nz, READY_F32_ZC);
@@ -213,10 +214,10 @@ readyStatus readyPlanCreate(const readyShape* shape, const int32_t* layer_ids, r
     p->n_o = (int)cdiv(s.d, READY_F32_OC);
     p->lds = ready_f32_lds(s.r, p->R, p->Nz, p->F, s.Hm);
     p->c_tk = 2 + READY_DONE_GROUPS + 1;
-    p->c_aq = p->c_tk + 8;
-    p->c_oq = p->c_aq + 8;
-    p->c_arx = p->c_oq + 8;
-    p->c_zdone = p->c_arx + 8;
+    p->c_aq = p->c_tk + READY_F32_QUEUES;
+    p->c_oq = p->c_aq + READY_F32_QUEUES;
+    p->c_arx = p->c_oq + READY_F32_QUEUES;
+    p->c_zdone = p->c_arx + READY_F32_QUEUES;
     p->c_sdone = p->c_zdone + 1;
     p->c_adone = p->c_sdone + 1;
     p->c_zcnt = p->c_adone + 1;
@@ -564,8 +565,10 @@ readyStatus ready_run_reader(const readyPlan* plan, const readyStates* states, c
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
       return READY_ERR_HIP;
-    const int64_t items = (int64_t)a.n_s + a.n_z + a.n_a + a.n_o;
-    const int grid = (int)std::min<int64_t>(items, 2 * (int64_t)cus);
+    // two workgroups per CU whatever the item count: each item then finds a
+    // workgroup that has not run another first, and the spare ones find
+    // their queues empty and finish
+    const int grid = (int)(2 * (int64_t)cus);
     if (ready_launch_reader_f32(a, grid, plan->lds, strm, stage_events(events, 1)) != hipSuccess) return READY_ERR_HIP;
     // the other stages run inside the same kernel: their marks (if any) are
     // recorded together after it

@@ -18,15 +18,16 @@
 //   O  per 32 columns of out: out = h + W2 a + b2 (step 5)
 // S and Z items never wait; an A item waits for every S item and every
 // column block of z; an O item waits for every A item.  Each kind sits in
-// eight queues, one per XCD (S items first, then Z items, in one queue set;
-// item i in queue i % 8), and a workgroup claims from the queues of the XCD
-// it runs on: all its S and Z items, then A items, then O items, claiming
-// the next item of a queue while it works on the current one (the claim's
-// round trip hides behind the item).  Before its first A item it reads the
-// XCDs' arrival flags: an XCD on which no workgroup of the launch has run
-// yet (other kernels hold it, say) is an orphan, and the workgroup drains
-// the orphan's S and Z queue, then after its own A queue the orphan's A
-// queue, and likewise for O.  So every item waits only for items that
+// 64 queues, 8 per XCD (S items first, then Z items, in one queue set; item
+// i in queue i % 64), so that few workgroups share a claim counter.  A
+// workgroup claims from one queue of each kind on the XCD it runs on: all
+// its S and Z items, then A items, then O items, claiming the next item of a
+// queue while it works on the current one (the claim's round trip hides
+// behind the item).  Before its first A item it reads the queues' arrival
+// flags: a queue that no workgroup of the launch has taken from yet (other
+// kernels hold its XCD, say, or the grid is smaller) is an orphan, and the
+// workgroup drains the orphan's S and Z queue, then after its own A queue
+// the orphan's A queue, and likewise for O.  So every item waits only for items that
 // running workgroups hold or take before they wait themselves, and the
 // launch completes whatever part of its grid is resident.  A and O items
 // request their weights before they wait.
@@ -704,13 +705,13 @@ __device__ void f32_o_item(const F32Args& a, int co, float* smem, int* s_flag) {
 // RR: the rank (8 or 16); RB: the rows the item loops are built for (8 or
 // 16, at least R).
 // The items of queue x of one kind, from position k on: thread 0 claims the
-// next position as an item starts; run(i) runs item i = x + 8 k.
+// next position as an item starts; run(i) runs item i = x + NQ k.
 template <typename Run>
 __device__ __forceinline__ void drain(uint32_t* qctr, int x, uint32_t size, uint32_t k, uint32_t* s_bc, Run run) {
   while (k < size) {
     uint32_t nxt = NO_ITEM;
     if (threadIdx.x == 0) nxt = count_up(ctr(qctr, x));
-    run(x + 8 * (int)k);
+    run(x + READY_F32_QUEUES * (int)k);
     __syncthreads();  // the LDS area is reused by the next item
     if (threadIdx.x == 0) *s_bc = nxt;
     __syncthreads();
@@ -728,11 +729,13 @@ __global__ __launch_bounds__(256, 2) void k_reader_f32(F32Args a) {
   __shared__ int s_last;
   const int tid = item_tid();
   const int g = blockIdx.x, G = gridDim.x;
-  const int xcc = hw_xcc();
+  // this workgroup's queues: 8 per XCD, so that few workgroups share a
+  // claim counter
+  const int xq = hw_xcc() + 8 * ((g >> 3) & 7);
   uint32_t first = NO_ITEM;
   if (tid == 0) {
-    first = count_up(ctr(a.lq, xcc));
-    st_coh_u32(ctr(a.arr_x, xcc), 1u);
+    first = count_up(ctr(a.lq, xq));
+    st_coh_u32(ctr(a.arr_x, xq), 1u);
   }
   const int accv = tid < a.B ? a.accept_idx[tid] : 0;
   if (a.counters[0] != a.magic) {
@@ -748,7 +751,7 @@ __global__ __launch_bounds__(256, 2) void k_reader_f32(F32Args a) {
   __syncthreads();
 
   const int nl = a.n_s + a.n_z;
-  auto qsize = [](int total, int x) { return (uint32_t)((total - x + 7) >> 3); };
+  auto qsize = [](int total, int x) { return (uint32_t)((total - x + READY_F32_QUEUES - 1) / READY_F32_QUEUES); };
   auto run_l = [&](int i) {
     if (i < a.n_s) {
       f32_s_item<RR>(a, i, s_acc, smem);
@@ -760,27 +763,27 @@ __global__ __launch_bounds__(256, 2) void k_reader_f32(F32Args a) {
   auto run_a = [&](int i) { f32_a_item<RR, RB>(a, i, smem, &s_flag); };
   auto run_o = [&](int i) { f32_o_item<RB>(a, i, smem, &s_flag); };
 
-  // S and Z items of this XCD's queue
-  drain(a.lq, xcc, qsize(nl, xcc), k0, s_bc, run_l);
+  // S and Z items of this workgroup's queue
+  drain(a.lq, xq, qsize(nl, xq), k0, s_bc, run_l);
   // the arrival flags, read in the trip of the first A claim; then the S and
-  // Z items of orphan XCDs
+  // Z items of orphan queues
   auto flag = [&](int l) { return ctr(a.arr_x, l); };
   uint32_t ka;
-  const uint32_t orph = (uint32_t)arrival_check(ctr(a.aq, xcc), 8, flag, &ka, s_bc);
-  for (uint32_t m = orph; m != 0; m &= m - 1) {
-    const int y = __ffs(m) - 1;
+  const uint64_t orph = arrival_check(ctr(a.aq, xq), READY_F32_QUEUES, flag, &ka, s_bc);
+  for (uint64_t m = orph; m != 0; m &= m - 1) {
+    const int y = __ffsll((unsigned long long)m) - 1;
     drain(a.lq, y, qsize(nl, y), claim_one(a.lq, y, qsize(nl, y), s_bc), s_bc, run_l);
   }
-  // A items: this XCD's queue, then the orphans'
-  drain(a.aq, xcc, qsize(a.n_a, xcc), ka, s_bc, run_a);
-  for (uint32_t m = orph; m != 0; m &= m - 1) {
-    const int y = __ffs(m) - 1;
+  // A items: this workgroup's queue, then the orphans'
+  drain(a.aq, xq, qsize(a.n_a, xq), ka, s_bc, run_a);
+  for (uint64_t m = orph; m != 0; m &= m - 1) {
+    const int y = __ffsll((unsigned long long)m) - 1;
     drain(a.aq, y, qsize(a.n_a, y), claim_one(a.aq, y, qsize(a.n_a, y), s_bc), s_bc, run_a);
   }
   // O items likewise
-  drain(a.oq, xcc, qsize(a.n_o, xcc), claim_one(a.oq, xcc, qsize(a.n_o, xcc), s_bc), s_bc, run_o);
-  for (uint32_t m = orph; m != 0; m &= m - 1) {
-    const int y = __ffs(m) - 1;
+  drain(a.oq, xq, qsize(a.n_o, xq), claim_one(a.oq, xq, qsize(a.n_o, xq), s_bc), s_bc, run_o);
+  for (uint64_t m = orph; m != 0; m &= m - 1) {
+    const int y = __ffsll((unsigned long long)m) - 1;
     drain(a.oq, y, qsize(a.n_o, y), claim_one(a.oq, y, qsize(a.n_o, y), s_bc), s_bc, run_o);
   }
 

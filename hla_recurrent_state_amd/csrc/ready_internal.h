@@ -148,8 +148,8 @@ struct F32Args {
   uint32_t* seq_invalid;           // [B]
   // Counters, READY_CTR_STRIDE words apart: [0] the workspace magic, [1]
   // abort flag, [2 .. 2 + READY_DONE_GROUPS] workgroups finished per group
-  // and overall, then per XCD the claim counters of the S and Z items, of the
-  // A items and of the O items and the arrival flags, then the finished
+  // and overall, then per queue the claim counters of the S and Z items, of
+  // the A items and of the O items and the arrival flags, then the finished
   // column blocks of z, the S items done, the A items done and the Z items
   // done per column block.  The last workgroup to finish clears all of them
   // but the magic.
@@ -158,10 +158,10 @@ struct F32Args {
   uint32_t magic;
   uint32_t* abort_flag;
   uint32_t* done;
-  uint32_t* lq;                    // [8]: S and Z items claimed per XCD queue
-  uint32_t* aq;                    // [8]: A items claimed per XCD queue
-  uint32_t* oq;                    // [8]: O items claimed per XCD queue
-  uint32_t* arr_x;                 // [8]: a workgroup of the launch has run on XCD x
+  uint32_t* lq;                    // [READY_F32_QUEUES]: S and Z items claimed per queue
+  uint32_t* aq;                    // [READY_F32_QUEUES]: A items claimed per queue
+  uint32_t* oq;                    // [READY_F32_QUEUES]: O items claimed per queue
+  uint32_t* arr_x;                 // [READY_F32_QUEUES]: a workgroup of the launch has taken from queue x
   uint32_t* zdone;
   uint32_t* sdone;
   uint32_t* adone;
@@ -173,6 +173,7 @@ struct F32Args {
   int B, P, n, M, H, r, d, F, Hm, R, Nz, shared, act;
   float state_eps, h_eps;
 };
+#define READY_F32_QUEUES 64        // claim queues of each item kind (8 per XCD)
 #define READY_F32_KC 256           // K chunk of a query item (4 waves x 64)
 #define READY_F32_ZC 64            // columns of z per query item (one per lane)
 #define READY_F32_AC 16            // columns of a per A item (4 waves x 4)
