@@ -417,6 +417,19 @@ __device__ __forceinline__ void tile_count(const FastArgs& a, int t, bool u_path
     __hip_atomic_fetch_add(ctr(a.sdone, q), u_path ? 0x10001u : 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// v + the value of lane l ^ 16 (pair_sum16) or l ^ 32 (pair_sum32), on the
+// VALU: v_permlane16_swap / v_permlane32_swap of v with itself leave the
+// partner's value in one result and v in the other, so their sum is the
+// pair's sum in every lane (the same bits as an exchange through LDS).
+__device__ __forceinline__ float pair_sum16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float pair_sum32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // P = V^T (S U^T) * scale for the tile in LDS (sS) and the U, V of one
 // reader in LDS (sU, sV): S U^T on the matrix cores, wave w taking rows
 // [32 w, 32 w + 32); then each lane sums V^T over its eight rows, and the
@@ -471,10 +484,7 @@ __device__ __forceinline__ void tile_project(const u32x4* sS, const uint16_t* sU
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-    for (int i = 0; i < RR; ++i) {
-      part[nb][i] += __shfl_xor(part[nb][i], 16, 64);
-      part[nb][i] += __shfl_xor(part[nb][i], 32, 64);
-    }
+    for (int i = 0; i < RR; ++i) part[nb][i] = pair_sum32(pair_sum16(part[nb][i]));
   if (lane < 16) {
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
