@@ -417,28 +417,15 @@ __device__ __forceinline__ void tile_count(const FastArgs& a, int t, bool u_path
     __hip_atomic_fetch_add(ctr(a.sdone, q), u_path ? 0x10001u : 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// v + the value of lane l ^ 16 (pair_sum16) or l ^ 32 (pair_sum32), on the
-// VALU: v_permlane16_swap / v_permlane32_swap of v with itself leave the
-// partner's value in one result and v in the other, so their sum is the
-// pair's sum in every lane (the same bits as an exchange through LDS).
-__device__ __forceinline__ float pair_sum16(float v) {
-  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-__device__ __forceinline__ float pair_sum32(float v) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
 // P = V^T (S U^T) * scale for the tile in LDS (sS) and the U, V of one
 // reader in LDS (sU, sV): S U^T on the matrix cores, wave w taking rows
-// [32 w, 32 w + 32); then each lane sums V^T over its eight rows, and the
-// four waves' partials meet in s_red.  P is stored device-coherently.
+// [32 w, 32 w + 32); then V^T (S U^T) over those rows on the matrix cores
+// too (S U^T enters as bf16), and the four waves' partials meet in s_red.
+// P is stored device-coherently.
 template <int RR>
 __device__ __forceinline__ void tile_project(const u32x4* sS, const uint16_t* sU, const uint16_t* sV, float* s_red,
                                              float scale, float* P, float* sP = nullptr) {
   constexpr int NB = (RR + 15) / 16;  // 16-column blocks of U^T
-  constexpr int VC = RR / 8;          // 16-byte chunks per V row
   constexpr int LU = READY_TILE + 8;  // padded U row in LDS (bf16)
   constexpr int WS = NB * RR * 16;    // per-wave partials of P
   const int tid = item_tid(), lane = tid & 63, wave = tid >> 6;
@@ -463,38 +450,45 @@ __device__ __forceinline__ void tile_project(const u32x4* sS, const uint16_t* sU
   }
 
   // acc[mb][nb][e] = (S U^T)[v = 32 w + 16 mb + 4 (l / 16) + e][i' = 16 nb + l % 16]
-  float part[NB][RR];
+  // P_w = V_w^T (S U^T)_w on the matrix cores (k = the wave's 32 rows v):
+  // with k taken in the order (mb, e), each lane's accumulators are
+  // already its B operand (rounded to bf16), and its A operand is
+  // V[v][16 mi + l % 16] at its 8 rows v.  The waves' partials, P rows i
+  // and columns i', go to s_red[w][i][i'] (16 NB columns a row).
+  f32x4 pacc[NB][NB];
+  u32x4 bop[NB];
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb)
+  for (int nb = 0; nb < NB; ++nb) {
+    const float w8[8] = {acc[0][nb][0], acc[0][nb][1], acc[0][nb][2], acc[0][nb][3],
+                         acc[1][nb][0], acc[1][nb][1], acc[1][nb][2], acc[1][nb][3]};
+    bop[nb] = pack_bf16x8(w8);
+  }
 #pragma unroll
-    for (int i = 0; i < RR; ++i) part[nb][i] = 0.0f;
+  for (int mi = 0; mi < NB; ++mi) {
+    const int i = 16 * mi + lrow;
+    uint32_t av[8];
 #pragma unroll
-  for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int v = 32 * wave + 16 * mb + 4 * lq + e;
-      float vrow[RR];
-#pragma unroll
-      for (int c = 0; c < VC; ++c) Elem<uint16_t>::unpack(*(const u32x4*)&sV[v * RR + 8 * c], vrow + 8 * c);
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-        for (int i = 0; i < RR; ++i) part[nb][i] += vrow[i] * acc[mb][nb][e];
+    for (int j = 0; j < 8; ++j) {
+      const int v = 32 * wave + 16 * (j >> 2) + 4 * lq + (j & 3);
+      av[j] = i < RR ? (uint32_t)sV[v * RR + i] : 0u;
     }
+    const u32x4 aop = {av[0] | (av[1] << 16), av[2] | (av[3] << 16), av[4] | (av[5] << 16), av[6] | (av[7] << 16)};
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb)
+    for (int nb = 0; nb < NB; ++nb) pacc[mi][nb] = mfma16x16x32(aop, bop[nb], f32x4{0.0f, 0.0f, 0.0f, 0.0f});
+  }
 #pragma unroll
-    for (int i = 0; i < RR; ++i) part[nb][i] = pair_sum32(pair_sum16(part[nb][i]));
-  if (lane < 16) {
+  for (int mi = 0; mi < NB; ++mi)
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-      for (int i = 0; i < RR; ++i) s_red[wave * WS + (nb * RR + i) * 16 + lane] = part[nb][i];
-  }
+      for (int e = 0; e < 4; ++e) {
+        const int i = 16 * mi + 4 * lq + e;
+        if (i < RR) s_red[wave * WS + i * 16 * NB + 16 * nb + lrow] = pacc[mi][nb][e];
+      }
   __syncthreads();
   for (int e = tid; e < RR * RR; e += 256) {
     const int i = e / RR, ip = e - (e / RR) * RR;
-    const int idx = ((ip >> 4) * RR + i) * 16 + (ip & 15);
+    const int idx = i * 16 * NB + ip;
     const float pv = ((s_red[idx] + s_red[WS + idx]) + (s_red[2 * WS + idx] + s_red[3 * WS + idx])) * scale;
     st_coh_f32(P + e, pv);
     if (sP) sP[e] = pv;
