@@ -978,8 +978,89 @@ __device__ __forceinline__ void mlp1_item(const FastArgs& a, int item, unsigned 
       }
     }
   };
-  if (want_feat) f_loop(std::true_type{});
-  else f_loop(std::false_type{});
+  // The same sums when the block's rows belong to at most PS sequences (one
+  // P load group): every row of the block in one pass, z of RG rows read
+  // from LDS first, then the rows' dot products, then their stores, so a
+  // thread waits for LDS once per RG rows rather than once per row.  Row rr
+  // takes the P rows of its sequence (index s within the block) by selects
+  // over the NS candidates.
+  auto f_rows = [&](auto feat_tag, auto ns_tag) {
+    constexpr bool FEAT = decltype(feat_tag)::value;
+    constexpr int NS = decltype(ns_tag)::value;
+    constexpr int RG = RR <= 8 ? 4 : (RR <= 16 ? 2 : 1);
+    for (int e0 = tid; e0 < nmi; e0 += 256) {
+      const int m = e0 / RR, i = e0 - (e0 / RR) * RR;
+      const int mz = a.shared ? 0 : m;
+      const int fcol = m * (RR + 1) + i;
+      if constexpr (PRE2) {
+        if (e0 == tid + 256) {
+#pragma unroll
+          for (int s = 0; s < PS; ++s) {
+#pragma unroll
+            for (int c = 0; c < CR4; ++c) pv[s][c] = pv2[s][c];
+          }
+        } else if (e0 != tid) {
+          load_p(e0, 0);
+        }
+      } else if (e0 != tid) {
+        load_p(e0, 0);
+      }
+      // sequence index of the current row, and the first row of the next
+      int sq = 0, bnd = (b0 + 1) * a.n - row0;
+#pragma unroll
+      for (int g0 = 0; g0 < READY_ABM; g0 += RG) {
+        float4 zr[RG][CR4];
+        float rs[RG], u[RG];
+#pragma unroll
+        for (int q = 0; q < RG; ++q) {
+#pragma unroll
+          for (int c = 0; c < CR4; ++c) zr[q][c] = *(const float4*)&z_s[(g0 + q) * Nz + mz * RR + 4 * c];
+          rs[q] = s_rs[g0 + q];
+        }
+#pragma unroll
+        for (int q = 0; q < RG; ++q) {
+          const bool next = g0 + q >= bnd;
+          sq += next ? 1 : 0;
+          bnd += next ? a.n : 0;
+          float acc = 0.0f;
+#pragma unroll
+          for (int c = 0; c < CR4; ++c) {
+            u32x4 pw = pv[0][c];
+#pragma unroll
+            for (int k = 1; k < NS; ++k) pw = sq == k ? pv[k][c] : pw;
+            const float4 pq = make_float4(__uint_as_float(pw.x), __uint_as_float(pw.y), __uint_as_float(pw.z),
+                                          __uint_as_float(pw.w));
+            const float4 zq = zr[q][c];
+            if constexpr (RR >= READY_UPATH_MIN_R) {
+              acc = dot4_acc(acc, pq, zq);
+            } else {
+              acc += pq.x * zq.x + pq.y * zq.y + pq.z * zq.z + pq.w * zq.w;
+            }
+          }
+          u[q] = __fmul_rn(acc, rs[q]);
+        }
+#pragma unroll
+        for (int q = 0; q < RG; ++q) {
+          if (g0 + q < rows) {
+            fsh[(g0 + q) * Fs + fcol] = f32_to_bf16_rne(u[q]);
+            if constexpr (FEAT) feat0[(g0 + q) * F + fcol] = u[q];
+          }
+        }
+      }
+    }
+  };
+  using two = std::integral_constant<int, 2>;
+  using all = std::integral_constant<int, PS>;
+  if (nseq <= 2) {
+    if (want_feat) f_rows(std::true_type{}, two{});
+    else f_rows(std::false_type{}, two{});
+  } else if (nseq <= PS) {
+    if (want_feat) f_rows(std::true_type{}, all{});
+    else f_rows(std::false_type{}, all{});
+  } else {
+    if (want_feat) f_loop(std::true_type{});
+    else f_loop(std::false_type{});
+  }
   __syncthreads();
   }
 
