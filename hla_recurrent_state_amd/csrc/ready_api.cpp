@@ -668,6 +668,8 @@ readyStatus ready_run_reader(const readyPlan* plan, const readyStates* states, c
     g.R = (int)R; g.N = (int)d; g.K = (int)Hm; g.kchunk = (int)Hm;
     g.vec_ok = (Hm % wvw == 0);
     g.bias = w->b2; g.h = h; g.out = o->out; g.delta = o->delta; g.seq_invalid = flags; g.n = s.n;
+    auto a16 = [](const void* q) { return ((uintptr_t)q & 15u) == 0u; };
+    g.epi_vec = (d % 8 == 0 && a16(h) && a16(o->out) && a16(o->delta)) ? 1 : 0;
     hipError_t e;
     const StageEvents ev = stage_events(events, 3);
     if (plan->g2.big) {

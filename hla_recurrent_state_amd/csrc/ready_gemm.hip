@@ -305,8 +305,10 @@ __global__ __launch_bounds__(256) void k_gemm_mfma(GemmArgs g) {
 // and ldw to keep 16-byte row chunks aligned.
 constexpr int GM_BM = READY_GM_TILE, GM_BN = READY_GM_TILE;
 
+// Residual epilogue staging: per wave, 16 rows x 64 columns of fp32 dh
+constexpr int GM_ELD = 68;
 template <typename TX, typename TO, int EPI, int GM_BK>
-__device__ __forceinline__ void gemm_mm_body(const GemmArgs& g, uint16_t* sX, uint16_t* sW) {
+__device__ __forceinline__ void gemm_mm_body(const GemmArgs& g, uint16_t* sX, uint16_t* sW, float* sE) {
   constexpr int GM_LD = GM_BK + 8;                 // padded LDS row
   constexpr bool XBF = sizeof(TX) == 2;
   constexpr int CPR = GM_BK / 8;                   // 16-byte bf16 chunks per row and step
@@ -319,11 +321,16 @@ __device__ __forceinline__ void gemm_mm_body(const GemmArgs& g, uint16_t* sX, ui
   // blockIdx.x runs over the output tiles, padded to a multiple of 8: the
   // tiles are numbered column-major (row tiles inner) and each XCD takes a
   // contiguous run of them, so the workgroups on one XCD share a few column
-  // panels of W and the row panels of X in its L2
+  // panels of W and the row panels of X in its L2.  With at most four column
+  // tiles (a narrow output, X the larger operand) they are numbered row-major
+  // instead, so the column tiles of one X row panel run on one XCD and the
+  // panel is read from HBM once.
   const int q = xcd_remap(blockIdx.x, gridDim.x, g.tiles_c * g.tiles_r);
   if (q < 0) return;
-  const int tc = q / g.tiles_r;
-  const int col0 = tc * GM_BN, ks = blockIdx.y, row0 = (q - tc * g.tiles_r) * GM_BM;
+  const bool rmaj = g.tiles_c <= 4;
+  const int tc = rmaj ? q % g.tiles_c : q / g.tiles_r;
+  const int tr = rmaj ? q / g.tiles_c : q - tc * g.tiles_r;
+  const int col0 = tc * GM_BN, ks = blockIdx.y, row0 = tr * GM_BM;
   const int kbeg = ks * g.kchunk;
   const int kend = min(g.K, kbeg + g.kchunk);
   const int nsteps = kend > kbeg ? (kend - kbeg + GM_BK - 1) / GM_BK : 0;
@@ -448,6 +455,58 @@ __device__ __forceinline__ void gemm_mm_body(const GemmArgs& g, uint16_t* sX, ui
     const int col = col0 + 64 * wc + 16 * j + lr;
     bias[j] = (EPI != EPI_PARTIAL && g.bias != nullptr && col < g.N) ? Elem<uint16_t>::ld(g.bias, col) : 0.0f;
   }
+  if constexpr (EPI == EPI_RESID) {
+    if (g.epi_vec) {
+      // out = h + dh in 16-byte pieces: each 16-row block of the wave's
+      // 64 x 64 goes through LDS (fp32), then a lane takes 8 consecutive
+      // columns of a row at a time (two pieces per lane and block), so h
+      // and out move in whole 16-byte chunks.  Same arithmetic as below.
+      float* E = sE + wave * 16 * GM_ELD;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) E[(4 * lg + e) * GM_ELD + 16 * j + lr] = acc[i][j][e] + bias[j];
+        __syncthreads();
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          const int c = lane + 64 * q;
+          const int rr = c >> 3, c8 = (c & 7) * 8;
+          const int64_t rho = row0 + 64 * wr + 16 * i + rr;
+          const int col = col0 + 64 * wc + c8;
+          if (rho < g.R && col < g.N && !g.seq_invalid[rho / g.n]) {
+            float dh[8];
+            *(float4*)&dh[0] = *(const float4*)&E[rr * GM_ELD + c8];
+            *(float4*)&dh[4] = *(const float4*)&E[rr * GM_ELD + c8 + 4];
+            const int64_t o = rho * g.N + col;
+            float hv[8];
+            if constexpr (sizeof(TO) == 2) {
+              Elem<uint16_t>::unpack(*(const u32x4*)((const uint16_t*)g.h + o), hv);
+            } else {
+              *(float4*)&hv[0] = *(const float4*)((const float*)g.h + o);
+              *(float4*)&hv[4] = *(const float4*)((const float*)g.h + o + 4);
+            }
+            float ov[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) ov[e] = hv[e] + dh[e];
+            if constexpr (sizeof(TO) == 2) {
+              *(u32x4*)((uint16_t*)g.out + o) = pack_bf16x8(ov);
+            } else {
+              *(float4*)((float*)g.out + o) = *(const float4*)&ov[0];
+              *(float4*)((float*)g.out + o + 4) = *(const float4*)&ov[4];
+            }
+            if (g.delta) {
+              *(float4*)(g.delta + o) = *(const float4*)&dh[0];
+              *(float4*)(g.delta + o + 4) = *(const float4*)&dh[4];
+            }
+          }
+        }
+        __syncthreads();
+      }
+      return;
+    }
+  }
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -474,19 +533,25 @@ __device__ __forceinline__ void gemm_mm_body(const GemmArgs& g, uint16_t* sX, ui
     }
 }
 
-// bf16 X: K steps of 64; fp32 X (twice the staging registers per K): steps of
-// 32.  Both keep three workgroups on a CU.
+// bf16 X: K steps of 64, three workgroups on a CU.  fp32 X (twice the
+// staging registers per K): steps of 64 as well where the launch has few
+// workgroups (the first MLP layer's K split: about one per CU, so the fewer,
+// longer steps matter more than a third workgroup); the residual form, with
+// a workgroup per output tile, keeps steps of 32 and three on a CU.
 template <typename TO, int EPI>
 __global__ __launch_bounds__(256, 3) void k_gemm_mm_bx(GemmArgs g) {
   __shared__ __attribute__((aligned(16))) uint16_t sX[GM_BM * (64 + 8)];
   __shared__ __attribute__((aligned(16))) uint16_t sW[GM_BN * (64 + 8)];
-  gemm_mm_body<uint16_t, TO, EPI, 64>(g, sX, sW);
+  __shared__ __attribute__((aligned(16))) float sE[EPI == EPI_RESID ? 4 * 16 * GM_ELD : 4];
+  gemm_mm_body<uint16_t, TO, EPI, 64>(g, sX, sW, sE);
 }
 template <typename TO, int EPI>
-__global__ __launch_bounds__(256, 3) void k_gemm_mm_fx(GemmArgs g) {
-  __shared__ __attribute__((aligned(16))) uint16_t sX[GM_BM * (32 + 8)];
-  __shared__ __attribute__((aligned(16))) uint16_t sW[GM_BN * (32 + 8)];
-  gemm_mm_body<float, TO, EPI, 32>(g, sX, sW);
+__global__ __launch_bounds__(256, EPI == EPI_RESID ? 3 : 2) void k_gemm_mm_fx(GemmArgs g) {
+  constexpr int BK = EPI == EPI_RESID ? 32 : 64;
+  __shared__ __attribute__((aligned(16))) uint16_t sX[GM_BM * (BK + 8)];
+  __shared__ __attribute__((aligned(16))) uint16_t sW[GM_BN * (BK + 8)];
+  __shared__ __attribute__((aligned(16))) float sE[EPI == EPI_RESID ? 4 * 16 * GM_ELD : 4];
+  gemm_mm_body<float, TO, EPI, BK>(g, sX, sW, sE);
 }
 
 // a = act(sum over K splits of the partial sums + bias), one thread per value

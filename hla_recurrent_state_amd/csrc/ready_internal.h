@@ -281,6 +281,7 @@ struct GemmArgs {
   float* delta;                    // [R][N] or null
   const int32_t* seq_invalid;      // [R / n]
   int n;
+  int epi_vec;                     // k_gemm_mm residual: N % 8 == 0 and h, out, delta 16-byte aligned
   int tiles_c, tiles_r;            // k_gemm_mm: column and row tiles (set by its launcher)
   int wave_k;                      // k_gemm: 4 columns per workgroup, K split over its waves
 };

@@ -99,6 +99,40 @@ def test_rank_ablation_sampled():
     assert np.array_equal(res["gathered"], want)
 
 
+def test_large_row_count_residual_epilogue():
+    """B = 256 (1792 rows), d = 2560, r = 64: the second MLP layer runs on
+    the 128 x 128 matrix-core GEMM with its 16-byte residual epilogue.  In
+    place (out is h), then with two out-of-range accept indices: those
+    sequences' out rows stay untouched, the sampled others match the oracle."""
+    cfg = make_shape("paper", B=256, H=1, t=8, r=64, d=2560, Hm=64)
+    inp = synth.make(cfg, seed=71)
+    _check(inp, seqs=[0, 1, 130, 255], inplace=True)
+    dev = _dev()
+    bad = synth.make(cfg, seed=71)
+    bad.accept_idx = bad.accept_idx.copy()
+    bad.accept_idx[[5, 200]] = cfg.P
+    import tests.gpu_util as gu
+    d = synth.device.to_device(bad, dev)
+    from hla_recurrent_state_amd import StateReader, READY_ERR_ACCEPT_IDX
+    reader = StateReader(gu.reader_shape(cfg), cfg.slots)
+    o = gu.alloc_outputs(cfg, dev)
+    sentinel_bits = 0x7FC1
+    o["out"].view(torch.int16).fill_(sentinel_bits)
+    reader(d["states"], d["accept_idx"], d["h"], d["weights"], o["gathered"], o["out"],
+           logrms=o["logrms"], delta=o["delta"], feat=o["feat"], dev_status=o["dev_status"])
+    torch.cuda.synchronize()
+    reader.close()
+    assert int(o["dev_status"].item()) == READY_ERR_ACCEPT_IDX
+    out = o["out"].view(torch.int16).cpu().numpy()
+    assert np.all(out[[5, 200]] == sentinel_bits)
+    from tests.gpu_util import compare, oracle_reference
+    res = {"gathered": o["gathered"].view(torch.int16).cpu().numpy().view(np.uint16),
+           "out": out.view(np.uint16), "logrms": o["logrms"].cpu().numpy(),
+           "delta": o["delta"].cpu().numpy(), "feat": o["feat"].cpu().numpy(), "dev_status": 0}
+    rep = compare(bad, res, oracle_reference(bad, [0, 4, 6, 199, 201, 255]))
+    assert rep["ok"], rep
+
+
 # ------------------------------------------------------------ multi-tile cases with ragged tails
 
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
