@@ -84,7 +84,7 @@ __device__ bool f32_wait(const F32Args& a, const uint32_t* c1, uint32_t w1, cons
                          int* s_flag) {
   if (threadIdx.x == 0) {
     uint32_t last;
-    *s_flag = wait_count2(c1, w1, c2, 0xffffffffu, w2, &last, a.abort_flag, a.dev_status) ? 1 : 0;
+    *s_flag = wait_count2<true>(c1, w1, c2, 0xffffffffu, w2, &last, a.abort_flag, a.dev_status) ? 1 : 0;
   }
   __syncthreads();
   const bool ok = *s_flag != 0;
