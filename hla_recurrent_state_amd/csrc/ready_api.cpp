@@ -151,7 +151,7 @@ readyStatus readyPlanCreate(const readyShape* shape, const int32_t* layer_ids, r
     const int64_t bmo = p->small ? 16 : std::min(READY_BMO_LARGE, READY_BMO_APPLY);
     const int64_t rows = std::max(p->R, 1);
     const int64_t zq = cdiv(fks, 8) * cdiv(rows, bmz) * cdiv(p->Nz, 64) + cdiv((int64_t)s.B * p->M, 8);
-    const int64_t oq = cdiv(rows, bmo) * cdiv(cdiv(s.d, READY_OCOLS), 8);
+    const int64_t oq = cdiv(rows, bmo) * cdiv(cdiv(s.d, p->small ? READY_OCOLS_SMALL : READY_OCOLS), 8);
     if (zq >= (1 << 24) || oq >= (1 << 24)) fits = false;
   }
   p->lds = fits ? ready_reader_lds(s.r, p->F, p->Nz, p->small) : 0;
@@ -186,7 +186,7 @@ readyStatus readyPlanCreate(const readyShape* shape, const int32_t* layer_ids, r
     // each per-XCD queue holds fewer than 2^24 items (checked above)
     p->n_s = s.B * p->M;
     p->n_a = (int)(nrba * cdiv(s.Hm, 64));
-    p->n_o = (int)(nrbo * cdiv(s.d, READY_OCOLS));
+    p->n_o = (int)(nrbo * cdiv(s.d, p->small ? READY_OCOLS_SMALL : READY_OCOLS));
     // counter slots: magic, abort, READY_DONE_GROUPS + 1 done counts, then
     // per tile of z, per row block of z, per 16 rows, per row block of out
     p->c_zcnt = 2 + READY_DONE_GROUPS + 1;

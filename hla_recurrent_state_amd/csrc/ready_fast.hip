@@ -1108,15 +1108,17 @@ __device__ __forceinline__ void mlp1_item(const FastArgs& a, int item, unsigned 
 // ---------------------------------------------------------------- O items
 
 // Rows [BM rb, BM rb + BM) and columns [OC cb, OC cb + OC) of out (OC =
-// READY_OCOLS); wave w computes columns OC cb + (OC / 4) w .. + OC / 4 - 1,
+// READY_OCOLS, READY_OCOLS_SMALL at most 16 rows); wave w computes columns
+// OC cb + (OC / 4) w .. + OC / 4 - 1,
 // 16 at a time.  The W2 rows of the lane's columns, the tile's h values and
 // the b2 chunk are loaded before waiting; after the A items of the rows are
 // counted, the a rows are staged in LDS by passes of 256 values of K
 // (device-coherent loads) for the matrix instructions.  The epilogue goes
 // through LDS so that h, out and delta move in 16-byte row chunks.
-template <int BM>
+template <int BM, int OC>
 __device__ __forceinline__ void mlp2_item(const FastArgs& a, int rb, int cb, unsigned char* smem) {
-  constexpr int OC = READY_OCOLS, KT = 256, LA = KT + 8, LO = OC + 4;
+  static_assert(OC <= READY_OCOLS, "the LDS area is sized for READY_OCOLS columns");
+  constexpr int KT = 256, LA = KT + 8, LO = OC + 4;
   constexpr int WCOL = OC / 4, H2 = WCOL / 16;  // columns per wave, 16-column blocks per wave
   static_assert(WCOL % 16 == 0, "whole 16-column blocks per wave");
   constexpr int SA = BM * LA * 2, SO = BM * LO * 4;
@@ -1339,7 +1341,8 @@ __global__ __launch_bounds__(256, (MODE == READY_MODE_PREPARE && RR <= 16) ? 3 :
 
   // queue sizes
   const int ztiles = cdiv_d(a.R, BMZ) * cdiv_d(a.Nz, 64);
-  const int ncb = cdiv_d(a.d, READY_OCOLS), nrbo = cdiv_d(a.R, BMO);
+  constexpr int OCK = SMALL ? READY_OCOLS_SMALL : READY_OCOLS;
+  const int ncb = cdiv_d(a.d, OCK), nrbo = cdiv_d(a.R, BMO);
   auto z_size = [&](int x) { return zao ? (uint32_t)(((a.ksplit - x + 7) >> 3) * ztiles) : 0u; };
   auto a_size = [&](int x) { return (uint32_t)((a.n_a - x + 7) >> 3); };
   auto o_size = [&](int x) { return (uint32_t)(nrbo * ((ncb - x + 7) >> 3)); };
@@ -1411,7 +1414,7 @@ __global__ __launch_bounds__(256, (MODE == READY_MODE_PREPARE && RR <= 16) ? 3 :
         continue;
       }
       const int ncx = (ncb - (int)x + 7) >> 3;  // column blocks of queue x
-      mlp2_item<BMO>(a, (int)i / ncx, (int)x + 8 * ((int)i % ncx), smem);
+      mlp2_item<BMO, OCK>(a, (int)i / ncx, (int)x + 8 * ((int)i % ncx), smem);
       i = claim_one(a.oq, (int)x, no, s_tk);
     }
   } else {

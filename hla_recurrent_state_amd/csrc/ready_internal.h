@@ -220,6 +220,11 @@ inline size_t ready_f32_lds(int r, int R, int Nz, int F, int Hm) {
 #define READY_ZCHUNK_SMALL 384
 #define READY_ZCHUNK_LARGE 640
 #define READY_OCOLS 128
+// columns of out per O item at most 16 rows (more, shorter items where the
+// O items follow a short chain)
+#ifndef READY_OCOLS_SMALL
+#define READY_OCOLS_SMALL 64
+#endif
 #define READY_ABM 8                // rows of an A item (and of a state-tile count)
 #ifndef READY_UPATH_MIN_R
 #define READY_UPATH_MIN_R 24        // the state tiles form f themselves from this rank on
