@@ -42,7 +42,9 @@ sys.path.insert(0, ROOT)
 
 METRIC = "state-reader µs per 7-token draft block (B=1); committed-state GB/s at B=64"
 HBM_PEAK_GBS = 8000.0
-KERNEL_SRC = os.path.join(ROOT, "hla_recurrent_state_amd", "csrc", "ready_fast.hip")
+# the sources k_reader is compiled from: the kernel and the headers it includes
+KERNEL_SRC = [os.path.join(ROOT, "hla_recurrent_state_amd", "csrc", f)
+              for f in ("ready_fast.hip", "ready_sync.h", "ready_common.h", "ready_internal.h")]
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "k_reader_batched_pmc.md")
 
 
@@ -119,8 +121,11 @@ def reader_kernel_bytes(cfg):
 
 
 def kernel_src_hash():
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for path in KERNEL_SRC:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def read_traffic():

@@ -76,7 +76,7 @@ __device__ __forceinline__ uint32_t count_up(uint32_t* c) {
 __device__ __forceinline__ uint32_t* ctr(uint32_t* base, int i) { return base + READY_CTR_STRIDE * i; }
 
 // Poll *c until it reaches `want`, backing off from about 100 ns to about
-// 0.4 us between polls so that waiting workgroups do not flood the memory
+// 0.2 us between polls so that waiting workgroups do not flood the memory
 // channel that holds the counter.  Bounded:
 // after about a second, or as soon as another workgroup has given up, it
 // raises the abort flag, reports READY_ERR_SYNC_TIMEOUT and returns false.
@@ -94,7 +94,7 @@ __device__ bool wait_count(const uint32_t* c, uint32_t want, uint32_t* abort_fla
     switch (nap) {  // s_sleep takes an immediate operand
       case 0: __builtin_amdgcn_s_sleep(4); break;
       case 1: __builtin_amdgcn_s_sleep(8); break;
-      default: __builtin_amdgcn_s_sleep(16); break;
+      default: __builtin_amdgcn_s_sleep(8); break;
     }
     if (nap < 2) ++nap;
   }
@@ -125,7 +125,7 @@ __device__ bool wait_count2(const uint32_t* c1, uint32_t w1, const uint32_t* c2,
       switch (nap) {
         case 0: __builtin_amdgcn_s_sleep(4); break;
         case 1: __builtin_amdgcn_s_sleep(8); break;
-        default: __builtin_amdgcn_s_sleep(16); break;
+        default: __builtin_amdgcn_s_sleep(8); break;
       }
       if (nap < 2) ++nap;
     }
